@@ -1,0 +1,298 @@
+"""Pins for the float64 CPU oracle (CPU only).
+
+Each test ties the oracle to something other than itself: numpy's IEEE
+conversions, exhaustive enumeration, exact rational arithmetic
+(``fractions.Fraction``), ``numpy.matmul`` on weights that lie exactly on the
+quantization grid, a hand-worked example (tests/golden/hand_example.json),
+and the special cases and invariants of the layer definition in SPEAR
+(gist.science technical summary, section 2.1A; per-channel RTN baseline from
+section 3.1).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+from w4_gemm_error_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f16bits(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float16)).view(np.uint16)
+
+
+def pack_canonical(q):
+    """codes uint8 [N, K] -> canonical uint8 [N, K/2] (even k in the low nibble)."""
+    q = np.asarray(q, dtype=np.uint8)
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def on_grid_layer(rng, N, K, G):
+    """Random codes (every group holds a 0 and a 15), integer zeros and fp16 scales;
+    returns codes, scale/zero bits and the exact weights (q - z) * s."""
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    ng = K // G
+    for n in range(N):
+        for gi in range(ng):
+            pos = rng.choice(G, size=2, replace=False) + gi * G
+            q[n, pos[0]] = 0
+            q[n, pos[1]] = 15
+    z = rng.integers(0, 16, size=(N, ng)).astype(np.float64)
+    s = np.exp2(rng.uniform(-9, -4, size=(N, ng))).astype(np.float16).astype(np.float64)
+    W = (q.astype(np.float64) - np.repeat(z, G, 1)) * np.repeat(s, G, 1)
+    return q, f16bits(s), f16bits(z), W
+
+
+# ---------------------------------------------------------------- formats
+
+def test_half_to_double_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle.half_to_double(b) for b in bits[::7]])
+    r = ref[::7]
+    same = (got == r) | (np.isnan(got) & np.isnan(r))
+    assert same.all()
+
+
+def test_double_to_half_matches_numpy_rounding():
+    rng = np.random.default_rng(1)
+    xs = list(rng.standard_normal(3000) * np.exp2(rng.uniform(-30, 17, 3000)))
+    # exact halfway points between neighbouring halves, subnormals, overflow edge
+    h = np.arange(0, 0x7bff, 97, dtype=np.uint16).view(np.float16).astype(np.float64)
+    h1 = (np.arange(0, 0x7bff, 97, dtype=np.uint16) + 1).view(np.float16).astype(np.float64)
+    xs += list((h + h1) / 2) + list(-(h + h1) / 2)
+    xs += [0.0, -0.0, 2.0 ** -25, 3 * 2.0 ** -26, 65504.0, 65519.99, 65520.0, 1e6, -1e6]
+    for x in xs:
+        with np.errstate(over="ignore"):
+            want = int(np.array(x, dtype=np.float64).astype(np.float16).view(np.uint16))
+        assert oracle.double_to_half(x) == want, x
+
+
+def test_bf16_widening():
+    for b in [0x0000, 0x3F80, 0xC000, 0x4170, 0x0001, 0x7F7F]:
+        want = np.array([b << 16], np.uint32).view(np.float32)[0]
+        assert oracle.bf16_to_double(b) == float(want)
+
+
+# ---------------------------------------------------------------- codes
+
+def test_unpack_exhaustive_bytes():
+    N, K = 1, 512
+    qc = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    q = oracle.unpack_codes(qc, N, K)
+    for b in range(256):
+        assert q[0, 2 * b] == (b & 15) and q[0, 2 * b + 1] == (b >> 4)
+
+
+# ---------------------------------------------------------------- RTN
+
+@pytest.mark.parametrize("G", [64, 128, 256])
+def test_rtn_grid_identity(G):
+    rng = np.random.default_rng(2)
+    N, K = 12, 256
+    q, s, z, W = on_grid_layer(rng, N, K, G)
+    W32 = W.astype(np.float32)
+    assert np.array_equal(W32.astype(np.float64), W)  # the grid is exact in float32
+    qc, s2, z2 = oracle.rtn_quantize(W32, G)
+    assert np.array_equal(oracle.unpack_codes(qc, N, K), q)
+    assert np.array_equal(s2, s) and np.array_equal(z2, z)
+
+
+def test_rtn_brute_force_exact():
+    rng = np.random.default_rng(3)
+    N, K, G = 6, 64, 32
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[2, 5:9] = 0.0
+    qc, s, z = oracle.rtn_quantize(W, G)
+    q = oracle.unpack_codes(qc, N, K)
+    sv = s.view(np.float16).astype(np.float64)
+    zv = z.view(np.float16).astype(np.float64)
+    for n in range(N):
+        for gi in range(K // G):
+            w = W[n, gi * G:(gi + 1) * G].astype(np.float64)
+            lo, hi = min(w.min(), 0.0), max(w.max(), 0.0)
+            assert sv[n, gi] == float(np.float16((hi - lo) / 15.0))
+            assert zv[n, gi] == float(np.clip(np.rint(-lo / sv[n, gi]), 0, 15))
+            S, Z = Fraction(sv[n, gi]), Fraction(zv[n, gi])
+            for k in range(G):
+                wk = Fraction(float(w[k]))
+                errs = [abs(wk - (c - Z) * S) for c in range(16)]
+                assert errs[q[n, gi * G + k]] == min(errs)
+
+
+def test_rtn_degenerate_group():
+    W = np.zeros((2, 64), np.float32)
+    W[1, :32] = 0.01
+    qc, s, z = oracle.rtn_quantize(W, 32)
+    q = oracle.unpack_codes(qc, 2, 64)
+    assert (q[0] == 0).all() and (s[0] == 0x3C00).all() and (z[0] == 0).all()
+    assert (q[1, 32:] == 0).all() and s[1, 1] == 0x3C00
+    # a one-sided group: range [0, 0.01] -> z = 0, max code 15
+    assert z[1, 0] == 0 and q[1, :32].max() == 15
+
+
+# ---------------------------------------------------------------- forward
+
+def run(M, N, K, r, G, X, qc, s, z, A, B, wg, bg, act="fp16", rows=None):
+    return oracle.forward(X, qc, s, z, A, B, wg, bg, N=N, K=K, r=r, group_size=G,
+                          act=act, rows=rows)
+
+
+def test_hand_worked_example():
+    d = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    M, K, N, r, G = d["M"], d["K"], d["N"], d["r"], d["group_size"]
+    qc = pack_canonical(np.array(d["codes"]))
+    assert np.array_equal(qc, np.array(d["canonical_bytes"], np.uint8))
+    out = run(M, N, K, r, G, f16bits(d["X"]), qc, f16bits(d["scale"]), f16bits(d["zero"]),
+              f16bits(d["A"]), f16bits(d["B"]), f16bits(d["w_g"]), d["b_g"])
+    e = d["expected"]
+    for key in ("Y0", "T", "C", "g", "Y"):
+        assert np.array_equal(out[key], np.array(e[key], np.float64)), key
+
+
+@pytest.mark.parametrize("act", ["fp16", "bf16"])
+def test_tiny_exact_rational(act):
+    rng = np.random.default_rng(4)
+    M, N, K, r, G = 3, 5, 8, 2, 4
+    q, s, z, _ = on_grid_layer(rng, N, K, G)
+    Xb = synth.to_act_bits(rng.standard_normal((M, K)) * 3, act)
+    Ab = synth.to_act_bits(rng.standard_normal((K, r)) * 0.1, act)
+    Bb = synth.to_act_bits(rng.standard_normal((r, N)) * 0.1, act)
+    wgb = synth.to_act_bits(rng.standard_normal(K) * 0.2, act)
+    bg = 0.3
+    out = run(M, N, K, r, G, Xb, pack_canonical(q), s, z, Ab, Bb, wgb, bg, act=act)
+    F = lambda a: [[Fraction(float(v)) for v in row] for row in np.atleast_2d(a)]
+    X = F(synth.act_bits_to_f64(Xb, act))
+    A = F(synth.act_bits_to_f64(Ab, act))
+    B = F(synth.act_bits_to_f64(Bb, act))
+    wg = [Fraction(float(v)) for v in synth.act_bits_to_f64(wgb, act)]
+    sv = F(s.view(np.float16).astype(np.float64))
+    zv = F(z.view(np.float16).astype(np.float64))
+    for m in range(M):
+        T = [sum(X[m][k] * A[k][j] for k in range(K)) for j in range(r)]
+        lg = sum(X[m][k] * wg[k] for k in range(K)) + Fraction(bg)
+        g = float(expit(float(lg)))
+        assert out["g"][m] == pytest.approx(g, rel=1e-15, abs=0)
+        for j in range(r):
+            assert out["T"][m, j] == pytest.approx(float(T[j]), rel=1e-13, abs=1e-300)
+        for n in range(N):
+            y0 = sum(X[m][k] * (int(q[n, k]) - zv[n][k // G]) * sv[n][k // G] for k in range(K))
+            c = sum(T[j] * B[j][n] for j in range(r))
+            y = float(y0) + g * float(c)
+            assert out["Y0"][m, n] == pytest.approx(float(y0), rel=1e-13, abs=1e-300)
+            assert out["C"][m, n] == pytest.approx(float(c), rel=1e-13, abs=1e-300)
+            assert out["Y"][m, n] == pytest.approx(y, rel=1e-12, abs=1e-12)
+
+
+@pytest.mark.parametrize("G", [128, 512])
+def test_on_grid_weights_reproduce_matmul(G):
+    rng = np.random.default_rng(5)
+    M, N, K = 7, 48, 512
+    q, s, z, W = on_grid_layer(rng, N, K, G)
+    Xb = f16bits(rng.standard_normal((M, K)))
+    out = run(M, N, K, 0, G, Xb, pack_canonical(q), s, z, None, None, None, 0.0)
+    ref = np.matmul(Xb.view(np.float16).astype(np.float64), W.T)
+    np.testing.assert_allclose(out["Y0"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    assert np.array_equal(out["Y"], out["Y0"])
+
+
+def cfg1_inputs(seed=0, M=16):
+    d = synth.make_layer(1, M, seed)
+    qc, s, z = oracle.rtn_quantize(d["W"], d["group_size"])
+    return d, qc, s, z
+
+
+def test_special_cases_reduce_to_plain_w4():
+    d, qc, s, z = cfg1_inputs()
+    M, N, K, r, G = d["M"], d["N"], d["K"], d["r"], d["group_size"]
+    base = run(M, N, K, 0, G, d["X"], qc, s, z, None, None, None, 0.0)
+    full = run(M, N, K, r, G, d["X"], qc, s, z, d["A"], d["B"], d["w_g"], d["b_g"])
+    assert np.array_equal(full["Y0"], base["Y"])                     # r = 0 is the plain W4 layer
+    off = run(M, N, K, r, G, d["X"], qc, s, z, d["A"], d["B"], d["w_g"], -math.inf)
+    assert np.array_equal(off["Y"], base["Y"]) and (off["g"] == 0).all()   # gate closed
+    zA = run(M, N, K, r, G, d["X"], qc, s, z, np.zeros_like(d["A"]), d["B"], d["w_g"], 0.0)
+    zB = run(M, N, K, r, G, d["X"], qc, s, z, d["A"], np.zeros_like(d["B"]), d["w_g"], 0.0)
+    assert np.array_equal(zA["Y"], base["Y"]) and np.array_equal(zB["Y"], base["Y"])
+
+
+def test_open_gate_is_static_low_rank_compensation():
+    rng = np.random.default_rng(6)
+    M, N, K, r, G = 9, 40, 256, 8, 128
+    q, s, z, W = on_grid_layer(rng, N, K, G)
+    Xb = f16bits(rng.standard_normal((M, K)))
+    Ab = f16bits(rng.standard_normal((K, r)) * 0.05)
+    Bb = f16bits(rng.standard_normal((r, N)) * 0.05)
+    out = run(M, N, K, r, G, Xb, pack_canonical(q), s, z, Ab, Bb, None, math.inf)
+    assert (out["g"] == 1.0).all()
+    X = Xb.view(np.float16).astype(np.float64)
+    A = Ab.view(np.float16).astype(np.float64)
+    B = Bb.view(np.float16).astype(np.float64)
+    ref = np.matmul(X, W.T + np.matmul(A, B))
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
+
+
+def test_gate_and_low_rank_against_numpy():
+    d, qc, s, z = cfg1_inputs()
+    M, N, K, r, G = d["M"], d["N"], d["K"], d["r"], d["group_size"]
+    out = run(M, N, K, r, G, d["X"], qc, s, z, d["A"], d["B"], d["w_g"], d["b_g"])
+    X = synth.act_bits_to_f64(d["X"], "fp16")
+    T = np.matmul(X, synth.act_bits_to_f64(d["A"], "fp16"))
+    np.testing.assert_allclose(out["T"], T, rtol=1e-12, atol=1e-12 * np.abs(T).max())
+    g = expit(np.matmul(X, synth.act_bits_to_f64(d["w_g"], "fp16")) + d["b_g"])
+    np.testing.assert_allclose(out["g"], g, rtol=1e-12, atol=1e-15)
+    C = np.matmul(out["T"], synth.act_bits_to_f64(d["B"], "fp16"))
+    np.testing.assert_allclose(out["C"], C, rtol=1e-12, atol=1e-12 * np.abs(C).max())
+
+
+def test_gate_invariants():
+    d, qc, s, z = cfg1_inputs()
+    M, N, K, r, G = d["M"], d["N"], d["K"], d["r"], d["group_size"]
+    out = run(M, N, K, r, G, d["X"], qc, s, z, d["A"], d["B"], d["w_g"], d["b_g"])
+    dY = out["Y"] - out["Y0"]
+    C, g = out["C"], out["g"]
+    big = np.abs(C) > 1e-9
+    ratio = np.where(big, dY / np.where(big, C, 1.0), np.nan)
+    for m in range(M):
+        rm = ratio[m][big[m]]
+        np.testing.assert_allclose(rm, g[m], rtol=1e-6, atol=1e-9)
+        if 0.0 < g[m] < 1.0:
+            assert (np.abs(dY[m][big[m]]) < np.abs(C[m][big[m]])).all()
+            assert (np.sign(dY[m][big[m]]) == np.sign(C[m][big[m]])).all()
+
+
+def test_equivariance_and_row_subsets():
+    d, qc, s, z = cfg1_inputs()
+    M, N, K, r, G = d["M"], d["N"], d["K"], d["r"], d["group_size"]
+    args = (d["X"], qc, s, z, d["A"], d["B"], d["w_g"], d["b_g"])
+    full = run(M, N, K, r, G, *args)
+    rng = np.random.default_rng(7)
+    pm = rng.permutation(M)
+    tp = run(M, N, K, r, G, d["X"][pm], *args[1:])
+    assert np.array_equal(tp["Y"], full["Y"][pm])
+    pn = rng.permutation(N)
+    cp = run(M, N, K, r, G, d["X"], qc[pn], s[pn], z[pn], d["A"], d["B"][:, pn], d["w_g"], d["b_g"])
+    assert np.array_equal(cp["Y"], full["Y"][:, pn])
+    B2 = f16bits(2.0 * synth.act_bits_to_f64(d["B"], "fp16"))
+    b2 = run(M, N, K, r, G, d["X"], qc, s, z, d["A"], B2, d["w_g"], d["b_g"])
+    assert np.array_equal(b2["C"], 2.0 * full["C"])
+    rows = [5, 0, 15, 5]
+    sub = run(M, N, K, r, G, *args, rows=rows)
+    assert np.array_equal(sub["Y"], full["Y"][rows])
+
+
+def test_synth_shapes_and_outliers():
+    d = synth.make_layer(2, 4, seed=0)
+    assert d["X"].shape == (4, 4096) and d["W"].shape == (14336, 4096)
+    assert len(d["outlier_channels"]) == 41
+    d5 = synth.make_layer(5, 2, seed=0, N=256)
+    assert d5["act"] == "bf16" and len(d5["outlier_channels"]) == 41
+    d3 = synth.make_layer(3, 256, seed=0, N=64)
+    g = expit(synth.act_bits_to_f64(d3["X"], "fp16") @ synth.act_bits_to_f64(d3["w_g"], "fp16") + d3["b_g"])
+    inside = np.mean((g > 0.05) & (g < 0.95))
+    assert inside > 0.9

@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for the W4 + EC linear layer.
+
+This module only draws random numbers and casts them to the activation
+format; it holds none of the layer's arithmetic (no quantizer, no product),
+so both the GPU library's tests and the CPU oracle can take their inputs from
+it.  The pages measure on trained checkpoints and perplexity / accuracy
+datasets that are not available here; seeded tensors shaped like the linear
+layers of 8B- and 70B-class decoder models stand in for them.
+
+Draw order per call, from ``numpy.random.default_rng(seed)``:
+W, X, outlier channel set, A, B, w_g (or the gate direction w0).
+
+Outliers: ``round(frac * K)`` input channels (columns of X), drawn without
+replacement, shared by every token, multiplied after drawing; then X is cast
+to the activation format.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    Ms: tuple
+    K: int
+    N: int
+    r: int
+    group_size: int          # == K means one scale/zero per output channel
+    act: str                 # "fp16" or "bf16"
+    outlier_frac: float
+    outlier_scale: float
+    gate: str                # "plain": w_g ~ N(0, 0.05), b_g = 0; "calibrated": g spans (0.05, 0.95)
+    w_std: float = 0.02
+    ab_std: float = 0.01
+    wg_std: float = 0.05
+
+
+CONFIGS = {
+    1: LayerConfig("tiny", (16,), 512, 512, 8, 512, "fp16", 0.01, 20.0, "plain"),
+    2: LayerConfig("decode_up_proj_8b", (1, 4, 16), 4096, 14336, 64, 4096, "fp16", 0.01, 20.0, "plain"),
+    3: LayerConfig("prefill_out_proj_8b", (2048,), 4096, 4096, 64, 4096, "fp16", 0.01, 20.0, "calibrated"),
+    4: LayerConfig("batched_down_proj_8b_g128", (256,), 14336, 4096, 128, 128, "fp16", 0.01, 20.0, "plain"),
+    5: LayerConfig("mlp_70b_bf16", (64, 4096), 8192, 28672, 128, 8192, "bf16", 0.005, 30.0, "plain"),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def to_act_bits(x: np.ndarray, act: str) -> np.ndarray:
+    """Round float values to the activation format; return its bit patterns."""
+    if act == "fp16":
+        return np.ascontiguousarray(np.asarray(x).astype(np.float16)).view(np.uint16)
+    if act == "bf16":
+        return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+    raise ValueError(act)
+
+
+def act_bits_to_f64(bits: np.ndarray, act: str) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if act == "fp16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def make_layer(cfg, M: int, seed: int = 0, *, K=None, N=None, r=None,
+               group_size=None) -> dict:
+    """Inputs for one layer call.  ``cfg`` is a config id or a LayerConfig;
+    K, N, r, group_size override its shape (same distributions).
+
+    Returns a dict: X (act bits [M, K]), W (float32 [N, K]), A (act bits
+    [K, r]), B (act bits [r, N]), w_g (act bits [K]), b_g (float), the shape,
+    ``act`` and the outlier channel indices.
+    """
+    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    K = c.K if K is None else int(K)
+    N = c.N if N is None else int(N)
+    r = c.r if r is None else int(r)
+    G = (c.group_size if c.group_size != c.K else K) if group_size is None else int(group_size)
+    rng = np.random.default_rng(seed)
+
+    W = rng.standard_normal((N, K), dtype=np.float32) * np.float32(c.w_std)
+    X = rng.standard_normal((M, K))
+    n_out = int(round(c.outlier_frac * K))
+    out_ch = np.sort(rng.choice(K, size=n_out, replace=False)) if n_out > 0 else np.zeros(0, np.int64)
+    X[:, out_ch] *= c.outlier_scale
+    Xb = to_act_bits(X, c.act)
+    A = to_act_bits(rng.normal(0.0, c.ab_std, (K, r)), c.act)
+    B = to_act_bits(rng.normal(0.0, c.ab_std, (r, N)), c.act)
+    if c.gate == "plain":
+        w_g = to_act_bits(rng.normal(0.0, c.wg_std, (K,)), c.act)
+        b_g = 0.0
+    elif c.gate == "calibrated":
+        # A gate direction w0 ~ N(0, 1), rescaled so that the logits of the
+        # 1st and 99th percentile tokens land at logit(0.05) and logit(0.95):
+        # about 98 % of the tokens then get a gate inside (0.05, 0.95).
+        w0 = rng.standard_normal(K)
+        l0 = act_bits_to_f64(Xb, c.act) @ w0
+        p1, p99 = np.percentile(l0, [1.0, 99.0]) if M > 1 else (l0[0] - 1.0, l0[0] + 1.0)
+        span = max(p99 - p1, 1e-12)
+        cscale = 2.0 * np.log(0.95 / 0.05) / span
+        w_g = to_act_bits(cscale * w0, c.act)
+        b_g = float(-cscale * (p99 + p1) / 2.0)
+    else:
+        raise ValueError(c.gate)
+    return dict(X=Xb, W=W, A=A, B=B, w_g=w_g, b_g=b_g, M=M, K=K, N=N, r=r,
+                group_size=G, act=c.act, outlier_channels=out_ch, name=c.name)
