@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4 + EC linear layer (libw4ec) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-graph]
+
+One step is one call of the layer -- every stage of the hot path: the gate
+and X A pass, the int4 weight stream and dequantization, the main
+contraction and the gated rank-r epilogue -- over one batch of seeded
+synthetic tokens, with all inputs resident in HBM.  The packed weights and
+EC parameters are replicated R times (R x layer bytes >= 512 MB, twice the
+256 MB Infinity Cache) and the steps cycle through the copies, so every
+step streams its weights from HBM.
+
+Prints one JSON line: the whole-job rate (decode: algorithmic HBM GB/s;
+prefill: TFLOP/s), the dominant kernel's roofline from per-launch HIP
+events, and the float64 CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}   # dense fp16 / bf16 MFMA
+MALL_BYTES = 256 << 20
+
+# name -> (config id, tokens, entry point)
+WORKLOADS = {
+    "decode_up_proj_8b_m1": (2, 1, "decode"),
+    "decode_up_proj_8b_m4": (2, 4, "decode"),
+    "decode_up_proj_8b_m16": (2, 16, "decode"),
+    "tiny_m16": (1, 16, "decode"),
+    "prefill_out_proj_8b_m2048": (3, 2048, "prefill"),
+    "batched_down_proj_8b_g128_m256": (4, 256, "prefill"),
+    "mlp_70b_bf16_m64": (5, 64, "prefill"),
+    "mlp_70b_bf16_m4096": (5, 4096, "prefill"),
+}
+DEFAULT_WORKLOAD = "decode_up_proj_8b_m1"
+
+
+def layer_bytes(M, N, K, r, G, has_gate=True):
+    """Algorithmic HBM bytes of one call: packed codes, scale/zero, X, Y, A,
+    B and w_g, each moved once (the dequantized weights are never stored)."""
+    codes = N * K // 2
+    sz = N * (K // G) * 4
+    act = 2
+    return codes + sz + M * K * act + M * N * act + (K * r + r * N) * act + (K * act if has_gate else 0)
+
+
+def layer_flops(M, N, K, r):
+    """2MNK main product + 2MK(r+1) gate and X A + 2MrN rank-r product + 2MN gating/add."""
+    return 2 * M * N * K + 2 * M * K * (r + 1) + 2 * M * r * N + 2 * M * N
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4_gemm_error_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key):
+    """Measured HBM bytes per launch from the committed counter summary, if
+    it was taken on the kernels as they are now (same source digest)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = table.get(kernel_key)
+    if not e or e.get("source_digest") != source_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(d, phase, budget_s):
+    """The float64 oracle on the host, on a bounded sample of the workload."""
+    import oracle
+    qc, s, z = oracle.rtn_quantize(d["W"], d["group_size"])   # offline step, untimed
+    M, N, K, r, G = d["M"], d["N"], d["K"], d["r"], d["group_size"]
+    rows_per_call = M
+    rows = None
+    if M > 1:
+        # evaluate a prefix of the tokens: the oracle's cost is linear in them
+        est = N * K * 1.5e-9 / max(oracle.max_threads(), 1)   # ~s per token
+        rows_per_call = int(max(1, min(M, budget_s / 3 / max(est, 1e-9))))
+        rows = list(range(rows_per_call))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(d["X"], qc, s, z, d["A"], d["B"], d["w_g"], d["b_g"], N=N, K=K, r=r,
+                       group_size=G, act=d["act"], rows=rows, want_parts=False)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 1000:
+            break
+    per_call = el / n
+    frac = rows_per_call / M
+    if phase == "decode":
+        value = layer_bytes(rows_per_call, N, K, r, G) / per_call / 1e9
+        unit = "GB/s"
+    else:
+        value = layer_flops(rows_per_call, N, K, r) / per_call / 1e12
+        unit = "TFLOP/s"
+    sample = (f"{n} oracle call(s) of {rows_per_call} of {M} token(s) "
+              f"({frac:.3g} of the batch), {el:.1f} s total, weights quantized beforehand")
+    return {"value": round(value, 6), "unit": unit, "cores": int(oracle.max_threads()),
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work on the host")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the layer runs on one MI355X); "
+              "--gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4_gemm_error_amd as w4
+    from w4_gemm_error_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    w4.lib()   # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    cfg_id, M, phase = WORKLOADS[args.workload]
+    d = synth.make_layer(cfg_id, M, seed=args.seed)
+    N, K, r, G, act = d["N"], d["K"], d["r"], d["group_size"], d["act"]
+    tdt = torch.float16 if act == "fp16" else torch.bfloat16
+
+    def dev_act(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+    # weights: quantize + pack once (offline, untimed), then replicate
+    Wt = torch.from_numpy(d["W"]).to(dev)
+    q, s, z = w4.w4ec_quantize_rtn(Wt, G)
+    packed0 = w4.w4ec_pack(q, s, z, N, K, G)
+    del Wt, q, s, z
+    A0, B0, wg0 = dev_act(d["A"]), dev_act(d["B"]), dev_act(d["w_g"])
+    nbytes = layer_bytes(M, N, K, r, G)
+    weight_bytes = packed0.numel() + (A0.numel() + B0.numel() + wg0.numel()) * 2
+    R = max(1, -(-2 * MALL_BYTES // weight_bytes))
+    copies = [(packed0, A0, B0, wg0)] + [(packed0.clone(), A0.clone(), B0.clone(), wg0.clone())
+                                         for _ in range(R - 1)]
+    X = dev_act(d["X"])
+    Y = torch.empty((M, N), dtype=tdt, device=dev)
+    ws = torch.zeros(max(w4.w4ec_workspace_bytes(M, N, K, r, G), 256), dtype=torch.uint8, device=dev)
+    fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
+    b_g = d["b_g"]
+
+    def step(i):
+        p, A, B, wg = copies[i % R]
+        fn(X, p, A, B, wg, b_g, N=N, group_size=G, workspace=ws, Y=Y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, bracketed by synchronization
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(args.steps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(stream)
+        graph.replay()           # one untimed replay
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed_ms = start.elapsed_time(end)
+    ms_per_step = elapsed_ms / args.steps
+
+    # ---- dominant kernel: per-launch HIP events on the launch stream
+    n_ev = min(args.steps, 200)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3   # s
+    kdur = float(np.mean(durs))
+
+    flops = layer_flops(M, N, K, r)
+    if phase == "decode":
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = nbytes / kdur / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        kernel_key = f"decode_kernel/{args.workload}"
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = flops / kdur / 1e12
+        peak = MFMA_PEAK_TFLOPS[act]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+        kernel_key = f"prefill_call/{args.workload}"
+    roof["traffic"] = traffic_from_profiles(kernel_key)
+    roof["kernel_us"] = round(kdur * 1e6, 3)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(d, phase, args.cpu_budget)
+
+    out = {
+        "metric": "W4+EC linear: decode HBM GB/s & prefill TFLOP/s, % of MI355X roofline",
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": act,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "r": r, "group_size": G,
+                   "act": act, "phase": phase, "weight_copies": R,
+                   "launch": "hipgraph" if graph is not None else "eager",
+                   "bytes_per_step": nbytes, "flops_per_step": flops},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * w4ec.h -- C ABI of libw4ec: a weight-only 4-bit linear layer with an
+ * input-adaptive low-rank error compensator (EC), for AMD Instinct MI355X
+ * (gfx950) on one GPU.
+ *
+ * The operation (SPEAR, "A System for Post-Quantization Error-Adaptive
+ * Recovery Enabling Efficient Low-Bit LLM Serving"; gist.science technical
+ * summary, section 2.1A "input-adaptive error compensators").  The page
+ * writes the effective weight as the 4-bit weight plus a gated rank-r product
+ * B diag(gate(A x)) A; this library takes the gate as one scalar per token,
+ * g = sigmoid(x . w_g + b_g), with the page's scale alpha folded into B:
+ *
+ *   Y[m,n] = sum_k X[m,k] Wd[n,k]  +  g[m] * sum_j T[m,j] B[j,n]
+ *   Wd[n,k] = (q[n,k] - z[n,k/G]) * s[n,k/G]       q in 0..15 (4-bit codes)
+ *   T[m,j]  = sum_k X[m,k] A[k,j]
+ *   g[m]    = 1 / (1 + exp(-(sum_k X[m,k] w_g[k] + b_g)))
+ *
+ * Section 2.2A of the same summary splits the work by phase: a decode step
+ * (few tokens, memory bound) runs the EC inside the low-bit GEMM's epilogue
+ * in a single kernel -> w4ec_linear_decode; a prefill step (many tokens,
+ * compute bound) -> w4ec_linear_prefill, here also with the gated correction
+ * fused into the GEMM epilogue (an extension of the reduction by r terms)
+ * after a prepass that computes the gate and X A in one read of X.
+ *
+ * Conventions for every call:
+ *  - Pointers named as "device" are HIP device pointers owned by the caller.
+ *    The library never allocates or frees memory and keeps no state between
+ *    calls except what the caller's workspace holds.
+ *  - All arrays are row-major and contiguous.  X, Y and the workspace must be
+ *    16-byte aligned; the packed blob 256-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on it unless stated otherwise.
+ *  - Activations X, Y and the EC parameters A, B, w_g share one dtype
+ *    (`act_dtype`: W4EC_FP16 or W4EC_BF16); scale and zero are always fp16
+ *    (passed as uint16_t bit patterns).  Accumulation is fp32.
+ *  - Shapes: N >= 1; K a multiple of 128; group_size G == K (one scale/zero
+ *    per output channel) or a multiple of 128 that divides K; 0 <= r <= 256.
+ *  - Errors are returned as w4ec_status values before anything is launched;
+ *    a failed launch returns W4EC_ERR_HIP.  No C++ exception crosses the ABI.
+ *  - Y must not alias any input.  The same inputs give a bit-identical Y
+ *    (all cross-workgroup sums run in a fixed order; no float atomics).
+ */
+#ifndef W4EC_H_
+#define W4EC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4EC_OK = 0,
+    W4EC_ERR_INVALID_ARG = -1,  /* null pointer, bad shape, misalignment, bad zero point */
+    W4EC_ERR_UNSUPPORTED = -2,  /* shape outside what this build supports (see above)   */
+    W4EC_ERR_WORKSPACE = -3,    /* workspace missing or smaller than w4ec_workspace_bytes */
+    W4EC_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed           */
+} w4ec_status;
+
+typedef enum { W4EC_FP16 = 0, W4EC_BF16 = 1 } w4ec_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* w4ec_status_str(int status);
+
+/* Size in bytes of the packed device blob for an N x K layer with group size
+ * G (codes, scales and zero points in the layout the kernels read).
+ * Returns 0 for unsupported shapes. */
+size_t w4ec_packed_bytes(int N, int K, int group_size);
+
+/* Round-to-nearest asymmetric int4 quantization on the GPU -- the per-channel
+ * RTN baseline of the SPEAR summary's results (section 3.1), here also per
+ * group of G input features.  Per row n and group:
+ *   lo = min(min w, 0), hi = max(max w, 0), s = fp16((hi - lo) / 15)
+ *   z = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + z, 0, 15)
+ * computed in float64 (s clamped to the largest finite half; a group whose s
+ * rounds to 0 gets s = 1, z = 0).  W must be finite.
+ *   W      device, float32 [N, K]
+ *   q_canon device, uint8 [N, K/2]: code k in the low nibble of byte k/2 when
+ *          k is even, in the high nibble when k is odd
+ *   scale, zero  device, fp16 bits [N, K/G]  (zero is an integer 0..15)   */
+int w4ec_quantize_rtn(const float* W, int N, int K, int group_size,
+                      uint8_t* q_canon, uint16_t* scale, uint16_t* zero,
+                      void* stream);
+
+/* Re-lay canonical codes and fp16 scale/zero into the device blob (an
+ * offline step; weights are prepared once).  `zero` must hold integers in
+ * 0..15.  This call synchronizes `stream` to check the zero points and
+ * returns W4EC_ERR_INVALID_ARG if one is not such an integer (the blob is
+ * then unusable).
+ *   q_canon device uint8 [N, K/2]; scale, zero device fp16 bits [N, K/G];
+ *   packed  device, w4ec_packed_bytes(N, K, G) bytes, 256-byte aligned.   */
+int w4ec_pack(const uint8_t* q_canon, const uint16_t* scale, const uint16_t* zero,
+              int N, int K, int group_size, void* packed, void* stream);
+
+/* Exact inverse of w4ec_pack (a test hook): blob -> canonical codes and
+ * fp16 scale/zero, same layouts as w4ec_pack's inputs.  Asynchronous. */
+int w4ec_unpack(const void* packed, int N, int K, int group_size,
+                uint8_t* q_canon, uint16_t* scale, uint16_t* zero, void* stream);
+
+/* Workspace bytes needed by w4ec_linear_decode / w4ec_linear_prefill for
+ * this shape (the larger of the two when both apply).  The workspace holds
+ * the gated rank-r activations, partial sums and the counters through which
+ * workgroups hand over partial results.  It must be zero-filled once when
+ * allocated; every call leaves its counters at zero again, so it can be
+ * reused by later calls on the same stream without clearing.  Two calls
+ * that overlap in time must not share a workspace. */
+size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size);
+
+/* The layer, decode phase: 1 <= M <= 16 tokens, one kernel launch.
+ *   X     device act [M, K]          packed  device blob from w4ec_pack
+ *   A     device act [K, r]          B       device act [r, N]
+ *   w_g   device act [K], or NULL (then x . w_g = 0 and g = sigmoid(b_g);
+ *         b_g = -INFINITY closes the gate, +INFINITY opens it fully)
+ *   b_g   gate bias (fp32, by value)
+ *   Y     device act [M, N] (output)
+ *   r     EC rank; r == 0 is the plain W4 layer (A, B, w_g ignored, may be NULL)
+ * Returns W4EC_ERR_UNSUPPORTED for M > 16. */
+int w4ec_linear_decode(const void* X, const void* packed, const void* A, const void* B,
+                       const void* w_g, float b_g, void* Y,
+                       int M, int N, int K, int r, int group_size, int act_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* The layer, prefill phase: any M >= 1 (tiled MFMA GEMM, two launches: the
+ * gate / X A prepass, then the GEMM with the gated correction in its
+ * epilogue).  Arguments as for w4ec_linear_decode. */
+int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const void* B,
+                        const void* w_g, float b_g, void* Y,
+                        int M, int N, int K, int r, int group_size, int act_dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4EC_H_ */

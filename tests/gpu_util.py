@@ -1,0 +1,80 @@
+"""Shared helpers for the GPU parity tests: move seeded inputs to the GPU,
+run the HIP path through the C ABI binding, run the oracle on the same
+inputs, and compare to the stated tolerance."""
+import numpy as np
+
+import oracle
+import w4_gemm_error_amd as w4
+from w4_gemm_error_amd import synth
+
+# max |Y_gpu - Y_oracle| <= TOL * (max_n |Y_oracle[m, n]| + 1), per token m.
+# fp16: fp32 accumulation, fp16 output rounding.  bf16: 8x wider, the ratio
+# of the two formats' unit roundoffs (2^-8 / 2^-11): rounding the exact
+# result to bf16 alone already exceeds the fp16 bound.
+TOL = {"fp16": 2e-3, "bf16": 1.6e-2}
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def dev_act(bits, act):
+    t = torch()
+    x = t.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return x.view(t.float16 if act == "fp16" else t.bfloat16).cuda()
+
+
+def host_bits(tensor):
+    t = torch()
+    return tensor.detach().cpu().contiguous().view(t.int16).numpy().view(np.uint16)
+
+
+def act_f64(bits, act):
+    return synth.act_bits_to_f64(bits, act)
+
+
+def gpu_quantize(d):
+    t = torch()
+    W = t.from_numpy(d["W"]).cuda()
+    q, s, z = w4.w4ec_quantize_rtn(W, d["group_size"])
+    packed = w4.w4ec_pack(q, s, z, d["N"], d["K"], d["group_size"])
+    del W
+    return q, s, z, packed
+
+
+def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=None):
+    act = d["act"]
+    r = d["r"] if r is None else r
+    X = dev_act(d["X"], act)
+    A = dev_act(d["A"][:, :r], act) if r > 0 else None
+    B = dev_act(d["B"][:r], act) if r > 0 else None
+    wg = dev_act(d["w_g"], act) if (r > 0 and with_gate) else None
+    bg = d["b_g"] if b_g is None else b_g
+    fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
+    Y = fn(X, packed, A, B, wg, bg, N=d["N"], group_size=d["group_size"], workspace=workspace)
+    torch().cuda.synchronize()
+    return host_bits(Y)
+
+
+def oracle_layer(d, codes, *, r=None, b_g=None, with_gate=True, rows=None):
+    qc, s, z = codes
+    r = d["r"] if r is None else r
+    A = d["A"][:, :r] if r > 0 else None
+    B = d["B"][:r] if r > 0 else None
+    wg = d["w_g"] if with_gate else None
+    bg = d["b_g"] if b_g is None else b_g
+    return oracle.forward(d["X"], qc, s, z, A, B, wg, bg, N=d["N"], K=d["K"], r=r,
+                          group_size=d["group_size"], act=d["act"], rows=rows, want_parts=False)["Y"]
+
+
+def assert_close(Y_bits, Y_ref, act, what=""):
+    Yg = act_f64(Y_bits, act)
+    assert Yg.shape == Y_ref.shape, (Yg.shape, Y_ref.shape)
+    assert np.isfinite(Yg).all(), f"{what}: non-finite output"
+    bound = TOL[act] * (np.abs(Y_ref).max(axis=1, keepdims=True) + 1.0)
+    ratio = np.abs(Yg - Y_ref) / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (f"{what}: max err/tol {ratio.max():.3f} at {worst}: "
+                                f"gpu {Yg[worst]:.6g} oracle {Y_ref[worst]:.6g}")
+    return float(ratio.max())

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI (CPU only; no kernel is launched).
+
+Every call below fails validation, which happens before any HIP call, so
+these run without a GPU.  Device pointers are fake, suitably aligned
+addresses that are never dereferenced.
+"""
+import ctypes
+import math
+
+import pytest
+
+import w4_gemm_error_amd as w4
+
+
+def test_library_exports_every_header_symbol():
+    declared = w4.header_symbols()
+    assert set(declared) >= {"w4ec_pack", "w4ec_linear_decode", "w4ec_linear_prefill",
+                             "w4ec_quantize_rtn", "w4ec_unpack", "w4ec_packed_bytes",
+                             "w4ec_workspace_bytes", "w4ec_status_str"}
+    assert w4.exported_symbols() == declared
+
+
+def test_status_strings():
+    for code, name in [(0, "W4EC_OK"), (-1, "W4EC_ERR_INVALID_ARG"), (-2, "W4EC_ERR_UNSUPPORTED"),
+                       (-3, "W4EC_ERR_WORKSPACE"), (-4, "W4EC_ERR_HIP"), (7, "W4EC_UNKNOWN_STATUS")]:
+        assert w4.w4ec_status_str(code) == name
+
+
+def test_packed_bytes():
+    # header + N/16 * K/128 panels of 1 KB + (K/G) * Npad scale/zero dwords
+    assert w4.w4ec_packed_bytes(512, 512, 512) == 256 + 32 * 4 * 1024 + 512 * 4
+    assert w4.w4ec_packed_bytes(14336, 4096, 4096) == 256 + 14336 * 4096 // 2 + 14336 * 4
+    assert w4.w4ec_packed_bytes(4096, 14336, 128) == 256 + 4096 * 14336 // 2 + 112 * 4096 * 4
+    assert w4.w4ec_packed_bytes(20, 256, 256) == 256 + 2 * 2 * 1024 + 32 * 4   # N padded to 32
+    assert w4.w4ec_packed_bytes(16, 100, 100) == 0      # K not a multiple of 128
+    assert w4.w4ec_packed_bytes(16, 512, 96) == 0       # group not a multiple of 128
+    assert w4.w4ec_packed_bytes(0, 512, 512) == 0
+
+
+def test_workspace_bytes():
+    assert w4.w4ec_workspace_bytes(1, 14336, 4096, 64, 4096) > 0
+    assert w4.w4ec_workspace_bytes(2048, 4096, 4096, 64, 4096) >= 2048 * 64 * 2   # gated T for every token
+    assert w4.w4ec_workspace_bytes(256, 4096, 14336, 128, 128) >= 256 * 4096 * 4  # split-K partial tiles
+    assert w4.w4ec_workspace_bytes(1, 512, 512, 300, 512) == 0   # rank above 256
+    assert w4.w4ec_workspace_bytes(0, 512, 512, 8, 512) == 0
+
+
+FAKE = 0x7F0000000000   # 256-byte aligned, never dereferenced
+
+
+def call(name, X=FAKE, packed=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
+         w_g=FAKE + 0x400000, b_g=0.0, Y=FAKE + 0x500000, M=4, N=512, K=512, r=8, G=512,
+         act=0, ws=FAKE + 0x600000, ws_bytes=1 << 30):
+    fn = getattr(w4.lib(), name)
+    P = ctypes.c_void_p
+    return fn(P(X) if X else None, P(packed) if packed else None, P(A) if A else None,
+              P(B) if B else None, P(w_g) if w_g else None, b_g, P(Y) if Y else None,
+              M, N, K, r, G, act, P(ws) if ws else None, ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["w4ec_linear_decode", "w4ec_linear_prefill"])
+def test_layer_argument_errors(name):
+    E = w4
+    assert call(name, M=0) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, r=-1) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, N=0) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, K=500) == E.W4EC_ERR_UNSUPPORTED
+    assert call(name, G=96) == E.W4EC_ERR_UNSUPPORTED
+    assert call(name, r=257) == E.W4EC_ERR_UNSUPPORTED
+    assert call(name, act=5) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, X=0) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, packed=0) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, Y=0) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, A=0) == E.W4EC_ERR_INVALID_ARG            # r > 0 needs A and B
+    assert call(name, X=FAKE + 8) == E.W4EC_ERR_INVALID_ARG     # misaligned
+    assert call(name, packed=FAKE + 0x100010) == E.W4EC_ERR_INVALID_ARG
+    assert call(name, Y=FAKE) == E.W4EC_ERR_INVALID_ARG         # aliases X
+    assert call(name, ws=0) == E.W4EC_ERR_WORKSPACE
+    assert call(name, ws_bytes=64) == E.W4EC_ERR_WORKSPACE
+    assert call(name, ws=FAKE + 0x600010) == E.W4EC_ERR_WORKSPACE
+
+
+def test_decode_rejects_more_than_16_tokens():
+    assert call("w4ec_linear_decode", M=17) == w4.W4EC_ERR_UNSUPPORTED
+
+
+def test_weight_prep_argument_errors():
+    L = w4.lib()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    assert L.w4ec_quantize_rtn(None, 16, 256, 256, f, f, f, None) == w4.W4EC_ERR_INVALID_ARG
+    assert L.w4ec_quantize_rtn(f, 16, 256, 100, f, f, f, None) == w4.W4EC_ERR_INVALID_ARG
+    assert L.w4ec_pack(f, f, f, 16, 200, 200, f, None) == w4.W4EC_ERR_UNSUPPORTED
+    assert L.w4ec_pack(f, f, f, 16, 256, 256, P(FAKE + 16), None) == w4.W4EC_ERR_INVALID_ARG
+    assert L.w4ec_pack(None, f, f, 16, 256, 256, f, None) == w4.W4EC_ERR_INVALID_ARG
+    assert L.w4ec_unpack(None, 16, 256, 256, f, f, f, None) == w4.W4EC_ERR_INVALID_ARG
+    assert L.w4ec_unpack(f, 16, 256, 64, f, f, f, None) == w4.W4EC_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(w4, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(w4, "_lib", None)
+    with pytest.raises(ImportError):
+        w4.lib()

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Codes are compared bit for bit; Y within
+max|err| <= 2e-3 (fp16) / 1.6e-2 (bf16) * (max_n |Y_oracle[m, n]| + 1) per token.
+Small cases span several tiles with ragged tails in M and N; the five
+workload shapes run at full size with the oracle evaluating sampled tokens.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import w4_gemm_error_amd as w4
+from w4_gemm_error_amd import synth
+
+from gpu_util import (assert_close, dev_act, gpu_layer, gpu_quantize, host_bits, oracle_layer,
+                      torch)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- weight prep
+
+@pytest.mark.parametrize("N,K,G", [(512, 512, 512), (300, 1024, 128), (37, 384, 128)])
+def test_quantize_bit_exact(N, K, G):
+    _print(f"quantize N={N} K={K} G={G}")
+    d = synth.make_layer(1, 1, seed=3, N=N, K=K, group_size=G)
+    q, s, z, _ = gpu_quantize(d)
+    oq, os_, oz = oracle.rtn_quantize(d["W"], G)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(host_bits(s), os_)
+    assert np.array_equal(host_bits(z), oz)
+
+
+@pytest.mark.parametrize("N,K,G", [(37, 384, 128), (512, 512, 512), (64, 1024, 256)])
+def test_pack_unpack_round_trip(N, K, G):
+    _print(f"pack/unpack N={N} K={K} G={G}")
+    t = torch()
+    rng = np.random.default_rng(11)
+    qc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    qc.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)        # every byte value
+    s = rng.uniform(1e-3, 1e-1, size=(N, K // G)).astype(np.float16)
+    z = rng.integers(0, 16, size=(N, K // G)).astype(np.float16)
+    packed = w4.w4ec_pack(t.from_numpy(qc).cuda(), t.from_numpy(s).cuda(), t.from_numpy(z).cuda(), N, K, G)
+    assert packed.numel() == w4.w4ec_packed_bytes(N, K, G)
+    q2, s2, z2 = w4.w4ec_unpack(packed, N, K, G)
+    t.cuda.synchronize()
+    assert np.array_equal(q2.cpu().numpy(), qc)
+    assert np.array_equal(s2.cpu().numpy().view(np.uint16), s.view(np.uint16))
+    assert np.array_equal(z2.cpu().numpy().view(np.uint16), z.view(np.uint16))
+
+
+def test_pack_rejects_non_integer_zero():
+    t = torch()
+    N, K = 16, 128
+    q = t.zeros((N, K // 2), dtype=t.uint8, device="cuda")
+    s = t.ones((N, 1), dtype=t.float16, device="cuda")
+    z = t.full((N, 1), 7.5, dtype=t.float16, device="cuda")
+    with pytest.raises(w4.W4ECError) as e:
+        w4.w4ec_pack(q, s, z, N, K, K)
+    assert e.value.status == w4.W4EC_ERR_INVALID_ARG
+    z = t.full((N, 1), 16.0, dtype=t.float16, device="cuda")
+    with pytest.raises(w4.W4ECError):
+        w4.w4ec_pack(q, s, z, N, K, K)
+
+
+# ---------------------------------------------------------------- small layers
+
+SMALL = [
+    # phase, act, M, N, K, r, G
+    ("decode", "fp16", 1, 512, 512, 8, 512),
+    ("decode", "fp16", 3, 528, 640, 72, 640),
+    ("decode", "fp16", 16, 512, 512, 8, 128),
+    ("decode", "bf16", 5, 272, 384, 40, 384),
+    ("decode", "bf16", 16, 512, 512, 8, 128),
+    ("decode", "fp16", 7, 48, 1280, 256, 256),
+    ("prefill", "fp16", 17, 528, 640, 72, 640),
+    ("prefill", "fp16", 300, 512, 512, 8, 512),
+    ("prefill", "fp16", 129, 784, 1024, 64, 128),
+    ("prefill", "bf16", 100, 528, 512, 40, 512),
+    ("prefill", "bf16", 200, 512, 768, 16, 128),
+    ("prefill", "fp16", 2, 512, 512, 8, 512),
+    ("prefill", "fp16", 64, 1024, 2048, 130, 2048),
+]
+
+
+def small_layer(act, M, N, K, r, G, seed=5):
+    cfg = synth.CONFIGS[5] if act == "bf16" else synth.CONFIGS[1]
+    return synth.make_layer(cfg, M, seed=seed, N=N, K=K, r=r, group_size=G)
+
+
+@pytest.mark.parametrize("phase,act,M,N,K,r,G", SMALL)
+def test_small_layer_parity(phase, act, M, N, K, r, G):
+    _print(f"small {phase} {act} M={M} N={N} K={K} r={r} G={G}")
+    d = small_layer(act, M, N, K, r, G)
+    q, s, z, packed = gpu_quantize(d)
+    codes = oracle.rtn_quantize(d["W"], G)
+    assert np.array_equal(q.cpu().numpy(), codes[0])
+    Y = gpu_layer(d, packed, phase)
+    ref = oracle_layer(d, codes)
+    assert_close(Y, ref, act, f"{phase} {act} M={M}")
+
+
+@pytest.mark.parametrize("phase", ["decode", "prefill"])
+def test_special_cases(phase):
+    _print(f"special cases {phase}")
+    M = 9 if phase == "decode" else 40
+    d = small_layer("fp16", M, 528, 512, 24, 512, seed=8)
+    _, _, _, packed = gpu_quantize(d)
+    codes = oracle.rtn_quantize(d["W"], 512)
+    plain = gpu_layer(d, packed, phase, r=0)
+    assert_close(plain, oracle_layer(d, codes, r=0), "fp16", "r=0")
+    closed = gpu_layer(d, packed, phase, b_g=-math.inf)
+    assert np.array_equal(synth.act_bits_to_f64(closed, "fp16"), synth.act_bits_to_f64(plain, "fp16"))
+    opened = gpu_layer(d, packed, phase, b_g=math.inf, with_gate=False)
+    assert_close(opened, oracle_layer(d, codes, b_g=math.inf, with_gate=False), "fp16", "g=1")
+    nogate = gpu_layer(d, packed, phase, b_g=0.25, with_gate=False)
+    assert_close(nogate, oracle_layer(d, codes, b_g=0.25, with_gate=False), "fp16", "w_g=None")
+
+
+@pytest.mark.parametrize("phase,M", [("decode", 16), ("prefill", 256)])
+def test_deterministic_and_workspace_reuse(phase, M):
+    _print(f"determinism {phase} M={M}")
+    t = torch()
+    d = synth.make_layer(4, M, seed=2, N=1024, K=2048)   # group 128, split-K in prefill
+    _, _, _, packed = gpu_quantize(d)
+    ws = t.zeros(w4.w4ec_workspace_bytes(M, d["N"], d["K"], d["r"], d["group_size"]),
+                 dtype=t.uint8, device="cuda")
+    first = gpu_layer(d, packed, phase, workspace=ws)
+    for _ in range(5):
+        again = gpu_layer(d, packed, phase, workspace=ws)
+        assert np.array_equal(again, first)
+    if phase == "decode":
+        assert int(ws[:16].view(t.int32).abs().sum().item()) == 0   # counters back at zero, no timeout
+
+
+def test_phase_dispatch_agrees():
+    _print("decode vs prefill on the same 16 tokens")
+    d = small_layer("fp16", 16, 512, 1024, 32, 1024, seed=9)
+    _, _, _, packed = gpu_quantize(d)
+    a = synth.act_bits_to_f64(gpu_layer(d, packed, "decode"), "fp16")
+    b = synth.act_bits_to_f64(gpu_layer(d, packed, "prefill"), "fp16")
+    ref = oracle_layer(d, oracle.rtn_quantize(d["W"], 1024))
+    bound = 2e-3 * (np.abs(ref).max(axis=1, keepdims=True) + 1.0)
+    assert (np.abs(a - b) <= 2 * bound).all()
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+FULL = [
+    # cfg, M, phase, sampled rows (None = all)
+    (1, 16, "decode", None),
+    (2, 1, "decode", None),
+    (2, 4, "decode", None),
+    (2, 16, "decode", None),
+    (3, 2048, "prefill", [0, 1, 77, 1023, 1500, 2047]),
+    (4, 256, "prefill", [0, 5, 128, 255]),
+    (5, 64, "prefill", [0, 31, 63]),
+    (5, 4096, "prefill", [0, 2049, 4095]),
+]
+
+
+@pytest.mark.parametrize("cfg,M,phase,rows", FULL)
+def test_full_size_parity(cfg, M, phase, rows):
+    _print(f"full cfg{cfg} M={M} {phase}")
+    d = synth.make_layer(cfg, M, seed=0)
+    q, s, z, packed = gpu_quantize(d)
+    codes = oracle.rtn_quantize(d["W"], d["group_size"])
+    assert np.array_equal(q.cpu().numpy(), codes[0])
+    assert np.array_equal(host_bits(s), codes[1]) and np.array_equal(host_bits(z), codes[2])
+    del q, s, z
+    Y = gpu_layer(d, packed, phase)
+    ref = oracle_layer(d, codes, rows=rows)
+    Ysub = Y if rows is None else Y[rows]
+    worst = assert_close(Ysub, ref, d["act"], f"cfg{cfg} M={M}")
+    _print(f"  worst err/tol {worst:.3f}")

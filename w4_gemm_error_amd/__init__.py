@@ -1,0 +1,263 @@
+"""libw4ec Python binding: the W4 + input-adaptive EC linear layer on MI355X.
+
+A thin ctypes layer over the C ABI in ``include/w4ec.h`` with the same
+function names.  It only marshals arguments: torch supplies device memory
+and the current HIP stream; every step of the layer runs in the library's
+HIP kernels.  If ``libw4ec.so`` has not been built, importing the functions
+raises -- there is no fallback.
+
+Build: ``python -m w4_gemm_error_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+__all__ = [
+    "W4ECError", "lib", "exported_symbols", "header_symbols",
+    "W4EC_OK", "W4EC_ERR_INVALID_ARG", "W4EC_ERR_UNSUPPORTED", "W4EC_ERR_WORKSPACE", "W4EC_ERR_HIP",
+    "W4EC_FP16", "W4EC_BF16", "DECODE_MAX_M",
+    "w4ec_status_str", "w4ec_packed_bytes", "w4ec_workspace_bytes",
+    "w4ec_quantize_rtn", "w4ec_pack", "w4ec_unpack",
+    "w4ec_linear_decode", "w4ec_linear_prefill", "w4ec_linear",
+    "PackedLayer",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4ec.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "w4ec.h")
+
+W4EC_OK = 0
+W4EC_ERR_INVALID_ARG = -1
+W4EC_ERR_UNSUPPORTED = -2
+W4EC_ERR_WORKSPACE = -3
+W4EC_ERR_HIP = -4
+W4EC_FP16 = 0
+W4EC_BF16 = 1
+DECODE_MAX_M = 16
+
+_lock = threading.Lock()
+_lib = None
+
+
+class W4ECError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {w4ec_status_str(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4ec.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m w4_gemm_error_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.w4ec_status_str.argtypes = [I]
+        L.w4ec_status_str.restype = ctypes.c_char_p
+        L.w4ec_packed_bytes.argtypes = [I, I, I]
+        L.w4ec_packed_bytes.restype = Z
+        L.w4ec_workspace_bytes.argtypes = [I, I, I, I, I]
+        L.w4ec_workspace_bytes.restype = Z
+        L.w4ec_quantize_rtn.argtypes = [P, I, I, I, P, P, P, P]
+        L.w4ec_quantize_rtn.restype = I
+        L.w4ec_pack.argtypes = [P, P, P, I, I, I, P, P]
+        L.w4ec_pack.restype = I
+        L.w4ec_unpack.argtypes = [P, I, I, I, P, P, P, P]
+        L.w4ec_unpack.restype = I
+        for name in ("w4ec_linear_decode", "w4ec_linear_prefill"):
+            fn = getattr(L, name)
+            fn.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, P, Z, P]
+            fn.restype = I
+        _lib = L
+        return L
+
+
+def header_symbols() -> list:
+    """Function names declared in include/w4ec.h."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4ec_[a-z_]+)\s*\(", text)))
+
+
+def exported_symbols() -> list:
+    L = lib()
+    return [s for s in header_symbols() if hasattr(L, s)]
+
+
+# ---------------------------------------------------------------- host-only calls
+
+def w4ec_status_str(status: int) -> str:
+    return lib().w4ec_status_str(int(status)).decode()
+
+
+def w4ec_packed_bytes(N: int, K: int, group_size: int) -> int:
+    return int(lib().w4ec_packed_bytes(N, K, group_size))
+
+
+def w4ec_workspace_bytes(M: int, N: int, K: int, r: int, group_size: int) -> int:
+    return int(lib().w4ec_workspace_bytes(M, N, K, r, group_size))
+
+
+# ---------------------------------------------------------------- device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, what: str):
+    if status != W4EC_OK:
+        raise W4ECError(status, what)
+
+
+def _need_cuda(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _act_code(dtype) -> int:
+    torch = _torch()
+    if dtype == torch.float16:
+        return W4EC_FP16
+    if dtype == torch.bfloat16:
+        return W4EC_BF16
+    raise ValueError(f"activation dtype {dtype} is not fp16/bf16")
+
+
+def w4ec_quantize_rtn(W, group_size: int, *, stream=None):
+    """RTN int4 on the GPU: W float32 [N, K] -> (codes uint8 [N, K/2],
+    scale fp16 [N, K/G], zero fp16 [N, K/G])."""
+    torch = _torch()
+    _need_cuda(W, "W", torch.float32)
+    N, K = W.shape
+    G = int(group_size)
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    s = torch.empty((N, K // G), dtype=torch.float16, device=W.device)
+    z = torch.empty((N, K // G), dtype=torch.float16, device=W.device)
+    _check(lib().w4ec_quantize_rtn(_ptr(W), N, K, G, _ptr(q), _ptr(s), _ptr(z), _stream_handle(stream)),
+           "w4ec_quantize_rtn")
+    return q, s, z
+
+
+def w4ec_pack(q_canon, scale, zero, N: int, K: int, group_size: int, *, packed=None, stream=None):
+    """Canonical codes + fp16 scale/zero -> device blob (uint8 tensor).  Synchronizes the stream."""
+    torch = _torch()
+    _need_cuda(q_canon, "q_canon", torch.uint8)
+    _need_cuda(scale, "scale", torch.float16)
+    _need_cuda(zero, "zero", torch.float16)
+    nbytes = w4ec_packed_bytes(N, K, group_size)
+    if nbytes == 0:
+        raise W4ECError(W4EC_ERR_UNSUPPORTED, "w4ec_packed_bytes")
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=q_canon.device)
+    _check(lib().w4ec_pack(_ptr(q_canon), _ptr(scale), _ptr(zero), N, K, group_size, _ptr(packed),
+                           _stream_handle(stream)), "w4ec_pack")
+    return packed
+
+
+def w4ec_unpack(packed, N: int, K: int, group_size: int, *, stream=None):
+    torch = _torch()
+    _need_cuda(packed, "packed", torch.uint8)
+    G = int(group_size)
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=packed.device)
+    s = torch.empty((N, K // G), dtype=torch.float16, device=packed.device)
+    z = torch.empty((N, K // G), dtype=torch.float16, device=packed.device)
+    _check(lib().w4ec_unpack(_ptr(packed), N, K, G, _ptr(q), _ptr(s), _ptr(z), _stream_handle(stream)),
+           "w4ec_unpack")
+    return q, s, z
+
+
+def _layer_call(name, X, packed, A, B, w_g, b_g, N, group_size, workspace, Y, stream):
+    torch = _torch()
+    acts = (torch.float16, torch.bfloat16)
+    _need_cuda(X, "X", acts)
+    act = X.dtype
+    M, K = X.shape
+    r = 0 if A is None else int(A.shape[1])
+    for t, nm in ((A, "A"), (B, "B"), (w_g, "w_g")):
+        _need_cuda(t, nm, act)
+    _need_cuda(packed, "packed", torch.uint8)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=act, device=X.device)
+    _need_cuda(Y, "Y", act)
+    if workspace is None:
+        nb = w4ec_workspace_bytes(M, N, K, r, group_size)
+        workspace = torch.zeros(max(nb, 256), dtype=torch.uint8, device=X.device)
+    fn = getattr(lib(), name)
+    st = fn(_ptr(X), _ptr(packed), _ptr(A), _ptr(B), _ptr(w_g), float(b_g), _ptr(Y),
+            M, N, K, r, int(group_size), _act_code(act), _ptr(workspace), workspace.numel(),
+            _stream_handle(stream))
+    _check(st, name)
+    return Y
+
+
+def w4ec_linear_decode(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):
+    """Y = X Wd^T + g (X A) B for 1 <= M <= 16 tokens (one kernel launch)."""
+    return _layer_call("w4ec_linear_decode", X, packed, A, B, w_g, b_g, N, group_size, workspace, Y, stream)
+
+
+def w4ec_linear_prefill(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):
+    """Y = X Wd^T + g (X A) B for any M >= 1 (prepass + tiled MFMA GEMM)."""
+    return _layer_call("w4ec_linear_prefill", X, packed, A, B, w_g, b_g, N, group_size, workspace, Y, stream)
+
+
+def w4ec_linear(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):
+    """Phase-adaptive dispatch: decode kernel for M <= 16 tokens, prefill otherwise."""
+    fn = w4ec_linear_decode if X.shape[0] <= DECODE_MAX_M else w4ec_linear_prefill
+    return fn(X, packed, A, B, w_g, b_g, N=N, group_size=group_size, workspace=workspace, Y=Y, stream=stream)
+
+
+class PackedLayer:
+    """A quantized layer held on the GPU: packed weights, EC parameters and a
+    reusable (zero-initialised) workspace sized for the largest M seen."""
+
+    def __init__(self, packed, A, B, w_g, b_g, *, N, K, group_size):
+        self.packed, self.A, self.B, self.w_g, self.b_g = packed, A, B, w_g, float(b_g)
+        self.N, self.K, self.group_size = int(N), int(K), int(group_size)
+        self.r = 0 if A is None else int(A.shape[1])
+        self._ws = None
+
+    @classmethod
+    def from_float(cls, W, A, B, w_g, b_g, *, group_size, stream=None):
+        N, K = W.shape
+        q, s, z = w4ec_quantize_rtn(W, group_size, stream=stream)
+        packed = w4ec_pack(q, s, z, N, K, group_size, stream=stream)
+        return cls(packed, A, B, w_g, b_g, N=N, K=K, group_size=group_size)
+
+    def workspace(self, M):
+        torch = _torch()
+        nb = max(w4ec_workspace_bytes(M, self.N, self.K, self.r, self.group_size), 256)
+        if self._ws is None or self._ws.numel() < nb:
+            self._ws = torch.zeros(nb, dtype=torch.uint8, device=self.packed.device)
+        return self._ws
+
+    def __call__(self, X, *, Y=None, phase=None, stream=None):
+        M = X.shape[0]
+        ws = self.workspace(M)
+        if phase is None:
+            phase = "decode" if M <= DECODE_MAX_M else "prefill"
+        fn = w4ec_linear_decode if phase == "decode" else w4ec_linear_prefill
+        return fn(X, self.packed, self.A, self.B, self.w_g, self.b_g, N=self.N,
+                  group_size=self.group_size, workspace=ws, Y=Y, stream=stream)

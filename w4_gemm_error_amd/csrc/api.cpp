@@ -1,0 +1,267 @@
+// api.cpp -- the C ABI of libw4ec (declared in include/w4ec.h): argument
+// validation, launch plans, workspace sizing and dispatch to the kernels.
+// Validation makes no HIP call, so every argument error is reported before
+// anything touches the device.
+#include "w4ec.h"
+
+#include <hip/hip_runtime.h>
+
+#include <new>
+
+#include "w4ec_common.h"
+#include "w4ec_launch.h"
+
+using namespace w4ec;
+
+namespace {
+
+constexpr int MAX_RANK = 256;
+constexpr int DECODE_MAX_M = 16;
+constexpr int TARGET_WGS = 256;   // one workgroup per CU for the large-tile kernels
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_weight_shape(int N, int K, int G)
+{
+    if (N <= 0 || K <= 0 || G <= 0)
+        return W4EC_ERR_INVALID_ARG;
+    if (K % PANEL_K != 0)
+        return W4EC_ERR_UNSUPPORTED;
+    if (G != K && (G % PANEL_K != 0 || K % G != 0))
+        return W4EC_ERR_UNSUPPORTED;
+    if ((long long)N * K > (1LL << 40))
+        return W4EC_ERR_UNSUPPORTED;
+    return W4EC_OK;
+}
+
+DecodePlan make_decode_plan(int M, int N, int K, int r)
+{
+    DecodePlan p{};
+    const int NB = (N + PANEL_N - 1) / PANEL_N;
+    p.KS = 256;
+    p.P = r > 0 ? (K + p.KS - 1) / p.KS : 0;
+    p.RC = r + 1;
+    p.r_pad = (r + 31) / 32 * 32;
+    p.CB = M <= 4 ? 1 : 2;
+    p.n_main = (NB + p.CB - 1) / p.CB;
+    size_t off = 0;
+    p.off_flags = off;
+    off += 256;
+    p.off_partial = off;
+    off = align_up(off + (size_t)p.P * 16 * p.RC * sizeof(float), 256);
+    p.off_tg = off;
+    off = align_up(off + (size_t)16 * p.r_pad * 2, 256);
+    p.bytes = off;
+    return p;
+}
+
+PrefillPlan make_prefill_plan(int M, int N, int K, int r)
+{
+    PrefillPlan p{};
+    const int NB = (N + PANEL_N - 1) / PANEL_N;
+    const int KB = K / PANEL_K;
+    p.BM = M <= 64 ? 64 : 128;
+    p.BN = 256;
+    p.mt = (M + p.BM - 1) / p.BM;
+    p.nt = (NB * PANEL_N + p.BN - 1) / p.BN;
+    p.ksplit = 1;
+    while ((long long)p.mt * p.nt * p.ksplit < TARGET_WGS && KB / (2 * p.ksplit) >= 4 && p.ksplit < 16)
+        p.ksplit *= 2;
+    p.Mpad = p.mt * p.BM;
+    p.RC = r + 1;
+    p.r_pad = (r + 31) / 32 * 32;
+    p.pre_bm = 64;
+    p.pre_mt = (M + 63) / 64;
+    int ks = 1;
+    while ((long long)p.pre_mt * ks < TARGET_WGS && K / (2 * ks) >= 128 && ks < 64)
+        ks *= 2;
+    p.pre_kc = ((K + ks - 1) / ks + 31) / 32 * 32;
+    p.pre_ks = (K + p.pre_kc - 1) / p.pre_kc;
+
+    size_t off = 0;
+    p.off_err = off;
+    off += 256;
+    p.off_pre_cnt = off;
+    off = align_up(off + (size_t)p.pre_mt * 4, 256);
+    p.off_gemm_cnt = off;
+    off = align_up(off + (size_t)p.mt * p.nt * 4, 256);
+    p.off_pre_partial = off;
+    if (r > 0)
+        off = align_up(off + (size_t)p.pre_ks * p.pre_mt * 64 * p.RC * sizeof(float), 256);
+    p.off_tg = off;
+    if (r > 0)
+        off = align_up(off + (size_t)p.Mpad * p.r_pad * 2, 256);
+    p.off_gemm_partial = off;
+    if (p.ksplit > 1)
+        off = align_up(off + (size_t)p.ksplit * p.Mpad * p.nt * p.BN * sizeof(float), 256);
+    p.bytes = off;
+    return p;
+}
+
+int check_layer_args(const void* X, const void* packed, const void* A, const void* B,
+                     const void* Y, int M, int N, int K, int r, int G, int act,
+                     const void* ws, size_t ws_bytes, size_t need)
+{
+    if (M <= 0 || r < 0)
+        return W4EC_ERR_INVALID_ARG;
+    int rc = check_weight_shape(N, K, G);
+    if (rc != W4EC_OK)
+        return rc;
+    if (r > MAX_RANK)
+        return W4EC_ERR_UNSUPPORTED;
+    if (act != W4EC_FP16 && act != W4EC_BF16)
+        return W4EC_ERR_INVALID_ARG;
+    if (!X || !packed || !Y)
+        return W4EC_ERR_INVALID_ARG;
+    if (r > 0 && (!A || !B))
+        return W4EC_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(packed, 256))
+        return W4EC_ERR_INVALID_ARG;
+    if (r > 0 && (!aligned(A, 2) || !aligned(B, 2)))
+        return W4EC_ERR_INVALID_ARG;
+    if (X == Y || packed == Y || (r > 0 && (A == Y || B == Y)))
+        return W4EC_ERR_INVALID_ARG;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+        return W4EC_ERR_WORKSPACE;
+    return W4EC_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? W4EC_OK : W4EC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* w4ec_status_str(int status)
+{
+    switch (status) {
+    case W4EC_OK: return "W4EC_OK";
+    case W4EC_ERR_INVALID_ARG: return "W4EC_ERR_INVALID_ARG";
+    case W4EC_ERR_UNSUPPORTED: return "W4EC_ERR_UNSUPPORTED";
+    case W4EC_ERR_WORKSPACE: return "W4EC_ERR_WORKSPACE";
+    case W4EC_ERR_HIP: return "W4EC_ERR_HIP";
+    default: return "W4EC_UNKNOWN_STATUS";
+    }
+}
+
+size_t w4ec_packed_bytes(int N, int K, int group_size)
+{
+    if (check_weight_shape(N, K, group_size) != W4EC_OK)
+        return 0;
+    return blob_geom(N, K, group_size).bytes;
+}
+
+int w4ec_quantize_rtn(const float* W, int N, int K, int group_size, uint8_t* q_canon,
+                      uint16_t* scale, uint16_t* zero, void* stream)
+{
+    if (N <= 0 || K <= 0 || group_size <= 0 || K % 2 != 0 || group_size % 2 != 0 || K % group_size != 0)
+        return W4EC_ERR_INVALID_ARG;
+    if (!W || !q_canon || !scale || !zero)
+        return W4EC_ERR_INVALID_ARG;
+    if (!aligned(W, 4) || !aligned(scale, 2) || !aligned(zero, 2))
+        return W4EC_ERR_INVALID_ARG;
+    if (K / group_size > 65535 || N > 65535 * 64)
+        return W4EC_ERR_UNSUPPORTED;
+    if (N > 65535)
+        return W4EC_ERR_UNSUPPORTED;
+    return hip_status(launch_rtn_quantize(W, N, K, group_size, q_canon, scale, zero, (hipStream_t)stream));
+}
+
+int w4ec_pack(const uint8_t* q_canon, const uint16_t* scale, const uint16_t* zero,
+              int N, int K, int group_size, void* packed, void* stream)
+{
+    int rc = check_weight_shape(N, K, group_size);
+    if (rc != W4EC_OK)
+        return rc;
+    if (!q_canon || !scale || !zero || !packed)
+        return W4EC_ERR_INVALID_ARG;
+    if (!aligned(packed, 256) || !aligned(scale, 2) || !aligned(zero, 2))
+        return W4EC_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_pack(q_canon, scale, zero, N, K, group_size, packed, st);
+    if (e != hipSuccess)
+        return W4EC_ERR_HIP;
+    BlobHeader hdr;
+    e = hipMemcpyAsync(&hdr, packed, sizeof hdr, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return W4EC_ERR_HIP;
+    return hdr.bad_zero ? W4EC_ERR_INVALID_ARG : W4EC_OK;
+}
+
+int w4ec_unpack(const void* packed, int N, int K, int group_size, uint8_t* q_canon,
+                uint16_t* scale, uint16_t* zero, void* stream)
+{
+    int rc = check_weight_shape(N, K, group_size);
+    if (rc != W4EC_OK)
+        return rc;
+    if (!packed || !q_canon || !scale || !zero)
+        return W4EC_ERR_INVALID_ARG;
+    if (!aligned(packed, 256) || !aligned(scale, 2) || !aligned(zero, 2))
+        return W4EC_ERR_INVALID_ARG;
+    return hip_status(launch_unpack(packed, N, K, group_size, q_canon, scale, zero, (hipStream_t)stream));
+}
+
+size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size)
+{
+    if (M <= 0 || r < 0 || r > MAX_RANK || check_weight_shape(N, K, group_size) != W4EC_OK)
+        return 0;
+    size_t b = make_prefill_plan(M, N, K, r).bytes;
+    if (M <= DECODE_MAX_M) {
+        size_t d = make_decode_plan(M, N, K, r).bytes;
+        if (d > b)
+            b = d;
+    }
+    return b;
+}
+
+int w4ec_linear_decode(const void* X, const void* packed, const void* A, const void* B,
+                       const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                       int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream)
+{
+    if (M > DECODE_MAX_M)
+        return W4EC_ERR_UNSUPPORTED;
+    DecodePlan p{};
+    size_t need = 0;
+    if (M > 0 && r >= 0 && r <= MAX_RANK && check_weight_shape(N, K, group_size) == W4EC_OK) {
+        p = make_decode_plan(M, N, K, r);
+        need = r > 0 ? p.bytes : 0;
+    }
+    int rc = check_layer_args(X, packed, A, B, Y, M, N, K, r, group_size, act_dtype,
+                              workspace, workspace_bytes, need);
+    if (rc != W4EC_OK)
+        return rc;
+    if (w_g && !((uintptr_t)w_g % 2 == 0))
+        return W4EC_ERR_INVALID_ARG;
+    LayerArgs a{X, packed, r > 0 ? A : nullptr, r > 0 ? B : nullptr, r > 0 ? w_g : nullptr,
+                b_g, Y, M, N, K, r, group_size, act_dtype, (char*)workspace};
+    return hip_status(launch_decode(a, p, (hipStream_t)stream));
+}
+
+int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const void* B,
+                        const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                        int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    PrefillPlan p{};
+    size_t need = 0;
+    if (M > 0 && r >= 0 && r <= MAX_RANK && check_weight_shape(N, K, group_size) == W4EC_OK) {
+        p = make_prefill_plan(M, N, K, r);
+        need = (r > 0 || p.ksplit > 1) ? p.bytes : 0;
+    }
+    int rc = check_layer_args(X, packed, A, B, Y, M, N, K, r, group_size, act_dtype,
+                              workspace, workspace_bytes, need);
+    if (rc != W4EC_OK)
+        return rc;
+    if (w_g && !((uintptr_t)w_g % 2 == 0))
+        return W4EC_ERR_INVALID_ARG;
+    LayerArgs a{X, packed, r > 0 ? A : nullptr, r > 0 ? B : nullptr, r > 0 ? w_g : nullptr,
+                b_g, Y, M, N, K, r, group_size, act_dtype, (char*)workspace};
+    return hip_status(launch_prefill(a, p, (hipStream_t)stream));
+}
+
+}  // extern "C"

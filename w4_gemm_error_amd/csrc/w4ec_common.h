@@ -1,0 +1,284 @@
+// w4ec_common.h -- internal to libw4ec: device types, the packed blob layout,
+// int4 dequantization and MFMA wrappers for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4ec {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { ACT_F16 = 0, ACT_BF16 = 1 };
+
+// ------------------------------------------------------------ blob layout
+//
+// header (256 B) | codes | scale/zero
+//
+// codes: panels of 16 output columns x 128 input features, 1024 bytes each,
+// ordered [column block cb][k block kb].  Inside a panel, lane l (0..63) of
+// a wavefront owns bytes [16 l, 16 l + 16): four dwords, dword s (0..3)
+// holding the 8 codes of column 16 cb + (l & 15) at
+//   k = 128 kb + 32 s + 8 (l >> 4) + t,  t = 0..7.
+// That is exactly the B operand of v_mfma_f32_16x16x32_{f16,bf16} for four
+// consecutive 32-deep steps, so one 16-byte load per lane feeds 4 MFMAs.
+// Within a dword, code t sits in nibble (t even ? t/2 : 4 + t/2): masking
+// with 0x000F000F / 0x00F000F0 after shifts of 0 and 8 then yields the
+// pairs (t0,t1) (t2,t3) (t4,t5) (t6,t7) in the two halves of a register.
+//
+// scale/zero: for group gi and column n (padded to a multiple of 16),
+// one dword at index gi * Npad + n: fp16 scale in the low half, fp16 zero in
+// the high half.  Padded columns hold codes 0 and scale = zero = 0.
+constexpr int PANEL_K = 128;
+constexpr int PANEL_N = 16;
+constexpr int PANEL_BYTES = 1024;
+constexpr size_t HEADER_BYTES = 256;
+constexpr uint32_t BLOB_MAGIC = 0x43453457u;  // "W4EC"
+
+struct BlobHeader {
+    uint32_t magic;
+    int32_t N, K, G;
+    uint32_t bad_zero;   // set by the pack kernel when a zero point is not an integer in 0..15
+};
+
+__host__ __device__ inline int nibble_of(int t) { return (t & 1) ? 4 + (t >> 1) : (t >> 1); }
+
+struct BlobGeom {
+    int N, K, G, NB, KB, Npad, NG;
+    size_t codes_off, sz_off, bytes;
+};
+
+__host__ __device__ inline BlobGeom blob_geom(int N, int K, int G)
+{
+    BlobGeom g;
+    g.N = N; g.K = K; g.G = G;
+    g.NB = (N + PANEL_N - 1) / PANEL_N;
+    g.KB = K / PANEL_K;
+    g.Npad = g.NB * PANEL_N;
+    g.NG = K / G;
+    g.codes_off = HEADER_BYTES;
+    g.sz_off = g.codes_off + (size_t)g.NB * g.KB * PANEL_BYTES;
+    g.bytes = g.sz_off + (size_t)g.NG * g.Npad * 4;
+    return g;
+}
+
+// ------------------------------------------------------------ memory helpers
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Streamed once per call: ask for non-temporal (streaming) caching.
+__device__ inline u32x4 ld16_stream(const void* p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+template <int ACT> __device__ inline float act_to_f32(uint16_t v)
+{
+    if constexpr (ACT == ACT_F16) {
+        return (float)__builtin_bit_cast(_Float16, v);
+    } else {
+        return __uint_as_float((uint32_t)v << 16);
+    }
+}
+
+// float -> act bits, round to nearest even.
+template <int ACT> __device__ inline uint16_t f32_to_act(float f)
+{
+    if constexpr (ACT == ACT_F16) {
+        return __builtin_bit_cast(uint16_t, (_Float16)f);
+    } else {
+        __bf16 b = (__bf16)f;
+        return __builtin_bit_cast(uint16_t, b);
+    }
+}
+
+// ------------------------------------------------------------ MFMA
+
+template <int ACT> __device__ inline floatx4 mfma16x16x32(u32x4 a, u32x4 b, floatx4 c)
+{
+    if constexpr (ACT == ACT_F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+// ------------------------------------------------------------ dequant
+//
+// One dword of 8 codes (blob nibble order) -> 8 operand values in natural
+// k order, as four registers of two 16-bit values.
+//
+// fp16: (0x6400 | c) is the half 1024 + c, and (0x6400 | c << 4) is
+// 1024 + 16 c; both are exact.  Subtracting 1024 + z, or scaling by 1/16
+// and subtracting 64 + z, gives c - z exactly for an integer zero point z in
+// 0..15 (every intermediate is an integer or a sixteenth well inside the
+// half's 11-bit significand).
+struct DqF16 {
+    half2_t off_lo;  // -(1024 + z)
+    half2_t off_hi;  // -(64 + z)
+};
+
+__device__ inline DqF16 dq_f16_consts(float z)
+{
+    DqF16 c;
+    _Float16 a = (_Float16)(-(1024.0f + z));
+    _Float16 b = (_Float16)(-(64.0f + z));
+    c.off_lo = (half2_t){a, a};
+    c.off_hi = (half2_t){b, b};
+    return c;
+}
+
+__device__ inline u32x4 dequant_f16(uint32_t w, const DqF16& c)
+{
+    const uint32_t MAGIC = 0x64006400u;
+    const half2_t sixteenth = (half2_t){(_Float16)0.0625f, (_Float16)0.0625f};
+    uint32_t w8 = w >> 8;
+    half2_t p0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | MAGIC);
+    half2_t p1 = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | MAGIC);
+    half2_t p2 = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | MAGIC);
+    half2_t p3 = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | MAGIC);
+    p0 = p0 + c.off_lo;
+    p1 = __builtin_elementwise_fma(p1, sixteenth, c.off_hi);
+    p2 = p2 + c.off_lo;
+    p3 = __builtin_elementwise_fma(p3, sixteenth, c.off_hi);
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, p0);
+    r.y = __builtin_bit_cast(uint32_t, p1);
+    r.z = __builtin_bit_cast(uint32_t, p2);
+    r.w = __builtin_bit_cast(uint32_t, p3);
+    return r;
+}
+
+// Same, multiplied by the scale s (rounded once, to fp16).  Each element
+// goes through a scalar first: clang reads the wrong lane when
+// __builtin_bit_cast is applied directly to an ext-vector element access.
+__device__ inline half2_t h2_of(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ inline uint32_t u32_of(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ inline u32x4 dequant_f16_scaled(uint32_t w, const DqF16& c, half2_t s2)
+{
+    const u32x4 q = dequant_f16(w, c);
+    const uint32_t q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
+    u32x4 r;
+    r.x = u32_of(h2_of(q0) * s2);
+    r.y = u32_of(h2_of(q1) * s2);
+    r.z = u32_of(h2_of(q2) * s2);
+    r.w = u32_of(h2_of(q3) * s2);
+    return r;
+}
+
+// bf16: build 2^23 + c as a float (0x4B000000 | c), subtract 2^23 + z
+// exactly, and keep the upper half of the float -- exact for the small
+// integer c - z (and for (c - z) * s the bf16 conversion rounds to nearest
+// even).
+__device__ inline uint32_t bf16_pair_from_f32(float lo, float hi)
+{
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ inline float nib_f32(uint32_t w, int p, float off)
+{
+    return __uint_as_float(0x4B000000u | ((w >> (4 * p)) & 0xFu)) + off;
+}
+
+// off = -(2^23 + z)
+__device__ inline u32x4 dequant_bf16(uint32_t w, float off)
+{
+    u32x4 r;
+    r.x = bf16_pair_from_f32(nib_f32(w, 0, off), nib_f32(w, 4, off));
+    r.y = bf16_pair_from_f32(nib_f32(w, 1, off), nib_f32(w, 5, off));
+    r.z = bf16_pair_from_f32(nib_f32(w, 2, off), nib_f32(w, 6, off));
+    r.w = bf16_pair_from_f32(nib_f32(w, 3, off), nib_f32(w, 7, off));
+    return r;
+}
+
+__device__ inline u32x4 dequant_bf16_scaled(uint32_t w, float off, float s)
+{
+    u32x4 r;
+    r.x = bf16_pair_from_f32(nib_f32(w, 0, off) * s, nib_f32(w, 4, off) * s);
+    r.y = bf16_pair_from_f32(nib_f32(w, 1, off) * s, nib_f32(w, 5, off) * s);
+    r.z = bf16_pair_from_f32(nib_f32(w, 2, off) * s, nib_f32(w, 6, off) * s);
+    r.w = bf16_pair_from_f32(nib_f32(w, 3, off) * s, nib_f32(w, 7, off) * s);
+    return r;
+}
+
+// ------------------------------------------------------------ gate
+
+__device__ inline float sigmoid_f32(float l)
+{
+    if (l >= 0.0f)
+        return 1.0f / (1.0f + expf(-l));
+    float e = expf(l);
+    return e / (1.0f + e);
+}
+
+// ------------------------------------------------------------ cross-workgroup hand-over
+//
+// Agent-scope release/acquire: on gfx950 these write back / invalidate the
+// per-XCD L2 as needed, so data written by a workgroup on one XCD is seen by
+// a workgroup on another.
+
+__device__ inline void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ inline void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ inline uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint32_t atomic_load_acquire(const uint32_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void atomic_store_release(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void atomic_store_relaxed(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A bounded wait: every waiter gives up after roughly a second so that a
+// broken hand-over can never hang the GPU; it then records the failure.
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
+
+// ------------------------------------------------------------ launch plans
+// (shared by the host dispatch and the workspace sizing)
+
+struct DecodePlan {
+    int P;          // EC workgroups (K slices) -- 0 when r == 0
+    int KS;         // k per EC slice
+    int RC;         // partial columns: r (low rank) + 1 (gate logit)
+    int r_pad;      // r rounded up to 32
+    int CB;         // column blocks per main workgroup
+    int n_main;     // main workgroups
+    size_t off_flags, off_partial, off_tg, bytes;
+};
+
+struct PrefillPlan {
+    int BM;         // tokens per GEMM tile (64 or 128)
+    int BN;         // columns per GEMM tile (256)
+    int mt, nt;     // tiles along M and N
+    int ksplit;     // GEMM split over K
+    int pre_bm;     // tokens per prepass workgroup (64)
+    int pre_mt;     // prepass tiles along M
+    int pre_ks;     // prepass split over K
+    int pre_kc;     // k per prepass split (multiple of 32)
+    int RC, r_pad, Mpad;
+    size_t off_pre_cnt, off_gemm_cnt, off_err, off_pre_partial, off_tg, off_gemm_partial, bytes;
+};
+
+}  // namespace w4ec

@@ -1,0 +1,34 @@
+// w4ec_launch.h -- internal host-side launchers (one per kernel family).
+// The C ABI in api.cpp validates arguments, builds a plan and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4ec_common.h"
+
+namespace w4ec {
+
+hipError_t launch_rtn_quantize(const float* W, int N, int K, int G, uint8_t* qc,
+                               uint16_t* scale, uint16_t* zero, hipStream_t st);
+hipError_t launch_pack(const uint8_t* qc, const uint16_t* scale, const uint16_t* zero,
+                       int N, int K, int G, void* packed, hipStream_t st);
+hipError_t launch_unpack(const void* packed, int N, int K, int G, uint8_t* qc,
+                         uint16_t* scale, uint16_t* zero, hipStream_t st);
+
+struct LayerArgs {
+    const void* X;
+    const void* packed;
+    const void* A;
+    const void* B;
+    const void* w_g;
+    float b_g;
+    void* Y;
+    int M, N, K, r, G, act;
+    char* ws;
+};
+
+hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
+hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
+
+}  // namespace w4ec
