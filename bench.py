@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work on the host")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--rank", type=int, default=None,
+                    help="EC rank override (0 = the plain W4 layer, for the EC overhead ratio)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,7 +148,7 @@ def main():
     w4.lib()   # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     cfg_id, M, phase = WORKLOADS[args.workload]
-    d = synth.make_layer(cfg_id, M, seed=args.seed)
+    d = synth.make_layer(cfg_id, M, seed=args.seed, r=args.rank)
     N, K, r, G, act = d["N"], d["K"], d["r"], d["group_size"], d["act"]
     tdt = torch.float16 if act == "fp16" else torch.bfloat16
 
@@ -158,11 +160,19 @@ def main():
     q, s, z = w4.w4ec_quantize_rtn(Wt, G)
     packed0 = w4.w4ec_pack(q, s, z, N, K, G)
     del Wt, q, s, z
-    A0, B0, wg0 = dev_act(d["A"]), dev_act(d["B"]), dev_act(d["w_g"])
-    nbytes = layer_bytes(M, N, K, r, G)
-    weight_bytes = packed0.numel() + (A0.numel() + B0.numel() + wg0.numel()) * 2
+    if r > 0:
+        A0, B0, wg0 = dev_act(d["A"]), dev_act(d["B"]), dev_act(d["w_g"])
+        ec_elems = A0.numel() + B0.numel() + wg0.numel()
+    else:
+        A0 = B0 = wg0 = None
+        ec_elems = 0
+    nbytes = layer_bytes(M, N, K, r, G, has_gate=r > 0)
+    weight_bytes = packed0.numel() + ec_elems * 2
     R = max(1, -(-2 * MALL_BYTES // weight_bytes))
-    copies = [(packed0, A0, B0, wg0)] + [(packed0.clone(), A0.clone(), B0.clone(), wg0.clone())
+    def clone(t):
+        return None if t is None else t.clone()
+
+    copies = [(packed0, A0, B0, wg0)] + [(packed0.clone(), clone(A0), clone(B0), clone(wg0))
                                          for _ in range(R - 1)]
     X = dev_act(d["X"])
     Y = torch.empty((M, N), dtype=tdt, device=dev)

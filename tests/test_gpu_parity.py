@@ -179,3 +179,29 @@ def test_full_size_parity(cfg, M, phase, rows):
     Ysub = Y if rows is None else Y[rows]
     worst = assert_close(Ysub, ref, d["act"], f"cfg{cfg} M={M}")
     _print(f"  worst err/tol {worst:.3f}")
+
+
+def test_shared_workspace_across_shapes_and_phases():
+    """One workspace serves interleaved decode / prefill calls of different
+    ranks and shapes: every call's counters and flags must be back at zero."""
+    _print("shared workspace")
+    t = torch()
+    layers = []
+    for (M, N, K, r, G) in [(1, 528, 512, 64, 512), (16, 512, 1024, 128, 128), (40, 512, 512, 8, 512),
+                            (3, 256, 768, 256, 256), (200, 784, 1024, 64, 128)]:
+        d = small_layer("fp16", M, N, K, r, G, seed=M + r)
+        _, _, _, packed = gpu_quantize(d)
+        layers.append((d, packed))
+    need = max(w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], d["r"], d["group_size"]) for d, _ in layers)
+    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    ref = {}
+    for i, (d, packed) in enumerate(layers):
+        for phase in ("decode", "prefill"):
+            if phase == "decode" and d["M"] > 16:
+                continue
+            ref[(i, phase)] = gpu_layer(d, packed, phase)          # own fresh workspace
+    for rep in range(3):
+        for (i, phase), y in ref.items():
+            d, packed = layers[i]
+            got = gpu_layer(d, packed, phase, workspace=ws)
+            assert np.array_equal(got, y), (i, phase, rep)

@@ -36,23 +36,56 @@ int check_weight_shape(int N, int K, int G)
     return W4EC_OK;
 }
 
+// Workspace layout, shared by both entry points so that one workspace can
+// serve decode and prefill calls in any order:
+//   [0, CTRL_BYTES)   control words that every call returns to zero --
+//                     decode flags, prefill hand-over counters, the decode
+//                     replica slots; never overwritten by data
+//   [CTRL_BYTES, ...) per-call data (partial sums, gated activations), fully
+//                     written before it is read within a call
+constexpr size_t CTRL_BYTES = 1 << 20;
+constexpr size_t OFF_DEC_FLAGS = 0;           // 256 B
+constexpr size_t OFF_PRE_CNT = 256;           // prepass counters, <= 256 of them
+constexpr size_t OFF_GEMM_CNT = 256 + 1024;   // split-K tile counters, <= 256 of them
+constexpr size_t OFF_DEC_REP = 64 << 10;      // DEC_NREP decode slots of DEC_REP_CTRL_STRIDE bytes
+static_assert(OFF_DEC_REP + DEC_NREP * DEC_REP_CTRL_STRIDE <= CTRL_BYTES, "control region");
+
 DecodePlan make_decode_plan(int M, int N, int K, int r)
 {
     DecodePlan p{};
     const int NB = (N + PANEL_N - 1) / PANEL_N;
-    p.KS = 256;
-    p.P = r > 0 ? (K + p.KS - 1) / p.KS : 0;
     p.RC = r + 1;
     p.r_pad = (r + 31) / 32 * 32;
-    p.CB = M <= 4 ? 1 : 2;
+    if (r > 0) {
+        // each EC workgroup loads its whole slice in one trip: KS x r <= 16384
+        // elements (8 16-byte chunks per thread), KS a multiple of 64, <= 256;
+        // and its transposed slice in LDS ((r + 1) rounded to 16 rows of KS + 8
+        // halves) stays within 40 KB, so that 4 workgroups fit on a CU
+        const int cols = (r + 1 + 15) / 16 * 16;
+        int ks = 256;
+        while (ks > 64 && ((long)ks * r > 16384 || (long)cols * (ks + 8) * 2 > 40960))
+            ks -= 64;
+        p.KS = ks;
+        p.P = (K + p.KS - 1) / p.KS;
+    }
+    p.xlds = decode_use_xlds(M, K);
+    p.CB = (M <= 4 || p.xlds) ? 1 : 2;
     p.n_main = (NB + p.CB - 1) / p.CB;
-    size_t off = 0;
-    p.off_flags = off;
-    off += 256;
+    p.single = M <= 4 ? 1 : 0;
+    p.stage_first = r > 0 ? 1 : 0;
+    p.off_flags = OFF_DEC_FLAGS;
+    p.off_rep_ctrl = OFF_DEC_REP;
+    size_t off = CTRL_BYTES;
     p.off_partial = off;
-    off = align_up(off + (size_t)p.P * 16 * p.RC * sizeof(float), 256);
-    p.off_tg = off;
-    off = align_up(off + (size_t)16 * p.r_pad * 2, 256);
+    if (r > 0 && !p.single)
+        off = align_up(off + (size_t)p.P * 16 * p.RC * sizeof(float), 4096);
+    p.off_rep_data = off;
+    if (r > 0) {
+        const size_t ne2 = ((size_t)M * p.RC + 1) / 2;    // float pairs per partial
+        const size_t per = p.single ? (size_t)p.P * ne2 * 8 : (size_t)M * p.r_pad * 2;
+        p.rep_data_stride = align_up(per, 4096);
+        off += (size_t)DEC_NREP * p.rep_data_stride;
+    }
     p.bytes = off;
     return p;
 }
@@ -70,26 +103,22 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
     while ((long long)p.mt * p.nt * p.ksplit < TARGET_WGS && KB / (2 * p.ksplit) >= 4 && p.ksplit < 16)
         p.ksplit *= 2;
     p.Mpad = p.mt * p.BM;
-    p.RC = r + 1;
     p.r_pad = (r + 31) / 32 * 32;
-    p.pre_bm = 64;
     p.pre_mt = (M + 63) / 64;
     int ks = 1;
-    while ((long long)p.pre_mt * ks < TARGET_WGS && K / (2 * ks) >= 128 && ks < 64)
+    while ((long long)p.pre_mt * ks < TARGET_WGS && K / (2 * ks) >= 256 && ks < 8)
         ks *= 2;
-    p.pre_kc = ((K + ks - 1) / ks + 31) / 32 * 32;
+    p.pre_kc = ((K + ks - 1) / ks + 63) / 64 * 64;
     p.pre_ks = (K + p.pre_kc - 1) / p.pre_kc;
+    // counters exist only for split work, which is chosen only while the
+    // workgroup count is below TARGET_WGS: at most 256 of each
+    p.off_pre_cnt = OFF_PRE_CNT;
+    p.off_gemm_cnt = OFF_GEMM_CNT;
 
-    size_t off = 0;
-    p.off_err = off;
-    off += 256;
-    p.off_pre_cnt = off;
-    off = align_up(off + (size_t)p.pre_mt * 4, 256);
-    p.off_gemm_cnt = off;
-    off = align_up(off + (size_t)p.mt * p.nt * 4, 256);
+    size_t off = CTRL_BYTES;
     p.off_pre_partial = off;
-    if (r > 0)
-        off = align_up(off + (size_t)p.pre_ks * p.pre_mt * 64 * p.RC * sizeof(float), 256);
+    if (r > 0 && p.pre_ks > 1)
+        off = align_up(off + (size_t)p.pre_mt * p.pre_ks * 4 * 17 * 64 * 16, 256);
     p.off_tg = off;
     if (r > 0)
         off = align_up(off + (size_t)p.Mpad * p.r_pad * 2, 256);

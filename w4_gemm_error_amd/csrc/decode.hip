@@ -2,35 +2,51 @@
 //
 // SPEAR (gist.science technical summary, section 2.2A): in the decode phase
 // the layer is memory bound, and the EC is folded into the low-bit GEMM's
-// epilogue so that no second launch sits on the critical path.  Here one
-// grid does all of it:
+// epilogue so that no second launch sits on the critical path.  One grid
+// does all of it:
 //
-//  * workgroups [0, P): "EC" role.  Each reads one K-slice of X, A and w_g
-//    and writes partial sums of T = X A and of the gate logit X . w_g.  The
-//    last of them to finish (arrival counter) adds the P partials in a fixed
-//    order, applies the sigmoid gate and stores T_g = g * T in the
-//    activation format, then raises a ready flag.
+//  * workgroups [0, P): "EC" role.  Each loads one K-slice of X, A and w_g
+//    in a single trip, forms the partial sums of T = X A and of the gate
+//    logit X . w_g with MFMAs, and hands them over (below).  They have the
+//    lowest ids, so they are dispatched before any main workgroup.
 //  * workgroups [P, P + n_main): "main" role.  Each owns CB blocks of 16
-//    output columns; its four wavefronts split K.  A wavefront streams its
-//    share of the packed weights with one 16-byte load per lane per panel
-//    (16 columns x 128 k), turns the codes into (q - z) with a few integer
-//    and packed-half operations, and accumulates X Wd^T with
-//    v_mfma_f32_16x16x32 (X rows are the 16 MFMA rows; unused rows are zero).
-//    Per-group sums are scaled by s when the group changes.  After an LDS
-//    reduction over the wavefronts, the epilogue waits for the ready flag
-//    and extends the reduction by the r rank terms: acc += T_g B, again as
-//    MFMAs, then rounds and stores Y.
+//    output columns; its four wavefronts split K.  A wavefront keeps a ring
+//    of in-flight 16-byte panel loads (16 columns x 128 k of packed codes per
+//    load), turns the codes into (q - z) with a few integer and packed-half
+//    operations and accumulates X Wd^T with v_mfma_f32_16x16x32 (the tokens
+//    are the 16 MFMA rows); sums are scaled by s whenever the group changes.
+//    After an LDS reduction over the wavefronts, the epilogue extends the
+//    reduction by the r rank terms, acc += T_g B, as MFMAs, then rounds and
+//    stores Y.
 //
-// The EC workgroups have the lowest ids, so they are dispatched before any
-// main workgroup can occupy the GPU while waiting; the wait is bounded.
-// The last main workgroup returns the counters to zero.
+// Hand-over of the gated rank-r activations T_g = g * T.  While the weight
+// stream saturates HBM, every dependent trip to memory costs microseconds,
+// and hundreds of workgroups polling or reading one spot pile onto one
+// memory channel; so the data is published in DEC_NREP replica slots spread
+// over the channels, main workgroup i using slot i mod DEC_NREP:
+//  * few tokens ("single" hand-over): each EC workgroup writes its partial
+//    sums into every slot and bumps each slot's arrival count; a main
+//    workgroup waits for P arrivals in its slot and adds the P partials in a
+//    fixed order itself;
+//  * more tokens: the last EC workgroup to arrive adds the partials, applies
+//    the gate and writes T_g into every slot, then raises each slot's flag.
+// The last reader of a slot returns its control words to zero.  All waits
+// are bounded.  Hand-over data moves with device-coherent accesses (see
+// w4ec_common.h), so no cache-wide write-back or invalidate is needed.
+#include <type_traits>
+
+#include "ec_tile.h"
 #include "w4ec_common.h"
 #include "w4ec_launch.h"
 
 namespace w4ec {
 
 constexpr int DEC_THREADS = 256;
-constexpr int EC_KS_MAX = 256;
+constexpr int DEC_EC_MAXI = 5;     // column blocks per wavefront in the EC role (17 / 4)
+constexpr int DEC_XLDS_CHUNKS = 8; // 16-byte chunks of staged activations per thread
+constexpr int DEC_EC_KSMAX = 256;  // k per EC slice (at most)
+constexpr int DEC_EC_CHUNKS = 8;   // 16-byte chunks of A per thread: KS * r / 8 / 256
+constexpr size_t DEC_SUM_STAGE_BYTES = 16 * 1024;  // LDS staging of hand-over partial sums
 
 struct DecodeKArgs {
     const uint16_t* X;
@@ -43,231 +59,511 @@ struct DecodeKArgs {
     uint16_t* Y;
     int M, N, K, r, r_pad, G, NB, KB, Npad;
     int P, KS, RC, n_main;
-    uint32_t* flags;   // [0] EC arrivals, [1] ready, [2] main done, [3] wait timed out
-    float* partial;    // [P][16][RC]
-    uint16_t* tg;      // [16][r_pad], activation format
+    int single;          // 1: per-slot partial sums; 0: last EC workgroup reduces
+    int stage_first;     // main workgroups stage X before issuing weight loads
+    uint32_t* flags;     // [0] EC arrivals (two-level), [2] a wait timed out
+    float* partial;      // two-level: [P][16][RC]
+    uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [0] arrivals / ready, [1] readers done
+    uint8_t* rep_data;   // DEC_NREP slots of rep_data_stride bytes
+    size_t rep_data_stride;
 };
 
-template <int ACT>
-__device__ void decode_ec_role(const DecodeKArgs& a, float* smem)
+__device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
 {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int b = blockIdx.x;
-    const int M = a.M;
-    const int k0 = b * a.KS;
-    const int len = min(a.KS, a.K - k0);
-    float* xs = smem;                        // [16][EC_KS_MAX]
-    float* redT = smem + 16 * EC_KS_MAX;     // [4][16][64]
-    float* gsum = redT + 4 * 16 * 64;        // [4][16]
-    float* gsh = gsum + 64;                  // [16]
-
-    for (int idx = tid; idx < M * len; idx += DEC_THREADS) {
-        int m = idx / len, kk = idx - m * len;
-        xs[m * EC_KS_MAX + kk] = act_to_f32<ACT>(a.X[(size_t)m * a.K + k0 + kk]);
-    }
-    __syncthreads();
-
-    // gate logit partial: thread t takes k0 + t
-    {
-        float wv = 0.0f;
-        if (a.w_g && tid < len)
-            wv = act_to_f32<ACT>(a.w_g[k0 + tid]);
-        for (int m = 0; m < M; ++m) {
-            float v = (tid < len) ? xs[m * EC_KS_MAX + tid] * wv : 0.0f;
-            for (int off = 32; off > 0; off >>= 1)
-                v += __shfl_xor(v, off);
-            if (lane == 0)
-                gsum[wave * 16 + m] = v;
-        }
-    }
-
-    // T partial: lane = column, wavefront = k phase (k0 + wave + 4i)
-    for (int c0 = 0; c0 < a.r; c0 += 64) {
-        const int c = c0 + lane;
-        float acc[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-            acc[m] = 0.0f;
-        if (c < a.r) {
-            for (int kk = wave; kk < len; kk += 4) {
-                float av = act_to_f32<ACT>(a.A[(size_t)(k0 + kk) * a.r + c]);
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (m < M)
-                        acc[m] += xs[m * EC_KS_MAX + kk] * av;
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-            redT[(wave * 16 + m) * 64 + lane] = acc[m];
-        __syncthreads();
-        float* part = a.partial + (size_t)b * 16 * a.RC;
-        for (int idx = tid; idx < M * 64; idx += DEC_THREADS) {
-            int m = idx >> 6, cl = idx & 63;
-            if (c0 + cl < a.r) {
-                float s = redT[(0 * 16 + m) * 64 + cl] + redT[(1 * 16 + m) * 64 + cl] +
-                          redT[(2 * 16 + m) * 64 + cl] + redT[(3 * 16 + m) * 64 + cl];
-                part[m * a.RC + c0 + cl] = s;
-            }
-        }
-        __syncthreads();
-    }
-    if (tid < M) {
-        float s = gsum[0 * 16 + tid] + gsum[1 * 16 + tid] + gsum[2 * 16 + tid] + gsum[3 * 16 + tid];
-        a.partial[(size_t)b * 16 * a.RC + tid * a.RC + a.r] = s;
-    }
-
-    // hand over: the last EC workgroup reduces all slices
-    fence_release();
-    __syncthreads();
-    __shared__ uint32_t s_old;
-    if (tid == 0)
-        s_old = atomic_add_acq_rel(&a.flags[0], 1u);
-    __syncthreads();
-    if (s_old != (uint32_t)(a.P - 1))
-        return;
-    fence_acquire();
-    if (tid < 16) {
-        float g = 0.0f;
-        if (tid < M) {
-            float l = 0.0f;
-            for (int p = 0; p < a.P; ++p)
-                l += a.partial[((size_t)p * 16 + tid) * a.RC + a.r];
-            g = sigmoid_f32(l + a.b_g);
-        }
-        gsh[tid] = g;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 16 * a.r_pad; idx += DEC_THREADS) {
-        int m = idx / a.r_pad, j = idx - m * a.r_pad;
-        float v = 0.0f;
-        if (m < M && j < a.r) {
-            float t = 0.0f;
-            for (int p = 0; p < a.P; ++p)
-                t += a.partial[((size_t)p * 16 + m) * a.RC + j];
-            v = gsh[m] * t;
-        }
-        a.tg[idx] = f32_to_act<ACT>(v);
-    }
-    fence_release();
-    __syncthreads();
-    if (tid == 0)
-        atomic_store_release(&a.flags[1], 1u);
+    return reinterpret_cast<uint32_t*>(a.rep_ctrl + (size_t)slot * DEC_REP_CTRL_STRIDE) + i;
 }
 
-template <int ACT, int CB, int U>
-__device__ void decode_main_role(const DecodeKArgs& a, float* smem)
+// EC role: every global load of the slice (A, w_g, X) is issued before any
+// is used; the slice (KS x r <= 16384 elements, KS <= 256) is transposed
+// into LDS, then each wavefront runs the MFMAs for its column blocks
+// (cb = w, w + 4, ...).
+template <int ACT>
+__device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 {
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = tid >> 6;
-    const int cb0 = (blockIdx.x - a.P) * CB;
+    const int p = blockIdx.x;
+    const int koff = 8 * (l >> 4);
+    const int r = a.r;
     const int M = a.M;
+    const int kbeg = p * a.KS;
+    const int len = min(a.KS, a.K - kbeg);          // multiple of 64
+    const int xrow = min(l & 15, M - 1);
+    const int CBE = ec_col_blocks(r);
+    const int cols = CBE * 16;
+    const int S = len + 8;                           // LDS row stride in halves (16-byte aligned rows)
+    uint16_t* at = reinterpret_cast<uint16_t*>(smem);
+    const bool vec = (r & 7) == 0;
+    const int cpr = r >> 3;
+    const int nch = len * cpr;
+    // The main workgroups sharing this CU wait for these results: give the
+    // EC wavefronts the first pick of the CU's issue slots.
+    __builtin_amdgcn_s_setprio(3);
+
+    // 1. all loads in flight at once
+    u32x4 xf[DEC_EC_KSMAX / 32];
+    const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + koff;
+#pragma unroll
+    for (int s = 0; s < DEC_EC_KSMAX / 32; ++s)
+        if (32 * s < len)
+            xf[s] = ld16(xp + 32 * s);
+    u32x4 ach[DEC_EC_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < DEC_EC_CHUNKS; ++i) {
+        const int ch = tid + DEC_THREADS * i;
+        if (vec && ch < nch) {
+            const int kk = ch / cpr, cc = (ch % cpr) * 8;   // a row's chunks are adjacent: coalesced
+            ach[i] = ld16(a.A + (size_t)(kbeg + kk) * r + cc);
+        }
+    }
+    const uint16_t gv = (a.w_g && tid < len) ? a.w_g[kbeg + tid] : (uint16_t)0;
+
+    // 2. [A | w_g] slice, transposed: at[c][k]
+    for (int idx = tid; idx < (cols - r) * len; idx += DEC_THREADS) {
+        const int c = r + idx / len, kk = idx % len;
+        if (c > r || !a.w_g)
+            at[c * S + kk] = 0;
+    }
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < DEC_EC_CHUNKS; ++i) {
+            const int ch = tid + DEC_THREADS * i;
+            if (ch < nch) {
+                const int kk = ch / cpr, cc = (ch % cpr) * 8;   // a row's chunks are adjacent: coalesced
+                const u32x4 v = ach[i];
+                const uint32_t q0 = v.x, q1 = v.y, q2 = v.z, q3 = v.w;
+                uint16_t* dst = at + cc * S + kk;
+                dst[0 * S] = (uint16_t)(q0 & 0xFFFF);
+                dst[1 * S] = (uint16_t)(q0 >> 16);
+                dst[2 * S] = (uint16_t)(q1 & 0xFFFF);
+                dst[3 * S] = (uint16_t)(q1 >> 16);
+                dst[4 * S] = (uint16_t)(q2 & 0xFFFF);
+                dst[5 * S] = (uint16_t)(q2 >> 16);
+                dst[6 * S] = (uint16_t)(q3 & 0xFFFF);
+                dst[7 * S] = (uint16_t)(q3 >> 16);
+            }
+        }
+    } else {
+        for (int idx = tid; idx < len * r; idx += DEC_THREADS) {
+            const int kk = idx / r, c = idx - kk * r;
+            at[c * S + kk] = a.A[(size_t)(kbeg + kk) * r + c];
+        }
+    }
+    if (a.w_g && tid < len)
+        at[r * S + tid] = gv;
+    __syncthreads();
+
+    // 3. MFMAs over the slice
+    floatx4 acc[DEC_EC_MAXI];
+#pragma unroll
+    for (int i = 0; i < DEC_EC_MAXI; ++i) {
+        acc[i] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        const int cb = w + 4 * i;
+        if (cb < CBE) {
+            const uint16_t* bp = at + (cb * 16 + (l & 15)) * S + koff;
+#pragma unroll
+            for (int s = 0; s < DEC_EC_KSMAX / 32; ++s)
+                if (32 * s < len)
+                    acc[i] = mfma16x16x32<ACT>(xf[s], *reinterpret_cast<const u32x4*>(bp + 32 * s), acc[i]);
+        }
+    }
+    const int nrep = min(DEC_NREP, a.n_main);       // slots that have readers
+
+    if (a.single) {
+        // 4a. this slice's partial sums -> LDS [M][RC] -> every replica slot
+        __syncthreads();                             // all MFMAs have read the slice
+        float* part = reinterpret_cast<float*>(smem);
+#pragma unroll
+        for (int i = 0; i < DEC_EC_MAXI; ++i) {
+            const int c = (w + 4 * i) * 16 + (l & 15);
+            if (w + 4 * i < CBE && c < a.RC) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 4 * (l >> 4) + v;
+                    if (m < M)
+                        part[m * a.RC + c] = acc[i][v];
+                }
+            }
+        }
+        const int ne = M * a.RC;
+        const int ne2 = (ne + 1) >> 1;               // float pairs per partial (padded)
+        if (tid == 0 && (ne & 1))
+            part[ne] = 0.0f;
+        __syncthreads();
+        const uint64_t* part2 = reinterpret_cast<const uint64_t*>(part);
+        for (int e = tid; e < nrep * ne2; e += DEC_THREADS) {
+            const int slot = e / ne2, i = e - slot * ne2;
+            uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride) +
+                            (size_t)p * ne2 + i;
+            __hip_atomic_store(dst, part2[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_all_mem();
+        __syncthreads();
+        if (tid < nrep)
+            atomic_add_dev(rep_word(a, tid, 0), 1u);
+        return;
+    }
+
+    // 4b. partial sums -> [P][16][RC]; the last EC workgroup reduces them
+    float* part = a.partial + (size_t)p * 16 * a.RC;
+#pragma unroll
+    for (int i = 0; i < DEC_EC_MAXI; ++i) {
+        const int c = (w + 4 * i) * 16 + (l & 15);
+        if (w + 4 * i < CBE && c < a.RC) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = 4 * (l >> 4) + v;
+                if (m < M)
+                    st4_dev(part + m * a.RC + c, acc[i][v]);
+            }
+        }
+    }
+    wait_all_mem();
+    __syncthreads();
+    __shared__ uint32_t s_old;
+    if (tid == 0)
+        s_old = atomic_add_dev(&a.flags[0], 1u);
+    __syncthreads();
+    if (s_old != (uint32_t)(a.P - 1))
+        return;
+    if (tid == 0)
+        atomic_store_dev(&a.flags[0], 0u);
+    float* tsum = reinterpret_cast<float*>(smem);          // [M][RC]
+    float* gl = tsum + 16 * a.RC;                           // [16]
+    uint16_t* tg = reinterpret_cast<uint16_t*>(gl + 16);    // [M][r_pad]
+    const int ne = M * a.RC;
+    for (int e = tid; e < ne; e += DEC_THREADS) {
+        const float* src = a.partial + e;
+        float t = 0.0f;
+        for (int q = 0; q < a.P; ++q)
+            t += ld4_dev(src + (size_t)q * 16 * a.RC);
+        tsum[e] = t;
+    }
+    __syncthreads();
+    if (tid < M)
+        gl[tid] = sigmoid_f32(tsum[tid * a.RC + r] + a.b_g);
+    __syncthreads();
+    const int nt = M * a.r_pad;
+    for (int e = tid; e < nt; e += DEC_THREADS) {
+        const int m = e / a.r_pad, c = e - m * a.r_pad;
+        tg[e] = f32_to_act<ACT>(c < r ? gl[m] * tsum[m * a.RC + c] : 0.0f);
+    }
+    __syncthreads();
+    const int n8 = nt / 4;                                  // 8-byte words of T_g
+    const uint64_t* tg8 = reinterpret_cast<const uint64_t*>(tg);
+    for (int e = tid; e < nrep * n8; e += DEC_THREADS) {
+        const int slot = e / n8, i = e - slot * n8;
+        uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride);
+        __hip_atomic_store(dst + i, tg8[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_all_mem();
+    __syncthreads();
+    if (tid < nrep)
+        atomic_store_dev(rep_word(a, tid, 0), 1u);
+}
+
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
+__device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
+{
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform
+    const int mb = blockIdx.x - a.P;
+    const int cb0 = mb * CB;
+    const int M = a.M;
+    const int K = a.K;
     const int KB = a.KB;
 
-    // this wavefront's panels along K
     const int per = KB >> 2, rem = KB & 3;
-    const int kbeg = w * per + min(w, rem);
     const int kcnt = per + (w < rem ? 1 : 0);
+    // a wavefront without panels (K < 512) still issues its (clamped) loads,
+    // from panel 0, and multiplies them by zero
+    const int kbeg = kcnt > 0 ? w * per + min(w, rem) : 0;
+    const int klast = max(kcnt - 1, 0);
 
     const int row = l & 15;
     const int koff = 8 * (l >> 4);
     const bool xrow = row < M;
-    const uint16_t* xp = a.X + (size_t)(xrow ? row : 0) * a.K + koff;
+
+    int n_l[CB];
+    const uint8_t* wp[CB];      // this lane's 16 bytes of panel (column block, kbeg)
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        const int cb = min(cb0 + j, a.NB - 1);      // a block past the end re-reads the last one (never stored)
+        n_l[j] = (cb0 + j) * PANEL_N + (l & 15);
+        wp[j] = a.codes + ((size_t)cb * KB + kbeg) * PANEL_BYTES + l * 16;
+    }
+    const int nsteps = a.r_pad >> 5;
+    const uint32_t* szp[CB];    // scale/zero of column n_l[j] (group of panel kbeg)
+    const int ppg = a.G / PANEL_K;                   // panels per group
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+        const int n = min(n_l[j], a.Npad - 1);
+        szp[j] = a.sz + (size_t)((kbeg * PANEL_K) / a.G) * a.Npad + n;
+    }
+
+    // Loads retire in issue order, so everything consumed before the first
+    // panel (scale/zero, the activations staged in LDS) is issued first;
+    // then a ring of DEPTH weight panels, consumed one by one as they arrive
+    // and refilled unconditionally (indices clamped to the wavefront's last
+    // panel, extra panels multiplied by zero) so that the ring's waits stay
+    // exact.  With an EC to wait for, the activations are staged completely
+    // before the first weight load, which lets the EC workgroups' loads reach
+    // memory ahead of the weight stream.
+    // (Every load below is issued unconditionally -- indices are clamped and
+    // unwanted values zeroed afterwards -- so that the compiler can count the
+    // loads in flight and wait for exactly the one it needs.)
+    constexpr bool XLDS = XCH > 0;
+    u32x4 wring[DEPTH][CB];
+    u32x4 xring[XLDS ? 1 : DEPTH][4];
+    uint32_t szring[GROUPED ? DEPTH : 1][CB];
+    uint32_t sz0[CB];
+#pragma unroll
+    for (int j = 0; j < CB; ++j)
+        sz0[j] = *szp[j];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
+    const int nxchunks = XLDS ? M * K / 8 : 1;       // 16-byte chunks of X (XCH per thread suffice)
+    u32x4 xstage[XLDS ? XCH : 1];
+    const uint16_t* xg = a.X + (size_t)(xrow ? row : 0) * K + (size_t)kbeg * PANEL_K + koff;
+    auto issue = [&](int u, int i) {                 // panel i (clamped) into ring slot u
+        const int ic = min(i, klast);
+        if constexpr (GROUPED) {
+            const int gi = ((kbeg + ic) * PANEL_K) / a.G - (kbeg * PANEL_K) / a.G;
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                szring[u][j] = szp[j][(size_t)gi * a.Npad];
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+            wring[u][j] = ld16_stream(wp[j] + (size_t)ic * PANEL_BYTES);
+        if constexpr (!XLDS) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xring[u][s] = ld16(xg + (size_t)ic * PANEL_K + 32 * s);
+        }
+    };
+    auto store_x = [&]() {
+#pragma unroll
+        for (int i = 0; i < XCH; ++i)
+            st16(xs + (size_t)min(tid + DEC_THREADS * i, nxchunks - 1) * 8, xstage[i]);
+        lds_barrier();
+    };
+    if constexpr (XLDS) {
+#pragma unroll
+        for (int i = 0; i < XCH; ++i)
+            xstage[i] = ld16(a.X + (size_t)min(tid + DEC_THREADS * i, nxchunks - 1) * 8);
+    }
+    // keep the issue order: the scheduler must not sink these loads below the
+    // weight loads (each wait would then cover the whole ring)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (XLDS && STAGE_FIRST)
+        store_x();
+#pragma unroll
+    for (int u = 0; u < DEPTH; ++u) {
+        issue(u, u);
+        __builtin_amdgcn_sched_barrier(0);   // slot u is issued u-th
+    }
+    if constexpr (XLDS && !STAGE_FIRST)
+        store_x();
 
     floatx4 acc[CB], accg[CB];
     float s_cur[CB];
     DqF16 dqh[CB];
     float dqb[CB];
-    int n_l[CB];
+    auto set_sz = [&](const uint32_t* v) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            s_cur[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
+            const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
+            if constexpr (ACT == ACT_F16)
+                dqh[j] = dq_f16_consts(z);
+            else
+                dqb[j] = -(8388608.0f + z);
+        }
+    };
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
         acc[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
         accg[j] = acc[j];
-        s_cur[j] = 0.0f;
-        dqh[j] = dq_f16_consts(0.0f);
-        dqb[j] = 0.0f;
-        n_l[j] = (cb0 + j) * PANEL_N + (l & 15);
     }
-    int cur_g = -1;
+    set_sz(sz0);
+    int left_in_group = ppg - (kbeg % ppg);          // panels until the group changes
 
-    for (int kc = 0; kc < kcnt; kc += U) {
-        u32x4 xf[U][4];
-        u32x4 wq[U][CB];
-        uint32_t szv[U][CB];
+    const uint16_t* xl = xs + (size_t)row * K + (size_t)kbeg * PANEL_K + koff;
+    // one chunk of DEPTH panels; REFILL: the ring is refilled for the next
+    // chunk (only while one follows, so no panel is loaded twice)
+    auto chunk = [&](int i0, auto refill_tag) {
+        constexpr bool REFILL = decltype(refill_tag)::value;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kc + u < kcnt) {
-                const int kb = kbeg + kc + u;
+        for (int u = 0; u < DEPTH; ++u) {
+            const int i = i0 + u;
+            const bool valid = i < kcnt;                // wavefront-uniform
+            u32x4 wv[CB];
+            u32x4 xf[4];
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                wv[j] = wring[u][j];
+            uint32_t szv[CB];
+            if constexpr (GROUPED) {
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    szv[j] = szring[u][j];
+            }
+            if constexpr (XLDS) {
+                const int ic = min(i, klast);
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
-                    xf[u][s] = xrow ? ld16(xp + (size_t)kb * PANEL_K + 32 * s) : (u32x4){0u, 0u, 0u, 0u};
+                    xf[s] = *reinterpret_cast<const u32x4*>(xl + (size_t)ic * PANEL_K + 32 * s);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    xf[s] = xring[u][s];
             }
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kc + u < kcnt) {
-                const int kb = kbeg + kc + u;
-                const int grp = (kb * PANEL_K) / a.G;
-#pragma unroll
-                for (int j = 0; j < CB; ++j) {
-                    if (cb0 + j < a.NB) {
-                        wq[u][j] = ld16_stream(a.codes + ((size_t)(cb0 + j) * KB + kb) * PANEL_BYTES + l * 16);
-                        szv[u][j] = a.sz[(size_t)grp * a.Npad + n_l[j]];
-                    } else {
-                        wq[u][j] = (u32x4){0u, 0u, 0u, 0u};
-                        szv[u][j] = 0u;
-                    }
-                }
+            for (int s = 0; s < 4; ++s)
+                xf[s] = (valid && xrow) ? xf[s] : (u32x4){0u, 0u, 0u, 0u};
+            if constexpr (REFILL) {
+                issue(u, i + DEPTH);
+                __builtin_amdgcn_sched_barrier(0);  // refill slot u as soon as it is consumed
             }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (kc + u < kcnt) {
-                const int kb = kbeg + kc + u;
-                const int grp = (kb * PANEL_K) / a.G;
-                if (grp != cur_g) {
+            if constexpr (GROUPED) {
+                if (valid && left_in_group == ppg && i > 0) {
 #pragma unroll
                     for (int j = 0; j < CB; ++j) {
                         acc[j] += s_cur[j] * accg[j];
                         accg[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
-                        const uint32_t v = szv[u][j];
-                        s_cur[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFF));
-                        const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-                        if constexpr (ACT == ACT_F16)
-                            dqh[j] = dq_f16_consts(z);
-                        else
-                            dqb[j] = -(8388608.0f + z);
                     }
-                    cur_g = grp;
-                }
-#pragma unroll
-                for (int j = 0; j < CB; ++j) {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        u32x4 bq;
-                        if constexpr (ACT == ACT_F16)
-                            bq = dequant_f16(wq[u][j][s], dqh[j]);
-                        else
-                            bq = dequant_bf16(wq[u][j][s], dqb[j]);
-                        accg[j] = mfma16x16x32<ACT>(xf[u][s], bq, accg[j]);
-                    }
+                    set_sz(szv);
                 }
             }
+#pragma unroll
+            for (int j = 0; j < CB; ++j) {
+                const uint32_t w0 = wv[j].x, w1 = wv[j].y, w2 = wv[j].z, w3 = wv[j].w;
+                const uint32_t ws[4] = {w0, w1, w2, w3};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    u32x4 bq;
+                    if constexpr (ACT == ACT_F16)
+                        bq = dequant_f16(ws[s], dqh[j]);
+                    else
+                        bq = dequant_bf16(ws[s], dqb[j]);
+                    accg[j] = mfma16x16x32<ACT>(xf[s], bq, accg[j]);
+                }
+            }
+            if constexpr (GROUPED) {
+                if (--left_in_group == 0)
+                    left_in_group = ppg;
+            }
         }
-    }
+    };
+    int i0 = 0;
+    for (; i0 + DEPTH < kcnt; i0 += DEPTH)
+        chunk(i0, std::true_type{});
+    chunk(i0, std::false_type{});
+
 #pragma unroll
     for (int j = 0; j < CB; ++j)
         acc[j] += s_cur[j] * accg[j];
 
-    // reduce the four K shares (fixed order)
-    floatx4* red = reinterpret_cast<floatx4*>(smem);   // [4][CB][64]
+    // B fragments for the epilogue (rank rows 32 rs + koff + t, column n),
+    // issued now so that they arrive during the reductions below
+    u32x4 bfr[CB][8];
+    if (a.r > 0) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            if ((j & 3) != w)
+                continue;
+#pragma unroll
+            for (int rs = 0; rs < 8; ++rs) {
+                if (rs < nsteps) {
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const int jr = 32 * rs + koff + t;
+                        hv[t] = (jr < a.r && n_l[j] < a.N) ? (uint32_t)a.B[(size_t)jr * a.N + n_l[j]] : 0u;
+                    }
+                    bfr[j][rs] = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
+                                         hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+                }
+            }
+        }
+    }
+
+    // ---- reduce the four K shares (fixed order); LDS is reused from here on
+    __syncthreads();
+    floatx4* red = reinterpret_cast<floatx4*>(smem);                       // [4][CB][64]
+    float* tsum = reinterpret_cast<float*>(smem + 4 * CB * 64 * 16);        // [M][RC]
+    float* gl = tsum + 16 * a.RC;                                           // [16]
+    uint16_t* tgl = reinterpret_cast<uint16_t*>(gl + 16);                   // [16][r_pad]
 #pragma unroll
     for (int j = 0; j < CB; ++j)
         red[(w * CB + j) * 64 + l] = acc[j];
-    __syncthreads();
+
+    // ---- gated rank-r activations from this workgroup's replica slot
+    const int slot = mb % DEC_NREP;
+    const uint8_t* sdata = a.rep_data + (size_t)slot * a.rep_data_stride;
+    if (a.r > 0) {
+        if (tid == 0) {
+            const uint32_t target = a.single ? (uint32_t)a.P : 1u;
+            uint32_t it = 0;
+            while (atomic_load_dev(rep_word(a, slot, 0)) < target) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++it >= SPIN_LIMIT) {
+                    atomic_store_dev(&a.flags[2], 1u);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        if (a.single) {
+            // the P partials of this slot, [P][ne2] float pairs: load a chunk of
+            // them at once into LDS, then add them up in slice order
+            const int ne = M * a.RC;
+            const int ne2 = (ne + 1) >> 1;
+            const uint64_t* src2 = reinterpret_cast<const uint64_t*>(sdata);
+            uint64_t* stage = reinterpret_cast<uint64_t*>(tgl + 16 * a.r_pad);   // [chunk][ne2]
+            const int pc = max(1, (int)(DEC_SUM_STAGE_BYTES / 8 / ne2));       // slices per chunk
+            float tacc[(4 * 257 + DEC_THREADS - 1) / DEC_THREADS];
+#pragma unroll
+            for (int i = 0; i < (int)(sizeof(tacc) / sizeof(float)); ++i)
+                tacc[i] = 0.0f;
+            for (int q0 = 0; q0 < a.P; q0 += pc) {
+                const int nq = min(pc, a.P - q0);
+                for (int e = tid; e < nq * ne2; e += DEC_THREADS)
+                    stage[e] = __hip_atomic_load(src2 + (size_t)q0 * ne2 + e, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+                const float* sf = reinterpret_cast<const float*>(stage);
+#pragma unroll
+                for (int i = 0; i < (int)(sizeof(tacc) / sizeof(float)); ++i) {
+                    const int e = tid + DEC_THREADS * i;
+                    if (e < ne)
+                        for (int q = 0; q < nq; ++q)
+                            tacc[i] += sf[q * 2 * ne2 + e];
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int i = 0; i < (int)(sizeof(tacc) / sizeof(float)); ++i) {
+                const int e = tid + DEC_THREADS * i;
+                if (e < ne)
+                    tsum[e] = tacc[i];
+            }
+            __syncthreads();
+            if (tid < 16)
+                gl[tid] = tid < M ? sigmoid_f32(tsum[tid * a.RC + a.r] + a.b_g) : 0.0f;
+            __syncthreads();
+            for (int e = tid; e < 16 * a.r_pad; e += DEC_THREADS) {
+                const int m = e / a.r_pad, c = e - m * a.r_pad;
+                const float v = (m < M && c < a.r) ? gl[m] * tsum[m * a.RC + c] : 0.0f;
+                tgl[e] = f32_to_act<ACT>(v);
+            }
+            __syncthreads();
+        }
+    } else {
+        __syncthreads();
+    }
 
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
@@ -279,40 +575,20 @@ __device__ void decode_main_role(const DecodeKArgs& a, float* smem)
         tot += red[(3 * CB + j) * 64 + l];
         const int n = n_l[j];
         if (a.r > 0) {
-            // B fragment rows koff + t of each 32-deep rank step, column n
-            u32x4 bfr[8];
-            const int nsteps = a.r_pad >> 5;
 #pragma unroll
             for (int rs = 0; rs < 8; ++rs) {
                 if (rs < nsteps) {
-                    uint32_t hv[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const int jr = 32 * rs + koff + t;
-                        hv[t] = (jr < a.r && n < a.N) ? (uint32_t)a.B[(size_t)jr * a.N + n] : 0u;
+                    u32x4 af = (u32x4){0u, 0u, 0u, 0u};
+                    if (a.single) {
+                        af = *reinterpret_cast<const u32x4*>(tgl + row * a.r_pad + 32 * rs + koff);
+                    } else if (xrow) {
+                        const uint64_t* src = reinterpret_cast<const uint64_t*>(
+                            sdata + ((size_t)row * a.r_pad + 32 * rs + koff) * 2);
+                        const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        af = (u32x4){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
                     }
-                    bfr[rs] = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
-                                      hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
-                }
-            }
-            // wait (bounded) for T_g
-            if (l == 0) {
-                uint32_t it = 0;
-                while (atomic_load_acquire(&a.flags[1]) == 0u) {
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++it >= SPIN_LIMIT) {
-                        atomic_store_relaxed(&a.flags[3], 1u);
-                        break;
-                    }
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            fence_acquire();
-#pragma unroll
-            for (int rs = 0; rs < 8; ++rs) {
-                if (rs < nsteps) {
-                    u32x4 af = ld16(a.tg + (size_t)row * a.r_pad + 32 * rs + koff);
-                    tot = mfma16x16x32<ACT>(af, bfr[rs], tot);
+                    tot = mfma16x16x32<ACT>(af, bfr[j][rs], tot);
                 }
             }
         }
@@ -326,39 +602,91 @@ __device__ void decode_main_role(const DecodeKArgs& a, float* smem)
         }
     }
 
+    // the last reader of a slot clears it for the next call
     if (a.r > 0) {
         __syncthreads();
         if (tid == 0) {
-            uint32_t old = atomic_add_acq_rel(&a.flags[2], 1u);
-            if (old == (uint32_t)(a.n_main - 1)) {
-                atomic_store_relaxed(&a.flags[0], 0u);
-                atomic_store_relaxed(&a.flags[1], 0u);
-                atomic_store_release(&a.flags[2], 0u);
+            const int readers = a.n_main / DEC_NREP + (slot < a.n_main % DEC_NREP ? 1 : 0);
+            const uint32_t old = atomic_add_dev(rep_word(a, slot, 1), 1u);
+            if (old == (uint32_t)(readers - 1)) {
+                atomic_store_dev(rep_word(a, slot, 0), 0u);
+                atomic_store_dev(rep_word(a, slot, 1), 0u);
             }
         }
     }
 }
 
-template <int ACT, int CB, int U>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
 __global__ __launch_bounds__(DEC_THREADS)
 void decode_kernel(DecodeKArgs a)
 {
-    // EC role: 16 x 256 staged activations + 4 x 16 x 64 reduction + small;
-    // main role: 4 x CB x 64 float4.
-    __shared__ float smem[16 * EC_KS_MAX + 4 * 16 * 64 + 64 + 16];
-    static_assert(4 * CB * 64 * 4 <= 16 * EC_KS_MAX + 4 * 16 * 64, "main-role LDS");
+    extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
     if ((int)blockIdx.x < a.P)
-        decode_ec_role<ACT>(a, smem);
+        decode_ec_role<ACT>(a, dsmem);
     else
-        decode_main_role<ACT, CB, U>(a, smem);
+        decode_main_role<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>(a, dsmem);
 }
 
-template <int ACT, int CB>
-static hipError_t launch_decode_t(const DecodeKArgs& k, hipStream_t st)
+// activations of at most this many bytes are staged in LDS by the main role
+// (8 chunks of 16 bytes per thread)
+constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS;
+
+bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
+
+size_t decode_lds_bytes(const DecodePlan& p, int M, int K, int r)
 {
-    dim3 grid(k.P + k.n_main);
-    hipLaunchKernelGGL((decode_kernel<ACT, CB, 4>), grid, dim3(DEC_THREADS), 0, st, k);
+    // main role, after the stream: wavefront reduction, partial sums, gate, T_g,
+    // staged hand-over partials
+    size_t b = (size_t)4 * p.CB * 64 * 16 + (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2 +
+               (p.single ? DEC_SUM_STAGE_BYTES + 16 : 0);
+    if (p.xlds) {
+        size_t xs = (size_t)M * K * 2;
+        if (xs > b) b = xs;
+    }
+    if (p.P > 0) {
+        size_t at = (size_t)((r + 1 + 15) / 16 * 16) * (p.KS + 8) * 2;      // transposed slice
+        size_t fin = (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2; // final reduction
+        if (at > b) b = at;
+        if (fin > b) b = fin;
+    }
+    return (b + 15) / 16 * 16;
+}
+
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
+static hipError_t launch_decode_t(const DecodeKArgs& k, size_t lds, hipStream_t st)
+{
+    auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(k.P + k.n_main), dim3(DEC_THREADS), lds, st, k);
     return hipGetLastError();
+}
+
+template <int ACT, bool GROUPED, bool STAGE_FIRST>
+static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, size_t lds, hipStream_t st)
+{
+    if (p.xlds) {
+        const size_t xch = ((size_t)k.M * k.K / 8 + DEC_THREADS - 1) / DEC_THREADS;
+        if (xch <= 2)
+            return launch_decode_t<ACT, 1, 2, 8, GROUPED, STAGE_FIRST>(k, lds, st);
+        return launch_decode_t<ACT, 1, DEC_XLDS_CHUNKS, 8, GROUPED, STAGE_FIRST>(k, lds, st);
+    }
+    if (p.CB == 1)
+        return launch_decode_t<ACT, 1, 0, 4, GROUPED, false>(k, lds, st);
+    return launch_decode_t<ACT, 2, 0, 4, GROUPED, false>(k, lds, st);
+}
+
+template <int ACT>
+static hipError_t launch_decode_act(const DecodeKArgs& k, const DecodePlan& p, size_t lds, hipStream_t st)
+{
+    if (k.G != k.K)
+        return p.stage_first ? launch_decode_grp<ACT, true, true>(k, p, lds, st)
+                             : launch_decode_grp<ACT, true, false>(k, p, lds, st);
+    return p.stage_first ? launch_decode_grp<ACT, false, true>(k, p, lds, st)
+                         : launch_decode_grp<ACT, false, false>(k, p, lds, st);
 }
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st)
@@ -376,15 +704,17 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.M = a.M; k.N = a.N; k.K = a.K; k.r = a.r; k.r_pad = p.r_pad; k.G = a.G;
     k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;
     k.P = p.P; k.KS = p.KS; k.RC = p.RC; k.n_main = p.n_main;
+    k.single = p.single;
+    k.stage_first = p.stage_first;
     k.flags = (uint32_t*)(a.ws + p.off_flags);
     k.partial = (float*)(a.ws + p.off_partial);
-    k.tg = (uint16_t*)(a.ws + p.off_tg);
-    if (a.act == ACT_F16) {
-        if (p.CB == 1) return launch_decode_t<ACT_F16, 1>(k, st);
-        return launch_decode_t<ACT_F16, 2>(k, st);
-    }
-    if (p.CB == 1) return launch_decode_t<ACT_BF16, 1>(k, st);
-    return launch_decode_t<ACT_BF16, 2>(k, st);
+    k.rep_ctrl = (uint8_t*)(a.ws + p.off_rep_ctrl);
+    k.rep_data = (uint8_t*)(a.ws + p.off_rep_data);
+    k.rep_data_stride = p.rep_data_stride;
+    const size_t lds = decode_lds_bytes(p, a.M, a.K, a.r);
+    if (a.act == ACT_F16)
+        return launch_decode_act<ACT_F16>(k, p, lds, st);
+    return launch_decode_act<ACT_BF16>(k, p, lds, st);
 }
 
 }  // namespace w4ec

@@ -22,6 +22,7 @@
 //    them in a fixed order, then runs the epilogue;
 //  * tile ids are remapped so that the workgroups an XCD receives (block ids
 //    congruent mod 8) share rows of X and columns of W in that XCD's L2.
+#include "ec_tile.h"
 #include "w4ec_common.h"
 #include "w4ec_launch.h"
 
@@ -37,114 +38,93 @@ struct PrepassKArgs {
     const uint16_t* A;
     const uint16_t* w_g;
     float b_g;
-    int M, K, r, r_pad, RC, kc, ks;
-    float* partial;     // [ks][mt*64][RC]
+    int M, K, r, r_pad, kc, ks;
+    floatx4* partial;   // [mt][ks][4 wavefronts][17 column blocks][64 lanes]
     uint32_t* cnt;      // [mt]
-    uint16_t* tg;       // [Mpad][r_pad]
-    int Mrows;          // mt * 64 (rows of the partial buffer)
+    uint16_t* tg;       // [Mpad][r_pad], activation format
 };
 
-constexpr int PRE_KT = 32;                 // k per staging step
-constexpr int PRE_LDS_STRIDE = PRE_KT + 8;  // halves per transposed row (padding vs bank conflicts)
-constexpr int PRE_MAX_CB = 17;             // (256 + 1 + 15) / 16
+constexpr int PRE_MAXI = 17;   // (256 + 1 + 15) / 16 column blocks of [A | w_g]
 
+// 64 tokens x one K slice per workgroup (wavefront w: tokens 16 w .. 16 w + 15).
+// With a split over K, the last workgroup of a token tile adds the slices'
+// fragments in a fixed order.  It then applies the gate and stores
+// T_g = g * T in the activation format for the GEMM epilogue.
 template <int ACT>
 __global__ __launch_bounds__(PF_THREADS)
 void prepass_kernel(PrepassKArgs a)
 {
+    __shared__ __attribute__((aligned(16))) uint16_t at[EC_LDS_HALVES];
+    __shared__ float gsh[64];
+    __shared__ uint32_t s_old;
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = tid >> 6;
-    const int m0 = blockIdx.x * 64;
+    const int mt = blockIdx.x;
     const int kz = blockIdx.y;
+    const int m0 = mt * 64;
     const int kbeg = kz * a.kc;
     const int kend = min(a.K, kbeg + a.kc);
-    const int CBE = (a.RC + 15) >> 4;
-    const int cols = CBE * 16;
+    const int xrow = min(m0 + 16 * w + (l & 15), a.M - 1);
+    const int CBE = ec_col_blocks(a.r);
 
-    // [A | w_g] staged transposed: at[c][k], c < cols, k < 32
-    __shared__ uint16_t at[PRE_MAX_CB * 16 * PRE_LDS_STRIDE];
-    __shared__ float gsh[64];
-    __shared__ uint32_t s_old;
+    floatx4 acc[PRE_MAXI];
+    ec_tile<ACT, 1, PRE_MAXI, 8>(a.X, a.K, xrow, a.A, a.w_g, a.r, kbeg, kend, 0, at, acc);
 
-    floatx4 acc[PRE_MAX_CB];
+    if (a.ks > 1) {
+        floatx4* mine = a.partial + ((size_t)(mt * a.ks + kz) * 4 + w) * PRE_MAXI * 64;
 #pragma unroll
-    for (int c = 0; c < PRE_MAX_CB; ++c)
-        acc[c] = (floatx4){0.f, 0.f, 0.f, 0.f};
-
-    const int row = min(m0 + 16 * w + (l & 15), a.M - 1);
-    const uint16_t* xp = a.X + (size_t)row * a.K + 8 * (l >> 4);
-
-    for (int k = kbeg; k < kend; k += PRE_KT) {
+        for (int i = 0; i < PRE_MAXI; ++i)
+            if (i < CBE)
+                st16_dev(mine + i * 64 + l, acc[i]);
+        wait_all_mem();
         __syncthreads();
-        for (int idx = tid; idx < PRE_KT * cols; idx += PF_THREADS) {
-            const int kk = idx / cols, c = idx - kk * cols;
-            uint16_t v = 0;
-            if (c < a.r)
-                v = a.A[(size_t)(k + kk) * a.r + c];
-            else if (c == a.r && a.w_g)
-                v = a.w_g[k + kk];
-            at[c * PRE_LDS_STRIDE + kk] = v;
-        }
+        if (tid == 0)
+            s_old = atomic_add_dev(&a.cnt[mt], 1u);
         __syncthreads();
-        const u32x4 xf = ld16(xp + k);
+        if (s_old != (uint32_t)(a.ks - 1))
+            return;
+        if (tid == 0)
+            atomic_store_dev(&a.cnt[mt], 0u);
 #pragma unroll
-        for (int cb = 0; cb < PRE_MAX_CB; ++cb) {
-            if (cb < CBE) {
-                const uint16_t* bp = at + (cb * 16 + (l & 15)) * PRE_LDS_STRIDE + 8 * (l >> 4);
-                u32x4 bf;
-                bf.x = *(const uint32_t*)(bp + 0);
-                bf.y = *(const uint32_t*)(bp + 2);
-                bf.z = *(const uint32_t*)(bp + 4);
-                bf.w = *(const uint32_t*)(bp + 6);
-                acc[cb] = mfma16x16x32<ACT>(xf, bf, acc[cb]);
+        for (int i = 0; i < PRE_MAXI; ++i) {
+            if (i < CBE) {
+                floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
+                for (int z = 0; z < a.ks; ++z)
+                    t += (z == kz) ? acc[i]
+                                   : ld16_dev(a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * PRE_MAXI * 64 + i * 64 + l);
+                acc[i] = t;
             }
         }
     }
 
-    // partial sums of this K slice: rows 4 (l >> 4) + v of the wavefront's 16
-    float* part = a.partial + (size_t)kz * a.Mrows * a.RC;
+    // gate: column r lives in block r / 16, lanes with (l & 15) == r % 16
+    const int cg = a.r >> 4;
 #pragma unroll
-    for (int cb = 0; cb < PRE_MAX_CB; ++cb) {
-        if (cb < CBE) {
-            const int c = cb * 16 + (l & 15);
-            if (c < a.RC) {
+    for (int i = 0; i < PRE_MAXI; ++i) {
+        if (i == cg && (l & 15) == (a.r & 15)) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = m0 + 16 * w + 4 * (l >> 4) + v;
-                    part[(size_t)m * a.RC + c] = acc[cb][v];
-                }
+            for (int v = 0; v < 4; ++v)
+                gsh[16 * w + 4 * (l >> 4) + v] = sigmoid_f32(acc[i][v] + a.b_g);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PRE_MAXI; ++i) {
+        const int c = i * 16 + (l & 15);
+        if (i < CBE && c < a.r_pad) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int mloc = 16 * w + 4 * (l >> 4) + v;
+                const float val = c < a.r ? gsh[mloc] * acc[i][v] : 0.0f;
+                a.tg[(size_t)(m0 + mloc) * a.r_pad + c] = f32_to_act<ACT>(val);
             }
         }
     }
-    fence_release();
-    __syncthreads();
-    if (tid == 0)
-        s_old = atomic_add_acq_rel(&a.cnt[blockIdx.x], 1u);
-    __syncthreads();
-    if (s_old != (uint32_t)(a.ks - 1))
-        return;
-    fence_acquire();
-    if (tid == 0)
-        atomic_store_relaxed(&a.cnt[blockIdx.x], 0u);
-    if (tid < 64) {
-        const int m = m0 + tid;
-        float lg = 0.0f;
-        for (int z = 0; z < a.ks; ++z)
-            lg += a.partial[((size_t)z * a.Mrows + m) * a.RC + a.r];
-        gsh[tid] = sigmoid_f32(lg + a.b_g);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 64 * a.r_pad; idx += PF_THREADS) {
-        const int mm = idx / a.r_pad, j = idx - mm * a.r_pad;
-        float v = 0.0f;
-        if (j < a.r) {
-            float t = 0.0f;
-            for (int z = 0; z < a.ks; ++z)
-                t += a.partial[((size_t)z * a.Mrows + m0 + mm) * a.RC + j];
-            v = gsh[mm] * t;
-        }
-        a.tg[(size_t)(m0 + mm) * a.r_pad + j] = f32_to_act<ACT>(v);
+    const int c0 = CBE * 16;
+    for (int e = tid; e < 64 * (a.r_pad - c0); e += PF_THREADS) {
+        const int mloc = e / (a.r_pad - c0), c = c0 + e % (a.r_pad - c0);
+        a.tg[(size_t)(m0 + mloc) * a.r_pad + c] = 0;
     }
 }
 
@@ -157,7 +137,7 @@ struct GemmKArgs {
     const uint16_t* B;
     const uint16_t* tg;
     uint16_t* Y;
-    float* partial;    // [ksplit][Mpad][NT*256]
+    floatx4* partial;  // [tile][ksplit][4][RB][4][64] fragments
     uint32_t* cnt;     // [mt*nt]
     int M, N, K, r, r_pad, G, NB, KB, Npad, mt, nt, ksplit, Mpad;
 };
@@ -328,44 +308,35 @@ void prefill_gemm_kernel(GemmKArgs a)
     }
 
     // ---- split-K hand-over: the last workgroup of the tile sums the partials
+    // (fragment layout [tile][split][wavefront][RB][4][64 lanes], 16 bytes per lane)
     if (a.ksplit > 1) {
-        const int ldp = a.nt * PF_BN;
-        float* mine = a.partial + (size_t)kz * a.Mpad * ldp;
+        const int tile = tm * a.nt + tn;
+        auto frag = [&](int z, int rb, int j) -> size_t {
+            return ((((size_t)tile * a.ksplit + z) * 4 + w) * RB * 4 + rb * 4 + j) * 64 + l;
+        };
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = m0 + rb * 16 + 4 * (l >> 4) + v;
-                    const int n = n0 + 64 * w + 16 * j + (l & 15);
-                    mine[(size_t)m * ldp + n] = acc[rb][j][v];
-                }
-        fence_release();
+                st16_dev(a.partial + frag(kz, rb, j), acc[rb][j]);
+        wait_all_mem();
         __syncthreads();
-        const int tile = tm * a.nt + tn;
         if (tid == 0)
-            s_old = atomic_add_acq_rel(&a.cnt[tile], 1u);
+            s_old = atomic_add_dev(&a.cnt[tile], 1u);
         __syncthreads();
         if (s_old != (uint32_t)(a.ksplit - 1))
             return;
-        fence_acquire();
         if (tid == 0)
-            atomic_store_relaxed(&a.cnt[tile], 0u);
+            atomic_store_dev(&a.cnt[tile], 0u);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = m0 + rb * 16 + 4 * (l >> 4) + v;
-                    const int n = n0 + 64 * w + 16 * j + (l & 15);
-                    float sum = 0.0f;
-                    for (int z = 0; z < a.ksplit; ++z)
-                        sum += (z == kz) ? acc[rb][j][v]
-                                         : a.partial[((size_t)z * a.Mpad + m) * ldp + n];
-                    acc[rb][j][v] = sum;
-                }
+            for (int j = 0; j < 4; ++j) {
+                floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
+                for (int z = 0; z < a.ksplit; ++z)
+                    t += (z == kz) ? acc[rb][j] : ld16_dev(a.partial + frag(z, rb, j));
+                acc[rb][j] = t;
+            }
     }
 
     // ---- epilogue: per-channel scale, gated rank-r correction, store
@@ -444,12 +415,11 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
         q.A = (const uint16_t*)a.A;
         q.w_g = (const uint16_t*)a.w_g;
         q.b_g = a.b_g;
-        q.M = a.M; q.K = a.K; q.r = a.r; q.r_pad = p.r_pad; q.RC = p.RC;
+        q.M = a.M; q.K = a.K; q.r = a.r; q.r_pad = p.r_pad;
         q.kc = p.pre_kc; q.ks = p.pre_ks;
-        q.partial = (float*)(a.ws + p.off_pre_partial);
+        q.partial = (floatx4*)(a.ws + p.off_pre_partial);
         q.cnt = (uint32_t*)(a.ws + p.off_pre_cnt);
         q.tg = tg;
-        q.Mrows = p.pre_mt * 64;
         dim3 grid(p.pre_mt, p.pre_ks);
         if (a.act == ACT_F16)
             hipLaunchKernelGGL(prepass_kernel<ACT_F16>, grid, dim3(PF_THREADS), 0, st, q);
@@ -466,7 +436,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
     k.B = (const uint16_t*)a.B;
     k.tg = tg;
     k.Y = (uint16_t*)a.Y;
-    k.partial = (float*)(a.ws + p.off_gemm_partial);
+    k.partial = (floatx4*)(a.ws + p.off_gemm_partial);
     k.cnt = (uint32_t*)(a.ws + p.off_gemm_cnt);
     k.M = a.M; k.N = a.N; k.K = a.K; k.r = a.r; k.r_pad = p.r_pad; k.G = a.G;
     k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;

@@ -224,29 +224,69 @@ __device__ inline float sigmoid_f32(float l)
 
 // ------------------------------------------------------------ cross-workgroup hand-over
 //
-// Agent-scope release/acquire: on gfx950 these write back / invalidate the
-// per-XCD L2 as needed, so data written by a workgroup on one XCD is seen by
-// a workgroup on another.
+// Partial results handed from one workgroup to another (possibly on another
+// XCD, with its own L2) are written and read with device-scope coherent
+// accesses (relaxed agent-scope atomics: global loads / stores with the sc1
+// bit), which gfx950 keeps coherent across XCDs per access.  The writer
+// waits for its stores to complete (s_waitcnt 0) and meets its workgroup at
+// a barrier before one thread bumps the arrival counter; a reader issues its
+// loads only after it has seen the counter.  No whole-cache write-back or
+// invalidate (what agent-scope fences compile to) is needed on either side.
 
-__device__ inline void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ inline void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-__device__ inline uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v)
+__device__ inline void st4_dev(float* p, float v)
 {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline uint32_t atomic_load_acquire(const uint32_t* p)
+__device__ inline float ld4_dev(const float* p)
 {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
 }
 
-__device__ inline void atomic_store_release(uint32_t* p, uint32_t v)
+__device__ inline void st16_dev(floatx4* p, floatx4 v)
 {
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t* q = reinterpret_cast<uint64_t*>(p);
+    const uint64_t lo = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+    const uint64_t hi = (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline void atomic_store_relaxed(uint32_t* p, uint32_t v)
+__device__ inline floatx4 ld16_dev(const floatx4* p)
+{
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (floatx4){__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+}
+
+// all of this thread's outstanding memory operations have completed
+__device__ inline void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wavefront's LDS operations (lgkmcnt 0) but, unlike __syncthreads(), not for
+// its global loads in flight (the s_waitcnt immediate keeps vmcnt and expcnt
+// at their maximum).
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+}
+
+__device__ inline uint32_t atomic_add_dev(uint32_t* p, uint32_t v)
+{
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint32_t atomic_load_dev(const uint32_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void atomic_store_dev(uint32_t* p, uint32_t v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -258,14 +298,21 @@ constexpr uint32_t SPIN_LIMIT = 1u << 22;
 // ------------------------------------------------------------ launch plans
 // (shared by the host dispatch and the workspace sizing)
 
+constexpr int DEC_NREP = 32;                    // replica slots of the decode hand-over
+constexpr size_t DEC_REP_CTRL_STRIDE = 4096;    // control words of one slot (own page)
+
 struct DecodePlan {
     int P;          // EC workgroups (K slices) -- 0 when r == 0
-    int KS;         // k per EC slice
+    int KS;         // k per EC slice (multiple of 64)
     int RC;         // partial columns: r (low rank) + 1 (gate logit)
     int r_pad;      // r rounded up to 32
     int CB;         // column blocks per main workgroup
     int n_main;     // main workgroups
-    size_t off_flags, off_partial, off_tg, bytes;
+    bool xlds;      // main workgroups stage the activations in LDS
+    int single;     // hand-over: 1 = per-slot partial sums, 0 = reduced by the last EC workgroup
+    int stage_first;  // main workgroups stage X before issuing weight loads
+    size_t rep_data_stride;  // bytes per replica slot of hand-over data
+    size_t off_flags, off_partial, off_rep_ctrl, off_rep_data, bytes;
 };
 
 struct PrefillPlan {
@@ -273,12 +320,11 @@ struct PrefillPlan {
     int BN;         // columns per GEMM tile (256)
     int mt, nt;     // tiles along M and N
     int ksplit;     // GEMM split over K
-    int pre_bm;     // tokens per prepass workgroup (64)
-    int pre_mt;     // prepass tiles along M
+    int pre_mt;     // prepass tiles of 64 tokens
     int pre_ks;     // prepass split over K
-    int pre_kc;     // k per prepass split (multiple of 32)
-    int RC, r_pad, Mpad;
-    size_t off_pre_cnt, off_gemm_cnt, off_err, off_pre_partial, off_tg, off_gemm_partial, bytes;
+    int pre_kc;     // k per prepass split (multiple of 64)
+    int r_pad, Mpad;
+    size_t off_pre_cnt, off_gemm_cnt, off_pre_partial, off_tg, off_gemm_partial, bytes;
 };
 
 }  // namespace w4ec

@@ -29,6 +29,7 @@ struct LayerArgs {
 };
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
+bool decode_use_xlds(int M, int K);
 hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
 
 }  // namespace w4ec
