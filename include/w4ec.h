@@ -26,8 +26,8 @@
  *  - Pointers named as "device" are HIP device pointers owned by the caller.
  *    The library never allocates or frees memory and keeps no state between
  *    calls except what the caller's workspace holds.
- *  - All arrays are row-major and contiguous.  X, Y and the workspace must be
- *    16-byte aligned; the packed blob 256-byte aligned.
+ *  - All arrays are row-major and contiguous.  X, Y, A, w_g and the workspace
+ *    must be 16-byte aligned; the packed blob 256-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous on it unless stated otherwise.
  *  - Activations X, Y and the EC parameters A, B, w_g share one dtype

@@ -39,13 +39,12 @@ int check_weight_shape(int N, int K, int G)
 // Workspace layout, shared by both entry points so that one workspace can
 // serve decode and prefill calls in any order:
 //   [0, CTRL_BYTES)   control words that every call returns to zero --
-//                     decode flags, prefill hand-over counters, the decode
+//                     decode flags, split-K tile counters, the decode
 //                     replica slots; never overwritten by data
 //   [CTRL_BYTES, ...) per-call data (partial sums, gated activations), fully
 //                     written before it is read within a call
 constexpr size_t CTRL_BYTES = 1 << 20;
 constexpr size_t OFF_DEC_FLAGS = 0;           // 256 B
-constexpr size_t OFF_PRE_CNT = 256;           // prepass counters, <= 256 of them
 constexpr size_t OFF_GEMM_CNT = 256 + 1024;   // split-K tile counters, <= 256 of them
 constexpr size_t OFF_DEC_REP = 64 << 10;      // DEC_NREP decode slots of DEC_REP_CTRL_STRIDE bytes
 static_assert(OFF_DEC_REP + DEC_NREP * DEC_REP_CTRL_STRIDE <= CTRL_BYTES, "control region");
@@ -57,13 +56,11 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
     p.RC = r + 1;
     p.r_pad = (r + 31) / 32 * 32;
     if (r > 0) {
-        // each EC workgroup loads its whole slice in one trip: KS x r <= 16384
-        // elements (8 16-byte chunks per thread), KS a multiple of 64, <= 256;
-        // and its transposed slice in LDS ((r + 1) rounded to 16 rows of KS + 8
-        // halves) stays within 40 KB, so that 4 workgroups fit on a CU
-        const int cols = (r + 1 + 15) / 16 * 16;
-        int ks = 256;
-        while (ks > 64 && ((long)ks * r > 16384 || (long)cols * (ks + 8) * 2 > 40960))
+        // each EC workgroup loads its whole slice in one trip (KS a multiple
+        // of 64, <= DEC_EC_KS); the slice and its gate vector in LDS stay
+        // within 40 KB, so that 4 workgroups fit on a CU
+        int ks = DEC_EC_KS;
+        while (ks > 64 && (((ks * ((r + 3) & ~3) + 16) * 2 + ks * 2) > 40960))
             ks -= 64;
         p.KS = ks;
         p.P = (K + p.KS - 1) / p.KS;
@@ -90,6 +87,8 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
     return p;
 }
 
+constexpr size_t PRE_LDS_MAX = 80 << 10;
+
 PrefillPlan make_prefill_plan(int M, int N, int K, int r)
 {
     PrefillPlan p{};
@@ -104,21 +103,27 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
         p.ksplit *= 2;
     p.Mpad = p.mt * p.BM;
     p.r_pad = (r + 31) / 32 * 32;
+    // prepass: 64-token tiles x K slices of at most 512, each slice of
+    // [A | w_g] held in LDS at once (two workgroups per CU)
     p.pre_mt = (M + 63) / 64;
-    int ks = 1;
-    while ((long long)p.pre_mt * ks < TARGET_WGS && K / (2 * ks) >= 256 && ks < 8)
-        ks *= 2;
-    p.pre_kc = ((K + ks - 1) / ks + 63) / 64 * 64;
-    p.pre_ks = (K + p.pre_kc - 1) / p.pre_kc;
-    // counters exist only for split work, which is chosen only while the
-    // workgroup count is below TARGET_WGS: at most 256 of each
-    p.off_pre_cnt = OFF_PRE_CNT;
+    p.pre_ks = 1;
+    p.pre_kc = K;
+    if (r > 0) {
+        int kcmax = 512;
+        while (kcmax > 64 && prepass_lds_bytes(r, kcmax) > PRE_LDS_MAX)
+            kcmax -= 64;
+        const int ks = (K + kcmax - 1) / kcmax;
+        p.pre_kc = ((K + ks - 1) / ks + 63) / 64 * 64;
+        p.pre_ks = (K + p.pre_kc - 1) / p.pre_kc;
+    }
+    // tile counters exist only for split work, which is chosen only while the
+    // workgroup count is below TARGET_WGS: at most 256 of them
     p.off_gemm_cnt = OFF_GEMM_CNT;
 
     size_t off = CTRL_BYTES;
     p.off_pre_partial = off;
-    if (r > 0 && p.pre_ks > 1)
-        off = align_up(off + (size_t)p.pre_mt * p.pre_ks * 4 * 17 * 64 * 16, 256);
+    if (r > 0)
+        off = align_up(off + (size_t)p.pre_mt * p.pre_ks * 4 * ((r + 15) / 16 + 1) * 64 * 16, 256);
     p.off_tg = off;
     if (r > 0)
         off = align_up(off + (size_t)p.Mpad * p.r_pad * 2, 256);
@@ -130,7 +135,7 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
 }
 
 int check_layer_args(const void* X, const void* packed, const void* A, const void* B,
-                     const void* Y, int M, int N, int K, int r, int G, int act,
+                     const void* w_g, const void* Y, int M, int N, int K, int r, int G, int act,
                      const void* ws, size_t ws_bytes, size_t need)
 {
     if (M <= 0 || r < 0)
@@ -148,7 +153,7 @@ int check_layer_args(const void* X, const void* packed, const void* A, const voi
         return W4EC_ERR_INVALID_ARG;
     if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(packed, 256))
         return W4EC_ERR_INVALID_ARG;
-    if (r > 0 && (!aligned(A, 2) || !aligned(B, 2)))
+    if (r > 0 && (!aligned(A, 16) || !aligned(B, 2) || !aligned(w_g, 16)))
         return W4EC_ERR_INVALID_ARG;
     if (X == Y || packed == Y || (r > 0 && (A == Y || B == Y)))
         return W4EC_ERR_INVALID_ARG;
@@ -260,7 +265,7 @@ int w4ec_linear_decode(const void* X, const void* packed, const void* A, const v
         p = make_decode_plan(M, N, K, r);
         need = r > 0 ? p.bytes : 0;
     }
-    int rc = check_layer_args(X, packed, A, B, Y, M, N, K, r, group_size, act_dtype,
+    int rc = check_layer_args(X, packed, A, B, w_g, Y, M, N, K, r, group_size, act_dtype,
                               workspace, workspace_bytes, need);
     if (rc != W4EC_OK)
         return rc;
@@ -282,7 +287,7 @@ int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const 
         p = make_prefill_plan(M, N, K, r);
         need = (r > 0 || p.ksplit > 1) ? p.bytes : 0;
     }
-    int rc = check_layer_args(X, packed, A, B, Y, M, N, K, r, group_size, act_dtype,
+    int rc = check_layer_args(X, packed, A, B, w_g, Y, M, N, K, r, group_size, act_dtype,
                               workspace, workspace_bytes, need);
     if (rc != W4EC_OK)
         return rc;

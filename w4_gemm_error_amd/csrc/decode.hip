@@ -33,6 +33,7 @@
 // The last reader of a slot returns its control words to zero.  All waits
 // are bounded.  Hand-over data moves with device-coherent accesses (see
 // w4ec_common.h), so no cache-wide write-back or invalidate is needed.
+#include <algorithm>
 #include <type_traits>
 
 #include "ec_tile.h"
@@ -45,8 +46,6 @@ constexpr int DEC_THREADS = 256;
 constexpr int DEC_EC_MAXI = 5;     // column blocks per wavefront in the EC role (17 / 4)
 constexpr int DEC_XLDS_CHUNKS = 8; // 16-byte chunks of staged activations per thread
 constexpr int DEC_EC_KSMAX = 256;  // k per EC slice (at most)
-constexpr int DEC_EC_CHUNKS = 8;   // 16-byte chunks of A per thread: KS * r / 8 / 256
-constexpr size_t DEC_SUM_STAGE_BYTES = 16 * 1024;  // LDS staging of hand-over partial sums
 
 struct DecodeKArgs {
     const uint16_t* X;
@@ -73,100 +72,66 @@ __device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
     return reinterpret_cast<uint32_t*>(a.rep_ctrl + (size_t)slot * DEC_REP_CTRL_STRIDE) + i;
 }
 
-// EC role: every global load of the slice (A, w_g, X) is issued before any
-// is used; the slice (KS x r <= 16384 elements, KS <= 256) is transposed
-// into LDS, then each wavefront runs the MFMAs for its column blocks
-// (cb = w, w + 4, ...).
+// EC role: every global load of the slice is issued at once -- the X
+// fragments into registers, the slice of [A | w_g] straight into LDS -- then
+// each wavefront runs the MFMAs for its column blocks (cb = w, w + 4, ...).
+template <int ACT, int NS>
+__device__ inline void dec_ec_mfma(const u32x4 (&xf)[DEC_EC_KSMAX / 32], const uint16_t* at, const uint16_t* wgl,
+                                   int r, bool gate, int w, floatx4 (&acc)[DEC_EC_MAXI])
+{
+    const int nb = ec_blocks(r);
+#pragma unroll
+    for (int i = 0; i < DEC_EC_MAXI; ++i) {
+        const int cb = w + 4 * i;
+        if (cb < nb) {
+            u32x4 bf[NS];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                bf[s] = ec_bfrag(at, wgl, r, gate, cb, 32 * s);
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                acc[i] = mfma16x16x32<ACT>(xf[s], bf[s], acc[i]);
+        }
+    }
+}
+
 template <int ACT>
 __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 {
     const int tid = threadIdx.x;
     const int l = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int p = blockIdx.x;
-    const int koff = 8 * (l >> 4);
     const int r = a.r;
     const int M = a.M;
     const int kbeg = p * a.KS;
     const int len = min(a.KS, a.K - kbeg);          // multiple of 64
     const int xrow = min(l & 15, M - 1);
-    const int CBE = ec_col_blocks(r);
-    const int cols = CBE * 16;
-    const int S = len + 8;                           // LDS row stride in halves (16-byte aligned rows)
+    const bool gate = a.w_g != nullptr;
     uint16_t* at = reinterpret_cast<uint16_t*>(smem);
-    const bool vec = (r & 7) == 0;
-    const int cpr = r >> 3;
-    const int nch = len * cpr;
+    uint16_t* wgl = at + len * ec_pitch(r) + 16;
     // The main workgroups sharing this CU wait for these results: give the
     // EC wavefronts the first pick of the CU's issue slots.
     __builtin_amdgcn_s_setprio(3);
 
-    // 1. all loads in flight at once
+    const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + 8 * (l >> 4);
     u32x4 xf[DEC_EC_KSMAX / 32];
-    const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + koff;
 #pragma unroll
     for (int s = 0; s < DEC_EC_KSMAX / 32; ++s)
-        if (32 * s < len)
-            xf[s] = ld16(xp + 32 * s);
-    u32x4 ach[DEC_EC_CHUNKS];
-#pragma unroll
-    for (int i = 0; i < DEC_EC_CHUNKS; ++i) {
-        const int ch = tid + DEC_THREADS * i;
-        if (vec && ch < nch) {
-            const int kk = ch / cpr, cc = (ch % cpr) * 8;   // a row's chunks are adjacent: coalesced
-            ach[i] = ld16(a.A + (size_t)(kbeg + kk) * r + cc);
-        }
-    }
-    const uint16_t gv = (a.w_g && tid < len) ? a.w_g[kbeg + tid] : (uint16_t)0;
-
-    // 2. [A | w_g] slice, transposed: at[c][k]
-    for (int idx = tid; idx < (cols - r) * len; idx += DEC_THREADS) {
-        const int c = r + idx / len, kk = idx % len;
-        if (c > r || !a.w_g)
-            at[c * S + kk] = 0;
-    }
-    if (vec) {
-#pragma unroll
-        for (int i = 0; i < DEC_EC_CHUNKS; ++i) {
-            const int ch = tid + DEC_THREADS * i;
-            if (ch < nch) {
-                const int kk = ch / cpr, cc = (ch % cpr) * 8;   // a row's chunks are adjacent: coalesced
-                const u32x4 v = ach[i];
-                const uint32_t q0 = v.x, q1 = v.y, q2 = v.z, q3 = v.w;
-                uint16_t* dst = at + cc * S + kk;
-                dst[0 * S] = (uint16_t)(q0 & 0xFFFF);
-                dst[1 * S] = (uint16_t)(q0 >> 16);
-                dst[2 * S] = (uint16_t)(q1 & 0xFFFF);
-                dst[3 * S] = (uint16_t)(q1 >> 16);
-                dst[4 * S] = (uint16_t)(q2 & 0xFFFF);
-                dst[5 * S] = (uint16_t)(q2 >> 16);
-                dst[6 * S] = (uint16_t)(q3 & 0xFFFF);
-                dst[7 * S] = (uint16_t)(q3 >> 16);
-            }
-        }
-    } else {
-        for (int idx = tid; idx < len * r; idx += DEC_THREADS) {
-            const int kk = idx / r, c = idx - kk * r;
-            at[c * S + kk] = a.A[(size_t)(kbeg + kk) * r + c];
-        }
-    }
-    if (a.w_g && tid < len)
-        at[r * S + tid] = gv;
+        xf[s] = ld16(xp + 32 * min(s, (len >> 5) - 1));   // steps past the slice are never used
+    ec_stage(a.A, a.w_g, r, kbeg, len, at, wgl);
+    wait_all_mem();
     __syncthreads();
 
-    // 3. MFMAs over the slice
     floatx4 acc[DEC_EC_MAXI];
 #pragma unroll
-    for (int i = 0; i < DEC_EC_MAXI; ++i) {
+    for (int i = 0; i < DEC_EC_MAXI; ++i)
         acc[i] = (floatx4){0.f, 0.f, 0.f, 0.f};
-        const int cb = w + 4 * i;
-        if (cb < CBE) {
-            const uint16_t* bp = at + (cb * 16 + (l & 15)) * S + koff;
-#pragma unroll
-            for (int s = 0; s < DEC_EC_KSMAX / 32; ++s)
-                if (32 * s < len)
-                    acc[i] = mfma16x16x32<ACT>(xf[s], *reinterpret_cast<const u32x4*>(bp + 32 * s), acc[i]);
-        }
+    switch (len >> 6) {
+    case 1: dec_ec_mfma<ACT, 2>(xf, at, wgl, r, gate, w, acc); break;
+    case 2: dec_ec_mfma<ACT, 4>(xf, at, wgl, r, gate, w, acc); break;
+    case 3: dec_ec_mfma<ACT, 6>(xf, at, wgl, r, gate, w, acc); break;
+    default: dec_ec_mfma<ACT, 8>(xf, at, wgl, r, gate, w, acc); break;
     }
     const int nrep = min(DEC_NREP, a.n_main);       // slots that have readers
 
@@ -176,8 +141,9 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
         float* part = reinterpret_cast<float*>(smem);
 #pragma unroll
         for (int i = 0; i < DEC_EC_MAXI; ++i) {
-            const int c = (w + 4 * i) * 16 + (l & 15);
-            if (w + 4 * i < CBE && c < a.RC) {
+            const int cb = w + 4 * i;
+            const int c = cb < ec_blocks(r) ? ec_col(r, cb, l & 15) : -1;
+            if (c >= 0) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int m = 4 * (l >> 4) + v;
@@ -191,12 +157,19 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
         if (tid == 0 && (ne & 1))
             part[ne] = 0.0f;
         __syncthreads();
+        // thread -> (pair i, slots s0, s0 + sstep, ...)
         const uint64_t* part2 = reinterpret_cast<const uint64_t*>(part);
-        for (int e = tid; e < nrep * ne2; e += DEC_THREADS) {
-            const int slot = e / ne2, i = e - slot * ne2;
-            uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride) +
-                            (size_t)p * ne2 + i;
-            __hip_atomic_store(dst, part2[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int sstep = ne2 <= DEC_THREADS ? DEC_THREADS / ne2 : 1;
+        const int s0 = ne2 <= DEC_THREADS ? tid / ne2 : 0;
+        if (s0 < sstep) {
+            for (int i = tid - s0 * ne2; i < ne2; i += DEC_THREADS) {
+                const uint64_t v = part2[i];
+                for (int slot = s0; slot < nrep; slot += sstep) {
+                    uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride) +
+                                    (size_t)p * ne2 + i;
+                    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
         }
         wait_all_mem();
         __syncthreads();
@@ -209,8 +182,9 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     float* part = a.partial + (size_t)p * 16 * a.RC;
 #pragma unroll
     for (int i = 0; i < DEC_EC_MAXI; ++i) {
-        const int c = (w + 4 * i) * 16 + (l & 15);
-        if (w + 4 * i < CBE && c < a.RC) {
+        const int cb = w + 4 * i;
+        const int c = cb < ec_blocks(r) ? ec_col(r, cb, l & 15) : -1;
+        if (c >= 0) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = 4 * (l >> 4) + v;
@@ -229,16 +203,45 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
         return;
     if (tid == 0)
         atomic_store_dev(&a.flags[0], 0u);
-    float* tsum = reinterpret_cast<float*>(smem);          // [M][RC]
+    float* red = reinterpret_cast<float*>(smem);            // [ng][ne] (ng > 1 only: <= 256 floats)
+    float* tsum = red + DEC_THREADS;                        // [M][RC]
     float* gl = tsum + 16 * a.RC;                           // [16]
     uint16_t* tg = reinterpret_cast<uint16_t*>(gl + 16);    // [M][r_pad]
     const int ne = M * a.RC;
-    for (int e = tid; e < ne; e += DEC_THREADS) {
+    // ng thread groups split the P slices (slice q -> group q mod ng); each
+    // thread keeps 8 loads in flight, and the groups' sums are added in
+    // group order, so the result does not depend on timing
+    const int ng = max(1, min(a.P, DEC_THREADS / ne));
+    const size_t qs = (size_t)16 * a.RC;
+    for (int e0 = tid; e0 < ne * ng; e0 += DEC_THREADS) {
+        const int g = e0 / ne, e = e0 - g * ne;
         const float* src = a.partial + e;
         float t = 0.0f;
-        for (int q = 0; q < a.P; ++q)
-            t += ld4_dev(src + (size_t)q * 16 * a.RC);
-        tsum[e] = t;
+        int q = g;
+        for (; q + 7 * ng < a.P; q += 8 * ng) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = ld4_dev(src + (size_t)(q + i * ng) * qs);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t += v[i];
+        }
+        for (; q < a.P; q += ng)
+            t += ld4_dev(src + (size_t)q * qs);
+        if (ng > 1)
+            red[e0] = t;
+        else
+            tsum[e] = t;
+    }
+    if (ng > 1) {
+        __syncthreads();
+        for (int e = tid; e < ne; e += DEC_THREADS) {
+            float t = red[e];
+            for (int g = 1; g < ng; ++g)
+                t += red[g * ne + e];
+            tsum[e] = t;
+        }
     }
     __syncthreads();
     if (tid < M)
@@ -252,10 +255,16 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     __syncthreads();
     const int n8 = nt / 4;                                  // 8-byte words of T_g
     const uint64_t* tg8 = reinterpret_cast<const uint64_t*>(tg);
-    for (int e = tid; e < nrep * n8; e += DEC_THREADS) {
-        const int slot = e / n8, i = e - slot * n8;
-        uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride);
-        __hip_atomic_store(dst + i, tg8[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int sstep = n8 <= DEC_THREADS ? DEC_THREADS / n8 : 1;   // thread -> (word, slots s0 + j sstep)
+    const int s0 = n8 <= DEC_THREADS ? tid / n8 : 0;
+    if (s0 < sstep) {
+        for (int i = tid - s0 * n8; i < n8; i += DEC_THREADS) {
+            const uint64_t v = tg8[i];
+            for (int slot = s0; slot < nrep; slot += sstep) {
+                uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride);
+                __hip_atomic_store(dst + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
     }
     wait_all_mem();
     __syncthreads();
@@ -517,48 +526,54 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
         __syncthreads();
         if (a.single) {
-            // the P partials of this slot, [P][ne2] float pairs: load a chunk of
-            // them at once into LDS, then add them up in slice order
+            // the P partials of this slot, [P][2 ne2] floats: ng thread groups
+            // split the slices (slice q -> group q mod ng), each thread keeping
+            // 8 loads in flight; the group sums are added in group order
             const int ne = M * a.RC;
             const int ne2 = (ne + 1) >> 1;
-            const uint64_t* src2 = reinterpret_cast<const uint64_t*>(sdata);
-            uint64_t* stage = reinterpret_cast<uint64_t*>(tgl + 16 * a.r_pad);   // [chunk][ne2]
-            const int pc = max(1, (int)(DEC_SUM_STAGE_BYTES / 8 / ne2));       // slices per chunk
-            float tacc[(4 * 257 + DEC_THREADS - 1) / DEC_THREADS];
+            const int ng = max(1, min(a.P, DEC_THREADS / ne));
+            const float* src = reinterpret_cast<const float*>(sdata);
+            const size_t qs = (size_t)2 * ne2;
+            float* gred = reinterpret_cast<float*>(tgl + 16 * a.r_pad);   // [ng][ne], ng > 1 only
+            for (int e0 = tid; e0 < ne * ng; e0 += DEC_THREADS) {
+                const int g = e0 / ne, e = e0 - g * ne;
+                const float* sp = src + e;
+                float t = 0.0f;
+                int q = g;
+                for (; q + 7 * ng < a.P; q += 8 * ng) {
+                    float v[8];
 #pragma unroll
-            for (int i = 0; i < (int)(sizeof(tacc) / sizeof(float)); ++i)
-                tacc[i] = 0.0f;
-            for (int q0 = 0; q0 < a.P; q0 += pc) {
-                const int nq = min(pc, a.P - q0);
-                for (int e = tid; e < nq * ne2; e += DEC_THREADS)
-                    stage[e] = __hip_atomic_load(src2 + (size_t)q0 * ne2 + e, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-                __syncthreads();
-                const float* sf = reinterpret_cast<const float*>(stage);
+                    for (int i = 0; i < 8; ++i)
+                        v[i] = ld4_dev(sp + (size_t)(q + i * ng) * qs);
 #pragma unroll
-                for (int i = 0; i < (int)(sizeof(tacc) / sizeof(float)); ++i) {
-                    const int e = tid + DEC_THREADS * i;
-                    if (e < ne)
-                        for (int q = 0; q < nq; ++q)
-                            tacc[i] += sf[q * 2 * ne2 + e];
+                    for (int i = 0; i < 8; ++i)
+                        t += v[i];
                 }
-                __syncthreads();
+                for (; q < a.P; q += ng)
+                    t += ld4_dev(sp + (size_t)q * qs);
+                if (ng > 1)
+                    gred[e0] = t;
+                else
+                    tsum[e] = t;
             }
-#pragma unroll
-            for (int i = 0; i < (int)(sizeof(tacc) / sizeof(float)); ++i) {
-                const int e = tid + DEC_THREADS * i;
-                if (e < ne)
-                    tsum[e] = tacc[i];
+            if (ng > 1) {
+                __syncthreads();
+                for (int e = tid; e < ne; e += DEC_THREADS) {
+                    float t = gred[e];
+                    for (int g = 1; g < ng; ++g)
+                        t += gred[g * ne + e];
+                    tsum[e] = t;
+                }
             }
             __syncthreads();
             if (tid < 16)
                 gl[tid] = tid < M ? sigmoid_f32(tsum[tid * a.RC + a.r] + a.b_g) : 0.0f;
             __syncthreads();
-            for (int e = tid; e < 16 * a.r_pad; e += DEC_THREADS) {
-                const int m = e / a.r_pad, c = e - m * a.r_pad;
-                const float v = (m < M && c < a.r) ? gl[m] * tsum[m * a.RC + c] : 0.0f;
-                tgl[e] = f32_to_act<ACT>(v);
-            }
+            // rows m >= M of T_g are left as they are: they only reach rows of
+            // the epilogue product that are never stored
+            for (int m = 0; m < M; ++m)
+                for (int c = tid; c < a.r_pad; c += DEC_THREADS)
+                    tgl[m * a.r_pad + c] = f32_to_act<ACT>(c < a.r ? gl[m] * tsum[m * a.RC + c] : 0.0f);
             __syncthreads();
         }
     } else {
@@ -633,29 +648,32 @@ constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS
 
 bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
 
-size_t decode_lds_bytes(const DecodePlan& p, int M, int K, int r)
+// LDS of the main role: the staged activations, then (after the stream)
+// the wavefront reduction, partial sums, gate, T_g and the hand-over group sums
+static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r)
 {
-    // main role, after the stream: wavefront reduction, partial sums, gate, T_g,
-    // staged hand-over partials
     size_t b = (size_t)4 * p.CB * 64 * 16 + (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2 +
-               (p.single ? DEC_SUM_STAGE_BYTES + 16 : 0);
-    if (p.xlds) {
-        size_t xs = (size_t)M * K * 2;
-        if (xs > b) b = xs;
-    }
-    if (p.P > 0) {
-        size_t at = (size_t)((r + 1 + 15) / 16 * 16) * (p.KS + 8) * 2;      // transposed slice
-        size_t fin = (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2; // final reduction
-        if (at > b) b = at;
-        if (fin > b) b = fin;
-    }
+               (p.single ? DEC_THREADS * 4 : 0);
+    if (p.xlds)
+        b = std::max(b, (size_t)M * K * 2);
     return (b + 15) / 16 * 16;
 }
 
+// LDS of the EC role: the staged slice and gate vector, then the final reduction
+static size_t ec_lds_bytes(const DecodePlan& p, int r)
+{
+    if (p.P == 0)
+        return 0;
+    const size_t at = (size_t)ec_slice_bytes(r, p.KS) + (size_t)p.KS * 2;
+    const size_t fin = (size_t)DEC_THREADS * 4 + (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2;
+    return (std::max(at, fin) + 15) / 16 * 16;
+}
+
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
-static hipError_t launch_decode_t(const DecodeKArgs& k, size_t lds, hipStream_t st)
+static hipError_t launch_decode_t(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>;
+    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r), ec_lds_bytes(p, k.r));
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
@@ -666,27 +684,27 @@ static hipError_t launch_decode_t(const DecodeKArgs& k, size_t lds, hipStream_t 
 }
 
 template <int ACT, bool GROUPED, bool STAGE_FIRST>
-static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, size_t lds, hipStream_t st)
+static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     if (p.xlds) {
         const size_t xch = ((size_t)k.M * k.K / 8 + DEC_THREADS - 1) / DEC_THREADS;
         if (xch <= 2)
-            return launch_decode_t<ACT, 1, 2, 8, GROUPED, STAGE_FIRST>(k, lds, st);
-        return launch_decode_t<ACT, 1, DEC_XLDS_CHUNKS, 8, GROUPED, STAGE_FIRST>(k, lds, st);
+            return launch_decode_t<ACT, 1, 2, 8, GROUPED, STAGE_FIRST>(k, p, st);
+        return launch_decode_t<ACT, 1, DEC_XLDS_CHUNKS, 8, GROUPED, STAGE_FIRST>(k, p, st);
     }
     if (p.CB == 1)
-        return launch_decode_t<ACT, 1, 0, 4, GROUPED, false>(k, lds, st);
-    return launch_decode_t<ACT, 2, 0, 4, GROUPED, false>(k, lds, st);
+        return launch_decode_t<ACT, 1, 0, 4, GROUPED, false>(k, p, st);
+    return launch_decode_t<ACT, 2, 0, 4, GROUPED, false>(k, p, st);
 }
 
 template <int ACT>
-static hipError_t launch_decode_act(const DecodeKArgs& k, const DecodePlan& p, size_t lds, hipStream_t st)
+static hipError_t launch_decode_act(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     if (k.G != k.K)
-        return p.stage_first ? launch_decode_grp<ACT, true, true>(k, p, lds, st)
-                             : launch_decode_grp<ACT, true, false>(k, p, lds, st);
-    return p.stage_first ? launch_decode_grp<ACT, false, true>(k, p, lds, st)
-                         : launch_decode_grp<ACT, false, false>(k, p, lds, st);
+        return p.stage_first ? launch_decode_grp<ACT, true, true>(k, p, st)
+                             : launch_decode_grp<ACT, true, false>(k, p, st);
+    return p.stage_first ? launch_decode_grp<ACT, false, true>(k, p, st)
+                         : launch_decode_grp<ACT, false, false>(k, p, st);
 }
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st)
@@ -711,10 +729,9 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.rep_ctrl = (uint8_t*)(a.ws + p.off_rep_ctrl);
     k.rep_data = (uint8_t*)(a.ws + p.off_rep_data);
     k.rep_data_stride = p.rep_data_stride;
-    const size_t lds = decode_lds_bytes(p, a.M, a.K, a.r);
     if (a.act == ACT_F16)
-        return launch_decode_act<ACT_F16>(k, p, lds, st);
-    return launch_decode_act<ACT_BF16>(k, p, lds, st);
+        return launch_decode_act<ACT_F16>(k, p, st);
+    return launch_decode_act<ACT_BF16>(k, p, st);
 }
 
 }  // namespace w4ec

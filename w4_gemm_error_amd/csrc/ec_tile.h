@@ -1,128 +1,107 @@
-// ec_tile.h -- internal to libw4ec: the gate / low-rank down-projection
-// pass, [T | l] = X [A | w_g], as MFMA tiles (shared by the decode kernel's
-// EC workgroups and the prefill prepass).
+// ec_tile.h -- internal to libw4ec: LDS staging of [A | w_g] slices for the
+// gate / low-rank down-projection, [T | l] = X [A | w_g], as MFMA tiles
+// (shared by the decode kernel's EC workgroups and the prefill prepass).
 //
-// A is row-major [K, r] (contiguous along the rank), but an MFMA operand
-// wants 8 consecutive k per lane; so each 64-deep slice of [A | w_g] is
-// staged transposed in LDS (at[c][k]) by the whole workgroup, from 16-byte
-// global loads that are prefetched into registers one slice ahead.
+// A is row-major [K, r]: a slice of rows [k0, k0 + kc) is one contiguous
+// block, copied verbatim into LDS with direct global-to-LDS 16-byte loads
+// (no registers, no per-element index arithmetic).  An MFMA B operand wants
+// 8 consecutive k of one column per lane; gfx950's LDS transpose read
+// (ds_read_b64_tr_b16) delivers exactly that from the row-major slice: in
+// each group of 16 lanes, output lane i, element j is element (i mod 4) of
+// the 8 bytes addressed by lane 4 j + i / 4.  So when lane 4 q + u of the
+// group points at row k + q, columns n0 + 4 u .. n0 + 4 u + 3, lane i
+// receives column n0 + i at rows k .. k + 3.
+//
+// Column blocks: cb < ec_a_blocks(r) hold 16 columns of A (columns >= r of
+// the last block read past the row and are discarded); block ec_a_blocks(r)
+// holds the gate vector as its column 0 (zero elsewhere, and all zero when
+// there is no gate, i.e. a zero gate logit).
 #pragma once
 
 #include "w4ec_common.h"
 
 namespace w4ec {
 
-constexpr int EC_KT = 64;                  // k per staged slice
-constexpr int EC_LDS_STRIDE = EC_KT + 8;   // halves per transposed row (16-byte aligned rows)
-constexpr int EC_MAX_COLS = 272;           // (256 + 1) rounded up to 16
-constexpr int EC_LDS_HALVES = EC_MAX_COLS * EC_LDS_STRIDE;
-constexpr int EC_THREADS = 256;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-__device__ inline int ec_col_blocks(int r) { return (r + 1 + 15) >> 4; }
+// halves per LDS row of an A slice (the transpose read needs 8-byte aligned rows)
+__host__ __device__ inline int ec_pitch(int r) { return (r + 3) & ~3; }
+// column blocks of A, and the total including the gate block
+__host__ __device__ inline int ec_a_blocks(int r) { return (r + 15) >> 4; }
+__host__ __device__ inline int ec_blocks(int r) { return ec_a_blocks(r) + 1; }
+// LDS bytes of a staged slice of kc rows (plus slack for the last block's
+// over-read) and of its gate vector
+__host__ __device__ inline int ec_slice_bytes(int r, int kc) { return (kc * ec_pitch(r) + 16) * 2; }
 
-// One workgroup (EC_THREADS threads) computes, for the 16 rows that the
-// calling wavefront's lanes point at (xrow = this lane's row, already
-// clamped to a valid token), the fragments of X[:, kbeg:kend) [A|w_g] for
-// column blocks cb = cb_first + i * CB_STEP (i < MAXI, cb < CBE), into
-// acc[i] (v_mfma_f32_16x16x32 C layout: column 16 cb + (l & 15), rows
-// 4 (l >> 4) + v).  kbeg, kend are multiples of 64.  All threads must call.
-//
-// ACH 16-byte chunks of A per thread are prefetched one slice ahead (enough
-// for 8 * ACH columns of A); chunks beyond that are read when stored.
-template <int ACT, int CB_STEP, int MAXI, int ACH>
-__device__ void ec_tile(const uint16_t* __restrict__ X, int K, int xrow,
-                        const uint16_t* __restrict__ A, const uint16_t* __restrict__ w_g, int r,
-                        int kbeg, int kend, int cb_first, uint16_t* at, floatx4 (&acc)[MAXI])
+// 16 bytes from global memory into LDS; lds_base is wavefront-uniform and
+// lane l's bytes land at lds_base + 16 l
+__device__ inline void copy16_to_lds(const void* src, void* lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Stage rows [k0, k0 + kc) of A into at[kc][ec_pitch(r)] and w_g[k0, k0 + kc)
+// into wgl[kc] (kc a multiple of 64, <= 512; k0 a multiple of 64).  Every
+// thread of the 256 calls; the caller waits for the loads (s_waitcnt
+// vmcnt) and synchronizes before reading.
+__device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* __restrict__ w_g, int r,
+                                int k0, int kc, uint16_t* at, uint16_t* wgl)
 {
     const int tid = threadIdx.x;
     const int l = tid & 63;
-    const int koff = 8 * (l >> 4);
-    const int CBE = ec_col_blocks(r);
-    const int cols = CBE * 16;
-    const bool vec = (r & 7) == 0;
-    const int cpr = r >> 3;                 // 16-byte chunks per row of A (vector path)
-    const int nch = EC_KT * cpr;            // chunks per slice (<= 64 * 32)
-
-#pragma unroll
-    for (int i = 0; i < MAXI; ++i)
-        acc[i] = (floatx4){0.f, 0.f, 0.f, 0.f};
-
-    // constant columns: padding beyond the gate, and the gate when absent
-    for (int idx = tid; idx < (cols - r) * EC_KT; idx += EC_THREADS) {
-        const int c = r + idx / EC_KT, kk = idx % EC_KT;
-        if (c > r || !w_g)
-            at[c * EC_LDS_STRIDE + kk] = 0;
-    }
-
-    const uint16_t* xp = X + (size_t)xrow * K + koff;
-    u32x4 ach[ACH];
-    uint16_t gv = 0;
-    u32x4 xn0, xn1;
-    auto gload = [&](int k) {
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < ACH; ++i) {
-                const int ch = tid + EC_THREADS * i;
-                if (ch < nch) {
-                    const int kk = ch % EC_KT, cc = (ch / EC_KT) * 8;
-                    ach[i] = ld16(A + (size_t)(k + kk) * r + cc);
-                }
-            }
-        }
-        if (w_g && tid < EC_KT)
-            gv = w_g[k + tid];
-        xn0 = ld16(xp + k);
-        xn1 = ld16(xp + k + 32);
-    };
-    auto lstore = [&](int k) {
-        if (vec) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int ch = tid + EC_THREADS * i;
-                if (ch < nch) {
-                    const int kk = ch % EC_KT, cc = (ch / EC_KT) * 8;
-                    const u32x4 v = (i < ACH) ? ach[i < ACH ? i : 0] : ld16(A + (size_t)(k + kk) * r + cc);
-                    const uint32_t w0 = v.x, w1 = v.y, w2 = v.z, w3 = v.w;
-                    uint16_t* dst = at + cc * EC_LDS_STRIDE + kk;
-                    dst[0 * EC_LDS_STRIDE] = (uint16_t)(w0 & 0xFFFF);
-                    dst[1 * EC_LDS_STRIDE] = (uint16_t)(w0 >> 16);
-                    dst[2 * EC_LDS_STRIDE] = (uint16_t)(w1 & 0xFFFF);
-                    dst[3 * EC_LDS_STRIDE] = (uint16_t)(w1 >> 16);
-                    dst[4 * EC_LDS_STRIDE] = (uint16_t)(w2 & 0xFFFF);
-                    dst[5 * EC_LDS_STRIDE] = (uint16_t)(w2 >> 16);
-                    dst[6 * EC_LDS_STRIDE] = (uint16_t)(w3 & 0xFFFF);
-                    dst[7 * EC_LDS_STRIDE] = (uint16_t)(w3 >> 16);
-                }
-            }
-        } else {
-            for (int idx = tid; idx < EC_KT * r; idx += EC_THREADS) {
-                const int kk = idx / r, c = idx - kk * r;
-                at[c * EC_LDS_STRIDE + kk] = A[(size_t)(k + kk) * r + c];
-            }
-        }
-        if (w_g && tid < EC_KT)
-            at[r * EC_LDS_STRIDE + tid] = gv;
-    };
-
-    if (kbeg < kend)
-        gload(kbeg);
-    for (int k = kbeg; k < kend; k += EC_KT) {
-        __syncthreads();                 // the previous slice has been consumed
-        lstore(k);
-        const u32x4 x0 = xn0, x1 = xn1;
-        __syncthreads();
-        if (k + EC_KT < kend)
-            gload(k + EC_KT);
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int cb = cb_first + i * CB_STEP;
-            if (cb < CBE) {
-                const uint16_t* bp = at + (cb * 16 + (l & 15)) * EC_LDS_STRIDE + koff;
-                acc[i] = mfma16x16x32<ACT>(x0, *reinterpret_cast<const u32x4*>(bp), acc[i]);
-                acc[i] = mfma16x16x32<ACT>(x1, *reinterpret_cast<const u32x4*>(bp + 32), acc[i]);
-            }
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if ((r & 3) == 0) {
+        // pitch == r: the LDS slice is a byte copy of the global one (16-byte
+        // aligned: k0 r 2 is a multiple of 128)
+        const int bytes = kc * r * 2;
+        const char* src = reinterpret_cast<const char*>(A + (size_t)k0 * r);
+        for (int off = w * 1024; off < bytes; off += 4096)
+            if (off + 16 * l < bytes)
+                copy16_to_lds(src + off + 16 * l, reinterpret_cast<char*>(at) + off);
+    } else {
+        const int pitch = ec_pitch(r);
+        for (int idx = tid; idx < kc * r; idx += 256) {
+            const int kk = idx / r, c = idx - kk * r;
+            at[kk * pitch + c] = A[(size_t)(k0 + kk) * r + c];
         }
     }
+    if (w_g && w == 0 && 8 * l < kc)
+        copy16_to_lds(w_g + k0 + 8 * l, wgl);
+}
+
+// B fragment of v_mfma_f32_16x16x32 for column block cb, rows krow .. krow + 31
+// of the staged slice: lane l gets column 16 cb + (l & 15) at rows
+// krow + 8 (l >> 4) + t, t = 0..7.
+__device__ inline u32x4 ec_bfrag(const uint16_t* at, const uint16_t* wgl, int r, bool gate, int cb, int krow)
+{
+    const int l = threadIdx.x & 63;
+    const int g = l >> 4;
+    if (cb == ec_a_blocks(r)) {
+        if (!gate || (l & 15) != 0)
+            return (u32x4){0u, 0u, 0u, 0u};
+        return *reinterpret_cast<const u32x4*>(wgl + krow + 8 * g);
+    }
+    const int pitch = ec_pitch(r);
+    const int s = l & 15;
+    const uint16_t* p = at + (krow + 8 * g + (s >> 2)) * pitch + 16 * cb + 4 * (s & 3);
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * pitch));
+    return (u32x4){(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
+                   (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
+                   (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
+                   (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+}
+
+// Column of the [T | l] partial held by lane column j of block cb, or -1
+// when that column is discarded.
+__device__ inline int ec_col(int r, int cb, int j)
+{
+    if (cb == ec_a_blocks(r))
+        return j == 0 ? r : -1;
+    const int c = 16 * cb + j;
+    return c < r ? c : -1;
 }
 
 }  // namespace w4ec

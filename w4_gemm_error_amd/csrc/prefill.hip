@@ -7,7 +7,9 @@
 // separate kernel; this library instead folds the gated correction into the
 // GEMM epilogue as r extra terms of the reduction (T_g B), and keeps the only
 // part that needs a full pass over K -- the gate logit X . w_g and T = X A --
-// in a prepass that reads X once for all r + 1 columns.
+// in a prepass that reads X once for all r + 1 columns (K-sliced partial
+// sums), followed by a small kernel that adds the slices and applies the
+// gate.
 //
 // GEMM tiling for gfx950 (wave64, 16x16x32 MFMA, 160 KB LDS per CU):
 //  * workgroup tile BM x 256 (BM = 64 or 128 tokens), 4 wavefronts; wavefront
@@ -37,95 +39,116 @@ struct PrepassKArgs {
     const uint16_t* X;
     const uint16_t* A;
     const uint16_t* w_g;
-    float b_g;
-    int M, K, r, r_pad, kc, ks;
-    floatx4* partial;   // [mt][ks][4 wavefronts][17 column blocks][64 lanes]
-    uint32_t* cnt;      // [mt]
-    uint16_t* tg;       // [Mpad][r_pad], activation format
+    int M, K, r, kc, ks;
+    floatx4* partial;   // [pre_mt][ks][4 wavefronts][ec_blocks(r)][64 lanes]
 };
 
-constexpr int PRE_MAXI = 17;   // (256 + 1 + 15) / 16 column blocks of [A | w_g]
+constexpr int PRE_MAXB = 17;   // column blocks of [A | w_g] (r <= 256), gate block included
+constexpr int PRE_MAXS = 16;   // 32-k steps per workgroup (kc <= 512)
 
-// 64 tokens x one K slice per workgroup (wavefront w: tokens 16 w .. 16 w + 15).
-// With a split over K, the last workgroup of a token tile adds the slices'
-// fragments in a fixed order.  It then applies the gate and stores
-// T_g = g * T in the activation format for the GEMM epilogue.
+// One workgroup: 64 tokens (wavefront w: tokens 16 w .. 16 w + 15) x one K
+// slice of at most 512.  Every load is issued at once -- the X fragments
+// into registers, the slice of [A | w_g] straight into LDS -- then each
+// wavefront runs the MFMAs for all column blocks and stores its fragments.
+// The slices are added by ec_reduce_kernel, in slice order.
 template <int ACT>
 __global__ __launch_bounds__(PF_THREADS)
 void prepass_kernel(PrepassKArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t at[EC_LDS_HALVES];
-    __shared__ float gsh[64];
-    __shared__ uint32_t s_old;
+    extern __shared__ __attribute__((aligned(16))) uint8_t psmem[];
     const int tid = threadIdx.x;
     const int l = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mt = blockIdx.x;
-    const int kz = blockIdx.y;
-    const int m0 = mt * 64;
-    const int kbeg = kz * a.kc;
-    const int kend = min(a.K, kbeg + a.kc);
-    const int xrow = min(m0 + 16 * w + (l & 15), a.M - 1);
-    const int CBE = ec_col_blocks(a.r);
+    const int z = blockIdx.y;
+    const int kbeg = z * a.kc;
+    const int len = min(a.kc, a.K - kbeg);          // multiple of 64
+    const int xrow = min(mt * 64 + 16 * w + (l & 15), a.M - 1);
+    const int nb = ec_blocks(a.r);
+    const bool gate = a.w_g != nullptr;
+    uint16_t* at = reinterpret_cast<uint16_t*>(psmem);
+    uint16_t* wgl = at + len * ec_pitch(a.r) + 16;
 
-    floatx4 acc[PRE_MAXI];
-    ec_tile<ACT, 1, PRE_MAXI, 8>(a.X, a.K, xrow, a.A, a.w_g, a.r, kbeg, kend, 0, at, acc);
+    const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + 8 * (l >> 4);
+    u32x4 xf[PRE_MAXS];
+#pragma unroll
+    for (int s = 0; s < PRE_MAXS; ++s)
+        if (32 * s < len)
+            xf[s] = ld16(xp + 32 * s);
+    ec_stage(a.A, a.w_g, a.r, kbeg, len, at, wgl);
+    wait_all_mem();
+    __syncthreads();
 
-    if (a.ks > 1) {
-        floatx4* mine = a.partial + ((size_t)(mt * a.ks + kz) * 4 + w) * PRE_MAXI * 64;
+    floatx4 acc[PRE_MAXB];
 #pragma unroll
-        for (int i = 0; i < PRE_MAXI; ++i)
-            if (i < CBE)
-                st16_dev(mine + i * 64 + l, acc[i]);
-        wait_all_mem();
-        __syncthreads();
-        if (tid == 0)
-            s_old = atomic_add_dev(&a.cnt[mt], 1u);
-        __syncthreads();
-        if (s_old != (uint32_t)(a.ks - 1))
-            return;
-        if (tid == 0)
-            atomic_store_dev(&a.cnt[mt], 0u);
+    for (int cb = 0; cb < PRE_MAXB; ++cb) {
+        acc[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        if (cb < nb) {
 #pragma unroll
-        for (int i = 0; i < PRE_MAXI; ++i) {
-            if (i < CBE) {
-                floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
-                for (int z = 0; z < a.ks; ++z)
-                    t += (z == kz) ? acc[i]
-                                   : ld16_dev(a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * PRE_MAXI * 64 + i * 64 + l);
-                acc[i] = t;
-            }
+            for (int s = 0; s < PRE_MAXS; ++s)
+                if (32 * s < len)
+                    acc[cb] = mfma16x16x32<ACT>(xf[s], ec_bfrag(at, wgl, a.r, gate, cb, 32 * s), acc[cb]);
         }
     }
-
-    // gate: column r lives in block r / 16, lanes with (l & 15) == r % 16
-    const int cg = a.r >> 4;
+    floatx4* mine = a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * nb * 64;
 #pragma unroll
-    for (int i = 0; i < PRE_MAXI; ++i) {
-        if (i == cg && (l & 15) == (a.r & 15)) {
+    for (int cb = 0; cb < PRE_MAXB; ++cb)
+        if (cb < nb)
+            mine[cb * 64 + l] = acc[cb];
+}
+
+struct EcReduceKArgs {
+    const floatx4* partial;
+    uint16_t* tg;       // [Mpad][r_pad], activation format
+    float b_g;
+    int r, r_pad, ks;
+};
+
+// One workgroup per 16 tokens: adds the K slices' fragments in slice order,
+// applies the gate and stores T_g = g * T (zero in columns r .. r_pad - 1).
+template <int ACT>
+__global__ __launch_bounds__(PF_THREADS)
+void ec_reduce_kernel(EcReduceKArgs a)
+{
+    constexpr int TP = 260;                          // LDS row of T: r + 1 <= 257 columns
+    __shared__ float tl[16][TP];
+    __shared__ float gl[16];
+    const int tid = threadIdx.x;
+    const int rb = blockIdx.x;                       // rows 16 rb .. 16 rb + 15
+    const int mt = rb >> 2, w = rb & 3;
+    const int ne = ec_blocks(a.r) * 64;              // fragments per slice of this row block
+    const floatx4* base = a.partial + ((size_t)mt * a.ks * 4 + w) * ne;
+    const size_t zs = (size_t)4 * ne;
+    for (int e = tid; e < ne; e += PF_THREADS) {
+        const floatx4* src = base + e;
+        floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
+        int z = 0;
+        for (; z + 8 <= a.ks; z += 8) {
+            floatx4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = src[(size_t)(z + i) * zs];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t += v[i];
+        }
+        for (; z < a.ks; ++z)
+            t += src[(size_t)z * zs];
+        const int l = e & 63;
+        const int c = ec_col(a.r, e >> 6, l & 15);
+        if (c >= 0) {
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                gsh[16 * w + 4 * (l >> 4) + v] = sigmoid_f32(acc[i][v] + a.b_g);
+                tl[4 * (l >> 4) + v][c] = t[v];
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PRE_MAXI; ++i) {
-        const int c = i * 16 + (l & 15);
-        if (i < CBE && c < a.r_pad) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int mloc = 16 * w + 4 * (l >> 4) + v;
-                const float val = c < a.r ? gsh[mloc] * acc[i][v] : 0.0f;
-                a.tg[(size_t)(m0 + mloc) * a.r_pad + c] = f32_to_act<ACT>(val);
-            }
-        }
-    }
-    const int c0 = CBE * 16;
-    for (int e = tid; e < 64 * (a.r_pad - c0); e += PF_THREADS) {
-        const int mloc = e / (a.r_pad - c0), c = c0 + e % (a.r_pad - c0);
-        a.tg[(size_t)(m0 + mloc) * a.r_pad + c] = 0;
-    }
+    if (tid < 16)
+        gl[tid] = sigmoid_f32(tl[tid][a.r] + a.b_g);
+    __syncthreads();
+    for (int row = 0; row < 16; ++row)
+        for (int c = tid; c < a.r_pad; c += PF_THREADS)
+            a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = f32_to_act<ACT>(c < a.r ? gl[row] * tl[row][c] : 0.0f);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -405,6 +428,11 @@ static hipError_t launch_gemm_act(const GemmKArgs& k, int BM, bool grouped, hipS
     return grouped ? launch_gemm_t<ACT, 128, true>(k, st) : launch_gemm_t<ACT, 128, false>(k, st);
 }
 
+size_t prepass_lds_bytes(int r, int kc)
+{
+    return (size_t)ec_slice_bytes(r, kc) + (size_t)kc * 2;
+}
+
 hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st)
 {
     BlobGeom g = blob_geom(a.N, a.K, a.G);
@@ -414,18 +442,28 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
         q.X = (const uint16_t*)a.X;
         q.A = (const uint16_t*)a.A;
         q.w_g = (const uint16_t*)a.w_g;
-        q.b_g = a.b_g;
-        q.M = a.M; q.K = a.K; q.r = a.r; q.r_pad = p.r_pad;
+        q.M = a.M; q.K = a.K; q.r = a.r;
         q.kc = p.pre_kc; q.ks = p.pre_ks;
         q.partial = (floatx4*)(a.ws + p.off_pre_partial);
-        q.cnt = (uint32_t*)(a.ws + p.off_pre_cnt);
-        q.tg = tg;
-        dim3 grid(p.pre_mt, p.pre_ks);
-        if (a.act == ACT_F16)
-            hipLaunchKernelGGL(prepass_kernel<ACT_F16>, grid, dim3(PF_THREADS), 0, st, q);
-        else
-            hipLaunchKernelGGL(prepass_kernel<ACT_BF16>, grid, dim3(PF_THREADS), 0, st, q);
+        const size_t lds = prepass_lds_bytes(a.r, p.pre_kc);
+        auto pk = a.act == ACT_F16 ? prepass_kernel<ACT_F16> : prepass_kernel<ACT_BF16>;
+        if (lds > 64 * 1024) {
+            hipError_t e = hipFuncSetAttribute((const void*)pk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess)
+                return e;
+        }
+        hipLaunchKernelGGL(pk, dim3(p.pre_mt, p.pre_ks), dim3(PF_THREADS), lds, st, q);
         hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        EcReduceKArgs rq;
+        rq.partial = q.partial;
+        rq.tg = tg;
+        rq.b_g = a.b_g;
+        rq.r = a.r; rq.r_pad = p.r_pad; rq.ks = p.pre_ks;
+        auto rk = a.act == ACT_F16 ? ec_reduce_kernel<ACT_F16> : ec_reduce_kernel<ACT_BF16>;
+        hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4), dim3(PF_THREADS), 0, st, rq);
+        e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }

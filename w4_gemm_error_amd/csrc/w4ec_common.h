@@ -298,6 +298,7 @@ constexpr uint32_t SPIN_LIMIT = 1u << 22;
 // ------------------------------------------------------------ launch plans
 // (shared by the host dispatch and the workspace sizing)
 
+constexpr int DEC_EC_KS = 256;   // at most this many k per decode EC workgroup
 constexpr int DEC_NREP = 32;                    // replica slots of the decode hand-over
 constexpr size_t DEC_REP_CTRL_STRIDE = 4096;    // control words of one slot (own page)
 
@@ -322,9 +323,9 @@ struct PrefillPlan {
     int ksplit;     // GEMM split over K
     int pre_mt;     // prepass tiles of 64 tokens
     int pre_ks;     // prepass split over K
-    int pre_kc;     // k per prepass split (multiple of 64)
+    int pre_kc;     // k per prepass split (multiple of 64, <= 512)
     int r_pad, Mpad;
-    size_t off_pre_cnt, off_gemm_cnt, off_pre_partial, off_tg, off_gemm_partial, bytes;
+    size_t off_gemm_cnt, off_pre_partial, off_tg, off_gemm_partial, bytes;
 };
 
 }  // namespace w4ec

@@ -31,5 +31,6 @@ struct LayerArgs {
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
 bool decode_use_xlds(int M, int K);
 hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
+size_t prepass_lds_bytes(int r, int kc);
 
 }  // namespace w4ec
