@@ -24,6 +24,8 @@
 //    them in a fixed order, then runs the epilogue;
 //  * tile ids are remapped so that the workgroups an XCD receives (block ids
 //    congruent mod 8) share rows of X and columns of W in that XCD's L2.
+#include <type_traits>
+
 #include "ec_tile.h"
 #include "w4ec_common.h"
 #include "w4ec_launch.h"
@@ -32,6 +34,12 @@ namespace w4ec {
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_BN = 256;
+// GEMM: 8 wavefronts (two per SIMD, so that one's dequantization and loads
+// run under the other's MFMAs), each owning JW = 2 column blocks (32
+// columns) of the 256-column tile for all BM rows
+constexpr int GEMM_THREADS = 512;
+constexpr int NW = GEMM_THREADS / 64;
+constexpr int JW = PF_BN / PANEL_N / NW;
 
 // ---------------------------------------------------------------- prepass
 
@@ -160,7 +168,7 @@ struct GemmKArgs {
     const uint16_t* B;
     const uint16_t* tg;
     uint16_t* Y;
-    floatx4* partial;  // [tile][ksplit][4][RB][4][64] fragments
+    floatx4* partial;  // [tile][ksplit][NW][RB][JW][64] fragments
     uint32_t* cnt;     // [mt*nt]
     int M, N, K, r, r_pad, G, NB, KB, Npad, mt, nt, ksplit, Mpad;
 };
@@ -183,164 +191,248 @@ __device__ inline void tile_of(int bid, int mt, int nt, int& tm, int& tn)
     tn = in / gm;
 }
 
+constexpr int YT_PITCH = 264;    // halves per LDS row of the output tile (256 + 8: staggered banks)
+
+template <int BM>
+constexpr int gemm_lds_bytes()
+{
+    return (2 * BM * PANEL_K * 2 > BM * YT_PITCH * 2) ? 2 * BM * PANEL_K * 2 : BM * YT_PITCH * 2;
+}
+
 template <int ACT, int BM, bool GROUPED>
-__global__ __launch_bounds__(PF_THREADS, 1)
+__global__ __launch_bounds__(GEMM_THREADS, BM == 64 ? 2 : 1)
 void prefill_gemm_kernel(GemmKArgs a)
 {
     constexpr int RB = BM / 16;            // 16-row blocks per tile
     constexpr int XROW_BYTES = PANEL_K * 2; // 256 bytes per staged row
-    constexpr int XLOADS = BM * XROW_BYTES / 16 / PF_THREADS;  // 16-byte loads per thread per step
-    __shared__ __attribute__((aligned(16))) uint8_t xs[2][BM * XROW_BYTES];
+    constexpr int XLOADS = BM * XROW_BYTES / 16 / GEMM_THREADS;  // 16-byte loads per thread per step
+    // weight ring: D 128-k steps per wavefront (even, so that the two
+    // activation register sets below alternate with the ring slots)
+    constexpr int D = BM == 128 ? 4 : 2;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[gemm_lds_bytes<BM>()];
     __shared__ uint32_t s_old;
 
     const int tid = threadIdx.x;
     const int l = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tm, tn;
     tile_of(blockIdx.x, a.mt, a.nt, tm, tn);
     const int kz = blockIdx.y;
     const int m0 = tm * BM;
     const int n0 = tn * PF_BN;
-    const int cbw = n0 / PANEL_N + 4 * w;   // first column block of this wavefront
+    const int cbw = n0 / PANEL_N + JW * w;  // first column block of this wavefront
 
     const int kb0 = (int)(((long)kz * a.KB) / a.ksplit);
-    const int kb1 = (int)(((long)(kz + 1) * a.KB) / a.ksplit);
+    const int nk = (int)(((long)(kz + 1) * a.KB) / a.ksplit) - kb0;   // >= 1 steps of 128 k
 
-    // X tile staging: thread -> (row, chunk) for each of its loads
+    // X tile staging: thread -> (row, chunk) for each of its loads; 16-byte
+    // chunks XOR-swizzled by row in LDS
     const uint16_t* xsrc[XLOADS];
     int xdst[XLOADS];
 #pragma unroll
     for (int i = 0; i < XLOADS; ++i) {
-        const int rr = i * (PF_THREADS / 16) + (tid >> 4);
+        const int rr = i * (GEMM_THREADS / 16) + (tid >> 4);
         const int ch = tid & 15;
         const int gm = min(m0 + rr, a.M - 1);
-        xsrc[i] = a.X + (size_t)gm * a.K + ch * 8;
+        xsrc[i] = a.X + (size_t)gm * a.K + (size_t)kb0 * PANEL_K + ch * 8;
         xdst[i] = rr * XROW_BYTES + ((ch ^ (rr & 15)) << 4);
     }
 
-    floatx4 acc[RB][4];
+    int n_j[JW];
+    bool colok[JW];
+    const uint8_t* wsrc[JW];    // this lane's 16 bytes of the first panel of each column block
+    const uint32_t* szsrc[JW];  // scale/zero of this lane's column, group of step 0
+#pragma unroll
+    for (int j = 0; j < JW; ++j) {
+        n_j[j] = (cbw + j) * PANEL_N + (l & 15);
+        colok[j] = (cbw + j) < a.NB;
+        const int cb = min(cbw + j, a.NB - 1);       // past the end: re-read the last block, never stored
+        wsrc[j] = a.codes + ((size_t)cb * a.KB + kb0) * PANEL_BYTES + l * 16;
+        szsrc[j] = a.sz + (size_t)((kb0 * PANEL_K) / a.G) * a.Npad + min(n_j[j], a.Npad - 1);
+    }
+
+    floatx4 acc[RB][JW];
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JW; ++j)
             acc[i][j] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    int n_j[4];
-    bool colok[4];
+    // scale/zero of the current group
+    DqF16 dqh[JW];
+    float dqb[JW];
+    half2_t sh2[JW];
+    float sf[JW];
+    auto set_sz = [&](const uint32_t* v) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        n_j[j] = (cbw + j) * PANEL_N + (l & 15);
-        colok[j] = (cbw + j) < a.NB;
-    }
-
-    // per-channel zero points (and, when grouped, per-group scale/zero)
-    DqF16 dqh[4];
-    float dqb[4];
-    half2_t sh2[4];
-    float sf[4];
-    auto load_sz = [&](int grp) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t v = colok[j] ? a.sz[(size_t)grp * a.Npad + n_j[j]] : 0u;
-            const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFF));
-            const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
-            sf[j] = (float)s;
-            sh2[j] = (half2_t){s, s};
+        for (int j = 0; j < JW; ++j) {
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
+            const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
+            sf[j] = (float)sv;
+            sh2[j] = (half2_t){sv, sv};
             dqh[j] = dq_f16_consts(z);
             dqb[j] = -(8388608.0f + z);
         }
     };
-    int cur_g = (kb0 * PANEL_K) / a.G;
-    load_sz(cur_g);
 
-    u32x4 xr[XLOADS];
-    u32x4 wv[4], wn[4];
-    auto load_x = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < XLOADS; ++i)
-            xr[i] = ld16(xsrc[i] + (size_t)kb * PANEL_K);
+    // Every load below is unconditional (indices clamped to the last step),
+    // so the compiler can count the loads in flight and wait for exactly
+    // the one it needs: the weight ring keeps D - 1 steps in flight behind
+    // the one being multiplied.
+    u32x4 wr[D][JW];
+    uint32_t szr[GROUPED ? D : 1][JW];
+    u32x4 xr[2][XLOADS];        // activations of steps i + 1 and i + 2
+    auto issue_w1 = [&](int u, int i, int j) __attribute__((always_inline)) {
+        const int ic = min(i, nk - 1);
+        if constexpr (GROUPED) {
+            const int gi = ((kb0 + ic) * PANEL_K) / a.G - (kb0 * PANEL_K) / a.G;
+            szr[u][j] = szsrc[j][(size_t)gi * a.Npad];
+        }
+        wr[u][j] = ld16_stream(wsrc[j] + (size_t)ic * PANEL_BYTES);
     };
-    auto load_w = [&](int kb, u32x4* dst) {
+    auto issue_w = [&](int u, int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dst[j] = colok[j] ? ld16_stream(a.codes + ((size_t)(cbw + j) * a.KB + kb) * PANEL_BYTES + l * 16)
-                              : (u32x4){0u, 0u, 0u, 0u};
+        for (int j = 0; j < JW; ++j)
+            issue_w1(u, i, j);
     };
-    auto store_x = [&](int buf) {
+    // part p of 4 (XLOADS / 4 loads each, or all of them with part == -1)
+    auto load_x = [&](int set, int i, int part = -1) __attribute__((always_inline)) {
+        const int ic = min(i, nk - 1);
+        constexpr int PER = XLOADS >= 4 ? XLOADS / 4 : 1;
 #pragma unroll
-        for (int i = 0; i < XLOADS; ++i)
-            st16(&xs[buf][xdst[i]], xr[i]);
+        for (int x = 0; x < XLOADS; ++x)
+            if (part < 0 || x / PER == part)
+                xr[set][x] = ld16(xsrc[x] + (size_t)ic * PANEL_K);
+    };
+    auto store_x = [&](int set, int buf) __attribute__((always_inline)) {
+        uint8_t* dst = smem + buf * (BM * XROW_BYTES);   // arithmetic, not a choice between captures
+#pragma unroll
+        for (int x = 0; x < XLOADS; ++x)
+            st16(dst + xdst[x], xr[set][x]);
     };
 
-    if (kb0 < kb1) {
-        load_x(kb0);
-        load_w(kb0, wv);
-        store_x(0);
+    if constexpr (!GROUPED) {
+        uint32_t v[JW];
+#pragma unroll
+        for (int j = 0; j < JW; ++j)
+            v[j] = *szsrc[j];
+        set_sz(v);
     }
+    load_x(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        issue_w(u, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    store_x(0, 0);
     __syncthreads();
 
-    for (int kb = kb0; kb < kb1; ++kb) {
-        const int cur = (kb - kb0) & 1;
-        const bool more = kb + 1 < kb1;
-        if (more) {
-            load_x(kb + 1);
-            load_w(kb + 1, wn);
-        }
-        if constexpr (GROUPED) {
-            const int grp = (kb * PANEL_K) / a.G;
-            if (grp != cur_g) {
-                cur_g = grp;
-                load_sz(grp);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            u32x4 af[RB];
+    const int ppg = a.G / PANEL_K;                   // steps per group
+    // hook(s) runs before the MFMAs of k-step s: it spreads the step's global
+    // loads over the step, so that they never arrive at the vector cache as
+    // one burst that stalls the wavefront at its issue
+    auto compute = [&](int i, const u32x4 (&wv)[JW], auto hook) __attribute__((always_inline)) {
+        const uint8_t* xsb = smem + (i & 1) * (BM * XROW_BYTES);
+        auto read_a = [&](int s, u32x4 (&af)[RB]) __attribute__((always_inline)) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const int rr = rb * 16 + (l & 15);
                 const int ch = 4 * s + (l >> 4);
-                af[rb] = *reinterpret_cast<const u32x4*>(&xs[cur][rr * XROW_BYTES + ((ch ^ (l & 15)) << 4)]);
+                af[rb] = *reinterpret_cast<const u32x4*>(xsb + rr * XROW_BYTES + ((ch ^ (l & 15)) << 4));
             }
+        };
+        // A operands of the next k-step are read from LDS while the current
+        // one's MFMAs run
+        u32x4 afc[RB], afn[RB];
+        read_a(0, afc);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+        for (int s = 0; s < 4; ++s) {
+            __builtin_amdgcn_sched_barrier(0);
+            hook(s);
+            __builtin_amdgcn_sched_barrier(0);   // keep this k-step's loads here
+            if (s < 3)
+                read_a(s + 1, afn);
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+                const uint32_t q = wv[j][s];
                 u32x4 bq;
                 if constexpr (ACT == ACT_F16) {
                     if constexpr (GROUPED)
-                        bq = dequant_f16_scaled(wv[j][s], dqh[j], sh2[j]);
+                        bq = dequant_f16_scaled(q, dqh[j], sh2[j]);
                     else
-                        bq = dequant_f16(wv[j][s], dqh[j]);
+                        bq = dequant_f16(q, dqh[j]);
                 } else {
                     if constexpr (GROUPED)
-                        bq = dequant_bf16_scaled(wv[j][s], dqb[j], sf[j]);
+                        bq = dequant_bf16_scaled(q, dqb[j], sf[j]);
                     else
-                        bq = dequant_bf16(wv[j][s], dqb[j]);
+                        bq = dequant_bf16(q, dqb[j]);
                 }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    acc[rb][j] = mfma16x16x32<ACT>(af[rb], bq, acc[rb][j]);
+                    acc[rb][j] = mfma16x16x32<ACT>(afc[rb], bq, acc[rb][j]);
+            }
+            if (s < 3) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    afc[rb] = afn[rb];
             }
         }
-        if (more) {
-            store_x(cur ^ 1);
+    };
+    // one chunk of D steps; REFILL: the ring slot of each step is refilled
+    // with the step D later (only while a full chunk follows)
+    auto chunk = [&](int i0, auto refill_tag) __attribute__((always_inline)) {
+        constexpr bool REFILL = decltype(refill_tag)::value;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wv[j] = wn[j];
+        for (int u = 0; u < D; ++u) {
+            const int i = i0 + u;                           // i0 is a multiple of D: i & 1 == u & 1
+            u32x4 wv[JW];                                   // this step's panels: slot u is free to refill
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                wv[j] = wr[u][j];
+            // per k-step s: a quarter of the activations of step i + 2 (into
+            // the set stored one step ago) and, when refilling, column block
+            // s of step i + D
+            auto hook = [&](int s) __attribute__((always_inline)) {
+                load_x(u & 1, i + 2, s);
+                if constexpr (REFILL) {
+                    if (s < JW)
+                        issue_w1(u, i + D, s);
+                }
+            };
+            if (i < nk) {                                   // uniform
+                if constexpr (GROUPED) {
+                    if (i == 0 || ((kb0 + i) % ppg) == 0)
+                        set_sz(szr[u]);
+                }
+                compute(i, wv, hook);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    hook(s);
+            }
+            store_x((u + 1) & 1, (u + 1) & 1);             // step i + 1, loaded one step ago
+            __syncthreads();
         }
-        __syncthreads();
-    }
+    };
+    int i0 = 0;
+    for (; i0 + D < nk; i0 += D)
+        chunk(i0, std::true_type{});
+    chunk(i0, std::false_type{});
 
     // ---- split-K hand-over: the last workgroup of the tile sums the partials
-    // (fragment layout [tile][split][wavefront][RB][4][64 lanes], 16 bytes per lane)
+    // (fragment layout [tile][split][wavefront][RB][JW][64 lanes], 16 bytes per lane)
     if (a.ksplit > 1) {
         const int tile = tm * a.nt + tn;
         auto frag = [&](int z, int rb, int j) -> size_t {
-            return ((((size_t)tile * a.ksplit + z) * 4 + w) * RB * 4 + rb * 4 + j) * 64 + l;
+            return ((((size_t)tile * a.ksplit + z) * NW + w) * RB * JW + rb * JW + j) * 64 + l;
         };
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JW; ++j)
                 st16_dev(a.partial + frag(kz, rb, j), acc[rb][j]);
         wait_all_mem();
         __syncthreads();
@@ -354,7 +446,7 @@ void prefill_gemm_kernel(GemmKArgs a)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
                 for (int z = 0; z < a.ksplit; ++z)
                     t += (z == kz) ? acc[rb][j] : ld16_dev(a.partial + frag(z, rb, j));
@@ -362,21 +454,21 @@ void prefill_gemm_kernel(GemmKArgs a)
             }
     }
 
-    // ---- epilogue: per-channel scale, gated rank-r correction, store
+    // ---- epilogue: per-channel scale, gated rank-r correction
     if constexpr (!GROUPED) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JW; ++j)
                 acc[rb][j] *= sf[j];
     }
     if (a.r > 0) {
         const int koff = 8 * (l >> 4);
         const int nsteps = a.r_pad >> 5;
         for (int rs = 0; rs < nsteps; ++rs) {
-            u32x4 bfr[4];
+            u32x4 bfr[JW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JW; ++j) {
                 uint32_t hv[8];
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
@@ -391,32 +483,46 @@ void prefill_gemm_kernel(GemmKArgs a)
                 const int m = m0 + rb * 16 + (l & 15);
                 const u32x4 af = ld16(a.tg + (size_t)m * a.r_pad + 32 * rs + koff);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < JW; ++j)
                     acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
             }
         }
     }
+
+    // ---- store: round to the activation format into an LDS tile, then
+    // write whole rows of the tile with 16-byte stores
+    uint16_t* yt = reinterpret_cast<uint16_t*>(smem);   // [BM][YT_PITCH]; the last step's barrier freed it
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n_j[j];
-            if (n >= a.N)
-                continue;
+        for (int j = 0; j < JW; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = m0 + rb * 16 + 4 * (l >> 4) + v;
-                if (m < a.M)
-                    a.Y[(size_t)m * a.N + n] = f32_to_act<ACT>(acc[rb][j][v]);
-            }
+            for (int v = 0; v < 4; ++v)
+                yt[(rb * 16 + 4 * (l >> 4) + v) * YT_PITCH + 16 * JW * w + 16 * j + (l & 15)] =
+                    f32_to_act<ACT>(acc[rb][j][v]);
+    __syncthreads();
+    const bool vec = (a.N & 7) == 0;
+    for (int e = tid; e < BM * (PF_BN / 8); e += GEMM_THREADS) {
+        const int row = e >> 5, c8 = (e & 31) * 8;
+        const int m = m0 + row, n = n0 + c8;
+        if (m >= a.M || n >= a.N)
+            continue;
+        const uint16_t* src = yt + row * YT_PITCH + c8;
+        uint16_t* dst = a.Y + (size_t)m * a.N + n;
+        if (vec) {
+            st16(dst, *reinterpret_cast<const u32x4*>(src));
+        } else {
+            for (int t = 0; t < 8 && n + t < a.N; ++t)
+                dst[t] = src[t];
         }
+    }
 }
 
 template <int ACT, int BM, bool GROUPED>
 static hipError_t launch_gemm_t(const GemmKArgs& k, hipStream_t st)
 {
     dim3 grid(k.mt * k.nt, k.ksplit);
-    hipLaunchKernelGGL((prefill_gemm_kernel<ACT, BM, GROUPED>), grid, dim3(PF_THREADS), 0, st, k);
+    hipLaunchKernelGGL((prefill_gemm_kernel<ACT, BM, GROUPED>), grid, dim3(GEMM_THREADS), 0, st, k);
     return hipGetLastError();
 }
 

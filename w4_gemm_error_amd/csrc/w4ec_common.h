@@ -116,11 +116,13 @@ template <int ACT> __device__ inline floatx4 mfma16x16x32(u32x4 a, u32x4 b, floa
 // One dword of 8 codes (blob nibble order) -> 8 operand values in natural
 // k order, as four registers of two 16-bit values.
 //
-// fp16: (0x6400 | c) is the half 1024 + c, and (0x6400 | c << 4) is
-// 1024 + 16 c; both are exact.  Subtracting 1024 + z, or scaling by 1/16
-// and subtracting 64 + z, gives c - z exactly for an integer zero point z in
-// 0..15 (every intermediate is an integer or a sixteenth well inside the
-// half's 11-bit significand).
+// fp16: (0x6400 | c) is the half 1024 + c, and (0x5400 | c << 4) is the
+// half 64 + c (exponent 21: the nibble in mantissa bits 4..7 counts whole
+// units); both are exact.  Subtracting 1024 + z, or 64 + z, gives c - z
+// exactly for an integer zero point z in 0..15.  Each half pair is built
+// with one AND-OR, written out because the compiler splits it into two
+// instructions; its result only feeds packed adds, never an MFMA operand
+// directly.
 struct DqF16 {
     half2_t off_lo;  // -(1024 + z)
     half2_t off_hi;  // -(64 + z)
@@ -136,32 +138,35 @@ __device__ inline DqF16 dq_f16_consts(float z)
     return c;
 }
 
-__device__ inline u32x4 dequant_f16(uint32_t w, const DqF16& c)
+// (a & mask) | b
+__device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b)
 {
-    const uint32_t MAGIC = 0x64006400u;
-    const half2_t sixteenth = (half2_t){(_Float16)0.0625f, (_Float16)0.0625f};
-    uint32_t w8 = w >> 8;
-    half2_t p0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) | MAGIC);
-    half2_t p1 = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) | MAGIC);
-    half2_t p2 = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) | MAGIC);
-    half2_t p3 = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) | MAGIC);
-    p0 = p0 + c.off_lo;
-    p1 = __builtin_elementwise_fma(p1, sixteenth, c.off_hi);
-    p2 = p2 + c.off_lo;
-    p3 = __builtin_elementwise_fma(p3, sixteenth, c.off_hi);
-    u32x4 r;
-    r.x = __builtin_bit_cast(uint32_t, p0);
-    r.y = __builtin_bit_cast(uint32_t, p1);
-    r.z = __builtin_bit_cast(uint32_t, p2);
-    r.w = __builtin_bit_cast(uint32_t, p3);
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
     return r;
 }
 
-// Same, multiplied by the scale s (rounded once, to fp16).  Each element
-// goes through a scalar first: clang reads the wrong lane when
+// Elements go through a scalar first: clang reads the wrong lane when
 // __builtin_bit_cast is applied directly to an ext-vector element access.
 __device__ inline half2_t h2_of(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 __device__ inline uint32_t u32_of(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ inline u32x4 dequant_f16(uint32_t w, const DqF16& c)
+{
+    const uint32_t w8 = w >> 8;
+    const half2_t p0 = h2_of(and_or(w, 0x000F000Fu, 0x64006400u)) + c.off_lo;
+    const half2_t p1 = h2_of(and_or(w, 0x00F000F0u, 0x54005400u)) + c.off_hi;
+    const half2_t p2 = h2_of(and_or(w8, 0x000F000Fu, 0x64006400u)) + c.off_lo;
+    const half2_t p3 = h2_of(and_or(w8, 0x00F000F0u, 0x54005400u)) + c.off_hi;
+    u32x4 r;
+    r.x = u32_of(p0);
+    r.y = u32_of(p1);
+    r.z = u32_of(p2);
+    r.w = u32_of(p3);
+    return r;
+}
+
+// Same, multiplied by the scale s (rounded once, to fp16).
 
 __device__ inline u32x4 dequant_f16_scaled(uint32_t w, const DqF16& c, half2_t s2)
 {
