@@ -121,9 +121,12 @@ int w4ec_linear_decode(const void* X, const void* packed, const void* A, const v
                        int M, int N, int K, int r, int group_size, int act_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* The layer, prefill phase: any M >= 1 (tiled MFMA GEMM, two launches: the
- * gate / X A prepass, then the GEMM with the gated correction in its
- * epilogue).  Arguments as for w4ec_linear_decode. */
+/* The layer, prefill phase: any M >= 1 (tiled MFMA GEMM, three launches:
+ * the gate / X A prepass over K slices, the reduction of its slices with the
+ * gate, then the GEMM with the gated correction in its epilogue; for bf16
+ * activations with one zero point per channel the prepass also sums each
+ * token's activations, which the GEMM's zero-point term uses, so it runs
+ * even when r == 0).  Arguments as for w4ec_linear_decode. */
 int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const void* B,
                         const void* w_g, float b_g, void* Y,
                         int M, int N, int K, int r, int group_size, int act_dtype,

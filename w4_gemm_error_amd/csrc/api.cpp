@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <new>
 
 #include "w4ec_common.h"
@@ -99,16 +100,19 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
     p.mt = (M + p.BM - 1) / p.BM;
     p.nt = (NB * PANEL_N + p.BN - 1) / p.BN;
     p.ksplit = 1;
-    while ((long long)p.mt * p.nt * p.ksplit < TARGET_WGS && KB / (2 * p.ksplit) >= 4 && p.ksplit < 16)
+    // split K only while the workgroups still fit in one round (one per CU)
+    while ((long long)p.mt * p.nt * p.ksplit * 2 <= TARGET_WGS && KB / (2 * p.ksplit) >= 4 && p.ksplit < 16)
         p.ksplit *= 2;
     p.Mpad = p.mt * p.BM;
     p.r_pad = (r + 31) / 32 * 32;
     // prepass: 64-token tiles x K slices of at most 512, each slice of
     // [A | w_g] held in LDS at once (two workgroups per CU)
     p.pre_mt = (M + 63) / 64;
+    // (the prepass also runs with r == 0 for bf16 per-channel weights: the
+    // GEMM then needs each token's activation sum)
     p.pre_ks = 1;
     p.pre_kc = K;
-    if (r > 0) {
+    {
         int kcmax = 512;
         while (kcmax > 64 && prepass_lds_bytes(r, kcmax) > PRE_LDS_MAX)
             kcmax -= 64;
@@ -122,11 +126,12 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
 
     size_t off = CTRL_BYTES;
     p.off_pre_partial = off;
-    if (r > 0)
-        off = align_up(off + (size_t)p.pre_mt * p.pre_ks * 4 * ((r + 15) / 16 + 1) * 64 * 16, 256);
+    off = align_up(off + (size_t)p.pre_mt * p.pre_ks * 4 * ((r + 15) / 16 + 1) * 64 * 16, 256);
     p.off_tg = off;
     if (r > 0)
         off = align_up(off + (size_t)p.Mpad * p.r_pad * 2, 256);
+    p.off_rowsum = off;
+    off = align_up(off + (size_t)std::max(p.Mpad, p.pre_mt * 64) * sizeof(float), 256);
     p.off_gemm_partial = off;
     if (p.ksplit > 1)
         off = align_up(off + (size_t)p.ksplit * p.Mpad * p.nt * p.BN * sizeof(float), 256);
@@ -285,7 +290,8 @@ int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const 
     size_t need = 0;
     if (M > 0 && r >= 0 && r <= MAX_RANK && check_weight_shape(N, K, group_size) == W4EC_OK) {
         p = make_prefill_plan(M, N, K, r);
-        need = (r > 0 || p.ksplit > 1) ? p.bytes : 0;
+        const bool sums = act_dtype == W4EC_BF16 && group_size == K;   // bf16 zero-point term
+        need = (r > 0 || p.ksplit > 1 || sums) ? p.bytes : 0;
     }
     int rc = check_layer_args(X, packed, A, B, w_g, Y, M, N, K, r, group_size, act_dtype,
                               workspace, workspace_bytes, need);

@@ -87,7 +87,7 @@ __device__ inline void dec_ec_mfma(const u32x4 (&xf)[DEC_EC_KSMAX / 32], const u
             u32x4 bf[NS];
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-                bf[s] = ec_bfrag(at, wgl, r, gate, cb, 32 * s);
+                bf[s] = ec_bfrag(at, wgl, r, gate, 0u, cb, 32 * s);
 #pragma unroll
             for (int s = 0; s < NS; ++s)
                 acc[i] = mfma16x16x32<ACT>(xf[s], bf[s], acc[i]);

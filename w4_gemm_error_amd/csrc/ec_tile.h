@@ -14,8 +14,9 @@
 //
 // Column blocks: cb < ec_a_blocks(r) hold 16 columns of A (columns >= r of
 // the last block read past the row and are discarded); block ec_a_blocks(r)
-// holds the gate vector as its column 0 (zero elsewhere, and all zero when
-// there is no gate, i.e. a zero gate logit).
+// holds the gate vector as its column 0 (all zero when there is no gate,
+// i.e. a zero gate logit) and, on request, a column of ones as its column 1
+// (the token's sum of activations), zero elsewhere.
 #pragma once
 
 #include "w4ec_common.h"
@@ -73,12 +74,16 @@ __device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* 
 
 // B fragment of v_mfma_f32_16x16x32 for column block cb, rows krow .. krow + 31
 // of the staged slice: lane l gets column 16 cb + (l & 15) at rows
-// krow + 8 (l >> 4) + t, t = 0..7.
-__device__ inline u32x4 ec_bfrag(const uint16_t* at, const uint16_t* wgl, int r, bool gate, int cb, int krow)
+// krow + 8 (l >> 4) + t, t = 0..7.  one2: two ones in the activation format,
+// or 0 for no sum column.
+__device__ inline u32x4 ec_bfrag(const uint16_t* at, const uint16_t* wgl, int r, bool gate, uint32_t one2,
+                                 int cb, int krow)
 {
     const int l = threadIdx.x & 63;
     const int g = l >> 4;
     if (cb == ec_a_blocks(r)) {
+        if ((l & 15) == 1)
+            return (u32x4){one2, one2, one2, one2};
         if (!gate || (l & 15) != 0)
             return (u32x4){0u, 0u, 0u, 0u};
         return *reinterpret_cast<const u32x4*>(wgl + krow + 8 * g);
@@ -95,7 +100,7 @@ __device__ inline u32x4 ec_bfrag(const uint16_t* at, const uint16_t* wgl, int r,
 }
 
 // Column of the [T | l] partial held by lane column j of block cb, or -1
-// when that column is discarded.
+// when that column is discarded (the sum column is not part of it).
 __device__ inline int ec_col(int r, int cb, int j)
 {
     if (cb == ec_a_blocks(r))

@@ -47,6 +47,7 @@ struct PrepassKArgs {
     const uint16_t* X;
     const uint16_t* A;
     const uint16_t* w_g;
+    uint32_t one2;      // two ones in the activation format: also sum each token's activations (else 0)
     int M, K, r, kc, ks;
     floatx4* partial;   // [pre_mt][ks][4 wavefronts][ec_blocks(r)][64 lanes]
 };
@@ -95,7 +96,7 @@ void prepass_kernel(PrepassKArgs a)
 #pragma unroll
             for (int s = 0; s < PRE_MAXS; ++s)
                 if (32 * s < len)
-                    acc[cb] = mfma16x16x32<ACT>(xf[s], ec_bfrag(at, wgl, a.r, gate, cb, 32 * s), acc[cb]);
+                    acc[cb] = mfma16x16x32<ACT>(xf[s], ec_bfrag(at, wgl, a.r, gate, a.one2, cb, 32 * s), acc[cb]);
         }
     }
     floatx4* mine = a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * nb * 64;
@@ -108,55 +109,83 @@ void prepass_kernel(PrepassKArgs a)
 struct EcReduceKArgs {
     const floatx4* partial;
     uint16_t* tg;       // [Mpad][r_pad], activation format
+    float* rowsum;      // [Mpad] sums of each token's activations, or null
     float b_g;
     int r, r_pad, ks;
 };
 
-// One workgroup per 16 tokens: adds the K slices' fragments in slice order,
-// applies the gate and stores T_g = g * T (zero in columns r .. r_pad - 1).
+// One workgroup per (16 tokens, column block of T): adds the K slices'
+// fragments of that block and of the gate block in slice order, applies
+// the gate and stores its 16 columns of T_g = g * T (zero past r).
 template <int ACT>
 __global__ __launch_bounds__(PF_THREADS)
 void ec_reduce_kernel(EcReduceKArgs a)
 {
-    constexpr int TP = 260;                          // LDS row of T: r + 1 <= 257 columns
-    __shared__ float tl[16][TP];
+    __shared__ float tl[2][4][64][4];                // [block: mine, gate][quarter of the slices][lane][v]
     __shared__ float gl[16];
     const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int q = tid >> 6;                          // wavefront: a quarter of the slices
     const int rb = blockIdx.x;                       // rows 16 rb .. 16 rb + 15
+    const int cb = blockIdx.y;                       // column block of T (of ec_a_blocks(r))
     const int mt = rb >> 2, w = rb & 3;
-    const int ne = ec_blocks(a.r) * 64;              // fragments per slice of this row block
+    const int nb = ec_blocks(a.r);
+    const int ne = nb * 64;                          // fragments per slice of this row block
     const floatx4* base = a.partial + ((size_t)mt * a.ks * 4 + w) * ne;
     const size_t zs = (size_t)4 * ne;
-    for (int e = tid; e < ne; e += PF_THREADS) {
-        const floatx4* src = base + e;
+    // wavefront q adds slices q, q + 4, ... of both blocks (fixed order)
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const floatx4* src = base + (which == 0 ? cb : nb - 1) * 64 + l;
         floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
-        int z = 0;
-        for (; z + 8 <= a.ks; z += 8) {
+        int z = q;
+        for (; z + 28 < a.ks; z += 32) {
             floatx4 v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                v[i] = src[(size_t)(z + i) * zs];
+                v[i] = src[(size_t)(z + 4 * i) * zs];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 t += v[i];
         }
-        for (; z < a.ks; ++z)
+        for (; z < a.ks; z += 4)
             t += src[(size_t)z * zs];
-        const int l = e & 63;
-        const int c = ec_col(a.r, e >> 6, l & 15);
-        if (c >= 0) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                tl[4 * (l >> 4) + v][c] = t[v];
-        }
+        for (int v = 0; v < 4; ++v)
+            tl[which][q][l][v] = t[v];
     }
     __syncthreads();
-    if (tid < 16)
-        gl[tid] = sigmoid_f32(tl[tid][a.r] + a.b_g);
+    // gate logits of the 16 rows: lane column 0 of the gate block (row
+    // 4 g + v lives in lane 16 g, element v); their sums: lane column 1
+    if (tid < 16) {
+        const int lane = (tid >> 2) * 16;
+        const int v = tid & 3;
+        const float lg = ((tl[1][0][lane][v] + tl[1][1][lane][v]) + tl[1][2][lane][v]) + tl[1][3][lane][v];
+        gl[tid] = sigmoid_f32(lg + a.b_g);
+        if (a.rowsum && cb == 0)
+            a.rowsum[16 * rb + tid] =
+                ((tl[1][0][lane + 1][v] + tl[1][1][lane + 1][v]) + tl[1][2][lane + 1][v]) + tl[1][3][lane + 1][v];
+    }
     __syncthreads();
-    for (int row = 0; row < 16; ++row)
-        for (int c = tid; c < a.r_pad; c += PF_THREADS)
-            a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = f32_to_act<ACT>(c < a.r ? gl[row] * tl[row][c] : 0.0f);
+    // this block's 16 columns for the 16 rows: lane l holds column l & 15, rows 4 (l >> 4) + v
+    if (tid < 64) {
+        const int c = 16 * cb + (l & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = 4 * (l >> 4) + v;
+            const float t = ((tl[0][0][l][v] + tl[0][1][l][v]) + tl[0][2][l][v]) + tl[0][3][l][v];
+            if (c < a.r_pad)
+                a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = f32_to_act<ACT>(c < a.r ? gl[row] * t : 0.0f);
+        }
+    }
+    // columns of r_pad past the last block of A (r <= 16 (r_pad / 16 - 1) only when r_pad > 16 blocks)
+    if (cb == ec_a_blocks(a.r) - 1) {
+        for (int e = tid; e < 16 * a.r_pad; e += PF_THREADS) {
+            const int row = e / a.r_pad, c = e - row * a.r_pad;
+            if (c >= 16 * (cb + 1))
+                a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = 0;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -167,6 +196,7 @@ struct GemmKArgs {
     const uint32_t* sz;
     const uint16_t* B;
     const uint16_t* tg;
+    const float* rowsum;  // bf16 per-channel: sums of each token's activations over K
     uint16_t* Y;
     floatx4* partial;  // [tile][ksplit][NW][RB][JW][64] fragments
     uint32_t* cnt;     // [mt*nt]
@@ -205,10 +235,15 @@ void prefill_gemm_kernel(GemmKArgs a)
 {
     constexpr int RB = BM / 16;            // 16-row blocks per tile
     constexpr int XROW_BYTES = PANEL_K * 2; // 256 bytes per staged row
+    // bf16 with one zero point per column: the weights enter the MFMAs as
+    // 128 + c (one AND-OR per pair; bf16 has no packed subtract) and the
+    // epilogue subtracts (128 + z) times the token's activation sum
+    constexpr bool BIAS = ACT == ACT_BF16 && !GROUPED;
     constexpr int XLOADS = BM * XROW_BYTES / 16 / GEMM_THREADS;  // 16-byte loads per thread per step
     // weight ring: D 128-k steps per wavefront (even, so that the two
-    // activation register sets below alternate with the ring slots)
-    constexpr int D = BM == 128 ? 4 : 2;
+    // activation register sets below alternate with the ring slots); four
+    // steps keep ~64 KB of weights in flight per CU
+    constexpr int D = 4;
     __shared__ __attribute__((aligned(16))) uint8_t smem[gemm_lds_bytes<BM>()];
     __shared__ uint32_t s_old;
 
@@ -263,12 +298,14 @@ void prefill_gemm_kernel(GemmKArgs a)
     float dqb[JW];
     half2_t sh2[JW];
     float sf[JW];
+    float zf[JW];
     auto set_sz = [&](const uint32_t* v) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < JW; ++j) {
             const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
             const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
             sf[j] = (float)sv;
+            zf[j] = z;
             sh2[j] = (half2_t){sv, sv};
             dqh[j] = dq_f16_consts(z);
             dqb[j] = -(8388608.0f + z);
@@ -368,7 +405,7 @@ void prefill_gemm_kernel(GemmKArgs a)
                     if constexpr (GROUPED)
                         bq = dequant_bf16_scaled(q, dqb[j], sf[j]);
                     else
-                        bq = dequant_bf16(q, dqb[j]);
+                        bq = bf16_biased(q);
                 }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
@@ -454,7 +491,19 @@ void prefill_gemm_kernel(GemmKArgs a)
             }
     }
 
-    // ---- epilogue: per-channel scale, gated rank-r correction
+    // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r correction
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float sx = a.rowsum[m0 + rb * 16 + 4 * (l >> 4) + v];
+#pragma unroll
+                for (int j = 0; j < JW; ++j)
+                    acc[rb][j][v] -= (128.0f + zf[j]) * sx;
+            }
+        }
+    }
     if constexpr (!GROUPED) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -543,11 +592,14 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
 {
     BlobGeom g = blob_geom(a.N, a.K, a.G);
     uint16_t* tg = (uint16_t*)(a.ws + p.off_tg);
-    if (a.r > 0) {
+    const bool sums = a.act == ACT_BF16 && a.G == a.K;   // the GEMM's bf16 zero-point term
+    float* rowsum = (float*)(a.ws + p.off_rowsum);
+    if (a.r > 0 || sums) {
         PrepassKArgs q;
         q.X = (const uint16_t*)a.X;
         q.A = (const uint16_t*)a.A;
         q.w_g = (const uint16_t*)a.w_g;
+        q.one2 = !sums ? 0u : 0x3F803F80u;                   // bf16 ones
         q.M = a.M; q.K = a.K; q.r = a.r;
         q.kc = p.pre_kc; q.ks = p.pre_ks;
         q.partial = (floatx4*)(a.ws + p.off_pre_partial);
@@ -565,10 +617,11 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
         EcReduceKArgs rq;
         rq.partial = q.partial;
         rq.tg = tg;
+        rq.rowsum = sums ? rowsum : nullptr;
         rq.b_g = a.b_g;
         rq.r = a.r; rq.r_pad = p.r_pad; rq.ks = p.pre_ks;
         auto rk = a.act == ACT_F16 ? ec_reduce_kernel<ACT_F16> : ec_reduce_kernel<ACT_BF16>;
-        hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4), dim3(PF_THREADS), 0, st, rq);
+        hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4, a.r > 0 ? ec_a_blocks(a.r) : 1), dim3(PF_THREADS), 0, st, rq);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -579,6 +632,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
     k.sz = (const uint32_t*)((const char*)a.packed + g.sz_off);
     k.B = (const uint16_t*)a.B;
     k.tg = tg;
+    k.rowsum = rowsum;
     k.Y = (uint16_t*)a.Y;
     k.partial = (floatx4*)(a.ws + p.off_gemm_partial);
     k.cnt = (uint32_t*)(a.ws + p.off_gemm_cnt);

@@ -138,7 +138,9 @@ __device__ inline DqF16 dq_f16_consts(float z)
     return c;
 }
 
-// (a & mask) | b
+// (a & mask) | b.  Only for values that a VALU instruction consumes next:
+// the compiler does not see what the asm writes, so it cannot keep the wait
+// states an MFMA reading it directly would need.
 __device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b)
 {
     uint32_t r;
@@ -204,6 +206,21 @@ __device__ inline u32x4 dequant_bf16(uint32_t w, float off)
     r.y = bf16_pair_from_f32(nib_f32(w, 1, off), nib_f32(w, 5, off));
     r.z = bf16_pair_from_f32(nib_f32(w, 2, off), nib_f32(w, 6, off));
     r.w = bf16_pair_from_f32(nib_f32(w, 3, off), nib_f32(w, 7, off));
+    return r;
+}
+
+// bf16 (0x4300 | c) is 128 + c exactly, built per pair; the caller removes
+// 128 + z afterwards.  Written in plain C, not with and_or: these values
+// are MFMA operands, and the compiler must see the instructions that write
+// them to keep the VALU-to-MFMA wait states.
+__device__ inline u32x4 bf16_biased(uint32_t w)
+{
+    const uint32_t w8 = w >> 8;
+    u32x4 r;
+    r.x = (w & 0x000F000Fu) | 0x43004300u;
+    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.z = (w8 & 0x000F000Fu) | 0x43004300u;
+    r.w = ((w8 >> 4) & 0x000F000Fu) | 0x43004300u;
     return r;
 }
 
@@ -330,7 +347,7 @@ struct PrefillPlan {
     int pre_ks;     // prepass split over K
     int pre_kc;     // k per prepass split (multiple of 64, <= 512)
     int r_pad, Mpad;
-    size_t off_gemm_cnt, off_pre_partial, off_tg, off_gemm_partial, bytes;
+    size_t off_gemm_cnt, off_pre_partial, off_tg, off_rowsum, off_gemm_partial, bytes;
 };
 
 }  // namespace w4ec
