@@ -123,6 +123,19 @@ def test_special_cases(phase):
     assert_close(nogate, oracle_layer(d, codes, b_g=0.25, with_gate=False), "fp16", "w_g=None")
 
 
+@pytest.mark.parametrize("M,K,G", [(64, 512, 512), (130, 1024, 1024), (40, 768, 256)])
+def test_bf16_prefill_plain_w4(M, K, G):
+    """bf16 prefill with r = 0: the per-channel path subtracts the zero point
+    through each token's activation sum, which the prepass computes even
+    without a compensator; the grouped path dequantizes exactly."""
+    _print(f"bf16 prefill r=0 M={M} K={K} G={G}")
+    d = small_layer("bf16", M, 528, K, 16, G, seed=13)
+    _, _, _, packed = gpu_quantize(d)
+    codes = oracle.rtn_quantize(d["W"], G)
+    Y = gpu_layer(d, packed, "prefill", r=0)
+    assert_close(Y, oracle_layer(d, codes, r=0), "bf16", f"bf16 r=0 M={M}")
+
+
 @pytest.mark.parametrize("phase,M", [("decode", 16), ("prefill", 256)])
 def test_deterministic_and_workspace_reuse(phase, M):
     _print(f"determinism {phase} M={M}")

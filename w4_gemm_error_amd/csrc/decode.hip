@@ -399,7 +399,9 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     set_sz(sz0);
     int left_in_group = ppg - (kbeg % ppg);          // panels until the group changes
 
-    const uint16_t* xl = xs + (size_t)row * K + (size_t)kbeg * PANEL_K + koff;
+    // lanes of absent tokens read token M - 1's row (the same address in all
+    // of them: an LDS broadcast) and multiply zeros
+    const uint16_t* xl = xs + (size_t)min(row, M - 1) * K + (size_t)kbeg * PANEL_K + koff;
     // one chunk of DEPTH panels; REFILL: the ring is refilled for the next
     // chunk (only while one follows, so no panel is loaded twice)
     auto chunk = [&](int i0, auto refill_tag) {
