@@ -63,11 +63,14 @@ def layer_flops(M, N, K, r):
 
 
 def source_digest():
+    """Digest of the kernel sources' code: line comments and blank lines are
+    left out, so that a comment edit does not invalidate measured counters."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4_gemm_error_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            code = [ln.split("//", 1)[0].rstrip() for ln in f]
+        h.update(name.encode() + "\n".join(ln for ln in code if ln).encode())
     return h.hexdigest()[:16]
 
 
@@ -233,10 +236,11 @@ def main():
 
     # ---- dominant kernel.  A decode call is one kernel launch, so its
     # average launch duration is the timed region's event time over K (the
-    # steps run back to back inside the graph).  A prefill call is two
-    # launches (gate / X A prepass, then the GEMM); its figure is per call.
+    # steps run back to back inside the graph).  A prefill call is up to three
+    # launches (gate / X A partial sums, their reduction, then the GEMM); its
+    # figure is per call.
     kdur = elapsed_ms * 1e-3 / args.steps
-    kernel_name = "decode_kernel" if phase == "decode" else "prepass_kernel + prefill_gemm_kernel (per call)"
+    kernel_name = "decode_kernel" if phase == "decode" else "prepass_kernel + ec_reduce_kernel + prefill_gemm_kernel (per call)"
 
     flops = layer_flops(M, N, K, r)
     if phase == "decode":

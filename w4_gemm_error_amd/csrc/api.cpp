@@ -69,19 +69,16 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
     p.xlds = decode_use_xlds(M, K);
     p.CB = (M <= 4 || p.xlds) ? 1 : 2;
     p.n_main = (NB + p.CB - 1) / p.CB;
-    p.single = M <= 4 ? 1 : 0;
     p.stage_first = r > 0 ? 1 : 0;
     p.off_flags = OFF_DEC_FLAGS;
     p.off_rep_ctrl = OFF_DEC_REP;
     size_t off = CTRL_BYTES;
     p.off_partial = off;
-    if (r > 0 && !p.single)
+    if (r > 0)
         off = align_up(off + (size_t)p.P * 16 * p.RC * sizeof(float), 4096);
     p.off_rep_data = off;
     if (r > 0) {
-        const size_t ne2 = ((size_t)M * p.RC + 1) / 2;    // float pairs per partial
-        const size_t per = p.single ? (size_t)p.P * ne2 * 8 : (size_t)M * p.r_pad * 2;
-        p.rep_data_stride = align_up(per, 4096);
+        p.rep_data_stride = align_up((size_t)M * p.r_pad * 2, 4096);
         off += (size_t)DEC_NREP * p.rep_data_stride;
     }
     p.bytes = off;

@@ -23,13 +23,12 @@
 // stream saturates HBM, every dependent trip to memory costs microseconds,
 // and hundreds of workgroups polling or reading one spot pile onto one
 // memory channel; so the data is published in DEC_NREP replica slots spread
-// over the channels, main workgroup i using slot i mod DEC_NREP:
-//  * few tokens ("single" hand-over): each EC workgroup writes its partial
-//    sums into every slot and bumps each slot's arrival count; a main
-//    workgroup waits for P arrivals in its slot and adds the P partials in a
-//    fixed order itself;
-//  * more tokens: the last EC workgroup to arrive adds the partials, applies
-//    the gate and writes T_g into every slot, then raises each slot's flag.
+// over the channels, main workgroup i using slot i mod DEC_NREP.  Each EC
+// workgroup writes its partial sums; the last one to arrive adds them in a
+// fixed order, applies the gate and writes T_g into every slot, then raises
+// each slot's flag.  (Letting every main workgroup add the P partials itself
+// instead makes the grid as a whole read megabytes of partial sums, and
+// measured slower even for one token.)
 // The last reader of a slot returns its control words to zero.  All waits
 // are bounded.  Hand-over data moves with device-coherent accesses (see
 // w4ec_common.h), so no cache-wide write-back or invalidate is needed.
@@ -58,11 +57,10 @@ struct DecodeKArgs {
     uint16_t* Y;
     int M, N, K, r, r_pad, G, NB, KB, Npad;
     int P, KS, RC, n_main;
-    int single;          // 1: per-slot partial sums; 0: last EC workgroup reduces
     int stage_first;     // main workgroups stage X before issuing weight loads
-    uint32_t* flags;     // [0] EC arrivals (two-level), [2] a wait timed out
-    float* partial;      // two-level: [P][16][RC]
-    uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [0] arrivals / ready, [1] readers done
+    uint32_t* flags;     // [0] EC arrivals, [2] a wait timed out
+    float* partial;      // [P][16][RC]
+    uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [0] ready, [1] readers done
     uint8_t* rep_data;   // DEC_NREP slots of rep_data_stride bytes
     size_t rep_data_stride;
 };
@@ -79,19 +77,25 @@ template <int ACT, int NS>
 __device__ inline void dec_ec_mfma(const u32x4 (&xf)[DEC_EC_KSMAX / 32], const uint16_t* at, const uint16_t* wgl,
                                    int r, bool gate, int w, floatx4 (&acc)[DEC_EC_MAXI])
 {
-    const int nb = ec_blocks(r);
+    const int nba = ec_a_blocks(r);
 #pragma unroll
     for (int i = 0; i < DEC_EC_MAXI; ++i) {
-        const int cb = w + 4 * i;
-        if (cb < nb) {
-            u32x4 bf[NS];
+        const int cb = w + 4 * i;                    // wavefront-uniform
+        if (cb > nba)
+            break;
+        u32x4 bf[NS];
+        if (cb < nba) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-                bf[s] = ec_bfrag(at, wgl, r, gate, 0u, cb, 32 * s);
+                bf[s] = ec_bfrag_a(at, r, cb, 32 * s);
+        } else {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
-                acc[i] = mfma16x16x32<ACT>(xf[s], bf[s], acc[i]);
+                bf[s] = ec_bfrag_gate(wgl, gate, 0u, 32 * s);
         }
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            acc[i] = mfma16x16x32<ACT>(xf[s], bf[s], acc[i]);
     }
 }
 
@@ -135,50 +139,7 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     }
     const int nrep = min(DEC_NREP, a.n_main);       // slots that have readers
 
-    if (a.single) {
-        // 4a. this slice's partial sums -> LDS [M][RC] -> every replica slot
-        __syncthreads();                             // all MFMAs have read the slice
-        float* part = reinterpret_cast<float*>(smem);
-#pragma unroll
-        for (int i = 0; i < DEC_EC_MAXI; ++i) {
-            const int cb = w + 4 * i;
-            const int c = cb < ec_blocks(r) ? ec_col(r, cb, l & 15) : -1;
-            if (c >= 0) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = 4 * (l >> 4) + v;
-                    if (m < M)
-                        part[m * a.RC + c] = acc[i][v];
-                }
-            }
-        }
-        const int ne = M * a.RC;
-        const int ne2 = (ne + 1) >> 1;               // float pairs per partial (padded)
-        if (tid == 0 && (ne & 1))
-            part[ne] = 0.0f;
-        __syncthreads();
-        // thread -> (pair i, slots s0, s0 + sstep, ...)
-        const uint64_t* part2 = reinterpret_cast<const uint64_t*>(part);
-        const int sstep = ne2 <= DEC_THREADS ? DEC_THREADS / ne2 : 1;
-        const int s0 = ne2 <= DEC_THREADS ? tid / ne2 : 0;
-        if (s0 < sstep) {
-            for (int i = tid - s0 * ne2; i < ne2; i += DEC_THREADS) {
-                const uint64_t v = part2[i];
-                for (int slot = s0; slot < nrep; slot += sstep) {
-                    uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride) +
-                                    (size_t)p * ne2 + i;
-                    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
-        }
-        wait_all_mem();
-        __syncthreads();
-        if (tid < nrep)
-            atomic_add_dev(rep_word(a, tid, 0), 1u);
-        return;
-    }
-
-    // 4b. partial sums -> [P][16][RC]; the last EC workgroup reduces them
+    // partial sums -> [P][16][RC]; the last EC workgroup reduces them
     float* part = a.partial + (size_t)p * 16 * a.RC;
 #pragma unroll
     for (int i = 0; i < DEC_EC_MAXI; ++i) {
@@ -504,9 +465,6 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // ---- reduce the four K shares (fixed order); LDS is reused from here on
     __syncthreads();
     floatx4* red = reinterpret_cast<floatx4*>(smem);                       // [4][CB][64]
-    float* tsum = reinterpret_cast<float*>(smem + 4 * CB * 64 * 16);        // [M][RC]
-    float* gl = tsum + 16 * a.RC;                                           // [16]
-    uint16_t* tgl = reinterpret_cast<uint16_t*>(gl + 16);                   // [16][r_pad]
 #pragma unroll
     for (int j = 0; j < CB; ++j)
         red[(w * CB + j) * 64 + l] = acc[j];
@@ -514,73 +472,17 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // ---- gated rank-r activations from this workgroup's replica slot
     const int slot = mb % DEC_NREP;
     const uint8_t* sdata = a.rep_data + (size_t)slot * a.rep_data_stride;
-    if (a.r > 0) {
-        if (tid == 0) {
-            const uint32_t target = a.single ? (uint32_t)a.P : 1u;
-            uint32_t it = 0;
-            while (atomic_load_dev(rep_word(a, slot, 0)) < target) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++it >= SPIN_LIMIT) {
-                    atomic_store_dev(&a.flags[2], 1u);
-                    break;
-                }
+    if (a.r > 0 && tid == 0) {
+        uint32_t it = 0;
+        while (atomic_load_dev(rep_word(a, slot, 0)) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it >= SPIN_LIMIT) {
+                atomic_store_dev(&a.flags[2], 1u);
+                break;
             }
         }
-        __syncthreads();
-        if (a.single) {
-            // the P partials of this slot, [P][2 ne2] floats: ng thread groups
-            // split the slices (slice q -> group q mod ng), each thread keeping
-            // 8 loads in flight; the group sums are added in group order
-            const int ne = M * a.RC;
-            const int ne2 = (ne + 1) >> 1;
-            const int ng = max(1, min(a.P, DEC_THREADS / ne));
-            const float* src = reinterpret_cast<const float*>(sdata);
-            const size_t qs = (size_t)2 * ne2;
-            float* gred = reinterpret_cast<float*>(tgl + 16 * a.r_pad);   // [ng][ne], ng > 1 only
-            for (int e0 = tid; e0 < ne * ng; e0 += DEC_THREADS) {
-                const int g = e0 / ne, e = e0 - g * ne;
-                const float* sp = src + e;
-                float t = 0.0f;
-                int q = g;
-                for (; q + 7 * ng < a.P; q += 8 * ng) {
-                    float v[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        v[i] = ld4_dev(sp + (size_t)(q + i * ng) * qs);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        t += v[i];
-                }
-                for (; q < a.P; q += ng)
-                    t += ld4_dev(sp + (size_t)q * qs);
-                if (ng > 1)
-                    gred[e0] = t;
-                else
-                    tsum[e] = t;
-            }
-            if (ng > 1) {
-                __syncthreads();
-                for (int e = tid; e < ne; e += DEC_THREADS) {
-                    float t = gred[e];
-                    for (int g = 1; g < ng; ++g)
-                        t += gred[g * ne + e];
-                    tsum[e] = t;
-                }
-            }
-            __syncthreads();
-            if (tid < 16)
-                gl[tid] = tid < M ? sigmoid_f32(tsum[tid * a.RC + a.r] + a.b_g) : 0.0f;
-            __syncthreads();
-            // rows m >= M of T_g are left as they are: they only reach rows of
-            // the epilogue product that are never stored
-            for (int m = 0; m < M; ++m)
-                for (int c = tid; c < a.r_pad; c += DEC_THREADS)
-                    tgl[m * a.r_pad + c] = f32_to_act<ACT>(c < a.r ? gl[m] * tsum[m * a.RC + c] : 0.0f);
-            __syncthreads();
-        }
-    } else {
-        __syncthreads();
     }
+    __syncthreads();
 
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
@@ -596,9 +498,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
             for (int rs = 0; rs < 8; ++rs) {
                 if (rs < nsteps) {
                     u32x4 af = (u32x4){0u, 0u, 0u, 0u};
-                    if (a.single) {
-                        af = *reinterpret_cast<const u32x4*>(tgl + row * a.r_pad + 32 * rs + koff);
-                    } else if (xrow) {
+                    if (xrow) {
                         const uint64_t* src = reinterpret_cast<const uint64_t*>(
                             sdata + ((size_t)row * a.r_pad + 32 * rs + koff) * 2);
                         const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -651,11 +551,10 @@ constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS
 bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
 
 // LDS of the main role: the staged activations, then (after the stream)
-// the wavefront reduction, partial sums, gate, T_g and the hand-over group sums
+// the wavefront reduction
 static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r)
 {
-    size_t b = (size_t)4 * p.CB * 64 * 16 + (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2 +
-               (p.single ? DEC_THREADS * 4 : 0);
+    size_t b = (size_t)4 * p.CB * 64 * 16;
     if (p.xlds)
         b = std::max(b, (size_t)M * K * 2);
     return (b + 15) / 16 * 16;
@@ -724,7 +623,6 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.M = a.M; k.N = a.N; k.K = a.K; k.r = a.r; k.r_pad = p.r_pad; k.G = a.G;
     k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;
     k.P = p.P; k.KS = p.KS; k.RC = p.RC; k.n_main = p.n_main;
-    k.single = p.single;
     k.stage_first = p.stage_first;
     k.flags = (uint32_t*)(a.ws + p.off_flags);
     k.partial = (float*)(a.ws + p.off_partial);

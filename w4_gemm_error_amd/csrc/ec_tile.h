@@ -72,22 +72,13 @@ __device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* 
         copy16_to_lds(w_g + k0 + 8 * l, wgl);
 }
 
-// B fragment of v_mfma_f32_16x16x32 for column block cb, rows krow .. krow + 31
-// of the staged slice: lane l gets column 16 cb + (l & 15) at rows
-// krow + 8 (l >> 4) + t, t = 0..7.  one2: two ones in the activation format,
-// or 0 for no sum column.
-__device__ inline u32x4 ec_bfrag(const uint16_t* at, const uint16_t* wgl, int r, bool gate, uint32_t one2,
-                                 int cb, int krow)
+// B fragment of v_mfma_f32_16x16x32 for column block cb < ec_a_blocks(r),
+// rows krow .. krow + 31 of the staged slice: lane l gets column
+// 16 cb + (l & 15) at rows krow + 8 (l >> 4) + t, t = 0..7.
+__device__ inline u32x4 ec_bfrag_a(const uint16_t* at, int r, int cb, int krow)
 {
     const int l = threadIdx.x & 63;
     const int g = l >> 4;
-    if (cb == ec_a_blocks(r)) {
-        if ((l & 15) == 1)
-            return (u32x4){one2, one2, one2, one2};
-        if (!gate || (l & 15) != 0)
-            return (u32x4){0u, 0u, 0u, 0u};
-        return *reinterpret_cast<const u32x4*>(wgl + krow + 8 * g);
-    }
     const int pitch = ec_pitch(r);
     const int s = l & 15;
     const uint16_t* p = at + (krow + 8 * g + (s >> 2)) * pitch + 16 * cb + 4 * (s & 3);
@@ -97,6 +88,20 @@ __device__ inline u32x4 ec_bfrag(const uint16_t* at, const uint16_t* wgl, int r,
                    (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                    (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
                    (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+}
+
+// B fragment of the gate block (column block ec_a_blocks(r)), same rows:
+// column 0 is the gate vector (or zero without one), column 1 the ones of
+// one2 (two ones in the activation format, or 0), the rest zero.  Every lane
+// reads (a valid address) and then selects, so no lane diverges.
+__device__ inline u32x4 ec_bfrag_gate(const uint16_t* wgl, bool gate, uint32_t one2, int krow)
+{
+    const int l = threadIdx.x & 63;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(wgl + krow + 8 * (l >> 4));
+    const int j = l & 15;
+    const bool g = gate && j == 0;
+    const uint32_t o = j == 1 ? one2 : 0u;
+    return (u32x4){g ? v.x : o, g ? v.y : o, g ? v.z : o, g ? v.w : o};
 }
 
 // Column of the [T | l] partial held by lane column j of block cb, or -1

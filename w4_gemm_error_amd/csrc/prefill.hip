@@ -12,13 +12,19 @@
 // gate.
 //
 // GEMM tiling for gfx950 (wave64, 16x16x32 MFMA, 160 KB LDS per CU):
-//  * workgroup tile BM x 256 (BM = 64 or 128 tokens), 4 wavefronts; wavefront
-//    w owns columns [64 w, 64 w + 64) of the tile for all BM rows, so every
-//    packed weight is loaded and dequantized exactly once per tile, straight
-//    from HBM into registers (one 16-byte load per lane per 16 x 128 panel);
-//  * the X tile (BM x 128 per step) is staged in LDS, double buffered, with
-//    16-byte chunks XOR-swizzled by row so the MFMA A-operand reads are free
-//    of bank conflicts; all four wavefronts read it;
+//  * workgroup tile BM x 256 (BM = 64 or 128 tokens), 8 wavefronts (two per
+//    SIMD); wavefront w owns columns [32 w, 32 w + 32) of the tile for all BM
+//    rows, so every packed weight is loaded and dequantized exactly once per
+//    tile, straight from HBM into registers (one 16-byte load per lane per
+//    16 x 128 panel), through a ring of four 128-k steps in flight;
+//  * the X tile (BM x 128 per step) is loaded two steps ahead into registers
+//    and written to an LDS double buffer, with 16-byte chunks XOR-swizzled by
+//    row so the MFMA A-operand reads are free of bank conflicts; all eight
+//    wavefronts read it;
+//  * with bf16 and one zero point per column, the weights enter the MFMAs as
+//    128 + q and the epilogue subtracts (128 + z) times the token's sum of
+//    activations (from the prepass), which saves the per-element subtract
+//    that bf16 lacks in packed form;
 //  * split-K when the tile count alone cannot fill the 256 CUs: partial fp32
 //    tiles go to the workspace and the last-arriving workgroup of a tile adds
 //    them in a fixed order, then runs the epilogue;
@@ -88,15 +94,28 @@ void prepass_kernel(PrepassKArgs a)
     wait_all_mem();
     __syncthreads();
 
+    // per column block (wavefront-uniform branch), all fragment reads of the
+    // slice first, then the MFMAs
     floatx4 acc[PRE_MAXB];
+    const int nba = ec_a_blocks(a.r);
 #pragma unroll
     for (int cb = 0; cb < PRE_MAXB; ++cb) {
         acc[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
         if (cb < nb) {
+            u32x4 bf[PRE_MAXS];
+            if (cb < nba) {
+#pragma unroll
+                for (int s = 0; s < PRE_MAXS; ++s)
+                    bf[s] = ec_bfrag_a(at, a.r, cb, 32 * min(s, (len >> 5) - 1));
+            } else {
+#pragma unroll
+                for (int s = 0; s < PRE_MAXS; ++s)
+                    bf[s] = ec_bfrag_gate(wgl, gate, a.one2, 32 * min(s, (len >> 5) - 1));
+            }
 #pragma unroll
             for (int s = 0; s < PRE_MAXS; ++s)
                 if (32 * s < len)
-                    acc[cb] = mfma16x16x32<ACT>(xf[s], ec_bfrag(at, wgl, a.r, gate, a.one2, cb, 32 * s), acc[cb]);
+                    acc[cb] = mfma16x16x32<ACT>(xf[s], bf[s], acc[cb]);
         }
     }
     floatx4* mine = a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * nb * 64;

@@ -332,7 +332,6 @@ struct DecodePlan {
     int CB;         // column blocks per main workgroup
     int n_main;     // main workgroups
     bool xlds;      // main workgroups stage the activations in LDS
-    int single;     // hand-over: 1 = per-slot partial sums, 0 = reduced by the last EC workgroup
     int stage_first;  // main workgroups stage X before issuing weight loads
     size_t rep_data_stride;  // bytes per replica slot of hand-over data
     size_t off_flags, off_partial, off_rep_ctrl, off_rep_data, bytes;
