@@ -240,7 +240,12 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wavefront-uniform
     const int mb = blockIdx.x - a.P;
-    const int cb0 = mb * CB;
+    // Workgroups with ids congruent mod 8 run on one XCD; give each such
+    // class a contiguous range of column blocks, so that the lines of B,
+    // scale/zero and Y that neighbouring blocks share are fetched into one
+    // L2 rather than into eight.
+    const int q8 = a.n_main >> 3, r8 = a.n_main & 7, c8 = mb & 7;
+    const int cb0 = (c8 * q8 + min(c8, r8) + (mb >> 3)) * CB;
     const int M = a.M;
     const int K = a.K;
     const int KB = a.KB;
