@@ -149,7 +149,8 @@ def test_deterministic_and_workspace_reuse(phase, M):
         again = gpu_layer(d, packed, phase, workspace=ws)
         assert np.array_equal(again, first)
     if phase == "decode":
-        assert int(ws[:16].view(t.int32).abs().sum().item()) == 0   # counters back at zero, no timeout
+        # decode hand-over state (flags, counters, data) is back at zero, no wait timed out
+        assert int(t.count_nonzero(ws).item()) == 0
 
 
 def test_phase_dispatch_agrees():

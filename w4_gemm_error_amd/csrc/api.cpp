@@ -39,16 +39,22 @@ int check_weight_shape(int N, int K, int G)
 
 // Workspace layout, shared by both entry points so that one workspace can
 // serve decode and prefill calls in any order:
-//   [0, CTRL_BYTES)   control words that every call returns to zero --
-//                     decode flags, split-K tile counters, the decode
-//                     replica slots; never overwritten by data
-//   [CTRL_BYTES, ...) per-call data (partial sums, gated activations), fully
-//                     written before it is read within a call
-constexpr size_t CTRL_BYTES = 1 << 20;
+//   [0, CTRL_BYTES)   state that every call returns to zero and that no
+//                     call overwrites with anything else: decode flags,
+//                     split-K tile counters, the decode replica slots'
+//                     counters and data, the decode EC partial sums (decode
+//                     hand-over words announce themselves by being nonzero)
+//   [CTRL_BYTES, ...) per-call data of the prefill kernels (partial sums,
+//                     gated activations), fully written before it is read
+//                     within a call
+constexpr size_t CTRL_BYTES = 16 << 20;
 constexpr size_t OFF_DEC_FLAGS = 0;           // 256 B
 constexpr size_t OFF_GEMM_CNT = 256 + 1024;   // split-K tile counters, <= 256 of them
 constexpr size_t OFF_DEC_REP = 64 << 10;      // DEC_NREP decode slots of DEC_REP_CTRL_STRIDE bytes
-static_assert(OFF_DEC_REP + DEC_NREP * DEC_REP_CTRL_STRIDE <= CTRL_BYTES, "control region");
+constexpr size_t OFF_DEC_REP_DATA = 256 << 10;  // DEC_NREP slots of DEC_REP_DATA_STRIDE bytes
+constexpr size_t OFF_DEC_PARTIAL = 512 << 10;   // decode EC partial sums, up to CTRL_BYTES
+static_assert(OFF_DEC_REP + DEC_NREP * DEC_REP_CTRL_STRIDE <= OFF_DEC_REP_DATA, "control region");
+static_assert(OFF_DEC_REP_DATA + DEC_NREP * DEC_REP_DATA_STRIDE <= OFF_DEC_PARTIAL, "control region");
 
 DecodePlan make_decode_plan(int M, int N, int K, int r)
 {
@@ -72,16 +78,12 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
     p.stage_first = r > 0 ? 1 : 0;
     p.off_flags = OFF_DEC_FLAGS;
     p.off_rep_ctrl = OFF_DEC_REP;
-    size_t off = CTRL_BYTES;
-    p.off_partial = off;
-    if (r > 0)
-        off = align_up(off + (size_t)p.P * 16 * p.RC * sizeof(float), 4096);
-    p.off_rep_data = off;
-    if (r > 0) {
-        p.rep_data_stride = align_up((size_t)M * p.r_pad * 2, 4096);
-        off += (size_t)DEC_NREP * p.rep_data_stride;
-    }
-    p.bytes = off;
+    p.off_rep_data = OFF_DEC_REP_DATA;
+    p.off_partial = OFF_DEC_PARTIAL;
+    // the EC partial sums must fit the control region (K up to ~60k at
+    // r = 256 and 16 tokens, far more at lower rank or fewer tokens)
+    p.ok = r == 0 || OFF_DEC_PARTIAL + (size_t)p.P * M * p.RC * 4 <= CTRL_BYTES;
+    p.bytes = CTRL_BYTES;
     return p;
 }
 
@@ -265,6 +267,8 @@ int w4ec_linear_decode(const void* X, const void* packed, const void* A, const v
     size_t need = 0;
     if (M > 0 && r >= 0 && r <= MAX_RANK && check_weight_shape(N, K, group_size) == W4EC_OK) {
         p = make_decode_plan(M, N, K, r);
+        if (!p.ok)
+            return W4EC_ERR_UNSUPPORTED;
         need = r > 0 ? p.bytes : 0;
     }
     int rc = check_layer_args(X, packed, A, B, w_g, Y, M, N, K, r, group_size, act_dtype,

@@ -58,11 +58,10 @@ struct DecodeKArgs {
     int M, N, K, r, r_pad, G, NB, KB, Npad;
     int P, KS, RC, n_main;
     int stage_first;     // main workgroups stage X before issuing weight loads
-    uint32_t* flags;     // [0] EC arrivals, [2] a wait timed out
-    float* partial;      // [P][16][RC]
-    uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [0] ready, [1] readers done
-    uint8_t* rep_data;   // DEC_NREP slots of rep_data_stride bytes
-    size_t rep_data_stride;
+    uint32_t* flags;     // [2]: a wait timed out
+    uint32_t* partial;   // [P][M][RC] hand-over words
+    uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [1] readers done
+    uint8_t* rep_data;   // DEC_NREP slots of DEC_REP_DATA_STRIDE bytes: T_g [M][r_pad] as hand-over words
 };
 
 __device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
@@ -137,10 +136,11 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     case 3: dec_ec_mfma<ACT, 6>(xf, at, wgl, r, gate, w, acc); break;
     default: dec_ec_mfma<ACT, 8>(xf, at, wgl, r, gate, w, acc); break;
     }
-    const int nrep = min(DEC_NREP, a.n_main);       // slots that have readers
 
-    // partial sums -> [P][16][RC]; the last EC workgroup reduces them
-    float* part = a.partial + (size_t)p * 16 * a.RC;
+    // partial sums -> [P][M][RC] as hand-over words: stored and left, with no
+    // wait and no counter; EC workgroup 0 takes each one as it lands
+    const int qs = M * a.RC;                               // words per slice
+    uint32_t* part = a.partial + (size_t)p * qs;
 #pragma unroll
     for (int i = 0; i < DEC_EC_MAXI; ++i) {
         const int cb = w + 4 * i;
@@ -150,46 +150,72 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
             for (int v = 0; v < 4; ++v) {
                 const int m = 4 * (l >> 4) + v;
                 if (m < M)
-                    st4_dev(part + m * a.RC + c, acc[i][v]);
+                    atomic_store_dev(part + m * a.RC + c, hw_enc32(acc[i][v]));
             }
         }
     }
-    wait_all_mem();
-    __syncthreads();
-    __shared__ uint32_t s_old;
-    if (tid == 0)
-        s_old = atomic_add_dev(&a.flags[0], 1u);
-    __syncthreads();
-    if (s_old != (uint32_t)(a.P - 1))
+
+    // ---- this workgroup's share of the reduction: 8-byte words [w0, w1) of
+    // T_g = g * T ([M][r_pad] values, four per word), for which it adds the P
+    // slices of its T values and of every token's gate logit
+    const int n8 = M * a.r_pad / 4;
+    const int share = (n8 + a.P - 1) / a.P;
+    const int w0 = p * share, w1 = min(n8, w0 + share);
+    if (w0 >= w1)
         return;
-    if (tid == 0)
-        atomic_store_dev(&a.flags[0], 0u);
-    float* red = reinterpret_cast<float*>(smem);            // [ng][ne] (ng > 1 only: <= 256 floats)
-    float* tsum = red + DEC_THREADS;                        // [M][RC]
-    float* gl = tsum + 16 * a.RC;                           // [16]
-    uint16_t* tg = reinterpret_cast<uint16_t*>(gl + 16);    // [M][r_pad]
-    const int ne = M * a.RC;
-    // ng thread groups split the P slices (slice q -> group q mod ng); each
-    // thread keeps 8 loads in flight, and the groups' sums are added in
-    // group order, so the result does not depend on timing
-    const int ng = max(1, min(a.P, DEC_THREADS / ne));
-    const size_t qs = (size_t)16 * a.RC;
+    const int nw = w1 - w0;
+    const int nv = 4 * nw;                                  // T values, then M logits
+    const int ne = nv + M;
+    // ng thread groups split the P slices (slice q -> group q mod ng); ng
+    // depends on the shape only, so every workgroup adds a token's logit in
+    // the same order
+    const int ng = max(1, min(a.P, DEC_THREADS / (4 * share + M)));
+    __syncthreads();                                        // the slice in LDS is no longer read
+    const int tsum_off = ng > 1 ? ng * ne : 0;
+    float* red = reinterpret_cast<float*>(smem);            // [ng][ne] (ng > 1 only)
+    float* tsum = red + tsum_off;                           // [ne]
+    uint64_t* tw = reinterpret_cast<uint64_t*>(red + ((tsum_off + ne + 1) & ~1));   // [nw], 8-byte aligned
+    uint32_t it = 0;                                        // bounded wait, shared by all of this thread's waits
     for (int e0 = tid; e0 < ne * ng; e0 += DEC_THREADS) {
         const int g = e0 / ne, e = e0 - g * ne;
-        const float* src = a.partial + e;
-        float t = 0.0f;
-        int q = g;
-        for (; q + 7 * ng < a.P; q += 8 * ng) {
-            float v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = ld4_dev(src + (size_t)(q + i * ng) * qs);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                t += v[i];
+        int pe = (e - nv) * a.RC + r;                       // a logit ...
+        if (e < nv) {                                       // ... or a T value (none past column r)
+            const int v = 4 * w0 + e;
+            const int m = v / a.r_pad, c = v - m * a.r_pad;
+            pe = c < r ? m * a.RC + c : -1;
         }
-        for (; q < a.P; q += ng)
-            t += ld4_dev(src + (size_t)q * qs);
+        float t = 0.0f;
+        if (pe >= 0) {
+            const uint32_t* src = a.partial + pe;
+            for (int q = g; q < a.P; q += 8 * ng) {
+                // eight slices in flight; those not landed yet are loaded again together
+                uint32_t v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    v[i] = q + i * ng < a.P ? atomic_load_dev(src + (size_t)(q + i * ng) * qs) : 1u;
+                for (;;) {
+                    bool miss = false;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        miss |= v[i] == 0u;
+                    if (!miss)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                    if (++it >= SPIN_LIMIT) {
+                        atomic_store_dev(&a.flags[2], 1u);
+                        break;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (v[i] == 0u)                     // only slices < P can read as zero
+                            v[i] = atomic_load_dev(src + (size_t)(q + i * ng) * qs);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (q + i * ng < a.P)
+                        t += hw_dec32(v[i]);
+            }
+        }
         if (ng > 1)
             red[e0] = t;
         else
@@ -205,32 +231,35 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
         }
     }
     __syncthreads();
-    if (tid < M)
-        gl[tid] = sigmoid_f32(tsum[tid * a.RC + r] + a.b_g);
-    __syncthreads();
-    const int nt = M * a.r_pad;
-    for (int e = tid; e < nt; e += DEC_THREADS) {
-        const int m = e / a.r_pad, c = e - m * a.r_pad;
-        tg[e] = f32_to_act<ACT>(c < r ? gl[m] * tsum[m * a.RC + c] : 0.0f);
-    }
-    __syncthreads();
-    const int n8 = nt / 4;                                  // 8-byte words of T_g
-    const uint64_t* tg8 = reinterpret_cast<const uint64_t*>(tg);
-    const int sstep = n8 <= DEC_THREADS ? DEC_THREADS / n8 : 1;   // thread -> (word, slots s0 + j sstep)
-    const int s0 = n8 <= DEC_THREADS ? tid / n8 : 0;
-    if (s0 < sstep) {
-        for (int i = tid - s0 * n8; i < n8; i += DEC_THREADS) {
-            const uint64_t v = tg8[i];
-            for (int slot = s0; slot < nrep; slot += sstep) {
-                uint64_t* dst = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * a.rep_data_stride);
-                __hip_atomic_store(dst + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+    // gate, round to the activation format, pack four values per word
+    for (int i = tid; i < nw; i += DEC_THREADS) {
+        const int v0 = 4 * (w0 + i);
+        const int m = v0 / a.r_pad;
+        const float gm = sigmoid_f32(tsum[nv + m] + a.b_g);
+        uint64_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = v0 + k - m * a.r_pad;
+            word |= (uint64_t)hw_enc16(f32_to_act<ACT>(c < r ? gm * tsum[4 * i + k] : 0.0f)) << (16 * k);
         }
+        tw[i] = word;
     }
-    wait_all_mem();
     __syncthreads();
-    if (tid < nrep)
-        atomic_store_dev(rep_word(a, tid, 0), 1u);
+    const int nrep = min(DEC_NREP, a.n_main);               // slots that have readers
+    for (int i = tid; i < nw * nrep; i += DEC_THREADS) {
+        const int slot = i / nw, j = i - slot * nw;
+        st8_dev(reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * DEC_REP_DATA_STRIDE) + w0 + j, tw[j]);
+    }
+}
+
+// LDS of the main role: the staged activations (during the stream), the
+// wavefront reduction (after it) at the same offset, then the B columns
+__host__ __device__ inline size_t main_b_offset(int M, int K, bool xlds, int CB)
+{
+    size_t b = (size_t)4 * CB * 64 * 16;
+    if (xlds && (size_t)M * K * 2 > b)
+        b = (size_t)M * K * 2;
+    return (b + 15) / 16 * 16;
 }
 
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
@@ -299,6 +328,36 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         sz0[j] = *szp[j];
     uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
     const int nxchunks = XLDS ? M * K / 8 : 1;       // 16-byte chunks of X (XCH per thread suffice)
+    // The epilogue's B columns (rows [0, r_pad) of this workgroup's column
+    // blocks, 16-byte chunks of 8 columns) are loaded first, so that they do
+    // not queue behind the weight stream; they stay in registers during the
+    // stream and are parked in LDS after it.
+    u32x4 bstage[2 * CB];
+    {
+        const int nbch = CB * a.r_pad * 2;
+        const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
+#pragma unroll
+        for (int i = 0; i < 2 * CB; ++i) {
+            const int ch = tid + DEC_THREADS * i;
+            const int j = ch / (2 * a.r_pad), jr = (ch >> 1) - j * a.r_pad;
+            const int n0 = (cb0 + j) * PANEL_N + 8 * (ch & 1);
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (a.r > 0 && ch < nbch && jr < a.r) {
+                const uint16_t* src = a.B + (size_t)jr * a.N + n0;
+                if (bvec && n0 + 8 <= a.N) {
+                    v = ld16(src);
+                } else {
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        hv[t] = n0 + t < a.N ? (uint32_t)src[t] : 0u;
+                    v = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                hv[6] | (hv[7] << 16)};
+                }
+            }
+            bstage[i] = v;
+        }
+    }
     u32x4 xstage[XLDS ? XCH : 1];
     const uint16_t* xg = a.X + (size_t)(xrow ? row : 0) * K + (size_t)kbeg * PANEL_K + koff;
     auto issue = [&](int u, int i) {                 // panel i (clamped) into ring slot u
@@ -443,27 +502,15 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     for (int j = 0; j < CB; ++j)
         acc[j] += s_cur[j] * accg[j];
 
-    // B fragments for the epilogue (rank rows 32 rs + koff + t, column n),
-    // issued now so that they arrive during the reductions below
-    u32x4 bfr[CB][8];
+    // park B in LDS ([CB][r_pad][16] halves, past the staged activations and
+    // the reduction buffer; read after the barrier below)
+    uint16_t* bl = reinterpret_cast<uint16_t*>(smem + main_b_offset(M, K, XLDS, CB));
     if (a.r > 0) {
 #pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            if ((j & 3) != w)
-                continue;
-#pragma unroll
-            for (int rs = 0; rs < 8; ++rs) {
-                if (rs < nsteps) {
-                    uint32_t hv[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const int jr = 32 * rs + koff + t;
-                        hv[t] = (jr < a.r && n_l[j] < a.N) ? (uint32_t)a.B[(size_t)jr * a.N + n_l[j]] : 0u;
-                    }
-                    bfr[j][rs] = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
-                                         hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
-                }
-            }
+        for (int i = 0; i < 2 * CB; ++i) {
+            const int ch = tid + DEC_THREADS * i;
+            if (ch < CB * a.r_pad * 2)
+                st16(bl + (size_t)ch * 8, bstage[i]);
         }
     }
 
@@ -474,13 +521,36 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     for (int j = 0; j < CB; ++j)
         red[(w * CB + j) * 64 + l] = acc[j];
 
-    // ---- gated rank-r activations from this workgroup's replica slot
+    // ---- gated rank-r activations from this workgroup's replica slot, in
+    // the MFMA A-operand layout (row = token l & 15, ranks 32 rs + koff + t),
+    // taken as soon as every word has landed; a wavefront with an epilogue
+    // waits for them while the others are done
     const int slot = mb % DEC_NREP;
-    const uint8_t* sdata = a.rep_data + (size_t)slot * a.rep_data_stride;
-    if (a.r > 0 && tid == 0) {
+    uint64_t* sdata = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * DEC_REP_DATA_STRIDE);
+    u32x4 af[8];
+    if (a.r > 0 && w < CB) {
+        const uint64_t* src = sdata + (row * a.r_pad + koff) / 4;
         uint32_t it = 0;
-        while (atomic_load_dev(rep_word(a, slot, 0)) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
+        // read all of them, and again while any has not landed
+        for (;;) {
+            bool miss = false;
+#pragma unroll
+            for (int rs = 0; rs < 8; ++rs) {
+                if (rs < nsteps) {
+                    uint64_t lo = 0, hi = 0;
+                    if (xrow) {
+                        lo = ld8_dev(src + 8 * rs);
+                        hi = ld8_dev(src + 8 * rs + 1);
+                        miss |= (hw_missing16(lo) | hw_missing16(hi)) != 0;
+                        lo = ~lo;
+                        hi = ~hi;
+                    }
+                    af[rs] = (u32x4){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+                }
+            }
+            if (__builtin_amdgcn_ballot_w64(miss) == 0)
+                break;
+            __builtin_amdgcn_s_sleep(1);
             if (++it >= SPIN_LIMIT) {
                 atomic_store_dev(&a.flags[2], 1u);
                 break;
@@ -499,20 +569,16 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         tot += red[(3 * CB + j) * 64 + l];
         const int n = n_l[j];
         if (a.r > 0) {
+            const uint16_t* bj = bl + (size_t)j * a.r_pad * PANEL_N;
+            u32x4 bfr[8];
 #pragma unroll
-            for (int rs = 0; rs < 8; ++rs) {
-                if (rs < nsteps) {
-                    u32x4 af = (u32x4){0u, 0u, 0u, 0u};
-                    if (xrow) {
-                        const uint64_t* src = reinterpret_cast<const uint64_t*>(
-                            sdata + ((size_t)row * a.r_pad + 32 * rs + koff) * 2);
-                        const uint64_t lo = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        const uint64_t hi = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        af = (u32x4){(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-                    }
-                    tot = mfma16x16x32<ACT>(af, bfr[j][rs], tot);
-                }
-            }
+            for (int rs = 0; rs < 8; ++rs)
+                if (rs < nsteps)
+                    bfr[rs] = lds_bfrag(bj, PANEL_N, 0, 32 * rs);
+#pragma unroll
+            for (int rs = 0; rs < 8; ++rs)
+                if (rs < nsteps)
+                    tot = mfma16x16x32<ACT>(af[rs], bfr[rs], tot);
         }
         if (n < a.N) {
 #pragma unroll
@@ -524,16 +590,26 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
     }
 
-    // the last reader of a slot clears it for the next call
+    // The last reader of a slot returns the slot, and its share of the EC
+    // partial sums (whose reduction finished before any slot was written),
+    // to zero for the next call.
     if (a.r > 0) {
-        __syncthreads();
+        __shared__ int s_last;
         if (tid == 0) {
             const int readers = a.n_main / DEC_NREP + (slot < a.n_main % DEC_NREP ? 1 : 0);
-            const uint32_t old = atomic_add_dev(rep_word(a, slot, 1), 1u);
-            if (old == (uint32_t)(readers - 1)) {
-                atomic_store_dev(rep_word(a, slot, 0), 0u);
+            s_last = atomic_add_dev(rep_word(a, slot, 1), 1u) == (uint32_t)(readers - 1);
+        }
+        __syncthreads();
+        if (s_last) {
+            if (tid == 0)
                 atomic_store_dev(rep_word(a, slot, 1), 0u);
-            }
+            const int n8 = M * a.r_pad / 4;
+            for (int i = tid; i < n8; i += DEC_THREADS)
+                st8_dev(sdata + i, 0ull);
+            const int nrep = min(DEC_NREP, a.n_main);
+            const int np = a.P * M * a.RC;
+            for (int i = slot * DEC_THREADS + tid; i < np; i += nrep * DEC_THREADS)
+                atomic_store_dev(a.partial + i, 0u);
         }
     }
 }
@@ -555,23 +631,20 @@ constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS
 
 bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
 
-// LDS of the main role: the staged activations, then (after the stream)
-// the wavefront reduction
 static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r)
 {
-    size_t b = (size_t)4 * p.CB * 64 * 16;
-    if (p.xlds)
-        b = std::max(b, (size_t)M * K * 2);
-    return (b + 15) / 16 * 16;
+    return main_b_offset(M, K, p.xlds, p.CB) + (r > 0 ? (size_t)p.CB * p.r_pad * PANEL_N * 2 : 0);
 }
 
 // LDS of the EC role: the staged slice and gate vector, then the final reduction
-static size_t ec_lds_bytes(const DecodePlan& p, int r)
+static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
 {
     if (p.P == 0)
         return 0;
     const size_t at = (size_t)ec_slice_bytes(r, p.KS) + (size_t)p.KS * 2;
-    const size_t fin = (size_t)DEC_THREADS * 4 + (size_t)16 * (r + 1) * 4 + 64 + (size_t)16 * p.r_pad * 2;
+    // the reduction's share: [ng][ne] sums (<= 256 floats, or none), [ne] totals, [nw] words
+    const int share = (M * p.r_pad / 4 + p.P - 1) / p.P;
+    const size_t fin = ((size_t)DEC_THREADS + 4 * share + M + 2) * 4 + (size_t)share * 8;
     return (std::max(at, fin) + 15) / 16 * 16;
 }
 
@@ -579,7 +652,7 @@ template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
 static hipError_t launch_decode_t(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>;
-    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r), ec_lds_bytes(p, k.r));
+    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r), ec_lds_bytes(p, k.M, k.r));
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
@@ -630,10 +703,9 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.P = p.P; k.KS = p.KS; k.RC = p.RC; k.n_main = p.n_main;
     k.stage_first = p.stage_first;
     k.flags = (uint32_t*)(a.ws + p.off_flags);
-    k.partial = (float*)(a.ws + p.off_partial);
+    k.partial = (uint32_t*)(a.ws + p.off_partial);
     k.rep_ctrl = (uint8_t*)(a.ws + p.off_rep_ctrl);
     k.rep_data = (uint8_t*)(a.ws + p.off_rep_data);
-    k.rep_data_stride = p.rep_data_stride;
     if (a.act == ACT_F16)
         return launch_decode_act<ACT_F16>(k, p, st);
     return launch_decode_act<ACT_BF16>(k, p, st);

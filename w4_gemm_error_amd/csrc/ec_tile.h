@@ -72,22 +72,28 @@ __device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* 
         copy16_to_lds(w_g + k0 + 8 * l, wgl);
 }
 
-// B fragment of v_mfma_f32_16x16x32 for column block cb < ec_a_blocks(r),
-// rows krow .. krow + 31 of the staged slice: lane l gets column
-// 16 cb + (l & 15) at rows krow + 8 (l >> 4) + t, t = 0..7.
-__device__ inline u32x4 ec_bfrag_a(const uint16_t* at, int r, int cb, int krow)
+// B fragment of v_mfma_f32_16x16x32 from a row-major LDS array of 16-bit
+// values (pitch halves per row, a multiple of 4), columns c0 .. c0 + 15,
+// rows krow .. krow + 31: lane l gets column c0 + (l & 15) at rows
+// krow + 8 (l >> 4) + t, t = 0..7.
+__device__ inline u32x4 lds_bfrag(const uint16_t* base, int pitch, int c0, int krow)
 {
     const int l = threadIdx.x & 63;
     const int g = l >> 4;
-    const int pitch = ec_pitch(r);
     const int s = l & 15;
-    const uint16_t* p = at + (krow + 8 * g + (s >> 2)) * pitch + 16 * cb + 4 * (s & 3);
+    const uint16_t* p = base + (krow + 8 * g + (s >> 2)) * pitch + c0 + 4 * (s & 3);
     const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
     const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * pitch));
     return (u32x4){(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
                    (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16),
                    (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16),
                    (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
+}
+
+// B fragment for column block cb < ec_a_blocks(r) of the staged slice
+__device__ inline u32x4 ec_bfrag_a(const uint16_t* at, int r, int cb, int krow)
+{
+    return lds_bfrag(at, ec_pitch(r), 16 * cb, krow);
 }
 
 // B fragment of the gate block (column block ec_a_blocks(r)), same rows:

@@ -285,6 +285,36 @@ __device__ inline floatx4 ld16_dev(const floatx4* p)
                      __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
 }
 
+// Self-announcing hand-over words.  A value is stored as the bit complement
+// of its encoding, so the zero word that a cleared buffer holds means "not
+// written yet" and a reader can take each value as soon as it lands, with no
+// flag, counter or store acknowledgement in between.  The one encoding whose
+// complement is zero is an all-ones NaN; it is replaced by another NaN.
+__device__ inline uint32_t hw_enc32(float v)
+{
+    const uint32_t b = __float_as_uint(v);
+    return ~(b == 0xFFFFFFFFu ? 0xFFC00000u : b);
+}
+__device__ inline float hw_dec32(uint32_t w) { return __uint_as_float(~w); }
+// 16-bit values (fp16 or bf16; 0xFFC0 is a NaN in both)
+__device__ inline uint16_t hw_enc16(uint16_t b) { return (uint16_t)~(b == 0xFFFFu ? 0xFFC0u : b); }
+// nonzero iff a word of four 16-bit values holds one not written yet (a
+// zero lane)
+__device__ inline uint64_t hw_missing16(uint64_t w)
+{
+    return (w - 0x0001000100010001ull) & ~w & 0x8000800080008000ull;
+}
+
+__device__ inline uint64_t ld8_dev(const uint64_t* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void st8_dev(uint64_t* p, uint64_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // all of this thread's outstanding memory operations have completed
 __device__ inline void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -323,6 +353,7 @@ constexpr uint32_t SPIN_LIMIT = 1u << 22;
 constexpr int DEC_EC_KS = 256;   // at most this many k per decode EC workgroup
 constexpr int DEC_NREP = 32;                    // replica slots of the decode hand-over
 constexpr size_t DEC_REP_CTRL_STRIDE = 4096;    // control words of one slot (own page)
+constexpr size_t DEC_REP_DATA_STRIDE = 8192;    // T_g of one slot: up to 16 tokens x 256 ranks x 2 bytes
 
 struct DecodePlan {
     int P;          // EC workgroups (K slices) -- 0 when r == 0
@@ -333,7 +364,7 @@ struct DecodePlan {
     int n_main;     // main workgroups
     bool xlds;      // main workgroups stage the activations in LDS
     int stage_first;  // main workgroups stage X before issuing weight loads
-    size_t rep_data_stride;  // bytes per replica slot of hand-over data
+    bool ok;        // the shape fits the workspace's control region
     size_t off_flags, off_partial, off_rep_ctrl, off_rep_data, bytes;
 };
 
