@@ -99,12 +99,16 @@ int w4ec_unpack(const void* packed, int N, int K, int group_size,
                 uint8_t* q_canon, uint16_t* scale, uint16_t* zero, void* stream);
 
 /* Workspace bytes needed by w4ec_linear_decode / w4ec_linear_prefill for
- * this shape (the larger of the two when both apply).  The workspace holds
- * the gated rank-r activations, partial sums and the counters through which
- * workgroups hand over partial results.  It must be zero-filled once when
- * allocated; every call leaves its counters at zero again, so it can be
- * reused by later calls on the same stream without clearing.  Two calls
- * that overlap in time must not share a workspace. */
+ * this shape (the larger of the two when both apply; at least
+ * W4EC_WS_STATE_BYTES when r > 0).  The workspace holds the gated rank-r
+ * activations, partial sums and the counters through which workgroups hand
+ * over partial results.  It must be zero-filled once when allocated.  Its
+ * first W4EC_WS_STATE_BYTES bytes hold hand-over state that every call
+ * returns to zero (a nonzero byte there after a call has completed means a
+ * bounded wait inside a kernel timed out), so the workspace can be reused by
+ * later calls on the same stream, of any shape and either phase, without
+ * clearing.  Two calls that overlap in time must not share a workspace. */
+#define W4EC_WS_STATE_BYTES ((size_t)16 << 20)
 size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size);
 
 /* The layer, decode phase: 1 <= M <= 16 tokens, one kernel launch.
@@ -115,7 +119,9 @@ size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size);
  *   b_g   gate bias (fp32, by value)
  *   Y     device act [M, N] (output)
  *   r     EC rank; r == 0 is the plain W4 layer (A, B, w_g ignored, may be NULL)
- * Returns W4EC_ERR_UNSUPPORTED for M > 16. */
+ * Returns W4EC_ERR_UNSUPPORTED for M > 16, and for shapes whose EC partial
+ * sums exceed the workspace's state region (only with r near 256, 16
+ * tokens and K beyond about 60000). */
 int w4ec_linear_decode(const void* X, const void* packed, const void* A, const void* B,
                        const void* w_g, float b_g, void* Y,
                        int M, int N, int K, int r, int group_size, int act_dtype,

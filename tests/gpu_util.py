@@ -52,8 +52,16 @@ def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=N
     wg = dev_act(d["w_g"], act) if (r > 0 and with_gate) else None
     bg = d["b_g"] if b_g is None else b_g
     fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
+    if workspace is None:
+        t = torch()
+        need = w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], r, d["group_size"])
+        workspace = t.zeros(max(need, 256), dtype=t.uint8, device="cuda")
     Y = fn(X, packed, A, B, wg, bg, N=d["N"], group_size=d["group_size"], workspace=workspace)
     torch().cuda.synchronize()
+    # every call leaves the hand-over state at zero; a nonzero byte there
+    # would mean that a bounded wait timed out
+    state = workspace[: w4.W4EC_WS_STATE_BYTES]
+    assert int(torch().count_nonzero(state).item()) == 0, f"{phase}: hand-over state not at zero after the call"
     return host_bits(Y)
 
 

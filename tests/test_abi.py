@@ -102,3 +102,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(w4, "_lib", None)
     with pytest.raises(ImportError):
         w4.lib()
+
+
+def test_state_region_constant_matches_header():
+    """The binding's W4EC_WS_STATE_BYTES mirrors the header's definition."""
+    import re
+    text = open(w4.HEADER_PATH).read()
+    m = re.search(r"#define W4EC_WS_STATE_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "W4EC_WS_STATE_BYTES not found in the header"
+    assert int(m.group(1)) << int(m.group(2)) == w4.W4EC_WS_STATE_BYTES

@@ -18,7 +18,7 @@ import threading
 __all__ = [
     "W4ECError", "lib", "exported_symbols", "header_symbols",
     "W4EC_OK", "W4EC_ERR_INVALID_ARG", "W4EC_ERR_UNSUPPORTED", "W4EC_ERR_WORKSPACE", "W4EC_ERR_HIP",
-    "W4EC_FP16", "W4EC_BF16", "DECODE_MAX_M",
+    "W4EC_FP16", "W4EC_BF16", "DECODE_MAX_M", "W4EC_WS_STATE_BYTES",
     "w4ec_status_str", "w4ec_packed_bytes", "w4ec_workspace_bytes",
     "w4ec_quantize_rtn", "w4ec_pack", "w4ec_unpack",
     "w4ec_linear_decode", "w4ec_linear_prefill", "w4ec_linear",
@@ -37,6 +37,7 @@ W4EC_ERR_HIP = -4
 W4EC_FP16 = 0
 W4EC_BF16 = 1
 DECODE_MAX_M = 16
+W4EC_WS_STATE_BYTES = 16 << 20   # leading workspace bytes every call returns to zero
 
 _lock = threading.Lock()
 _lib = None

@@ -47,7 +47,7 @@ int check_weight_shape(int N, int K, int G)
 //   [CTRL_BYTES, ...) per-call data of the prefill kernels (partial sums,
 //                     gated activations), fully written before it is read
 //                     within a call
-constexpr size_t CTRL_BYTES = 16 << 20;
+constexpr size_t CTRL_BYTES = W4EC_WS_STATE_BYTES;
 constexpr size_t OFF_DEC_FLAGS = 0;           // 256 B
 constexpr size_t OFF_GEMM_CNT = 256 + 1024;   // split-K tile counters, <= 256 of them
 constexpr size_t OFF_DEC_REP = 64 << 10;      // DEC_NREP decode slots of DEC_REP_CTRL_STRIDE bytes
