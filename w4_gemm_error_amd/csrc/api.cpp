@@ -94,10 +94,15 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
     PrefillPlan p{};
     const int NB = (N + PANEL_N - 1) / PANEL_N;
     const int KB = K / PANEL_K;
-    p.BM = M <= 64 ? 64 : 128;
     p.BN = 256;
-    p.mt = (M + p.BM - 1) / p.BM;
     p.nt = (NB * PANEL_N + p.BN - 1) / p.BN;
+    p.BM = M <= 64 ? 64 : 128;
+    // With few tiles the K split that fills the chip writes and reads
+    // ksplit x M x N fp32 partial sums; when 128-token tiles would need a
+    // split of 4 or more, 64-token tiles halve that traffic.
+    if (p.BM == 128 && (long long)((M + 127) / 128) * p.nt * 4 <= TARGET_WGS)
+        p.BM = 64;
+    p.mt = (M + p.BM - 1) / p.BM;
     p.ksplit = 1;
     // split K only while the workgroups still fit in one round (one per CU)
     while ((long long)p.mt * p.nt * p.ksplit * 2 <= TARGET_WGS && KB / (2 * p.ksplit) >= 4 && p.ksplit < 16)

@@ -499,15 +499,39 @@ void prefill_gemm_kernel(GemmKArgs a)
             return;
         if (tid == 0)
             atomic_store_dev(&a.cnt[tile], 0u);
+        // splits added in order; all fragments of one split are in flight at once
+        floatx4 sum[RB][JW];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int j = 0; j < JW; ++j) {
-                floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
-                for (int z = 0; z < a.ksplit; ++z)
-                    t += (z == kz) ? acc[rb][j] : ld16_dev(a.partial + frag(z, rb, j));
-                acc[rb][j] = t;
+            for (int j = 0; j < JW; ++j)
+                sum[rb][j] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < a.ksplit; ++z) {
+            if (z == kz) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        sum[rb][j] += acc[rb][j];
+            } else {
+                floatx4 t[RB][JW];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        t[rb][j] = ld16_dev(a.partial + frag(z, rb, j));
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        sum[rb][j] += t[rb][j];
             }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                acc[rb][j] = sum[rb][j];
     }
 
     // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r correction
@@ -531,29 +555,81 @@ void prefill_gemm_kernel(GemmKArgs a)
                 acc[rb][j] *= sf[j];
     }
     if (a.r > 0) {
+        // The rank dimension in chunks of RCH: B rows [c0, c0 + RCH) of the
+        // tile's 256 columns and the same ranks of T_g for the tile's BM
+        // tokens are loaded with every load of the chunk in flight, parked in
+        // LDS, and read back as MFMA operands (B through the transpose read;
+        // its rows are padded to 272 halves so that the read is free of bank
+        // conflicts).  The last main-loop barrier freed the LDS.
+        constexpr int RCH = BM == 64 ? 32 : 64;
+        constexpr int BP = PF_BN + 16;                  // halves per LDS row of B
+        constexpr int TP = RCH + 8;                     // halves per LDS row of T_g
+        constexpr int BCH = RCH * (PF_BN / 8) / GEMM_THREADS;             // 16-byte B chunks per thread
+        constexpr int TCH = (BM * (RCH / 8) + GEMM_THREADS - 1) / GEMM_THREADS;
+        static_assert(RCH * BP * 2 + BM * TP * 2 <= gemm_lds_bytes<BM>(), "EC staging fits the LDS");
+        uint16_t* bl = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* tl = bl + RCH * BP;
+        const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
         const int koff = 8 * (l >> 4);
-        const int nsteps = a.r_pad >> 5;
-        for (int rs = 0; rs < nsteps; ++rs) {
-            u32x4 bfr[JW];
+        for (int c0 = 0; c0 < a.r_pad; c0 += RCH) {
+            u32x4 bv[BCH], tv[TCH];
 #pragma unroll
-            for (int j = 0; j < JW; ++j) {
-                uint32_t hv[8];
+            for (int i = 0; i < BCH; ++i) {
+                const int ch = tid + GEMM_THREADS * i;
+                const int jr = c0 + (ch >> 5), n = n0 + 8 * (ch & 31);
+                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+                if (jr < a.r) {
+                    const uint16_t* src = a.B + (size_t)jr * a.N + n;
+                    if (bvec && n + 8 <= a.N) {
+                        v = ld16(src);
+                    } else {
+                        uint32_t hv[8];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int jr = 32 * rs + koff + t;
-                    hv[t] = (jr < a.r && n_j[j] < a.N) ? (uint32_t)a.B[(size_t)jr * a.N + n_j[j]] : 0u;
+                        for (int t = 0; t < 8; ++t)
+                            hv[t] = n + t < a.N ? (uint32_t)src[t] : 0u;
+                        v = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                    hv[6] | (hv[7] << 16)};
+                    }
                 }
-                bfr[j] = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16),
-                                 hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+                bv[i] = v;
             }
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int m = m0 + rb * 16 + (l & 15);
-                const u32x4 af = ld16(a.tg + (size_t)m * a.r_pad + 32 * rs + koff);
+            for (int i = 0; i < TCH; ++i) {
+                const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
+                const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                // ranks past r_pad (a last chunk wider than the rest) are not loaded and not used
+                tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
+                                              : (u32x4){0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) {
+                const int ch = tid + GEMM_THREADS * i;
+                st16(bl + (ch >> 5) * BP + 8 * (ch & 31), bv[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < TCH; ++i) {
+                const int ch = tid + GEMM_THREADS * i;
+                if (ch < BM * (RCH / 8)) {
+                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                    st16(tl + rr * TP + 8 * cc, tv[i]);
+                }
+            }
+            __syncthreads();
+            const int ns = min(RCH, a.r_pad - c0) >> 5;
+            for (int rs = 0; rs < ns; ++rs) {
+                u32x4 bfr[JW];
 #pragma unroll
                 for (int j = 0; j < JW; ++j)
-                    acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
+                    bfr[j] = lds_bfrag(bl, BP, 16 * (JW * w + j), 32 * rs);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(tl + (rb * 16 + (l & 15)) * TP + 32 * rs + koff);
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
+                }
             }
+            __syncthreads();                            // before the next chunk or the output tile reuses the LDS
         }
     }
 
