@@ -62,12 +62,20 @@ def layer_flops(M, N, K, r):
     return 2 * M * N * K + 2 * M * K * (r + 1) + 2 * M * r * N + 2 * M * N
 
 
-def source_digest():
-    """Digest of the kernel sources' code: line comments and blank lines are
+# the sources each measured kernel is built from (its counters stay valid
+# while these are unchanged)
+KERNEL_SOURCES = {
+    "decode_kernel": ["decode.hip", "ec_tile.h", "w4ec_common.h", "w4ec_launch.h"],
+    "prefill_call": ["prefill.hip", "ec_tile.h", "w4ec_common.h", "w4ec_launch.h"],
+}
+
+
+def source_digest(kernel):
+    """Digest of a kernel's sources' code: line comments and blank lines are
     left out, so that a comment edit does not invalidate measured counters."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4_gemm_error_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), encoding="utf-8") as f:
             code = [ln.split("//", 1)[0].rstrip() for ln in f]
         h.update(name.encode() + "\n".join(ln for ln in code if ln).encode())
@@ -76,7 +84,7 @@ def source_digest():
 
 def traffic_from_profiles(kernel_key):
     """Measured HBM bytes per launch from the committed counter summary, if
-    it was taken on the kernels as they are now (same source digest)."""
+    it was taken on the kernel as it is now (same source digest)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -84,7 +92,7 @@ def traffic_from_profiles(kernel_key):
     except (OSError, ValueError):
         return None
     e = table.get(kernel_key)
-    if not e or e.get("source_digest") != source_digest():
+    if not e or e.get("source_digest") != source_digest(kernel_key.split("/")[0]):
         return None
     return e.get("bytes_per_launch")
 
