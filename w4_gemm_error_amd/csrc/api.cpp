@@ -73,7 +73,9 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
         p.P = (K + p.KS - 1) / p.KS;
     }
     p.xlds = decode_use_xlds(M, K);
-    p.CB = (M <= 4 || p.xlds) ? 1 : 2;
+    // more tokens: four column blocks per workgroup, so that each activation
+    // fragment loaded from L2 feeds four blocks' MFMAs
+    p.CB = (M <= 4 || p.xlds) ? 1 : 4;
     p.n_main = (NB + p.CB - 1) / p.CB;
     p.stage_first = r > 0 ? 1 : 0;
     p.off_flags = OFF_DEC_FLAGS;

@@ -673,7 +673,8 @@ static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, h
     }
     if (p.CB == 1)
         return launch_decode_t<ACT, 1, 0, 4, GROUPED, false>(k, p, st);
-    return launch_decode_t<ACT, 2, 0, 4, GROUPED, false>(k, p, st);
+    // four column blocks: a ring of two steps keeps the registers at two waves per SIMD
+    return launch_decode_t<ACT, 4, 0, 2, GROUPED, false>(k, p, st);
 }
 
 template <int ACT>
