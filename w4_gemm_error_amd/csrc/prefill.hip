@@ -61,6 +61,32 @@ struct PrepassKArgs {
 constexpr int PRE_MAXB = 17;   // column blocks of [A | w_g] (r <= 256), gate block included
 constexpr int PRE_MAXS = 16;   // 32-k steps per workgroup (kc <= 512)
 
+template <int ACT, int NS>
+__device__ inline void prepass_mfma(const u32x4 (&xf)[PRE_MAXS], const uint16_t* at, const uint16_t* wgl, int r,
+                                    bool gate, uint32_t one2, int nb, floatx4 (&acc)[PRE_MAXB])
+{
+    const int nba = ec_a_blocks(r);
+#pragma unroll
+    for (int cb = 0; cb < PRE_MAXB; ++cb) {
+        acc[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        if (cb < nb) {
+            u32x4 bf[NS];
+            if (cb < nba) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    bf[s] = ec_bfrag_a(at, r, cb, 32 * s);
+            } else {
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    bf[s] = ec_bfrag_gate(wgl, gate, one2, 32 * s);
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                acc[cb] = mfma16x16x32<ACT>(xf[s], bf[s], acc[cb]);
+        }
+    }
+}
+
 // One workgroup: 64 tokens (wavefront w: tokens 16 w .. 16 w + 15) x one K
 // slice of at most 512.  Every load is issued at once -- the X fragments
 // into registers, the slice of [A | w_g] straight into LDS -- then each
@@ -87,36 +113,25 @@ void prepass_kernel(PrepassKArgs a)
     const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + 8 * (l >> 4);
     u32x4 xf[PRE_MAXS];
 #pragma unroll
-    for (int s = 0; s < PRE_MAXS; ++s)
-        if (32 * s < len)
-            xf[s] = ld16(xp + 32 * s);
+    for (int s = 0; s < PRE_MAXS; ++s)                // steps past the slice are never used
+        xf[s] = ld16(xp + 32 * min(s, (len >> 5) - 1));
     ec_stage(a.A, a.w_g, a.r, kbeg, len, at, wgl);
     wait_all_mem();
     __syncthreads();
 
     // per column block (wavefront-uniform branch), all fragment reads of the
-    // slice first, then the MFMAs
+    // slice first, then the MFMAs; the step count is a template argument, so
+    // no MFMA of the chain sits behind a branch
     floatx4 acc[PRE_MAXB];
-    const int nba = ec_a_blocks(a.r);
-#pragma unroll
-    for (int cb = 0; cb < PRE_MAXB; ++cb) {
-        acc[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
-        if (cb < nb) {
-            u32x4 bf[PRE_MAXS];
-            if (cb < nba) {
-#pragma unroll
-                for (int s = 0; s < PRE_MAXS; ++s)
-                    bf[s] = ec_bfrag_a(at, a.r, cb, 32 * min(s, (len >> 5) - 1));
-            } else {
-#pragma unroll
-                for (int s = 0; s < PRE_MAXS; ++s)
-                    bf[s] = ec_bfrag_gate(wgl, gate, a.one2, 32 * min(s, (len >> 5) - 1));
-            }
-#pragma unroll
-            for (int s = 0; s < PRE_MAXS; ++s)
-                if (32 * s < len)
-                    acc[cb] = mfma16x16x32<ACT>(xf[s], bf[s], acc[cb]);
-        }
+    switch (len >> 6) {
+    case 1: prepass_mfma<ACT, 2>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    case 2: prepass_mfma<ACT, 4>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    case 3: prepass_mfma<ACT, 6>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    case 4: prepass_mfma<ACT, 8>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    case 5: prepass_mfma<ACT, 10>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    case 6: prepass_mfma<ACT, 12>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    case 7: prepass_mfma<ACT, 14>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+    default: prepass_mfma<ACT, 16>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
     }
     floatx4* mine = a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * nb * 64;
 #pragma unroll
