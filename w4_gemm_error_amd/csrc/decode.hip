@@ -614,8 +614,12 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     }
 }
 
+// One column block per workgroup (activations staged in LDS): the grid
+// holds ~900 workgroups, which fit the CUs in one round only at four
+// wavefronts per SIMD, i.e. within 128 registers (the grouped-scale variant
+// needs the bound to get there).
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
-__global__ __launch_bounds__(DEC_THREADS)
+__global__ __launch_bounds__(DEC_THREADS, (CB == 1 && XCH > 0) ? 4 : 1)
 void decode_kernel(DecodeKArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
