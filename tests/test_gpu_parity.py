@@ -79,6 +79,8 @@ SMALL = [
     ("decode", "bf16", 5, 272, 384, 40, 384),
     ("decode", "bf16", 16, 512, 512, 8, 128),
     ("decode", "fp16", 7, 48, 1280, 256, 256),
+    ("decode", "fp16", 16, 512, 20480, 256, 20480),    # more K slices than EC workgroups
+    ("decode", "bf16", 3, 512, 20480, 256, 1024),
     ("prefill", "fp16", 17, 528, 640, 72, 640),
     ("prefill", "fp16", 300, 512, 512, 8, 512),
     ("prefill", "fp16", 129, 784, 1024, 64, 128),

@@ -157,10 +157,16 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 
     // ---- this workgroup's share of the reduction: 8-byte words [w0, w1) of
     // T_g = g * T ([M][r_pad] values, four per word), for which it adds the P
-    // slices of its T values and of every token's gate logit
+    // slices of its T values and of every token's gate logit.  The last
+    // DEC_EC_RMAX EC workgroups reduce: workgroups start in id order, so every
+    // slice a reducer waits for belongs to a workgroup that has started, and
+    // the waiting workgroups never hold all the CU slots.
+    const int red0 = max(0, a.P - DEC_EC_RMAX);
+    if (p < red0)
+        return;
     const int n8 = M * a.r_pad / 4;
-    const int share = (n8 + a.P - 1) / a.P;
-    const int w0 = p * share, w1 = min(n8, w0 + share);
+    const int share = (n8 + (a.P - red0) - 1) / (a.P - red0);
+    const int w0 = (p - red0) * share, w1 = min(n8, w0 + share);
     if (w0 >= w1)
         return;
     const int nw = w1 - w0;
@@ -647,7 +653,8 @@ static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
         return 0;
     const size_t at = (size_t)ec_slice_bytes(r, p.KS) + (size_t)p.KS * 2;
     // the reduction's share: [ng][ne] sums (<= 256 floats, or none), [ne] totals, [nw] words
-    const int share = (M * p.r_pad / 4 + p.P - 1) / p.P;
+    const int nred = std::min(p.P, DEC_EC_RMAX);
+    const int share = (M * p.r_pad / 4 + nred - 1) / nred;
     const size_t fin = ((size_t)DEC_THREADS + 4 * share + M + 2) * 4 + (size_t)share * 8;
     return (std::max(at, fin) + 15) / 16 * 16;
 }

@@ -351,6 +351,7 @@ constexpr uint32_t SPIN_LIMIT = 1u << 22;
 // (shared by the host dispatch and the workspace sizing)
 
 constexpr int DEC_EC_KS = 256;   // at most this many k per decode EC workgroup
+constexpr int DEC_EC_RMAX = 128; // at most this many decode EC workgroups reduce (half the CUs)
 constexpr int DEC_NREP = 32;                    // replica slots of the decode hand-over
 constexpr size_t DEC_REP_CTRL_STRIDE = 4096;    // control words of one slot (own page)
 constexpr size_t DEC_REP_DATA_STRIDE = 8192;    // T_g of one slot: up to 16 tokens x 256 ranks x 2 bytes
