@@ -278,6 +278,13 @@ void prefill_gemm_kernel(GemmKArgs a)
     // activation register sets below alternate with the ring slots); four
     // steps keep ~64 KB of weights in flight per CU
     constexpr int D = 4;
+    // activation register sets: the activations of step i are loaded XS
+    // steps ahead.  Loads retire in issue order, so the wait for them also
+    // waits for every weight load issued before them: their distance bounds
+    // the weight ring's.  Four sets (as deep as the ring) where the
+    // registers allow.
+    constexpr int XS = BM == 64 ? 4 : 2;
+    static_assert(D % XS == 0, "activation sets must divide the ring");
     __shared__ __attribute__((aligned(16))) uint8_t smem[gemm_lds_bytes<BM>()];
     __shared__ uint32_t s_old;
 
@@ -352,7 +359,8 @@ void prefill_gemm_kernel(GemmKArgs a)
     // the one being multiplied.
     u32x4 wr[D][JW];
     uint32_t szr[GROUPED ? D : 1][JW];
-    u32x4 xr[2][XLOADS];        // activations of steps i + 1 and i + 2
+    uint32_t szcur[JW] = {};    // scale/zero of the current group (grouped)
+    u32x4 xr[XS][XLOADS];       // activations of steps i + 1, ..., i + XS
     auto issue_w1 = [&](int u, int i, int j) __attribute__((always_inline)) {
         const int ic = min(i, nk - 1);
         if constexpr (GROUPED) {
@@ -366,10 +374,10 @@ void prefill_gemm_kernel(GemmKArgs a)
         for (int j = 0; j < JW; ++j)
             issue_w1(u, i, j);
     };
-    // part p of 4 (XLOADS / 4 loads each, or all of them with part == -1)
+    // part p of 2 (XLOADS / 2 loads each, or all of them with part == -1)
     auto load_x = [&](int set, int i, int part = -1) __attribute__((always_inline)) {
         const int ic = min(i, nk - 1);
-        constexpr int PER = XLOADS >= 4 ? XLOADS / 4 : 1;
+        constexpr int PER = XLOADS >= 2 ? XLOADS / 2 : 1;
 #pragma unroll
         for (int x = 0; x < XLOADS; ++x)
             if (part < 0 || x / PER == part)
@@ -389,10 +397,11 @@ void prefill_gemm_kernel(GemmKArgs a)
             v[j] = *szsrc[j];
         set_sz(v);
     }
-    load_x(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_x(1, 1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int xs = 0; xs < XS; ++xs) {
+        load_x(xs, xs);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int u = 0; u < D; ++u) {
         issue_w(u, u);
@@ -463,20 +472,34 @@ void prefill_gemm_kernel(GemmKArgs a)
 #pragma unroll
             for (int j = 0; j < JW; ++j)
                 wv[j] = wr[u][j];
-            // per k-step s: a quarter of the activations of step i + 2 (into
-            // the set stored one step ago) and, when refilling, column block
-            // s of step i + D
+            // k-steps 0 and 1: half each of the activations of step i + XS
+            // (into the set stored one step ago); k-steps 2 and 3, when
+            // refilling: one column block each of the weights of step i + D.
+            // The weights go after the activations, so that the wait for
+            // these activations (at the end of step i + XS - 1) does not
+            // also wait for them.
+            static_assert(JW == 2, "one column block per late k-step");
             auto hook = [&](int s) __attribute__((always_inline)) {
-                load_x(u & 1, i + 2, s);
+                if (s < 2)
+                    load_x(u % XS, i + XS, s);
                 if constexpr (REFILL) {
-                    if (s < JW)
-                        issue_w1(u, i + D, s);
+                    if (s >= 2)
+                        issue_w1(u, i + D, s - 2);
                 }
             };
-            if (i < nk) {                                   // uniform
+            if (REFILL || i < nk) {                         // uniform; always true while refilling
                 if constexpr (GROUPED) {
-                    if (i == 0 || ((kb0 + i) % ppg) == 0)
-                        set_sz(szr[u]);
+                    // a new group's scale/zero, selected without a branch
+                    // (a branch here made the compiler drain every load in
+                    // flight at each step)
+                    const bool chg = i == 0 || ((kb0 + i) % ppg) == 0;
+                    uint32_t v[JW];
+#pragma unroll
+                    for (int j = 0; j < JW; ++j) {
+                        v[j] = chg ? szr[u][j] : szcur[j];
+                        szcur[j] = v[j];
+                    }
+                    set_sz(v);
                 }
                 compute(i, wv, hook);
             } else {
@@ -484,7 +507,7 @@ void prefill_gemm_kernel(GemmKArgs a)
                 for (int s = 0; s < 4; ++s)
                     hook(s);
             }
-            store_x((u + 1) & 1, (u + 1) & 1);             // step i + 1, loaded one step ago
+            store_x((u + 1) % XS, (u + 1) & 1);            // step i + 1, loaded XS - 1 steps ago
             __syncthreads();
         }
     };
