@@ -48,6 +48,7 @@ int check_weight_shape(int N, int K, int G)
 //                     gated activations), fully written before it is read
 //                     within a call
 constexpr size_t CTRL_BYTES = W4EC_WS_STATE_BYTES;
+
 constexpr size_t OFF_DEC_FLAGS = 0;           // 256 B
 constexpr size_t OFF_GEMM_CNT = 256 + 1024;   // split-K tile counters, <= 256 of them
 constexpr size_t OFF_DEC_REP = 64 << 10;      // DEC_NREP decode slots of DEC_REP_CTRL_STRIDE bytes
@@ -73,9 +74,11 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
         p.P = (K + p.KS - 1) / p.KS;
     }
     p.xlds = decode_use_xlds(M, K);
-    // more tokens: four column blocks per workgroup, so that each activation
-    // fragment loaded from L2 feeds four blocks' MFMAs
-    p.CB = (M <= 4 || p.xlds) ? 1 : 4;
+    // column blocks per workgroup: two when X is staged in LDS (X staged once
+    // for twice the weights); one for a few tokens with a long K; four for
+    // more tokens, so that each activation fragment loaded from L2 feeds
+    // four blocks' MFMAs
+    p.CB = p.xlds ? 2 : (M <= 4 ? 1 : 4);
     p.n_main = (NB + p.CB - 1) / p.CB;
     p.stage_first = r > 0 ? 1 : 0;
     p.off_flags = OFF_DEC_FLAGS;

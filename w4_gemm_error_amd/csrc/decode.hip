@@ -46,6 +46,7 @@ constexpr int DEC_EC_MAXI = 5;     // column blocks per wavefront in the EC role
 constexpr int DEC_XLDS_CHUNKS = 8; // 16-byte chunks of staged activations per thread
 constexpr int DEC_EC_KSMAX = 256;  // k per EC slice (at most)
 
+
 struct DecodeKArgs {
     const uint16_t* X;
     const uint8_t* codes;
@@ -620,12 +621,11 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     }
 }
 
-// One column block per workgroup (activations staged in LDS): the grid
-// holds ~900 workgroups, which fit the CUs in one round only at four
-// wavefronts per SIMD, i.e. within 128 registers (the grouped-scale variant
-// needs the bound to get there).
+// Two column blocks per workgroup (activations staged in LDS): the grid
+// holds ~450 workgroups, which fit the CUs in one round at two wavefronts
+// per SIMD, i.e. within 256 registers.
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
-__global__ __launch_bounds__(DEC_THREADS, (CB == 1 && XCH > 0) ? 4 : 1)
+__global__ __launch_bounds__(DEC_THREADS, CB == 2 ? 2 : 1)
 void decode_kernel(DecodeKArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
@@ -677,10 +677,13 @@ template <int ACT, bool GROUPED, bool STAGE_FIRST>
 static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     if (p.xlds) {
+        // two column blocks: each workgroup stages X once for twice the
+        // weights.  With one block, a token at 4096 k staged 8 KB of X from
+        // L2 per 32 KB of weights, and the call measured 0.3-0.4 us slower.
         const size_t xch = ((size_t)k.M * k.K / 8 + DEC_THREADS - 1) / DEC_THREADS;
         if (xch <= 2)
-            return launch_decode_t<ACT, 1, 2, 8, GROUPED, STAGE_FIRST>(k, p, st);
-        return launch_decode_t<ACT, 1, DEC_XLDS_CHUNKS, 8, GROUPED, STAGE_FIRST>(k, p, st);
+            return launch_decode_t<ACT, 2, 2, 8, GROUPED, STAGE_FIRST>(k, p, st);
+        return launch_decode_t<ACT, 2, DEC_XLDS_CHUNKS, 8, GROUPED, STAGE_FIRST>(k, p, st);
     }
     if (p.CB == 1)
         return launch_decode_t<ACT, 1, 0, 4, GROUPED, false>(k, p, st);
