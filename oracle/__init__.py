@@ -8,8 +8,10 @@ leg of ``bench.py`` use it.  It shares no code with the HIP library
 The arithmetic lives in ``w4ec_oracle.c`` (plain C, float64, naive loops);
 this module builds it with gcc and marshals numpy arrays through ctypes.
 Method: SPEAR (gist.science technical summary), section 2.1A, effective
-weight W + B diag(gate) A with a per-token scalar gate sigmoid(x.w_g + b_g);
-the quantizer is the per-channel RTN baseline of its results section 3.1.
+weight W + B diag(gate) A with a per-token scalar gate sigmoid(x.w_g + b_g)
+(``forward``), or with one gate per rank component from a bottleneck MLP on
+T = X A (``forward_vgate``); the quantizer is the per-channel RTN baseline of
+its results section 3.1.
 """
 from __future__ import annotations
 
@@ -65,6 +67,9 @@ def _load():
         lib.w4o_forward.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P,
                                     ctypes.c_double, P, I, P, P, P, P, P]
         lib.w4o_forward.restype = I
+        lib.w4o_forward_vgate.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
+                                          P, I, P, P, P, P, P]
+        lib.w4o_forward_vgate.restype = I
         lib.w4o_max_threads.argtypes = []
         lib.w4o_max_threads.restype = I
         _lib = lib
@@ -178,3 +183,48 @@ def forward(X, qc, scale, zero, A, B, w_g, b_g, *, N, K, r, group_size,
         out.update(Y0=Y0, T=T, g=g, C=C)
     return out
 
+
+
+def forward_vgate(X, qc, scale, zero, A, B, G1, c1, G2, c2, *, N, K, r, h, group_size,
+                  act="fp16", rows=None, want_parts=True):
+    """The layer with a vector gate (one gate per rank component, from a
+    bottleneck MLP of width h on T = X A), in float64; see w4o_forward_vgate.
+
+    G1: act bits [r, h]; c1: act bits [h]; G2: act bits [h, r]; c2: act bits
+    [r].  Other arguments as forward().  Returns Y (and Y0, T, gamma, C when
+    want_parts) indexed by the evaluated rows.
+    """
+    lib = _load()
+    X = _c(X, np.uint16)
+    M = X.shape[0]
+    assert X.shape == (M, K) and r > 0 and h > 0
+    qc = _c(qc, np.uint8)
+    scale = _c(scale, np.uint16)
+    zero = _c(zero, np.uint16)
+    G = int(group_size)
+    assert qc.shape == (N, K // 2) and scale.shape == (N, K // G) and zero.shape == (N, K // G)
+    A, B = _c(A, np.uint16), _c(B, np.uint16)
+    G1, c1, G2, c2 = _c(G1, np.uint16), _c(c1, np.uint16), _c(G2, np.uint16), _c(c2, np.uint16)
+    assert A.shape == (K, r) and B.shape == (r, N)
+    assert G1.shape == (r, h) and c1.shape == (h,) and G2.shape == (h, r) and c2.shape == (r,)
+    rows_arr = None
+    n_rows = M
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+        n_rows = int(rows_arr.shape[0])
+    Y = np.empty((n_rows, N), np.float64)
+    Y0 = np.empty((n_rows, N), np.float64) if want_parts else None
+    C = np.empty((n_rows, N), np.float64) if want_parts else None
+    T = np.empty((n_rows, r), np.float64) if want_parts else None
+    gam = np.empty((n_rows, r), np.float64) if want_parts else None
+    act_bf16 = {"fp16": 0, "bf16": 1}[act]
+    rc = lib.w4o_forward_vgate(M, N, K, r, G, act_bf16, h, _ptr(X), _ptr(qc), _ptr(scale),
+                               _ptr(zero), _ptr(A), _ptr(B), _ptr(G1), _ptr(c1), _ptr(G2),
+                               _ptr(c2), _ptr(rows_arr), n_rows, _ptr(Y), _ptr(Y0), _ptr(T),
+                               _ptr(gam), _ptr(C))
+    if rc != 0:
+        raise RuntimeError("oracle forward_vgate failed (bad arguments)")
+    out = {"Y": Y}
+    if want_parts:
+        out.update(Y0=Y0, T=T, gamma=gam, C=C)
+    return out

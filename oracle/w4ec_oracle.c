@@ -299,6 +299,139 @@ int w4o_forward(int M, int N, int K, int r, int G, int act_bf16,
     return bad ? -1 : 0;
 }
 
+/* The layer with a vector gate: one gate per rank component, for a subset
+ * of tokens.  The SPEAR summary (section 2.1A) writes the compensated weight
+ * as W + alpha B diag(gamma(A x)) A, with gamma a small bottleneck MLP on the
+ * rank-r projection; it names neither the MLP's activation nor its width.
+ * Read here as a two-layer bottleneck of width h with a ReLU, and a sigmoid
+ * on its output so that each component is a gate in (0, 1) like the scalar
+ * gate; alpha is folded into B as in w4o_forward:
+ *
+ *   T[m,j]     = sum_k X[m,k] * A[k,j]
+ *   u[m,i]     = max(0, sum_j T[m,j] * G1[j,i] + c1[i])          i < h
+ *   gamma[m,j] = sigmoid(sum_i u[m,i] * G2[i,j] + c2[j])         j < r
+ *   C[m,n]     = sum_j gamma[m,j] * T[m,j] * B[j,n]
+ *   Y[m,n]     = Y0[m,n] + C[m,n]
+ *
+ *   G1 act bits [r][h], c1 act bits [h], G2 act bits [h][r], c2 act bits [r]
+ * Other arguments and outputs as w4o_forward, with gamma [n_rows][r] in
+ * place of g.  Returns 0, or -1 on bad arguments or allocation failure. */
+int w4o_forward_vgate(int M, int N, int K, int r, int G, int act_bf16, int h,
+                      const uint16_t* X, const uint8_t* qc,
+                      const uint16_t* scale, const uint16_t* zero,
+                      const uint16_t* A, const uint16_t* B,
+                      const uint16_t* G1, const uint16_t* c1,
+                      const uint16_t* G2, const uint16_t* c2,
+                      const int* rows, int n_rows,
+                      double* Y, double* Y0, double* T, double* gamma, double* C)
+{
+    if (M < 0 || N <= 0 || K <= 0 || r <= 0 || h <= 0 || G <= 0 || K % G || K % 2 || !Y)
+        return -1;
+    if (!A || !B || !G1 || !c1 || !G2 || !c2)
+        return -1;
+    if (!rows)
+        n_rows = M;
+    if (n_rows <= 0)
+        return 0;
+    int ngroups = K / G;
+
+    double* xd = (double*)malloc(sizeof(double) * (size_t)n_rows * K);
+    double* td = (double*)malloc(sizeof(double) * (size_t)n_rows * r);
+    double* gd = (double*)malloc(sizeof(double) * (size_t)n_rows * r);
+    double* ud = (double*)malloc(sizeof(double) * (size_t)n_rows * h);
+    if (!xd || !td || !gd || !ud) {
+        free(xd); free(td); free(gd); free(ud);
+        return -1;
+    }
+    for (int i = 0; i < n_rows; ++i) {
+        int m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) {
+            free(xd); free(td); free(gd); free(ud);
+            return -1;
+        }
+        for (int k = 0; k < K; ++k)
+            xd[(size_t)i * K + k] = act_to_double(X[(size_t)m * K + k], act_bf16);
+    }
+
+    /* T = X A, then the bottleneck and the gate of every rank component,
+     * one token at a time. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < n_rows; ++i) {
+        const double* x = xd + (size_t)i * K;
+        double* t = td + (size_t)i * r;
+        double* u = ud + (size_t)i * h;
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += x[k] * act_to_double(A[(size_t)k * r + j], act_bf16);
+            t[j] = acc;
+        }
+        for (int q = 0; q < h; ++q) {
+            double acc = 0.0;
+            for (int j = 0; j < r; ++j)
+                acc += t[j] * act_to_double(G1[(size_t)j * h + q], act_bf16);
+            acc += act_to_double(c1[q], act_bf16);
+            u[q] = acc > 0.0 ? acc : 0.0;
+        }
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int q = 0; q < h; ++q)
+                acc += u[q] * act_to_double(G2[(size_t)q * r + j], act_bf16);
+            acc += act_to_double(c2[j], act_bf16);
+            gd[(size_t)i * r + j] = sigmoid(acc);
+        }
+    }
+
+    /* One output feature at a time: dequantize row n of W, then every token. */
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+        double* bc = (double*)malloc(sizeof(double) * (size_t)r);
+        if (!wd || !bc) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int n = 0; n < N; ++n) {
+            if (!wd || !bc)
+                continue;
+            for (int k = 0; k < K; ++k) {
+                int gi = k / G;
+                double s = w4o_half_to_double(scale[(size_t)n * ngroups + gi]);
+                double z = w4o_half_to_double(zero[(size_t)n * ngroups + gi]);
+                wd[k] = ((double)code_at(qc, K, n, k) - z) * s;
+            }
+            for (int j = 0; j < r; ++j)
+                bc[j] = act_to_double(B[(size_t)j * N + n], act_bf16);
+            for (int i = 0; i < n_rows; ++i) {
+                const double* x = xd + (size_t)i * K;
+                double y0 = 0.0;
+                for (int k = 0; k < K; ++k)
+                    y0 += x[k] * wd[k];
+                double c = 0.0;
+                for (int j = 0; j < r; ++j)
+                    c += gd[(size_t)i * r + j] * td[(size_t)i * r + j] * bc[j];
+                size_t o = (size_t)i * N + n;
+                Y[o] = y0 + c;
+                if (Y0) Y0[o] = y0;
+                if (C) C[o] = c;
+            }
+        }
+        free(wd);
+        free(bc);
+    }
+    if (T)
+        memcpy(T, td, sizeof(double) * (size_t)n_rows * r);
+    if (gamma)
+        memcpy(gamma, gd, sizeof(double) * (size_t)n_rows * r);
+    free(xd);
+    free(td);
+    free(gd);
+    free(ud);
+    return bad ? -1 : 0;
+}
+
 /* Threads an OpenMP region of this library will use. */
 int w4o_max_threads(void)
 {

@@ -296,3 +296,100 @@ def test_synth_shapes_and_outliers():
     g = expit(synth.act_bits_to_f64(d3["X"], "fp16") @ synth.act_bits_to_f64(d3["w_g"], "fp16") + d3["b_g"])
     inside = np.mean((g > 0.05) & (g < 0.95))
     assert inside > 0.9
+
+
+# ---------------------------------------------------------------- vector gate
+
+def vg_run(M, N, K, r, G, h, X, qc, s, z, A, B, G1, c1, G2, c2, rows=None):
+    return oracle.forward_vgate(X, qc, s, z, A, B, G1, c1, G2, c2, N=N, K=K, r=r, h=h,
+                                group_size=G, rows=rows)
+
+
+def vg_layer(rng, M=9, N=40, K=256, r=8, G=128):
+    q, s, z, W = on_grid_layer(rng, N, K, G)
+    Xb = f16bits(rng.standard_normal((M, K)))
+    Ab = f16bits(rng.standard_normal((K, r)) * 0.05)
+    Bb = f16bits(rng.standard_normal((r, N)) * 0.05)
+    f = lambda b: b.view(np.float16).astype(np.float64)
+    return dict(M=M, N=N, K=K, r=r, G=G, qc=pack_canonical(q), s=s, z=z, W=W, Xb=Xb, Ab=Ab, Bb=Bb,
+                X=f(Xb), A=f(Ab), B=f(Bb))
+
+
+def test_vgate_closed_gate_is_plain_w4():
+    L = vg_layer(np.random.default_rng(21))
+    h = 4
+    p = synth.make_vgate(L["r"], h, seed=1)
+    c2 = f16bits(np.full(L["r"], -np.inf))
+    out = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"], L["qc"], L["s"], L["z"],
+                 L["Ab"], L["Bb"], p["G1"], p["c1"], p["G2"], c2)
+    base = run(L["M"], L["N"], L["K"], 0, L["G"], L["Xb"], L["qc"], L["s"], L["z"], None, None, None, 0.0)
+    assert (out["gamma"] == 0.0).all() and np.array_equal(out["Y"], base["Y"])
+
+
+def test_vgate_open_gate_is_static_low_rank_compensation():
+    L = vg_layer(np.random.default_rng(22))
+    h = 3
+    p = synth.make_vgate(L["r"], h, seed=2)
+    G2 = f16bits(np.zeros((h, L["r"])))
+    c2 = f16bits(np.full(L["r"], np.inf))
+    out = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"], L["qc"], L["s"], L["z"],
+                 L["Ab"], L["Bb"], p["G1"], p["c1"], G2, c2)
+    assert (out["gamma"] == 1.0).all()
+    ref = np.matmul(L["X"], L["W"].T + np.matmul(L["A"], L["B"]))
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
+
+
+def test_vgate_constant_gate_against_numpy():
+    """G1 = 0: the bottleneck sees only its bias, so every token gets the same
+    gate vector sigmoid(relu(c1) G2 + c2), and the layer is X (W + A diag(gamma) B)^T."""
+    L = vg_layer(np.random.default_rng(23), r=12)
+    h = 5
+    rng = np.random.default_rng(24)
+    G1 = f16bits(np.zeros((L["r"], h)))
+    c1b = f16bits(rng.normal(0.0, 1.0, h))          # both signs: the ReLU matters
+    G2b = f16bits(rng.normal(0.0, 1.0, (h, L["r"])))
+    c2b = f16bits(rng.normal(0.0, 1.0, L["r"]))
+    out = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"], L["qc"], L["s"], L["z"],
+                 L["Ab"], L["Bb"], G1, c1b, G2b, c2b)
+    f = lambda b: b.view(np.float16).astype(np.float64)
+    gam = expit(np.matmul(np.maximum(f(c1b), 0.0), f(G2b)) + f(c2b))
+    np.testing.assert_allclose(out["gamma"], np.broadcast_to(gam, out["gamma"].shape), rtol=1e-13, atol=1e-15)
+    ref = np.matmul(L["X"], L["W"].T + np.matmul(L["A"] * gam[None, :], L["B"]))
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
+
+
+def test_vgate_permutation_bottleneck():
+    """h = r, G1 a permutation (u_i = relu(T_pi(i))), G2 = beta times the
+    inverse permutation: each component's gate is sigmoid(beta relu(T_j) + c2_j).
+    A transposed G1 or G2, or a misplaced ReLU, breaks the identity."""
+    L = vg_layer(np.random.default_rng(25), r=6)
+    r = h = L["r"]
+    pi = np.array([1, 2, 3, 4, 5, 0])              # one 6-cycle: no power below 6 is the identity
+    beta = 1.5
+    G1 = np.zeros((r, h)); G1[pi, np.arange(h)] = 1.0
+    G2 = np.zeros((h, r)); G2[np.arange(h), pi] = beta
+    c2b = f16bits(np.linspace(-1.0, 1.0, r))
+    out = vg_run(L["M"], L["N"], L["K"], r, L["G"], h, L["Xb"], L["qc"], L["s"], L["z"],
+                 L["Ab"], L["Bb"], f16bits(G1), f16bits(np.zeros(h)), f16bits(G2), c2b)
+    T = np.matmul(L["X"], L["A"])
+    assert (T < 0).any() and (T > 0).any()
+    gam = expit(beta * np.maximum(T, 0.0) + c2b.view(np.float16).astype(np.float64)[None, :])
+    np.testing.assert_allclose(out["T"], T, rtol=1e-12, atol=1e-12 * np.abs(T).max())
+    np.testing.assert_allclose(out["gamma"], gam, rtol=1e-12, atol=1e-15)
+    C = np.matmul(T * gam, L["B"])
+    np.testing.assert_allclose(out["C"], C, rtol=1e-11, atol=1e-11 * np.abs(C).max())
+    np.testing.assert_allclose(out["Y"], out["Y0"] + C, rtol=1e-11, atol=1e-11 * np.abs(C).max())
+
+
+def test_vgate_rows_and_token_permutation():
+    L = vg_layer(np.random.default_rng(26))
+    h = 4
+    p = synth.make_vgate(L["r"], h, seed=3)
+    args = (L["qc"], L["s"], L["z"], L["Ab"], L["Bb"], p["G1"], p["c1"], p["G2"], p["c2"])
+    full = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"], *args)
+    pm = np.random.default_rng(27).permutation(L["M"])
+    tp = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"][pm], *args)
+    assert np.array_equal(tp["Y"], full["Y"][pm])
+    rows = [3, 0, 8, 3]
+    sub = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"], *args, rows=rows)
+    assert np.array_equal(sub["Y"], full["Y"][rows])

@@ -112,3 +112,17 @@ def make_layer(cfg, M: int, seed: int = 0, *, K=None, N=None, r=None,
         raise ValueError(c.gate)
     return dict(X=Xb, W=W, A=A, B=B, w_g=w_g, b_g=b_g, M=M, K=K, N=N, r=r,
                 group_size=G, act=c.act, outlier_channels=out_ch, name=c.name)
+
+
+def make_vgate(r: int, h: int, act: str = "fp16", seed: int = 0, t_std: float = 1.0) -> dict:
+    """Seeded parameters of a vector gate (a bottleneck of width h on the
+    rank-r projection T): G1 [r, h], c1 [h], G2 [h, r], c2 [r] as act bits.
+    Scaled so that, for rows of T with standard deviation about t_std, the
+    gates spread over (0, 1) rather than saturating."""
+    rng = np.random.default_rng(1_000_003 + seed)
+    G1 = rng.normal(0.0, 1.0 / (t_std * np.sqrt(r)), (r, h))
+    c1 = rng.normal(0.0, 0.5, (h,))
+    G2 = rng.normal(0.0, 2.0 / np.sqrt(h), (h, r))
+    c2 = rng.normal(0.0, 1.0, (r,))
+    return {"G1": to_act_bits(G1, act), "c1": to_act_bits(c1, act),
+            "G2": to_act_bits(G2, act), "c2": to_act_bits(c2, act), "h": h}
