@@ -138,6 +138,35 @@ int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const 
                         int M, int N, int K, int r, int group_size, int act_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer with a vector gate: one gate per rank component instead of one
+ * per token.  The SPEAR summary (section 2.1A) writes the compensated weight
+ * as W + alpha B diag(gamma(A x)) A, with gamma a small bottleneck MLP on
+ * the rank-r projection; it names neither the MLP's activation nor its
+ * width.  This library reads gamma as a two-layer bottleneck of width h with
+ * a ReLU and a sigmoid output (alpha folded into B, as above):
+ *
+ *   T[m,j]     = sum_k X[m,k] A[k,j]
+ *   u[m,i]     = max(0, sum_j T[m,j] G1[j,i] + c1[i])          0 <= i < h
+ *   gamma[m,j] = 1 / (1 + exp(-(sum_i u[m,i] G2[i,j] + c2[j])))
+ *   Y[m,n]     = sum_k X[m,k] Wd[n,k] + sum_j gamma[m,j] T[m,j] B[j,n]
+ *
+ *   G1  device act [r, h]     c1  device act [h]
+ *   G2  device act [h, r]     c2  device act [r]     (2-byte aligned)
+ *   h   bottleneck width, 1 <= h <= 64 (W4EC_ERR_UNSUPPORTED above)
+ * The bottleneck runs in fp32 on the fp32 sums of T; T_g = gamma * T is
+ * rounded to the activation type, as in the scalar form.  Other arguments,
+ * limits, workspace and error behaviour as w4ec_linear_decode /
+ * w4ec_linear_prefill; with r == 0 the gate arguments are ignored. */
+int w4ec_linear_decode_vgate(const void* X, const void* packed, const void* A, const void* B,
+                             const void* G1, const void* c1, const void* G2, const void* c2,
+                             int h, void* Y, int M, int N, int K, int r, int group_size,
+                             int act_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+int w4ec_linear_prefill_vgate(const void* X, const void* packed, const void* A, const void* B,
+                              const void* G1, const void* c1, const void* G2, const void* c2,
+                              int h, void* Y, int M, int N, int K, int r, int group_size,
+                              int act_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

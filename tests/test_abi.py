@@ -15,6 +15,7 @@ import w4_gemm_error_amd as w4
 def test_library_exports_every_header_symbol():
     declared = w4.header_symbols()
     assert set(declared) >= {"w4ec_pack", "w4ec_linear_decode", "w4ec_linear_prefill",
+                             "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
                              "w4ec_quantize_rtn", "w4ec_unpack", "w4ec_packed_bytes",
                              "w4ec_workspace_bytes", "w4ec_status_str"}
     assert w4.exported_symbols() == declared
@@ -111,3 +112,31 @@ def test_state_region_constant_matches_header():
     m = re.search(r"#define W4EC_WS_STATE_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m, "W4EC_WS_STATE_BYTES not found in the header"
     assert int(m.group(1)) << int(m.group(2)) == w4.W4EC_WS_STATE_BYTES
+
+
+def call_vg(name, X=FAKE, packed=FAKE + 0x100000, A=FAKE + 0x200000, B=FAKE + 0x300000,
+            G1=FAKE + 0x400000, c1=FAKE + 0x410000, G2=FAKE + 0x420000, c2=FAKE + 0x430000, h=8,
+            Y=FAKE + 0x500000, M=4, N=512, K=512, r=8, G=512, act=0, ws=FAKE + 0x600000, ws_bytes=1 << 30):
+    fn = getattr(w4.lib(), name)
+    P = lambda v: ctypes.c_void_p(v) if v else None
+    return fn(P(X), P(packed), P(A), P(B), P(G1), P(c1), P(G2), P(c2), h, P(Y),
+              M, N, K, r, G, act, P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("name", ["w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"])
+def test_vgate_argument_errors(name):
+    E = w4
+    assert call_vg(name, h=0) == E.W4EC_ERR_INVALID_ARG
+    assert call_vg(name, h=65) == E.W4EC_ERR_UNSUPPORTED
+    for arg in ("G1", "c1", "G2", "c2"):
+        assert call_vg(name, **{arg: 0}) == E.W4EC_ERR_INVALID_ARG
+    assert call_vg(name, G2=FAKE + 0x420001) == E.W4EC_ERR_INVALID_ARG   # not 2-byte aligned
+    assert call_vg(name, M=0) == E.W4EC_ERR_INVALID_ARG
+    assert call_vg(name, r=257) == E.W4EC_ERR_UNSUPPORTED
+    assert call_vg(name, A=0) == E.W4EC_ERR_INVALID_ARG
+    assert call_vg(name, ws=0) == E.W4EC_ERR_WORKSPACE
+    assert call_vg(name, act=5) == E.W4EC_ERR_INVALID_ARG
+
+
+def test_vgate_decode_rejects_more_than_16_tokens():
+    assert call_vg("w4ec_linear_decode_vgate", M=17) == w4.W4EC_ERR_UNSUPPORTED

@@ -22,6 +22,7 @@ __all__ = [
     "w4ec_status_str", "w4ec_packed_bytes", "w4ec_workspace_bytes",
     "w4ec_quantize_rtn", "w4ec_pack", "w4ec_unpack",
     "w4ec_linear_decode", "w4ec_linear_prefill", "w4ec_linear",
+    "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
     "PackedLayer",
 ]
 
@@ -74,6 +75,10 @@ def lib() -> ctypes.CDLL:
         for name in ("w4ec_linear_decode", "w4ec_linear_prefill"):
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, P, Z, P]
+            fn.restype = I
+        for name in ("w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"):
+            fn = getattr(L, name)
+            fn.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P, Z, P]
             fn.restype = I
         _lib = L
         return L
@@ -212,6 +217,45 @@ def _layer_call(name, X, packed, A, B, w_g, b_g, N, group_size, workspace, Y, st
             _stream_handle(stream))
     _check(st, name)
     return Y
+
+
+def _layer_call_vgate(name, X, packed, A, B, G1, c1, G2, c2, N, group_size, workspace, Y, stream):
+    torch = _torch()
+    acts = (torch.float16, torch.bfloat16)
+    _need_cuda(X, "X", acts)
+    act = X.dtype
+    M, K = X.shape
+    r = 0 if A is None else int(A.shape[1])
+    for t, nm in ((A, "A"), (B, "B"), (G1, "G1"), (c1, "c1"), (G2, "G2"), (c2, "c2")):
+        _need_cuda(t, nm, act)
+    h = 0 if G1 is None else int(G1.shape[1])
+    _need_cuda(packed, "packed", torch.uint8)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=act, device=X.device)
+    _need_cuda(Y, "Y", act)
+    if workspace is None:
+        nb = w4ec_workspace_bytes(M, N, K, r, group_size)
+        workspace = torch.zeros(max(nb, 256), dtype=torch.uint8, device=X.device)
+    fn = getattr(lib(), name)
+    st = fn(_ptr(X), _ptr(packed), _ptr(A), _ptr(B), _ptr(G1), _ptr(c1), _ptr(G2), _ptr(c2), h,
+            _ptr(Y), M, N, K, r, int(group_size), _act_code(act), _ptr(workspace), workspace.numel(),
+            _stream_handle(stream))
+    _check(st, name)
+    return Y
+
+
+def w4ec_linear_decode_vgate(X, packed, A, B, G1, c1, G2, c2, *, N, group_size, workspace=None, Y=None,
+                             stream=None):
+    """Y = X Wd^T + (gamma * (X A)) B, gamma = sigmoid(relu((X A) G1 + c1) G2 + c2), 1 <= M <= 16."""
+    return _layer_call_vgate("w4ec_linear_decode_vgate", X, packed, A, B, G1, c1, G2, c2, N, group_size,
+                             workspace, Y, stream)
+
+
+def w4ec_linear_prefill_vgate(X, packed, A, B, G1, c1, G2, c2, *, N, group_size, workspace=None, Y=None,
+                              stream=None):
+    """The vector-gate layer for any M >= 1 (prepass, per-token bottleneck, tiled MFMA GEMM)."""
+    return _layer_call_vgate("w4ec_linear_prefill_vgate", X, packed, A, B, G1, c1, G2, c2, N, group_size,
+                             workspace, Y, stream)
 
 
 def w4ec_linear_decode(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):

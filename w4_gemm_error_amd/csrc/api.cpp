@@ -266,10 +266,54 @@ size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size)
     return b;
 }
 
-int w4ec_linear_decode(const void* X, const void* packed, const void* A, const void* B,
-                       const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
-                       int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
-                       void* stream)
+}  // extern "C"
+
+namespace {
+
+constexpr int VGATE_MAX_H = 64;   // widest bottleneck of the vector gate
+
+struct VGate {
+    const void* G1;
+    const void* c1;
+    const void* G2;
+    const void* c2;
+    int h;
+};
+
+// Vector-gate parameters, checked only when there is a compensator (r > 0).
+int check_vgate(const VGate* v, int r)
+{
+    if (!v || r == 0)
+        return W4EC_OK;
+    if (v->h < 1)
+        return W4EC_ERR_INVALID_ARG;
+    if (v->h > VGATE_MAX_H)
+        return W4EC_ERR_UNSUPPORTED;
+    if (!v->G1 || !v->c1 || !v->G2 || !v->c2)
+        return W4EC_ERR_INVALID_ARG;
+    if (!aligned(v->G1, 2) || !aligned(v->c1, 2) || !aligned(v->G2, 2) || !aligned(v->c2, 2))
+        return W4EC_ERR_INVALID_ARG;
+    return W4EC_OK;
+}
+
+LayerArgs layer_args(const void* X, const void* packed, const void* A, const void* B,
+                     const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                     int group_size, int act_dtype, void* workspace, const VGate* vg)
+{
+    LayerArgs a{X, packed, r > 0 ? A : nullptr, r > 0 ? B : nullptr, r > 0 ? w_g : nullptr,
+                b_g, Y, M, N, K, r, group_size, act_dtype, (char*)workspace};
+    if (vg && r > 0) {
+        a.w_g = nullptr;                 // the vector gate replaces the scalar one
+        a.G1 = vg->G1; a.c1 = vg->c1; a.G2 = vg->G2; a.c2 = vg->c2;
+        a.h = vg->h;
+    }
+    return a;
+}
+
+int decode_entry(const void* X, const void* packed, const void* A, const void* B,
+                 const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                 int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
+                 void* stream, const VGate* vg)
 {
     if (M > DECODE_MAX_M)
         return W4EC_ERR_UNSUPPORTED;
@@ -281,21 +325,24 @@ int w4ec_linear_decode(const void* X, const void* packed, const void* A, const v
             return W4EC_ERR_UNSUPPORTED;
         need = r > 0 ? p.bytes : 0;
     }
-    int rc = check_layer_args(X, packed, A, B, w_g, Y, M, N, K, r, group_size, act_dtype,
-                              workspace, workspace_bytes, need);
+    int rc = check_layer_args(X, packed, A, B, vg ? nullptr : w_g, Y, M, N, K, r, group_size,
+                              act_dtype, workspace, workspace_bytes, need);
     if (rc != W4EC_OK)
         return rc;
-    if (w_g && !((uintptr_t)w_g % 2 == 0))
+    rc = check_vgate(vg, r);
+    if (rc != W4EC_OK)
+        return rc;
+    if (!vg && w_g && !((uintptr_t)w_g % 2 == 0))
         return W4EC_ERR_INVALID_ARG;
-    LayerArgs a{X, packed, r > 0 ? A : nullptr, r > 0 ? B : nullptr, r > 0 ? w_g : nullptr,
-                b_g, Y, M, N, K, r, group_size, act_dtype, (char*)workspace};
+    LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
+                             workspace, vg);
     return hip_status(launch_decode(a, p, (hipStream_t)stream));
 }
 
-int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const void* B,
-                        const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
-                        int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
-                        void* stream)
+int prefill_entry(const void* X, const void* packed, const void* A, const void* B,
+                  const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                  int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
+                  void* stream, const VGate* vg)
 {
     PrefillPlan p{};
     size_t need = 0;
@@ -304,15 +351,60 @@ int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const 
         const bool sums = act_dtype == W4EC_BF16 && group_size == K;   // bf16 zero-point term
         need = (r > 0 || p.ksplit > 1 || sums) ? p.bytes : 0;
     }
-    int rc = check_layer_args(X, packed, A, B, w_g, Y, M, N, K, r, group_size, act_dtype,
-                              workspace, workspace_bytes, need);
+    int rc = check_layer_args(X, packed, A, B, vg ? nullptr : w_g, Y, M, N, K, r, group_size,
+                              act_dtype, workspace, workspace_bytes, need);
     if (rc != W4EC_OK)
         return rc;
-    if (w_g && !((uintptr_t)w_g % 2 == 0))
+    rc = check_vgate(vg, r);
+    if (rc != W4EC_OK)
+        return rc;
+    if (!vg && w_g && !((uintptr_t)w_g % 2 == 0))
         return W4EC_ERR_INVALID_ARG;
-    LayerArgs a{X, packed, r > 0 ? A : nullptr, r > 0 ? B : nullptr, r > 0 ? w_g : nullptr,
-                b_g, Y, M, N, K, r, group_size, act_dtype, (char*)workspace};
+    LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
+                             workspace, vg);
     return hip_status(launch_prefill(a, p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4ec_linear_decode(const void* X, const void* packed, const void* A, const void* B,
+                       const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                       int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream)
+{
+    return decode_entry(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const void* B,
+                        const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                        int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    return prefill_entry(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
+                         workspace, workspace_bytes, stream, nullptr);
+}
+
+int w4ec_linear_decode_vgate(const void* X, const void* packed, const void* A, const void* B,
+                             const void* G1, const void* c1, const void* G2, const void* c2,
+                             int h, void* Y, int M, int N, int K, int r, int group_size,
+                             int act_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const VGate vg{G1, c1, G2, c2, h};
+    return decode_entry(X, packed, A, B, nullptr, 0.0f, Y, M, N, K, r, group_size, act_dtype,
+                        workspace, workspace_bytes, stream, &vg);
+}
+
+int w4ec_linear_prefill_vgate(const void* X, const void* packed, const void* A, const void* B,
+                              const void* G1, const void* c1, const void* G2, const void* c2,
+                              int h, void* Y, int M, int N, int K, int r, int group_size,
+                              int act_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    const VGate vg{G1, c1, G2, c2, h};
+    return prefill_entry(X, packed, A, B, nullptr, 0.0f, Y, M, N, K, r, group_size, act_dtype,
+                         workspace, workspace_bytes, stream, &vg);
 }
 
 }  // extern "C"

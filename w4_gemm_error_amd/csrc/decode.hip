@@ -63,6 +63,12 @@ struct DecodeKArgs {
     uint32_t* partial;   // [P][M][RC] hand-over words
     uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [1] readers done
     uint8_t* rep_data;   // DEC_NREP slots of DEC_REP_DATA_STRIDE bytes: T_g [M][r_pad] as hand-over words
+    // vector gate (h > 0): gamma = sigmoid(relu(T G1 + c1) G2 + c2) per rank component
+    const uint16_t* G1;  // act [r][h]
+    const uint16_t* c1;  // act [h]
+    const uint16_t* G2;  // act [h][r]
+    const uint16_t* c2;  // act [r]
+    int h;
 };
 
 __device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
@@ -96,6 +102,114 @@ __device__ inline void dec_ec_mfma(const u32x4 (&xf)[DEC_EC_KSMAX / 32], const u
 #pragma unroll
         for (int s = 0; s < NS; ++s)
             acc[i] = mfma16x16x32<ACT>(xf[s], bf[s], acc[i]);
+    }
+}
+
+// Vector gate (SPEAR summary section 2.1A: W + B diag(gamma(A x)) A, gamma
+// a bottleneck MLP, read as gamma = sigmoid(relu(T G1 + c1) G2 + c2)).  The
+// gate of a rank component depends on the token's whole row of T, so the
+// reducers split tokens rather than words: reducer j of nred takes token
+// j mod M (with more reducers than tokens, the reducers of one token each
+// publish a share of its words) or tokens j, j + nred, ... (with fewer).
+// Every reducer of a token adds the P slices of the row in slice order and
+// runs the bottleneck in fp32, so all of them compute the same gates.
+template <int ACT>
+__device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, int nred)
+{
+    const int tid = threadIdx.x;
+    const int M = a.M, r = a.r, h = a.h;
+    const int w8 = a.r_pad / 4;                             // 8-byte words of a token's T_g
+    const int qs = M * a.RC;                                // words per slice
+    float* tT = reinterpret_cast<float*>(smem);             // [r_pad]
+    float* tU = tT + a.r_pad;                               // [h]
+    uint64_t* tw = reinterpret_cast<uint64_t*>(tU + ((h + 1) & ~1));   // [w8], 8-byte aligned
+    const int nrep = min(DEC_NREP, a.n_main);               // slots that have readers
+    int m0 = j, mstep = nred, wb = 0, we = w8;
+    if (nred >= M) {
+        m0 = j % M;
+        mstep = M;
+        const int cnt = (nred - 1 - m0) / M + 1, sub = j / M;
+        const int sh = (w8 + cnt - 1) / cnt;
+        wb = min(w8, sub * sh);
+        we = min(w8, wb + sh);
+        // Nothing to publish: read nothing either.  (A slot's last reader
+        // clears the partial sums once the slot is complete, and it is
+        // complete only when every reducer that reads them has written.)
+        if (wb >= we)
+            return;
+    }
+    uint32_t it = 0;                                        // bounded wait, shared by all waits
+    for (int m = m0; m < M; m += mstep) {
+        __syncthreads();                                    // LDS of the previous token is free
+        for (int c = tid; c < a.r_pad; c += DEC_THREADS) {
+            float t = 0.0f;
+            if (c < r) {
+                const uint32_t* src = a.partial + (size_t)m * a.RC + c;
+                for (int q = 0; q < a.P; q += 8) {
+                    // eight slices in flight; those not landed yet are loaded again together
+                    uint32_t v[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        v[i] = q + i < a.P ? atomic_load_dev(src + (size_t)(q + i) * qs) : 1u;
+                    for (;;) {
+                        bool miss = false;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            miss |= v[i] == 0u;
+                        if (!miss)
+                            break;
+                        __builtin_amdgcn_s_sleep(1);
+                        if (++it >= SPIN_LIMIT) {
+                            atomic_store_dev(&a.flags[2], 1u);
+                            break;
+                        }
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (v[i] == 0u)
+                                v[i] = atomic_load_dev(src + (size_t)(q + i) * qs);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (q + i < a.P)
+                            t += hw_dec32(v[i]);
+                }
+            }
+            tT[c] = t;
+        }
+        __syncthreads();
+        for (int i = tid; i < h; i += DEC_THREADS) {
+            float u = 0.0f;
+            for (int c = 0; c < r; ++c)
+                u += tT[c] * act_to_f32<ACT>(a.G1[(size_t)c * h + i]);
+            u += act_to_f32<ACT>(a.c1[i]);
+            tU[i] = fmaxf(u, 0.0f);
+        }
+        __syncthreads();
+        for (int i = tid; i < we - wb; i += DEC_THREADS) {
+            const int c0 = 4 * (wb + i);
+            uint64_t word = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int c = c0 + k;
+                float val = 0.0f;
+                if (c < r) {
+                    float zz = 0.0f;
+                    for (int q = 0; q < h; ++q)
+                        zz += tU[q] * act_to_f32<ACT>(a.G2[(size_t)q * r + c]);
+                    zz += act_to_f32<ACT>(a.c2[c]);
+                    val = sigmoid_f32(zz) * tT[c];
+                }
+                word |= (uint64_t)hw_enc16(f32_to_act<ACT>(val)) << (16 * k);
+            }
+            tw[i] = word;
+        }
+        __syncthreads();
+        const int nw = we - wb;
+        for (int i = tid; i < nw * nrep; i += DEC_THREADS) {
+            const int slot = i / nw, jj = i - slot * nw;
+            st8_dev(reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * DEC_REP_DATA_STRIDE) + (size_t)m * w8 + wb + jj,
+                    tw[jj]);
+        }
     }
 }
 
@@ -165,6 +279,11 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     const int red0 = max(0, a.P - DEC_EC_RMAX);
     if (p < red0)
         return;
+    if (a.h > 0) {
+        __syncthreads();                                    // the slice in LDS is no longer read
+        decode_vgate_reduce<ACT>(a, smem, p - red0, a.P - red0);
+        return;
+    }
     const int n8 = M * a.r_pad / 4;
     const int share = (n8 + (a.P - red0) - 1) / (a.P - red0);
     const int w0 = (p - red0) * share, w1 = min(n8, w0 + share);
@@ -656,7 +775,9 @@ static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
     const int nred = std::min(p.P, DEC_EC_RMAX);
     const int share = (M * p.r_pad / 4 + nred - 1) / nred;
     const size_t fin = ((size_t)DEC_THREADS + 4 * share + M + 2) * 4 + (size_t)share * 8;
-    return (std::max(at, fin) + 15) / 16 * 16;
+    // vector gate: [r_pad] T, [h] bottleneck (padded to even), [r_pad / 4] words
+    const size_t vg = ((size_t)p.r_pad + 64 + 2) * 4 + (size_t)p.r_pad / 4 * 8;
+    return (std::max(at, std::max(fin, vg)) + 15) / 16 * 16;
 }
 
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
@@ -721,6 +842,9 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.partial = (uint32_t*)(a.ws + p.off_partial);
     k.rep_ctrl = (uint8_t*)(a.ws + p.off_rep_ctrl);
     k.rep_data = (uint8_t*)(a.ws + p.off_rep_data);
+    k.G1 = (const uint16_t*)a.G1; k.c1 = (const uint16_t*)a.c1;
+    k.G2 = (const uint16_t*)a.G2; k.c2 = (const uint16_t*)a.c2;
+    k.h = a.r > 0 ? a.h : 0;
     if (a.act == ACT_F16)
         return launch_decode_act<ACT_F16>(k, p, st);
     return launch_decode_act<ACT_BF16>(k, p, st);

@@ -146,6 +146,11 @@ struct EcReduceKArgs {
     float* rowsum;      // [Mpad] sums of each token's activations, or null
     float b_g;
     int r, r_pad, ks;
+    const uint16_t* G1; // vector gate: act [r][h], [h], [h][r], [r]
+    const uint16_t* c1;
+    const uint16_t* G2;
+    const uint16_t* c2;
+    int h;
 };
 
 // One workgroup per (16 tokens, column block of T): adds the K slices'
@@ -219,6 +224,81 @@ void ec_reduce_kernel(EcReduceKArgs a)
             if (c >= 16 * (cb + 1))
                 a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = 0;
         }
+    }
+}
+
+// Vector gate (one gate per rank component; SPEAR summary section 2.1A,
+// W + B diag(gamma(A x)) A with gamma a bottleneck MLP, read as
+// gamma = sigmoid(relu(T G1 + c1) G2 + c2)).  One workgroup per 16 tokens:
+// it adds every column block of T over the K slices in slice order, runs
+// the bottleneck for each token in fp32 and stores T_g = gamma * T.
+constexpr int VG_HMAX = 64;     // largest bottleneck width
+constexpr int VG_RMAX = 256;    // largest rank
+
+template <int ACT>
+__global__ __launch_bounds__(PF_THREADS)
+void ec_reduce_vgate_kernel(EcReduceKArgs a)
+{
+    __shared__ float tT[16][VG_RMAX + 1];            // T of the 16 tokens (columns < r)
+    __shared__ float tU[16][VG_HMAX];                // bottleneck activations
+    const int tid = threadIdx.x;
+    const int rb = blockIdx.x;                       // rows 16 rb .. 16 rb + 15
+    const int mt = rb >> 2, w = rb & 3;
+    const int nb = ec_blocks(a.r), nba = ec_a_blocks(a.r);
+    const int ne = nb * 64;                          // fragments per slice of this row block
+    const floatx4* base = a.partial + ((size_t)mt * a.ks * 4 + w) * ne;
+    const size_t zs = (size_t)4 * ne;
+    // fragment e = (column block e / 64, lane e % 64): lane l holds column
+    // l % 16 of the block for rows 4 (l / 16) + v
+    for (int e = tid; e < ne; e += PF_THREADS) {
+        const int cb = e >> 6, l = e & 63;
+        const int col = l & 15;
+        if (cb >= nba && !(a.rowsum && col == 1))
+            continue;                                // the gate logit column is not used here
+        const floatx4* src = base + e;
+        floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
+        for (int z0 = 0; z0 < a.ks; z0 += 8) {
+            floatx4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = z0 + i < a.ks ? src[(size_t)(z0 + i) * zs] : (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                t += v[i];
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = 4 * (l >> 4) + v;
+            if (cb < nba) {
+                if (16 * cb + col < a.r)
+                    tT[row][16 * cb + col] = t[v];
+            } else {
+                a.rowsum[16 * rb + row] = t[v];      // the column of ones: each token's activation sum
+            }
+        }
+    }
+    __syncthreads();
+    const int r = a.r, h = a.h;
+    for (int e = tid; e < 16 * h; e += PF_THREADS) {
+        const int row = e / h, i = e - row * h;
+        float u = 0.0f;
+        for (int c = 0; c < r; ++c)
+            u += tT[row][c] * act_to_f32<ACT>(a.G1[(size_t)c * h + i]);
+        u += act_to_f32<ACT>(a.c1[i]);
+        tU[row][i] = fmaxf(u, 0.0f);
+    }
+    __syncthreads();
+    for (int e = tid; e < 16 * a.r_pad; e += PF_THREADS) {
+        const int row = e / a.r_pad, c = e - row * a.r_pad;
+        float val = 0.0f;
+        if (c < r) {
+            float zz = 0.0f;
+            for (int i = 0; i < h; ++i)
+                zz += tU[row][i] * act_to_f32<ACT>(a.G2[(size_t)i * r + c]);
+            zz += act_to_f32<ACT>(a.c2[c]);
+            val = sigmoid_f32(zz) * tT[row][c];
+        }
+        a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = f32_to_act<ACT>(val);
     }
 }
 
@@ -753,8 +833,16 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
         rq.rowsum = sums ? rowsum : nullptr;
         rq.b_g = a.b_g;
         rq.r = a.r; rq.r_pad = p.r_pad; rq.ks = p.pre_ks;
-        auto rk = a.act == ACT_F16 ? ec_reduce_kernel<ACT_F16> : ec_reduce_kernel<ACT_BF16>;
-        hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4, a.r > 0 ? ec_a_blocks(a.r) : 1), dim3(PF_THREADS), 0, st, rq);
+        rq.G1 = (const uint16_t*)a.G1; rq.c1 = (const uint16_t*)a.c1;
+        rq.G2 = (const uint16_t*)a.G2; rq.c2 = (const uint16_t*)a.c2;
+        rq.h = a.h;
+        if (a.r > 0 && a.h > 0) {
+            auto vk = a.act == ACT_F16 ? ec_reduce_vgate_kernel<ACT_F16> : ec_reduce_vgate_kernel<ACT_BF16>;
+            hipLaunchKernelGGL(vk, dim3(p.pre_mt * 4), dim3(PF_THREADS), 0, st, rq);
+        } else {
+            auto rk = a.act == ACT_F16 ? ec_reduce_kernel<ACT_F16> : ec_reduce_kernel<ACT_BF16>;
+            hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4, a.r > 0 ? ec_a_blocks(a.r) : 1), dim3(PF_THREADS), 0, st, rq);
+        }
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;

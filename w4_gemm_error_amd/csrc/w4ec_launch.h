@@ -26,6 +26,13 @@ struct LayerArgs {
     void* Y;
     int M, N, K, r, G, act;
     char* ws;
+    // vector gate (h > 0): one gate per rank component, from a bottleneck of
+    // width h on T = X A; w_g and b_g are then unused
+    const void* G1;   // act [r][h]
+    const void* c1;   // act [h]
+    const void* G2;   // act [h][r]
+    const void* c2;   // act [r]
+    int h;
 };
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
