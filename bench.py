@@ -48,18 +48,24 @@ WORKLOADS = {
 DEFAULT_WORKLOAD = "decode_up_proj_8b_m1"
 
 
-def layer_bytes(M, N, K, r, G, has_gate=True):
+def layer_bytes(M, N, K, r, G, has_gate=True, h=0):
     """Algorithmic HBM bytes of one call: packed codes, scale/zero, X, Y, A,
-    B and w_g, each moved once (the dequantized weights are never stored)."""
+    B and the gate parameters (w_g, or with a vector gate of width h its
+    G1, c1, G2, c2), each moved once (the dequantized weights are never
+    stored)."""
     codes = N * K // 2
     sz = N * (K // G) * 4
     act = 2
-    return codes + sz + M * K * act + M * N * act + (K * r + r * N) * act + (K * act if has_gate else 0)
+    gate = (2 * r * h + h + r) * act if h else (K * act if has_gate else 0)
+    return codes + sz + M * K * act + M * N * act + (K * r + r * N) * act + gate
 
 
-def layer_flops(M, N, K, r):
-    """2MNK main product + 2MK(r+1) gate and X A + 2MrN rank-r product + 2MN gating/add."""
-    return 2 * M * N * K + 2 * M * K * (r + 1) + 2 * M * r * N + 2 * M * N
+def layer_flops(M, N, K, r, h=0):
+    """2MNK main product + 2MK(r+1) gate and X A (with a vector gate of width
+    h: 2MKr for X A and 4Mrh for its bottleneck) + 2MrN rank-r product + 2MN
+    gating/add."""
+    gate = 2 * M * K * r + 4 * M * r * h if h else 2 * M * K * (r + 1)
+    return 2 * M * N * K + gate + 2 * M * r * N + 2 * M * N
 
 
 # the sources each measured kernel is built from (its counters stay valid
@@ -146,6 +152,10 @@ def main():
                          "(the reference point for the HBM byte counters)")
     ap.add_argument("--rank", type=int, default=None,
                     help="EC rank override (0 = the plain W4 layer, for the EC overhead ratio)")
+    ap.add_argument("--gate", choices=["scalar", "vector"], default="scalar",
+                    help="scalar: one gate per token, sigmoid(x.w_g + b_g); vector: one gate per "
+                         "rank component from a bottleneck MLP on X A")
+    ap.add_argument("--gate-width", type=int, default=16, help="bottleneck width h of the vector gate")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -183,16 +193,25 @@ def main():
     q, s, z = w4.w4ec_quantize_rtn(Wt, G)
     packed0 = w4.w4ec_pack(q, s, z, N, K, G)
     del Wt, q, s, z
-    if r > 0:
+    vector = args.gate == "vector" and r > 0
+    h = args.gate_width if vector else 0
+    if r > 0 and vector:
+        vg = synth.make_vgate(r, h, act, seed=args.seed, t_std=0.02 * K ** 0.5)
+        A0, B0 = dev_act(d["A"]), dev_act(d["B"])
+        wg0 = tuple(dev_act(vg[k]) for k in ("G1", "c1", "G2", "c2"))
+        ec_elems = A0.numel() + B0.numel() + sum(t.numel() for t in wg0)
+    elif r > 0:
         A0, B0, wg0 = dev_act(d["A"]), dev_act(d["B"]), dev_act(d["w_g"])
         ec_elems = A0.numel() + B0.numel() + wg0.numel()
     else:
         A0 = B0 = wg0 = None
         ec_elems = 0
-    nbytes = layer_bytes(M, N, K, r, G, has_gate=r > 0)
+    nbytes = layer_bytes(M, N, K, r, G, has_gate=r > 0, h=h)
     weight_bytes = packed0.numel() + ec_elems * 2
     R = max(1, -(-2 * MALL_BYTES // weight_bytes))
     def clone(t):
+        if isinstance(t, tuple):
+            return tuple(x.clone() for x in t)
         return None if t is None else t.clone()
 
     copies = [(packed0, A0, B0, wg0)] + [(packed0.clone(), clone(A0), clone(B0), clone(wg0))
@@ -200,12 +219,19 @@ def main():
     X = dev_act(d["X"])
     Y = torch.empty((M, N), dtype=tdt, device=dev)
     ws = torch.zeros(max(w4.w4ec_workspace_bytes(M, N, K, r, G), 256), dtype=torch.uint8, device=dev)
-    fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
     b_g = d["b_g"]
+    if vector:
+        fnv = w4.w4ec_linear_decode_vgate if phase == "decode" else w4.w4ec_linear_prefill_vgate
 
-    def step(i):
-        p, A, B, wg = copies[i % R]
-        fn(X, p, A, B, wg, b_g, N=N, group_size=G, workspace=ws, Y=Y)
+        def step(i):
+            p, A, B, gp = copies[i % R]
+            fnv(X, p, A, B, *gp, N=N, group_size=G, workspace=ws, Y=Y)
+    else:
+        fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
+
+        def step(i):
+            p, A, B, wg = copies[i % R]
+            fn(X, p, A, B, wg, b_g, N=N, group_size=G, workspace=ws, Y=Y)
 
     for i in range(args.warmup):
         step(i)
@@ -248,16 +274,17 @@ def main():
     # launches (gate / X A partial sums, their reduction, then the GEMM); its
     # figure is per call.
     kdur = elapsed_ms * 1e-3 / args.steps
-    kernel_name = "decode_kernel" if phase == "decode" else "prepass_kernel + ec_reduce_kernel + prefill_gemm_kernel (per call)"
+    reduce_name = "ec_reduce_vgate_kernel" if vector else "ec_reduce_kernel"
+    kernel_name = "decode_kernel" if phase == "decode" else f"prepass_kernel + {reduce_name} + prefill_gemm_kernel (per call)"
 
-    flops = layer_flops(M, N, K, r)
+    flops = layer_flops(M, N, K, r, h)
     if phase == "decode":
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
         achieved = nbytes / kdur / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        kernel_key = f"decode_kernel/{args.workload}"
+        kernel_key = f"decode_kernel/{args.workload}" + ("/vector_gate" if vector else "")
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -265,13 +292,13 @@ def main():
         peak = MFMA_PEAK_TFLOPS[act]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
-        kernel_key = f"prefill_call/{args.workload}"
+        kernel_key = f"prefill_call/{args.workload}" + ("/vector_gate" if vector else "")
     roof["traffic"] = traffic_from_profiles(kernel_key)
     roof["kernel"] = kernel_name
     roof["kernel_us"] = round(kdur * 1e6, 3)
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and not vector:
         cpu = cpu_baseline(d, phase, args.cpu_budget)
 
     out = {
@@ -288,7 +315,8 @@ def main():
         "dtype": act,
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "r": r, "group_size": G,
-                   "act": act, "phase": phase, "weight_copies": R,
+                   "act": act, "phase": phase, "gate": "vector" if vector else "scalar",
+                   **({"gate_width": h} if vector else {}), "weight_copies": R,
                    "launch": "hipgraph" if graph is not None else "eager",
                    "bytes_per_step": nbytes, "flops_per_step": flops},
         "roofline": roof,

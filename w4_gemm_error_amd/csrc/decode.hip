@@ -69,6 +69,7 @@ struct DecodeKArgs {
     const uint16_t* G2;  // act [h][r]
     const uint16_t* c2;  // act [r]
     int h;
+    int vg_staged;       // the gate parameters are copied to LDS (they fit)
 };
 
 __device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
@@ -120,9 +121,12 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
     const int M = a.M, r = a.r, h = a.h;
     const int w8 = a.r_pad / 4;                             // 8-byte words of a token's T_g
     const int qs = M * a.RC;                                // words per slice
-    float* tT = reinterpret_cast<float*>(smem);             // [r_pad]
-    float* tU = tT + a.r_pad;                               // [h]
-    uint64_t* tw = reinterpret_cast<uint64_t*>(tU + ((h + 1) & ~1));   // [w8], 8-byte aligned
+    float* tT = reinterpret_cast<float*>(smem);             // [r_pad] T of the token
+    float* tG = tT + a.r_pad;                               // [r_pad] gamma * T
+    float* tU = tG + a.r_pad;                               // [VG_HMAX] bottleneck
+    float* red = tU + VG_HMAX;                              // [VG_THREADS] partial sums
+    uint64_t* tw = reinterpret_cast<uint64_t*>(red + VG_THREADS);      // [w8], 8-byte aligned
+    uint16_t* gst = reinterpret_cast<uint16_t*>(tw + w8);   // staged gate parameters (if they fit)
     const int nrep = min(DEC_NREP, a.n_main);               // slots that have readers
     int m0 = j, mstep = nred, wb = 0, we = w8;
     if (nred >= M) {
@@ -138,6 +142,13 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
         if (wb >= we)
             return;
     }
+    // the gate parameters do not depend on T: their loads go out first and
+    // overlap the wait for the partial sums
+    const uint16_t *G1 = a.G1, *c1 = a.c1, *G2 = a.G2, *c2 = a.c2;
+    uint16_t gv[VG_SREG];
+    if (a.vg_staged)
+        vgate_stage_load(G1, c1, G2, c2, r, h, gv);
+    bool staged = false;
     uint32_t it = 0;                                        // bounded wait, shared by all waits
     for (int m = m0; m < M; m += mstep) {
         __syncthreads();                                    // LDS of the previous token is free
@@ -176,14 +187,14 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
             }
             tT[c] = t;
         }
-        __syncthreads();
-        for (int i = tid; i < h; i += DEC_THREADS) {
-            float u = 0.0f;
-            for (int c = 0; c < r; ++c)
-                u += tT[c] * act_to_f32<ACT>(a.G1[(size_t)c * h + i]);
-            u += act_to_f32<ACT>(a.c1[i]);
-            tU[i] = fmaxf(u, 0.0f);
+        if (a.vg_staged && !staged) {
+            vgate_stage_store(G1, c1, G2, c2, r, h, gv, gst);
+            staged = true;
         }
+        __syncthreads();
+        vgate_hidden<ACT>(tT, 0, 1, r, h, G1, c1, tU, red);
+        vgate_gates<ACT>(tU, 1, r, h, G2, c2, 4 * wb, min(r, 4 * we),
+                         [&](int, int c, float g) { tG[c] = g * tT[c]; });
         __syncthreads();
         for (int i = tid; i < we - wb; i += DEC_THREADS) {
             const int c0 = 4 * (wb + i);
@@ -191,15 +202,7 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int c = c0 + k;
-                float val = 0.0f;
-                if (c < r) {
-                    float zz = 0.0f;
-                    for (int q = 0; q < h; ++q)
-                        zz += tU[q] * act_to_f32<ACT>(a.G2[(size_t)q * r + c]);
-                    zz += act_to_f32<ACT>(a.c2[c]);
-                    val = sigmoid_f32(zz) * tT[c];
-                }
-                word |= (uint64_t)hw_enc16(f32_to_act<ACT>(val)) << (16 * k);
+                word |= (uint64_t)hw_enc16(f32_to_act<ACT>(c < r ? tG[c] : 0.0f)) << (16 * k);
             }
             tw[i] = word;
         }
@@ -775,8 +778,10 @@ static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
     const int nred = std::min(p.P, DEC_EC_RMAX);
     const int share = (M * p.r_pad / 4 + nred - 1) / nred;
     const size_t fin = ((size_t)DEC_THREADS + 4 * share + M + 2) * 4 + (size_t)share * 8;
-    // vector gate: [r_pad] T, [h] bottleneck (padded to even), [r_pad / 4] words
-    const size_t vg = ((size_t)p.r_pad + 64 + 2) * 4 + (size_t)p.r_pad / 4 * 8;
+    // vector gate: [r_pad] T, [r_pad] gated T, [VG_HMAX] bottleneck,
+    // [VG_THREADS] partial sums, [r_pad / 4] words, then (when they fit in
+    // what the slice needs anyway) the gate parameters
+    const size_t vg = ((size_t)2 * p.r_pad + VG_HMAX + VG_THREADS) * 4 + (size_t)p.r_pad / 4 * 8;
     return (std::max(at, std::max(fin, vg)) + 15) / 16 * 16;
 }
 
@@ -845,6 +850,13 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.G1 = (const uint16_t*)a.G1; k.c1 = (const uint16_t*)a.c1;
     k.G2 = (const uint16_t*)a.G2; k.c2 = (const uint16_t*)a.c2;
     k.h = a.r > 0 ? a.h : 0;
+    k.vg_staged = 0;
+    if (k.h > 0) {
+        // stage the gate parameters when they fit in the EC role's LDS
+        const size_t base = ((size_t)2 * p.r_pad + VG_HMAX + VG_THREADS) * 4 + (size_t)p.r_pad / 4 * 8;
+        k.vg_staged = vgate_stageable(a.r, a.h) &&
+                      base + (size_t)vgate_stage_elems(a.r, a.h) * 2 <= ec_lds_bytes(p, a.M, a.r);
+    }
     if (a.act == ACT_F16)
         return launch_decode_act<ACT_F16>(k, p, st);
     return launch_decode_act<ACT_BF16>(k, p, st);

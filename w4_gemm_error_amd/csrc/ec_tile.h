@@ -120,4 +120,146 @@ __device__ inline int ec_col(int r, int cb, int j)
     return c < r ? c : -1;
 }
 
+// ---------------------------------------------------------------- vector gate
+//
+// One gate per rank component (SPEAR summary section 2.1A: W + B diag(gamma(A
+// x)) A with gamma a bottleneck MLP, read as gamma = sigmoid(relu(T G1 + c1)
+// G2 + c2)), for nt <= VG_TMAX token rows of T held in LDS.  256 threads.
+constexpr int VG_HMAX = 64;     // widest bottleneck
+constexpr int VG_TMAX = 16;     // token rows per call
+constexpr int VG_THREADS = 256;
+
+// Staging of the gate parameters in LDS ([r h | h | h r | r] act values):
+// vgate_stage_load issues every load into registers (VG_SREG per thread,
+// so at most VG_SREG * VG_THREADS values: vgate_stageable), the caller
+// issues its own loads, then vgate_stage_store writes the values to LDS and
+// points G1 .. c2 at them.  The parameters do not depend on T, so their
+// trip to memory overlaps the one for T.
+constexpr int VG_SREG = 16;
+
+__host__ __device__ inline int vgate_stage_elems(int r, int h) { return 2 * r * h + r + h; }
+__host__ __device__ inline bool vgate_stageable(int r, int h) { return vgate_stage_elems(r, h) <= VG_SREG * VG_THREADS; }
+
+__device__ inline void vgate_stage_load(const uint16_t* G1, const uint16_t* c1, const uint16_t* G2,
+                                        const uint16_t* c2, int r, int h, uint16_t (&v)[VG_SREG])
+{
+    const int n1 = r * h, tot = vgate_stage_elems(r, h);
+#pragma unroll
+    for (int k = 0; k < VG_SREG; ++k) {
+        const int e = k * VG_THREADS + (int)threadIdx.x;
+        v[k] = 0;
+        if (e < n1)
+            v[k] = G1[e];
+        else if (e < n1 + h)
+            v[k] = c1[e - n1];
+        else if (e < 2 * n1 + h)
+            v[k] = G2[e - n1 - h];
+        else if (e < tot)
+            v[k] = c2[e - 2 * n1 - h];
+    }
+}
+
+__device__ inline void vgate_stage_store(const uint16_t*& G1, const uint16_t*& c1, const uint16_t*& G2,
+                                         const uint16_t*& c2, int r, int h, const uint16_t (&v)[VG_SREG],
+                                         uint16_t* dst)
+{
+    const int n1 = r * h, tot = vgate_stage_elems(r, h);
+#pragma unroll
+    for (int k = 0; k < VG_SREG; ++k) {
+        const int e = k * VG_THREADS + (int)threadIdx.x;
+        if (e < tot)
+            dst[e] = v[k];
+    }
+    G1 = dst;
+    c1 = dst + n1;
+    G2 = dst + n1 + h;
+    c2 = dst + 2 * n1 + h;
+}
+
+// u[t][i] = relu(sum_c T[t][c] G1[c][i] + c1[i]) into tU ([nt][VG_HMAX]).
+// Thread (chunk, i) adds a chunk of the r columns for every row: its G1
+// loads are coalesced (neighbouring threads read neighbouring i) and issued
+// eight at a time; the chunks' partial sums meet in `red`
+// ([nt][VG_THREADS] floats) and are added in chunk order.
+template <int ACT>
+__device__ void vgate_hidden(const float* tT, int ldT, int nt, int r, int h, const uint16_t* G1,
+                             const uint16_t* c1, float* tU, float* red)
+{
+    const int tid = threadIdx.x;
+    const int nch = VG_THREADS / h;
+    const int i = tid % h, ch = tid / h;
+    if (ch < nch) {
+        const int per = (r + nch - 1) / nch;
+        const int cb = min(r, ch * per), ce = min(r, cb + per);
+        float acc[VG_TMAX];
+#pragma unroll
+        for (int t = 0; t < VG_TMAX; ++t)
+            acc[t] = 0.0f;
+        for (int c0 = cb; c0 < ce; c0 += 8) {
+            float g[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                g[k] = c0 + k < ce ? act_to_f32<ACT>(G1[(size_t)(c0 + k) * h + i]) : 0.0f;
+#pragma unroll
+            for (int t = 0; t < VG_TMAX; ++t) {
+                if (t < nt) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (c0 + k < ce)
+                            acc[t] += tT[t * ldT + c0 + k] * g[k];
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < VG_TMAX; ++t)
+            if (t < nt)
+                red[(t * nch + ch) * h + i] = acc[t];
+    }
+    __syncthreads();
+    for (int e = tid; e < nt * h; e += VG_THREADS) {
+        const int t = e / h, q = e - t * h;
+        float u = 0.0f;
+        for (int c = 0; c < nch; ++c)
+            u += red[(t * nch + c) * h + q];
+        u += act_to_f32<ACT>(c1[q]);
+        tU[t * VG_HMAX + q] = fmaxf(u, 0.0f);
+    }
+    __syncthreads();
+}
+
+// gamma[t][c] = sigmoid(sum_i u[t][i] G2[i][c] + c2[c]) for the columns c
+// of [c_lo, c_hi), one thread per column (G2 loads coalesced, eight at a
+// time); out(t, c, gamma) receives each gate.
+template <int ACT, typename F>
+__device__ void vgate_gates(const float* tU, int nt, int r, int h, const uint16_t* G2, const uint16_t* c2,
+                            int c_lo, int c_hi, F&& out)
+{
+    for (int c = c_lo + (int)threadIdx.x; c < c_hi; c += VG_THREADS) {
+        float z[VG_TMAX];
+        const float bias = act_to_f32<ACT>(c2[c]);
+#pragma unroll
+        for (int t = 0; t < VG_TMAX; ++t)
+            z[t] = 0.0f;
+        for (int i0 = 0; i0 < h; i0 += 8) {
+            float g[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                g[k] = i0 + k < h ? act_to_f32<ACT>(G2[(size_t)(i0 + k) * r + c]) : 0.0f;
+#pragma unroll
+            for (int t = 0; t < VG_TMAX; ++t) {
+                if (t < nt) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (i0 + k < h)
+                            z[t] += tU[t * VG_HMAX + i0 + k] * g[k];
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < VG_TMAX; ++t)
+            if (t < nt)
+                out(t, c, sigmoid_f32(z[t] + bias));
+    }
+}
+
 }  // namespace w4ec

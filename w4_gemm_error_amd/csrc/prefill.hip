@@ -151,6 +151,7 @@ struct EcReduceKArgs {
     const uint16_t* G2;
     const uint16_t* c2;
     int h;
+    int vg_staged;      // the gate parameters are copied to (dynamic) LDS
 };
 
 // One workgroup per (16 tokens, column block of T): adds the K slices'
@@ -229,33 +230,43 @@ void ec_reduce_kernel(EcReduceKArgs a)
 
 // Vector gate (one gate per rank component; SPEAR summary section 2.1A,
 // W + B diag(gamma(A x)) A with gamma a bottleneck MLP, read as
-// gamma = sigmoid(relu(T G1 + c1) G2 + c2)).  One workgroup per 16 tokens:
-// it adds every column block of T over the K slices in slice order, runs
-// the bottleneck for each token in fp32 and stores T_g = gamma * T.
-constexpr int VG_HMAX = 64;     // largest bottleneck width
+// gamma = sigmoid(relu(T G1 + c1) G2 + c2)).  One workgroup per 4 tokens
+// (the 16 lanes of each MFMA fragment that hold them): it adds every column
+// block of T over the K slices in slice order, runs the bottleneck for the
+// 4 tokens in fp32 and stores T_g = gamma * T.
 constexpr int VG_RMAX = 256;    // largest rank
+constexpr int VG_NT = 4;        // tokens per workgroup
 
 template <int ACT>
 __global__ __launch_bounds__(PF_THREADS)
 void ec_reduce_vgate_kernel(EcReduceKArgs a)
 {
-    __shared__ float tT[16][VG_RMAX + 1];            // T of the 16 tokens (columns < r)
-    __shared__ float tU[16][VG_HMAX];                // bottleneck activations
+    static_assert(PF_THREADS == VG_THREADS, "the bottleneck helpers assume 256 threads");
+    __shared__ float tT[VG_NT][VG_RMAX + 1];         // T of the 4 tokens (columns < r)
+    __shared__ float tU[VG_NT * VG_HMAX];            // bottleneck activations
+    __shared__ float red[VG_NT * VG_THREADS];        // the bottleneck's partial sums
+    extern __shared__ __attribute__((aligned(16))) uint16_t gst[];   // staged gate parameters
     const int tid = threadIdx.x;
-    const int rb = blockIdx.x;                       // rows 16 rb .. 16 rb + 15
+    // the gate parameters do not depend on T: their loads go out first and
+    // overlap those of the partial sums
+    const uint16_t *G1 = a.G1, *c1 = a.c1, *G2 = a.G2, *c2 = a.c2;
+    uint16_t gv[VG_SREG];
+    if (a.vg_staged)
+        vgate_stage_load(G1, c1, G2, c2, a.r, a.h, gv);
+    const int rb = blockIdx.x >> 2, grp = blockIdx.x & 3;   // rows 16 rb + 4 grp .. + 3
     const int mt = rb >> 2, w = rb & 3;
     const int nb = ec_blocks(a.r), nba = ec_a_blocks(a.r);
     const int ne = nb * 64;                          // fragments per slice of this row block
     const floatx4* base = a.partial + ((size_t)mt * a.ks * 4 + w) * ne;
     const size_t zs = (size_t)4 * ne;
-    // fragment e = (column block e / 64, lane e % 64): lane l holds column
-    // l % 16 of the block for rows 4 (l / 16) + v
-    for (int e = tid; e < ne; e += PF_THREADS) {
-        const int cb = e >> 6, l = e & 63;
-        const int col = l & 15;
+    const int r = a.r, h = a.h;
+    // e = (column block e / 16, column e % 16): lane 16 grp + column holds
+    // rows 4 grp + v of that column
+    for (int e = tid; e < nb * 16; e += PF_THREADS) {
+        const int cb = e >> 4, col = e & 15;
         if (cb >= nba && !(a.rowsum && col == 1))
             continue;                                // the gate logit column is not used here
-        const floatx4* src = base + e;
+        const floatx4* src = base + cb * 64 + grp * 16 + col;
         floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
         for (int z0 = 0; z0 < a.ks; z0 += 8) {
             floatx4 v[8];
@@ -268,38 +279,25 @@ void ec_reduce_vgate_kernel(EcReduceKArgs a)
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int row = 4 * (l >> 4) + v;
             if (cb < nba) {
-                if (16 * cb + col < a.r)
-                    tT[row][16 * cb + col] = t[v];
+                if (16 * cb + col < r)
+                    tT[v][16 * cb + col] = t[v];
             } else {
-                a.rowsum[16 * rb + row] = t[v];      // the column of ones: each token's activation sum
+                a.rowsum[16 * rb + 4 * grp + v] = t[v];   // the column of ones: activation sums
             }
         }
     }
+    if (a.vg_staged)
+        vgate_stage_store(G1, c1, G2, c2, r, h, gv, gst);
     __syncthreads();
-    const int r = a.r, h = a.h;
-    for (int e = tid; e < 16 * h; e += PF_THREADS) {
-        const int row = e / h, i = e - row * h;
-        float u = 0.0f;
-        for (int c = 0; c < r; ++c)
-            u += tT[row][c] * act_to_f32<ACT>(a.G1[(size_t)c * h + i]);
-        u += act_to_f32<ACT>(a.c1[i]);
-        tU[row][i] = fmaxf(u, 0.0f);
-    }
-    __syncthreads();
-    for (int e = tid; e < 16 * a.r_pad; e += PF_THREADS) {
-        const int row = e / a.r_pad, c = e - row * a.r_pad;
-        float val = 0.0f;
-        if (c < r) {
-            float zz = 0.0f;
-            for (int i = 0; i < h; ++i)
-                zz += tU[row][i] * act_to_f32<ACT>(a.G2[(size_t)i * r + c]);
-            zz += act_to_f32<ACT>(a.c2[c]);
-            val = sigmoid_f32(zz) * tT[row][c];
-        }
-        a.tg[(size_t)(16 * rb + row) * a.r_pad + c] = f32_to_act<ACT>(val);
-    }
+    vgate_hidden<ACT>(&tT[0][0], VG_RMAX + 1, VG_NT, r, h, G1, c1, tU, red);
+    uint16_t* tg = a.tg + (size_t)(16 * rb + 4 * grp) * a.r_pad;
+    vgate_gates<ACT>(tU, VG_NT, r, h, G2, c2, 0, r, [&](int t, int c, float g) {
+        tg[(size_t)t * a.r_pad + c] = f32_to_act<ACT>(g * tT[t][c]);
+    });
+    const int pad = a.r_pad - r;
+    for (int e = tid; e < VG_NT * pad; e += PF_THREADS)
+        tg[(size_t)(e / pad) * a.r_pad + r + e % pad] = f32_to_act<ACT>(0.0f);
 }
 
 // ---------------------------------------------------------------- GEMM
@@ -838,7 +836,9 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
         rq.h = a.h;
         if (a.r > 0 && a.h > 0) {
             auto vk = a.act == ACT_F16 ? ec_reduce_vgate_kernel<ACT_F16> : ec_reduce_vgate_kernel<ACT_BF16>;
-            hipLaunchKernelGGL(vk, dim3(p.pre_mt * 4), dim3(PF_THREADS), 0, st, rq);
+            const size_t gbytes = (size_t)vgate_stage_elems(a.r, a.h) * 2;
+            rq.vg_staged = vgate_stageable(a.r, a.h);    // at most 8 KB
+            hipLaunchKernelGGL(vk, dim3(p.pre_mt * 16), dim3(PF_THREADS), rq.vg_staged ? gbytes : 0, st, rq);
         } else {
             auto rk = a.act == ACT_F16 ? ec_reduce_kernel<ACT_F16> : ec_reduce_kernel<ACT_BF16>;
             hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4, a.r > 0 ? ec_a_blocks(a.r) : 1), dim3(PF_THREADS), 0, st, rq);
