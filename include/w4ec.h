@@ -167,6 +167,36 @@ int w4ec_linear_prefill_vgate(const void* X, const void* packed, const void* A, 
                               int h, void* Y, int M, int N, int K, int r, int group_size,
                               int act_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Unfused and semi-fused prefill (the SPEAR summary, section 2.2A, runs the
+ * EC beside the low-bit GEMM in the prefill phase and adds its product
+ * afterwards).  These two calls split the EC off the fused prefill so that a
+ * caller can run
+ *     w4ec_prefill_ec_gate  (X -> T_g in its workspace), on one stream,
+ *     w4ec_linear_prefill with r = 0 (Y = X Wd^T), on another, then
+ *     w4ec_prefill_ec_apply (Y += T_g B) after both,
+ * e.g. as a graph with a fork and a join.  The result equals the fused
+ * layer's up to one more rounding of Y to the activation type.
+ *
+ * w4ec_prefill_ec_workspace_bytes: workspace for the two EC calls (their
+ * own; a concurrent GEMM needs a different one).  0 for unsupported shapes.
+ *
+ * w4ec_prefill_ec_gate: T_g = g * (X A) with g = sigmoid(X w_g + b_g), as in
+ * w4ec_linear_prefill, into the workspace.
+ *   X device act [M, K]; A device act [K, r]; w_g device act [K] or NULL;
+ *   1 <= r <= 256; K a multiple of 128.
+ *
+ * w4ec_prefill_ec_apply: Y += T_g B, with T_g from the last
+ * w4ec_prefill_ec_gate on this workspace (same M, K, r) and Y [M, N] holding
+ * the plain W4 product.  B device act [r, N]; Y device act [M, N], read and
+ * written; the workspace is only read.
+ * Both return W4EC_ERR_WORKSPACE for a missing, misaligned (256 B) or too
+ * small workspace, and validate before launching anything. */
+size_t w4ec_prefill_ec_workspace_bytes(int M, int K, int r);
+int w4ec_prefill_ec_gate(const void* X, const void* A, const void* w_g, float b_g, int M, int K,
+                         int r, int act_dtype, void* workspace, size_t workspace_bytes, void* stream);
+int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, int act_dtype,
+                          const void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -140,3 +140,35 @@ def test_vgate_argument_errors(name):
 
 def test_vgate_decode_rejects_more_than_16_tokens():
     assert call_vg("w4ec_linear_decode_vgate", M=17) == w4.W4EC_ERR_UNSUPPORTED
+
+
+def test_prefill_ec_split_argument_errors():
+    L = w4.lib()
+    P = ctypes.c_void_p
+    E = w4
+    assert w4.w4ec_prefill_ec_workspace_bytes(2048, 4096, 64) > w4.W4EC_WS_STATE_BYTES
+    assert w4.w4ec_prefill_ec_workspace_bytes(16, 100, 8) == 0       # K not a multiple of 128
+    assert w4.w4ec_prefill_ec_workspace_bytes(16, 512, 0) == 0       # needs a compensator
+    x, a, wg, y, b = (P(FAKE + i * 0x100000) for i in range(5))
+    ws = P(FAKE + 0x600000)
+    big = 1 << 30
+    gate = lambda **k: L.w4ec_prefill_ec_gate(k.get("X", x), k.get("A", a), k.get("w_g", wg), 0.0,
+                                              k.get("M", 64), k.get("K", 512), k.get("r", 8),
+                                              k.get("act", 0), k.get("ws", ws), k.get("wsb", big), None)
+    assert gate(M=0) == E.W4EC_ERR_INVALID_ARG
+    assert gate(r=0) == E.W4EC_ERR_INVALID_ARG
+    assert gate(K=500) == E.W4EC_ERR_UNSUPPORTED
+    assert gate(r=257) == E.W4EC_ERR_UNSUPPORTED
+    assert gate(X=None) == E.W4EC_ERR_INVALID_ARG
+    assert gate(A=P(FAKE + 8)) == E.W4EC_ERR_INVALID_ARG
+    assert gate(act=3) == E.W4EC_ERR_INVALID_ARG
+    assert gate(ws=None) == E.W4EC_ERR_WORKSPACE
+    assert gate(wsb=64) == E.W4EC_ERR_WORKSPACE
+    apply = lambda **k: L.w4ec_prefill_ec_apply(k.get("Y", y), k.get("B", b), k.get("M", 64), k.get("N", 512),
+                                                k.get("K", 512), k.get("r", 8), k.get("act", 0),
+                                                k.get("ws", ws), k.get("wsb", big), None)
+    assert apply(N=0) == E.W4EC_ERR_INVALID_ARG
+    assert apply(Y=None) == E.W4EC_ERR_INVALID_ARG
+    assert apply(B=y) == E.W4EC_ERR_INVALID_ARG                    # aliases Y
+    assert apply(K=96) == E.W4EC_ERR_UNSUPPORTED
+    assert apply(ws=P(FAKE + 0x600010)) == E.W4EC_ERR_WORKSPACE

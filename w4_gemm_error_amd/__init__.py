@@ -23,6 +23,7 @@ __all__ = [
     "w4ec_quantize_rtn", "w4ec_pack", "w4ec_unpack",
     "w4ec_linear_decode", "w4ec_linear_prefill", "w4ec_linear",
     "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
+    "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
     "PackedLayer",
 ]
 
@@ -76,6 +77,12 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, P, Z, P]
             fn.restype = I
+        L.w4ec_prefill_ec_workspace_bytes.argtypes = [I, I, I]
+        L.w4ec_prefill_ec_workspace_bytes.restype = Z
+        L.w4ec_prefill_ec_gate.argtypes = [P, P, P, F, I, I, I, I, P, Z, P]
+        L.w4ec_prefill_ec_gate.restype = I
+        L.w4ec_prefill_ec_apply.argtypes = [P, P, I, I, I, I, I, P, Z, P]
+        L.w4ec_prefill_ec_apply.restype = I
         for name in ("w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"):
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P, Z, P]
@@ -256,6 +263,35 @@ def w4ec_linear_prefill_vgate(X, packed, A, B, G1, c1, G2, c2, *, N, group_size,
     """The vector-gate layer for any M >= 1 (prepass, per-token bottleneck, tiled MFMA GEMM)."""
     return _layer_call_vgate("w4ec_linear_prefill_vgate", X, packed, A, B, G1, c1, G2, c2, N, group_size,
                              workspace, Y, stream)
+
+
+def w4ec_prefill_ec_workspace_bytes(M: int, K: int, r: int) -> int:
+    return int(lib().w4ec_prefill_ec_workspace_bytes(int(M), int(K), int(r)))
+
+
+def w4ec_prefill_ec_gate(X, A, w_g, b_g, *, workspace, stream=None):
+    """T_g = g * (X A) into `workspace` (the EC half of the unfused prefill)."""
+    torch = _torch()
+    _need_cuda(X, "X", (torch.float16, torch.bfloat16))
+    _need_cuda(A, "A", X.dtype)
+    _need_cuda(w_g, "w_g", X.dtype)
+    M, K = X.shape
+    r = int(A.shape[1])
+    st = lib().w4ec_prefill_ec_gate(_ptr(X), _ptr(A), _ptr(w_g), float(b_g), M, K, r, _act_code(X.dtype),
+                                    _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(st, "w4ec_prefill_ec_gate")
+
+
+def w4ec_prefill_ec_apply(Y, B, *, K, workspace, stream=None):
+    """Y += T_g B, with T_g from the last w4ec_prefill_ec_gate on `workspace`."""
+    torch = _torch()
+    _need_cuda(Y, "Y", (torch.float16, torch.bfloat16))
+    _need_cuda(B, "B", Y.dtype)
+    M, N = Y.shape
+    r = int(B.shape[0])
+    st = lib().w4ec_prefill_ec_apply(_ptr(Y), _ptr(B), M, N, int(K), r, _act_code(Y.dtype),
+                                     _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(st, "w4ec_prefill_ec_apply")
 
 
 def w4ec_linear_decode(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):

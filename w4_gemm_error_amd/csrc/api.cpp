@@ -387,6 +387,54 @@ int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const 
                          workspace, workspace_bytes, stream, nullptr);
 }
 
+// The prefill plan's EC regions (prepass partial sums, T_g) depend on M, K
+// and r only; any N gives the same offsets.
+static PrefillPlan ec_plan(int M, int K, int r) { return make_prefill_plan(M, 16, K, r); }
+
+size_t w4ec_prefill_ec_workspace_bytes(int M, int K, int r)
+{
+    if (M <= 0 || r < 1 || r > MAX_RANK || K <= 0 || K % PANEL_K != 0)
+        return 0;
+    const PrefillPlan p = ec_plan(M, K, r);
+    return p.off_tg + (size_t)((M + 63) / 64 * 64) * p.r_pad * 2;
+}
+
+int w4ec_prefill_ec_gate(const void* X, const void* A, const void* w_g, float b_g, int M, int K,
+                         int r, int act_dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (M <= 0 || r < 1 || K <= 0)
+        return W4EC_ERR_INVALID_ARG;
+    if (K % PANEL_K != 0 || r > MAX_RANK)
+        return W4EC_ERR_UNSUPPORTED;
+    if (act_dtype != W4EC_FP16 && act_dtype != W4EC_BF16)
+        return W4EC_ERR_INVALID_ARG;
+    if (!X || !A || !aligned(X, 16) || !aligned(A, 16) || !aligned(w_g, 16))
+        return W4EC_ERR_INVALID_ARG;
+    const size_t need = w4ec_prefill_ec_workspace_bytes(M, K, r);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return W4EC_ERR_WORKSPACE;
+    LayerArgs a{X, nullptr, A, nullptr, w_g, b_g, nullptr, M, 16, K, r, K, act_dtype, (char*)workspace};
+    return hip_status(launch_prefill_ec_gate(a, ec_plan(M, K, r), (hipStream_t)stream));
+}
+
+int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, int act_dtype,
+                          const void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (M <= 0 || N <= 0 || r < 1 || K <= 0)
+        return W4EC_ERR_INVALID_ARG;
+    if (K % PANEL_K != 0 || r > MAX_RANK)
+        return W4EC_ERR_UNSUPPORTED;
+    if (act_dtype != W4EC_FP16 && act_dtype != W4EC_BF16)
+        return W4EC_ERR_INVALID_ARG;
+    if (!Y || !B || !aligned(Y, 2) || !aligned(B, 2) || Y == B)
+        return W4EC_ERR_INVALID_ARG;
+    const size_t need = w4ec_prefill_ec_workspace_bytes(M, K, r);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return W4EC_ERR_WORKSPACE;
+    ApplyArgs a{Y, B, M, N, r, act_dtype, (char*)workspace};
+    return hip_status(launch_prefill_ec_apply(a, ec_plan(M, K, r), (hipStream_t)stream));
+}
+
 int w4ec_linear_decode_vgate(const void* X, const void* packed, const void* A, const void* B,
                              const void* G1, const void* c1, const void* G2, const void* c2,
                              int h, void* Y, int M, int N, int K, int r, int group_size,

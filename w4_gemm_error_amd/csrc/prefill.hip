@@ -300,6 +300,89 @@ void ec_reduce_vgate_kernel(EcReduceKArgs a)
         tg[(size_t)(e / pad) * a.r_pad + r + e % pad] = f32_to_act<ACT>(0.0f);
 }
 
+// ---------------------------------------------------------------- unfused EC
+//
+// The correction as a kernel of its own, for the unfused and semi-fused
+// prefill forms (SPEAR summary section 2.2A runs the EC beside the low-bit
+// GEMM and adds it afterwards): Y += T_g B, with T_g [rows][r_pad] from the
+// gate step and Y already holding the plain W4 product.  One workgroup per
+// 64 x 64 tile of Y; the B tile is staged in LDS and read back as MFMA
+// operands, T_g rows are the other operand, Y is read, added to and rounded
+// once more.
+constexpr int APPLY_TM = 64, APPLY_TN = 64;
+constexpr int APPLY_BP = APPLY_TN + 16;   // halves per staged B row
+
+struct ApplyKArgs {
+    uint16_t* Y;
+    const uint16_t* B;
+    const uint16_t* tg;
+    int M, N, r, r_pad;
+};
+
+template <int ACT>
+__global__ __launch_bounds__(PF_THREADS)
+void ec_apply_kernel(ApplyKArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t bl[256 * APPLY_BP];   // r_pad <= 256 rows
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = tid >> 6;
+    const int n0 = blockIdx.x * APPLY_TN;
+    const int m0 = blockIdx.y * APPLY_TM;
+    // B rows [0, r_pad) x columns [n0, n0 + 64): zero past r and past N
+    for (int e = tid; e < a.r_pad * (APPLY_TN / 8); e += PF_THREADS) {
+        const int j = e / (APPLY_TN / 8), c8 = e - j * (APPLY_TN / 8);
+        const int n = n0 + 8 * c8;
+        uint16_t v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            v[t] = (j < a.r && n + t < a.N) ? a.B[(size_t)j * a.N + n + t] : (uint16_t)0;
+        u32x4 q = (u32x4){v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                          v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16)};
+        st16(bl + (size_t)j * APPLY_BP + 8 * c8, q);
+    }
+    __syncthreads();
+    const int row = m0 + 16 * w + (l & 15);            // A-operand row of this lane
+    const uint16_t* tr = a.tg + (size_t)row * a.r_pad + 8 * (l >> 4);
+    floatx4 acc[APPLY_TN / 16];
+#pragma unroll
+    for (int j = 0; j < APPLY_TN / 16; ++j)
+        acc[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    for (int rs = 0; rs < a.r_pad / 32; ++rs) {
+        const u32x4 af = ld16(tr + 32 * rs);
+#pragma unroll
+        for (int j = 0; j < APPLY_TN / 16; ++j)
+            acc[j] = mfma16x16x32<ACT>(af, lds_bfrag(bl, APPLY_BP, 16 * j, 32 * rs), acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < APPLY_TN / 16; ++j) {
+        const int n = n0 + 16 * j + (l & 15);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = m0 + 16 * w + 4 * (l >> 4) + v;
+            if (m < a.M && n < a.N) {
+                uint16_t* y = a.Y + (size_t)m * a.N + n;
+                *y = f32_to_act<ACT>(act_to_f32<ACT>(*y) + acc[j][v]);
+            }
+        }
+    }
+}
+
+hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hipStream_t st)
+{
+    ApplyKArgs k;
+    k.Y = (uint16_t*)a.Y;
+    k.B = (const uint16_t*)a.B;
+    k.tg = (const uint16_t*)(a.ws + p.off_tg);
+    k.M = a.M; k.N = a.N; k.r = a.r; k.r_pad = p.r_pad;
+    dim3 grid((a.N + APPLY_TN - 1) / APPLY_TN, (a.M + APPLY_TM - 1) / APPLY_TM);
+    if (a.act == ACT_F16)
+        hipLaunchKernelGGL(ec_apply_kernel<ACT_F16>, grid, dim3(PF_THREADS), 0, st, k);
+    else
+        hipLaunchKernelGGL(ec_apply_kernel<ACT_BF16>, grid, dim3(PF_THREADS), 0, st, k);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- GEMM
 
 struct GemmKArgs {
@@ -799,13 +882,13 @@ size_t prepass_lds_bytes(int r, int kc)
     return (size_t)ec_slice_bytes(r, kc) + (size_t)kc * 2;
 }
 
-hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st)
+// The gate / X A prepass and its reduction: T_g (and, for the GEMM's bf16
+// per-channel zero-point term, each token's activation sum) in the workspace.
+static hipError_t launch_prefill_ec_part(const LayerArgs& a, const PrefillPlan& p, bool sums, hipStream_t st)
 {
-    BlobGeom g = blob_geom(a.N, a.K, a.G);
     uint16_t* tg = (uint16_t*)(a.ws + p.off_tg);
-    const bool sums = a.act == ACT_BF16 && a.G == a.K;   // the GEMM's bf16 zero-point term
     float* rowsum = (float*)(a.ws + p.off_rowsum);
-    if (a.r > 0 || sums) {
+    {
         PrepassKArgs q;
         q.X = (const uint16_t*)a.X;
         q.A = (const uint16_t*)a.A;
@@ -843,7 +926,23 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
             auto rk = a.act == ACT_F16 ? ec_reduce_kernel<ACT_F16> : ec_reduce_kernel<ACT_BF16>;
             hipLaunchKernelGGL(rk, dim3(p.pre_mt * 4, a.r > 0 ? ec_a_blocks(a.r) : 1), dim3(PF_THREADS), 0, st, rq);
         }
-        e = hipGetLastError();
+        return hipGetLastError();
+    }
+}
+
+hipError_t launch_prefill_ec_gate(const LayerArgs& a, const PrefillPlan& p, hipStream_t st)
+{
+    return launch_prefill_ec_part(a, p, false, st);
+}
+
+hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st)
+{
+    BlobGeom g = blob_geom(a.N, a.K, a.G);
+    uint16_t* tg = (uint16_t*)(a.ws + p.off_tg);
+    const bool sums = a.act == ACT_BF16 && a.G == a.K;   // the GEMM's bf16 zero-point term
+    float* rowsum = (float*)(a.ws + p.off_rowsum);
+    if (a.r > 0 || sums) {
+        hipError_t e = launch_prefill_ec_part(a, p, sums, st);
         if (e != hipSuccess)
             return e;
     }

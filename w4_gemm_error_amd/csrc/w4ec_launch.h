@@ -38,6 +38,16 @@ struct LayerArgs {
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
 bool decode_use_xlds(int M, int K);
 hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
+
+// unfused / semi-fused prefill pieces: T_g into the workspace, then Y += T_g B
+struct ApplyArgs {
+    void* Y;
+    const void* B;
+    int M, N, r, act;
+    char* ws;
+};
+hipError_t launch_prefill_ec_gate(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
+hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hipStream_t st);
 size_t prepass_lds_bytes(int r, int kc);
 
 }  // namespace w4ec
