@@ -137,6 +137,93 @@ def cpu_baseline(d, phase, budget_s):
             "kind": "oracle", "sample": sample}
 
 
+def split_prefill_step(torch, w4, path, X, Y, copies, R, b_g, M, N, K, r, G):
+    """One call of the unfused ("unfused": one stream) or semi-fused ("semi":
+    the gate step on a second stream beside the GEMM) prefill: T_g into an EC
+    workspace, the plain W4 GEMM into Y, then Y += T_g B."""
+    dev = X.device
+    ws_ec = torch.zeros(w4.w4ec_prefill_ec_workspace_bytes(M, K, r), dtype=torch.uint8, device=dev)
+    ws_mm = torch.zeros(max(w4.w4ec_workspace_bytes(M, N, K, 0, G), 256), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream() if path == "semi" else None
+
+    def step(i):
+        p, A, B, wg = copies[i % R]
+        if side is not None:
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                w4.w4ec_prefill_ec_gate(X, A, wg, b_g, workspace=ws_ec)
+            w4.w4ec_linear_prefill(X, p, None, None, None, 0.0, N=N, group_size=G, workspace=ws_mm, Y=Y)
+            cur.wait_stream(side)
+        else:
+            w4.w4ec_prefill_ec_gate(X, A, wg, b_g, workspace=ws_ec)
+            w4.w4ec_linear_prefill(X, p, None, None, None, 0.0, N=N, group_size=G, workspace=ws_mm, Y=Y)
+        w4.w4ec_prefill_ec_apply(Y, B, K=K, workspace=ws_ec)
+    return step
+
+
+def graph_time_us(torch, step, steps, warmup):
+    """Microseconds per step of `steps` calls captured in one graph (after
+    `warmup` eager calls and one untimed replay)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for i in range(steps):
+                step(i)
+    torch.cuda.current_stream().wait_stream(stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / steps
+
+
+def latency_table(torch, w4, synth, dev):
+    """Per-call latency of the fused, unfused and semi-fused prefill over a
+    grid of shapes: the input of an EC-aware scheduler that picks a path per
+    (M, r, N, K) (SPEAR summary, section 2.2A)."""
+    shapes = [(4096, 4096), (14336, 4096), (4096, 14336)]
+    for (N, K) in shapes:
+        W = torch.randn(N, K, device=dev) * 0.02
+        q, s, z = w4.w4ec_quantize_rtn(W, K)
+        packed = w4.w4ec_pack(q, s, z, N, K, K)
+        del W, q, s, z
+        R = max(2, -(-2 * MALL_BYTES // packed.numel()))
+        pk = [packed] + [packed.clone() for _ in range(R - 1)]
+        for M in (64, 256, 1024, 4096):
+            X = (torch.randn(M, K, device=dev)).half()
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            for r in (16, 64, 128):
+                A = (torch.randn(K, r, device=dev) * 0.01).half()
+                B = (torch.randn(r, N, device=dev) * 0.01).half()
+                wg = (torch.randn(K, device=dev) * 0.05).half()
+                copies = [(p, A, B, wg) for p in pk]
+                ws = torch.zeros(w4.w4ec_workspace_bytes(M, N, K, r, K), dtype=torch.uint8, device=dev)
+                steps = 20 if M * N * K > 1e11 else 50
+                res = {}
+                for path in ("fused", "unfused", "semi"):
+                    if path == "fused":
+                        def step(i, copies=copies, ws=ws):
+                            p, A_, B_, wg_ = copies[i % R]
+                            w4.w4ec_linear_prefill(X, p, A_, B_, wg_, 0.0, N=N, group_size=K, workspace=ws, Y=Y)
+                    else:
+                        step = split_prefill_step(torch, w4, path, X, Y, copies, R, 0.0, M, N, K, r, K)
+                    res[path] = round(graph_time_us(torch, step, steps, 5), 2)
+                best = min(res, key=res.get)
+                print(json.dumps({"M": M, "N": N, "K": K, "r": r, "us": res, "best": best,
+                                  "fused_over_best": round(res["fused"] / res[best], 3)}), flush=True)
+            del X, Y
+        del pk, packed
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +243,13 @@ def main():
                     help="scalar: one gate per token, sigmoid(x.w_g + b_g); vector: one gate per "
                          "rank component from a bottleneck MLP on X A")
     ap.add_argument("--gate-width", type=int, default=16, help="bottleneck width h of the vector gate")
+    ap.add_argument("--path", choices=["fused", "unfused", "semi"], default="fused",
+                    help="prefill only -- fused: the EC inside the GEMM's epilogue (default); unfused: gate "
+                         "step, plain W4 GEMM, then a T_g B kernel, on one stream; semi: the gate step on a "
+                         "second stream beside the GEMM, then the T_g B kernel")
+    ap.add_argument("--lut", action="store_true",
+                    help="prefill latency table: time the three paths over a grid of (M, r, N, K) and print "
+                         "one JSON line per point (no roofline / CPU legs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -180,6 +274,13 @@ def main():
         return
     w4.lib()   # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.lut:
+        latency_table(torch, w4, synth, dev)
+        return
+    if args.path != "fused" and (WORKLOADS[args.workload][2] != "prefill" or args.gate != "scalar"):
+        print("bench.py: --path unfused/semi applies to the prefill workloads with the scalar gate",
+              file=sys.stderr)
+        sys.exit(2)
     cfg_id, M, phase = WORKLOADS[args.workload]
     d = synth.make_layer(cfg_id, M, seed=args.seed, r=args.rank)
     N, K, r, G, act = d["N"], d["K"], d["r"], d["group_size"], d["act"]
@@ -226,6 +327,8 @@ def main():
         def step(i):
             p, A, B, gp = copies[i % R]
             fnv(X, p, A, B, *gp, N=N, group_size=G, workspace=ws, Y=Y)
+    elif args.path != "fused" and r > 0:
+        step = split_prefill_step(torch, w4, args.path, X, Y, copies, R, b_g, M, N, K, r, G)
     else:
         fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
 
@@ -276,6 +379,9 @@ def main():
     kdur = elapsed_ms * 1e-3 / args.steps
     reduce_name = "ec_reduce_vgate_kernel" if vector else "ec_reduce_kernel"
     kernel_name = "decode_kernel" if phase == "decode" else f"prepass_kernel + {reduce_name} + prefill_gemm_kernel (per call)"
+    if args.path != "fused" and r > 0:
+        kernel_name = (f"prepass_kernel + ec_reduce_kernel, prefill_gemm_kernel (r = 0), ec_apply_kernel "
+                       f"({args.path}, per call)")
 
     flops = layer_flops(M, N, K, r, h)
     if phase == "decode":
@@ -292,7 +398,8 @@ def main():
         peak = MFMA_PEAK_TFLOPS[act]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
-        kernel_key = f"prefill_call/{args.workload}" + ("/vector_gate" if vector else "")
+        kernel_key = f"prefill_call/{args.workload}" + ("/vector_gate" if vector else "") + \
+            ("" if args.path == "fused" else f"/{args.path}")
     roof["traffic"] = traffic_from_profiles(kernel_key)
     roof["kernel"] = kernel_name
     roof["kernel_us"] = round(kdur * 1e6, 3)
@@ -316,6 +423,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "r": r, "group_size": G,
                    "act": act, "phase": phase, "gate": "vector" if vector else "scalar",
+                   **({"path": args.path} if phase == "prefill" else {}),
                    **({"gate_width": h} if vector else {}), "weight_copies": R,
                    "launch": "hipgraph" if graph is not None else "eager",
                    "bytes_per_step": nbytes, "flops_per_step": flops},
