@@ -11,7 +11,8 @@ Method: SPEAR (gist.science technical summary), section 2.1A, effective
 weight W + B diag(gate) A with a per-token scalar gate sigmoid(x.w_g + b_g)
 (``forward``), or with one gate per rank component from a bottleneck MLP on
 T = X A (``forward_vgate``); the quantizer is the per-channel RTN baseline of
-its results section 3.1.
+its results section 3.1.  ``forward_serq`` is the single-factor correction
+over salient input channels of the SERQ summary (section 2).
 """
 from __future__ import annotations
 
@@ -70,6 +71,8 @@ def _load():
         lib.w4o_forward_vgate.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, P,
                                           P, I, P, P, P, P, P]
         lib.w4o_forward_vgate.restype = I
+        lib.w4o_forward_serq.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, P, P, P]
+        lib.w4o_forward_serq.restype = I
         lib.w4o_max_threads.argtypes = []
         lib.w4o_max_threads.restype = I
         _lib = lib
@@ -227,4 +230,38 @@ def forward_vgate(X, qc, scale, zero, A, B, G1, c1, G2, c2, *, N, K, r, h, group
     out = {"Y": Y}
     if want_parts:
         out.update(Y0=Y0, T=T, gamma=gam, C=C)
+    return out
+
+
+def forward_serq(X, qc, scale, zero, S, R, *, N, K, group_size, act="fp16", rows=None, want_parts=True):
+    """Y = X Wd^T + X[:, S] R in float64 (see w4o_forward_serq).  S: int32
+    [s] input-channel indices in [0, K); R: act bits [s, N]."""
+    lib = _load()
+    X = _c(X, np.uint16)
+    M = X.shape[0]
+    assert X.shape == (M, K)
+    qc, scale, zero = _c(qc, np.uint8), _c(scale, np.uint16), _c(zero, np.uint16)
+    G = int(group_size)
+    assert qc.shape == (N, K // 2) and scale.shape == (N, K // G) and zero.shape == (N, K // G)
+    S = np.zeros((1,), np.int32) if S is None else _c(S, np.int32)
+    s = 0 if R is None else int(np.asarray(R).shape[0])
+    R = np.zeros((1,), np.uint16) if R is None else _c(R, np.uint16)
+    if s > 0:
+        assert S.shape == (s,) and R.shape == (s, N)
+    rows_arr = None
+    n_rows = M
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+        n_rows = int(rows_arr.shape[0])
+    Y = np.empty((n_rows, N), np.float64)
+    Y0 = np.empty((n_rows, N), np.float64) if want_parts else None
+    C = np.empty((n_rows, N), np.float64) if want_parts else None
+    act_bf16 = {"fp16": 0, "bf16": 1}[act]
+    rc = lib.w4o_forward_serq(M, N, K, s, G, act_bf16, _ptr(X), _ptr(qc), _ptr(scale), _ptr(zero),
+                              _ptr(S), _ptr(R), _ptr(rows_arr), n_rows, _ptr(Y), _ptr(Y0), _ptr(C))
+    if rc != 0:
+        raise RuntimeError("oracle forward_serq failed (bad arguments)")
+    out = {"Y": Y}
+    if want_parts:
+        out.update(Y0=Y0, C=C)
     return out

@@ -432,6 +432,90 @@ int w4o_forward_vgate(int M, int N, int K, int r, int G, int act_bf16, int h,
     return bad ? -1 : 0;
 }
 
+/* Single-factor correction over salient input channels (SERQ summary,
+ * section 2, "saliency-aware error reconstruction"): the output is the
+ * quantized product plus the salient activation channels times one
+ * low-rank factor R, Y ~ X W + X_s R.  Read in the W4A16 setting of this
+ * library: X and R stay in the activation type (no activation or R
+ * quantization), and the salient channels are a list of input-channel
+ * indices S (an offline permutation makes them a contiguous block; any list,
+ * duplicates included, is accepted):
+ *
+ *   C[m,n] = sum_j X[m, S[j]] * R[j,n]        j < s
+ *   Y[m,n] = Y0[m,n] + C[m,n]
+ *
+ *   S int32 [s] with 0 <= S[j] < K;  R act bits [s][N]
+ * Other arguments and outputs as w4o_forward (Y0 and C may be NULL).
+ * Returns 0, or -1 on bad arguments or allocation failure. */
+int w4o_forward_serq(int M, int N, int K, int s, int G, int act_bf16,
+                     const uint16_t* X, const uint8_t* qc,
+                     const uint16_t* scale, const uint16_t* zero,
+                     const int32_t* S, const uint16_t* R,
+                     const int* rows, int n_rows,
+                     double* Y, double* Y0, double* C)
+{
+    if (M < 0 || N <= 0 || K <= 0 || s < 0 || G <= 0 || K % G || K % 2 || !Y)
+        return -1;
+    if (s > 0 && (!S || !R))
+        return -1;
+    for (int j = 0; j < s; ++j)
+        if (S[j] < 0 || S[j] >= K)
+            return -1;
+    if (!rows)
+        n_rows = M;
+    if (n_rows <= 0)
+        return 0;
+    int ngroups = K / G;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)n_rows * K);
+    if (!xd)
+        return -1;
+    for (int i = 0; i < n_rows; ++i) {
+        int m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) {
+            free(xd);
+            return -1;
+        }
+        for (int k = 0; k < K; ++k)
+            xd[(size_t)i * K + k] = act_to_double(X[(size_t)m * K + k], act_bf16);
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!wd) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int n = 0; n < N; ++n) {
+            if (!wd)
+                continue;
+            for (int k = 0; k < K; ++k) {
+                int gi = k / G;
+                double sc = w4o_half_to_double(scale[(size_t)n * ngroups + gi]);
+                double z = w4o_half_to_double(zero[(size_t)n * ngroups + gi]);
+                wd[k] = ((double)code_at(qc, K, n, k) - z) * sc;
+            }
+            for (int i = 0; i < n_rows; ++i) {
+                const double* x = xd + (size_t)i * K;
+                double y0 = 0.0;
+                for (int k = 0; k < K; ++k)
+                    y0 += x[k] * wd[k];
+                double c = 0.0;
+                for (int j = 0; j < s; ++j)
+                    c += x[S[j]] * act_to_double(R[(size_t)j * N + n], act_bf16);
+                size_t o = (size_t)i * N + n;
+                Y[o] = y0 + c;
+                if (Y0) Y0[o] = y0;
+                if (C) C[o] = c;
+            }
+        }
+        free(wd);
+    }
+    free(xd);
+    return bad ? -1 : 0;
+}
+
 /* Threads an OpenMP region of this library will use. */
 int w4o_max_threads(void)
 {

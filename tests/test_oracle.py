@@ -393,3 +393,57 @@ def test_vgate_rows_and_token_permutation():
     rows = [3, 0, 8, 3]
     sub = vg_run(L["M"], L["N"], L["K"], L["r"], L["G"], h, L["Xb"], *args, rows=rows)
     assert np.array_equal(sub["Y"], full["Y"][rows])
+
+
+# ---------------------------------------------------------------- salient-channel correction
+
+def sq_run(L, S, Rb, rows=None):
+    return oracle.forward_serq(L["Xb"], L["qc"], L["s"], L["z"], S, Rb, N=L["N"], K=L["K"],
+                               group_size=L["G"], rows=rows)
+
+
+def test_serq_empty_or_zero_factor_is_plain_w4():
+    L = vg_layer(np.random.default_rng(31))
+    base = run(L["M"], L["N"], L["K"], 0, L["G"], L["Xb"], L["qc"], L["s"], L["z"], None, None, None, 0.0)
+    none = sq_run(L, None, None)
+    assert np.array_equal(none["Y"], base["Y"])
+    S = np.array([3, 7, 7, 200], np.int32)
+    zero = sq_run(L, S, f16bits(np.zeros((4, L["N"]))))
+    assert np.array_equal(zero["Y"], base["Y"])
+
+
+def test_serq_all_channels_is_a_full_correction():
+    """S = every channel in order: Y = X (Wd^T + R) with R a full K x N matrix."""
+    L = vg_layer(np.random.default_rng(32))
+    rng = np.random.default_rng(33)
+    Rb = f16bits(rng.standard_normal((L["K"], L["N"])) * 0.01)
+    out = sq_run(L, np.arange(L["K"], dtype=np.int32), Rb)
+    ref = np.matmul(L["X"], L["W"].T + Rb.view(np.float16).astype(np.float64))
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
+
+
+def test_serq_gather_against_numpy():
+    """An unsorted subset with a repeated channel: C = X[:, S] R by numpy
+    indexing and matmul; the split Y = Y0 + C; rows of R follow S."""
+    L = vg_layer(np.random.default_rng(34))
+    rng = np.random.default_rng(35)
+    S = np.array([250, 3, 17, 3, 128, 0, 255], np.int32)
+    Rb = f16bits(rng.standard_normal((len(S), L["N"])) * 0.05)
+    out = sq_run(L, S, Rb)
+    C = np.matmul(L["X"][:, S], Rb.view(np.float16).astype(np.float64))
+    np.testing.assert_allclose(out["C"], C, rtol=1e-12, atol=1e-12 * np.abs(C).max())
+    ref = np.matmul(L["X"], L["W"].T) + C
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-11, atol=1e-11 * np.abs(ref).max())
+    # permuting the list and R's rows together changes nothing but the order of the sum
+    p = rng.permutation(len(S))
+    perm = sq_run(L, S[p], Rb[p])
+    np.testing.assert_allclose(perm["Y"], out["Y"], rtol=1e-13, atol=1e-13 * np.abs(out["Y"]).max())
+    rows = [4, 0, 4]
+    sub = sq_run(L, S, Rb, rows=rows)
+    assert np.array_equal(sub["Y"], out["Y"][rows])
+
+
+def test_serq_rejects_out_of_range_channels():
+    L = vg_layer(np.random.default_rng(36))
+    with pytest.raises(RuntimeError):
+        sq_run(L, np.array([0, L["K"]], np.int32), f16bits(np.zeros((2, L["N"]))))
