@@ -167,6 +167,32 @@ int w4ec_linear_prefill_vgate(const void* X, const void* packed, const void* A, 
                               int h, void* Y, int M, int N, int K, int r, int group_size,
                               int act_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Single-factor correction over salient input channels (SERQ summary,
+ * "Saliency-Aware Error Reconstruction for LLM Low-Bit Quantization",
+ * section 2): the quantized product plus the activation channels of the
+ * salient weight rows times one low-rank factor R,
+ *
+ *   Y[m,n] = sum_k X[m,k] Wd[n,k] + sum_j X[m, S[j]] R[j,n]      j < s
+ *
+ * read in the W4A16 setting of this library (X and R in the activation
+ * type; no activation or R quantization).  The page's offline permutation
+ * makes the salient channels one contiguous block; any index list works.
+ *   S  device int32 [s], channel indices in [0, K) (duplicates allowed);
+ *      an index outside that range is clamped to it and leaves a nonzero
+ *      word in the workspace's state region (the result is then undefined)
+ *   R  device act [s, N] (2-byte aligned)
+ *   s  0 <= s <= 256; s == 0 is the plain W4 layer (S, R ignored)
+ * The decode form needs no EC workgroups: each output workgroup gathers its
+ * operand from X itself.  Workspace as w4ec_workspace_bytes(M, N, K, s, G);
+ * other arguments and limits as w4ec_linear_decode / w4ec_linear_prefill. */
+int w4ec_linear_decode_serq(const void* X, const void* packed, const int32_t* S, const void* R,
+                            void* Y, int M, int N, int K, int s, int group_size, int act_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+int w4ec_linear_prefill_serq(const void* X, const void* packed, const int32_t* S, const void* R,
+                             void* Y, int M, int N, int K, int s, int group_size, int act_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Unfused and semi-fused prefill (the SPEAR summary, section 2.2A, runs the
  * EC beside the low-bit GEMM in the prefill phase and adds its product
  * afterwards).  These two calls split the EC off the fused prefill so that a

@@ -172,3 +172,26 @@ def test_prefill_ec_split_argument_errors():
     assert apply(B=y) == E.W4EC_ERR_INVALID_ARG                    # aliases Y
     assert apply(K=96) == E.W4EC_ERR_UNSUPPORTED
     assert apply(ws=P(FAKE + 0x600010)) == E.W4EC_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("name", ["w4ec_linear_decode_serq", "w4ec_linear_prefill_serq"])
+def test_serq_argument_errors(name):
+    fn = getattr(w4.lib(), name)
+    P = ctypes.c_void_p
+    E = w4
+
+    def c(X=FAKE, packed=FAKE + 0x100000, S=FAKE + 0x200000, R=FAKE + 0x300000, Y=FAKE + 0x500000,
+          M=4, N=512, K=512, s=8, G=512, act=0, ws=FAKE + 0x600000, wsb=1 << 30):
+        p = lambda v: P(v) if v else None
+        return fn(p(X), p(packed), p(S), p(R), p(Y), M, N, K, s, G, act, p(ws), wsb, None)
+
+    assert c(S=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(R=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(S=FAKE + 0x200002) == E.W4EC_ERR_INVALID_ARG        # not 4-byte aligned
+    assert c(R=FAKE + 0x300001) == E.W4EC_ERR_INVALID_ARG
+    assert c(s=257) == E.W4EC_ERR_UNSUPPORTED
+    assert c(s=-1) == E.W4EC_ERR_INVALID_ARG
+    assert c(M=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(X=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(R=FAKE + 0x500000) == E.W4EC_ERR_INVALID_ARG        # R aliases Y
+    assert c(ws=0) == E.W4EC_ERR_WORKSPACE

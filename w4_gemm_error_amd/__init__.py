@@ -24,6 +24,7 @@ __all__ = [
     "w4ec_linear_decode", "w4ec_linear_prefill", "w4ec_linear",
     "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
     "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
+    "w4ec_linear_decode_serq", "w4ec_linear_prefill_serq",
     "PackedLayer",
 ]
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.w4ec_prefill_ec_gate.restype = I
         L.w4ec_prefill_ec_apply.argtypes = [P, P, I, I, I, I, I, P, Z, P]
         L.w4ec_prefill_ec_apply.restype = I
+        for name in ("w4ec_linear_decode_serq", "w4ec_linear_prefill_serq"):
+            fn = getattr(L, name)
+            fn.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+            fn.restype = I
         for name in ("w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"):
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P, Z, P]
@@ -263,6 +268,37 @@ def w4ec_linear_prefill_vgate(X, packed, A, B, G1, c1, G2, c2, *, N, group_size,
     """The vector-gate layer for any M >= 1 (prepass, per-token bottleneck, tiled MFMA GEMM)."""
     return _layer_call_vgate("w4ec_linear_prefill_vgate", X, packed, A, B, G1, c1, G2, c2, N, group_size,
                              workspace, Y, stream)
+
+
+def _layer_call_serq(name, X, packed, S, R, N, group_size, workspace, Y, stream):
+    torch = _torch()
+    _need_cuda(X, "X", (torch.float16, torch.bfloat16))
+    act = X.dtype
+    M, K = X.shape
+    s = 0 if R is None else int(R.shape[0])
+    _need_cuda(S, "S", torch.int32)
+    _need_cuda(R, "R", act)
+    _need_cuda(packed, "packed", torch.uint8)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=act, device=X.device)
+    _need_cuda(Y, "Y", act)
+    if workspace is None:
+        nb = w4ec_workspace_bytes(M, N, K, s, group_size)
+        workspace = torch.zeros(max(nb, 256), dtype=torch.uint8, device=X.device)
+    st = getattr(lib(), name)(_ptr(X), _ptr(packed), _ptr(S), _ptr(R), _ptr(Y), M, N, K, s, int(group_size),
+                              _act_code(act), _ptr(workspace), workspace.numel(), _stream_handle(stream))
+    _check(st, name)
+    return Y
+
+
+def w4ec_linear_decode_serq(X, packed, S, R, *, N, group_size, workspace=None, Y=None, stream=None):
+    """Y = X Wd^T + X[:, S] R (salient-channel correction), 1 <= M <= 16; S int32 [s], R [s, N]."""
+    return _layer_call_serq("w4ec_linear_decode_serq", X, packed, S, R, N, group_size, workspace, Y, stream)
+
+
+def w4ec_linear_prefill_serq(X, packed, S, R, *, N, group_size, workspace=None, Y=None, stream=None):
+    """Y = X Wd^T + X[:, S] R (salient-channel correction) for any M >= 1."""
+    return _layer_call_serq("w4ec_linear_prefill_serq", X, packed, S, R, N, group_size, workspace, Y, stream)
 
 
 def w4ec_prefill_ec_workspace_bytes(M: int, K: int, r: int) -> int:

@@ -132,6 +132,7 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
     // tile counters exist only for split work, which is chosen only while the
     // workgroup count is below TARGET_WGS: at most 256 of them
     p.off_gemm_cnt = OFF_GEMM_CNT;
+    p.off_flags = OFF_DEC_FLAGS;
 
     size_t off = CTRL_BYTES;
     p.off_pre_partial = off;
@@ -313,7 +314,7 @@ LayerArgs layer_args(const void* X, const void* packed, const void* A, const voi
 int decode_entry(const void* X, const void* packed, const void* A, const void* B,
                  const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
                  int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
-                 void* stream, const VGate* vg)
+                 void* stream, const VGate* vg, const int32_t* S = nullptr)
 {
     if (M > DECODE_MAX_M)
         return W4EC_ERR_UNSUPPORTED;
@@ -336,13 +337,22 @@ int decode_entry(const void* X, const void* packed, const void* A, const void* B
         return W4EC_ERR_INVALID_ARG;
     LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
                              workspace, vg);
+    if (S && r > 0) {
+        // salient channels: the main workgroups gather their own operand,
+        // no EC workgroups and no hand-over
+        a.S = S;
+        a.A = nullptr;
+        a.w_g = nullptr;
+        p.P = 0;
+        p.stage_first = 0;
+    }
     return hip_status(launch_decode(a, p, (hipStream_t)stream));
 }
 
 int prefill_entry(const void* X, const void* packed, const void* A, const void* B,
                   const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
                   int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
-                  void* stream, const VGate* vg)
+                  void* stream, const VGate* vg, const int32_t* S = nullptr)
 {
     PrefillPlan p{};
     size_t need = 0;
@@ -362,6 +372,11 @@ int prefill_entry(const void* X, const void* packed, const void* A, const void* 
         return W4EC_ERR_INVALID_ARG;
     LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
                              workspace, vg);
+    if (S && r > 0) {
+        a.S = S;
+        a.A = nullptr;
+        a.w_g = nullptr;
+    }
     return hip_status(launch_prefill(a, p, (hipStream_t)stream));
 }
 
@@ -433,6 +448,37 @@ int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, in
         return W4EC_ERR_WORKSPACE;
     ApplyArgs a{Y, B, M, N, r, act_dtype, (char*)workspace};
     return hip_status(launch_prefill_ec_apply(a, ec_plan(M, K, r), (hipStream_t)stream));
+}
+
+// Salient-channel correction: the layer's checks with R standing in for A
+// (it is the operand whose presence r > 0 requires), plus S.
+static int check_serq(const int32_t* S, const void* R, int s)
+{
+    if (s > 0 && (!S || !R || !aligned(S, 4) || !aligned(R, 2)))
+        return W4EC_ERR_INVALID_ARG;
+    return W4EC_OK;
+}
+
+int w4ec_linear_decode_serq(const void* X, const void* packed, const int32_t* S, const void* R,
+                            void* Y, int M, int N, int K, int s, int group_size, int act_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_serq(S, R, s);
+    if (rc != W4EC_OK)
+        return rc;
+    return decode_entry(X, packed, s > 0 ? X : nullptr, R, nullptr, 0.0f, Y, M, N, K, s, group_size,
+                        act_dtype, workspace, workspace_bytes, stream, nullptr, S);
+}
+
+int w4ec_linear_prefill_serq(const void* X, const void* packed, const int32_t* S, const void* R,
+                             void* Y, int M, int N, int K, int s, int group_size, int act_dtype,
+                             void* workspace, size_t workspace_bytes, void* stream)
+{
+    int rc = check_serq(S, R, s);
+    if (rc != W4EC_OK)
+        return rc;
+    return prefill_entry(X, packed, s > 0 ? X : nullptr, R, nullptr, 0.0f, Y, M, N, K, s, group_size,
+                         act_dtype, workspace, workspace_bytes, stream, nullptr, S);
 }
 
 int w4ec_linear_decode_vgate(const void* X, const void* packed, const void* A, const void* B,

@@ -70,6 +70,7 @@ struct DecodeKArgs {
     const uint16_t* c2;  // act [r]
     int h;
     int vg_staged;       // the gate parameters are copied to LDS (they fit)
+    const int32_t* S;    // salient-channel correction: T = X[:, S] (no EC role), or null
 };
 
 __device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
@@ -657,7 +658,28 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     const int slot = mb % DEC_NREP;
     uint64_t* sdata = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * DEC_REP_DATA_STRIDE);
     u32x4 af[8];
-    if (a.r > 0 && w < CB) {
+    // salient channels (SERQ summary, section 2): the operand is the gather
+    // X[token][S[j]], made by the whole workgroup into LDS ([M][r_pad], past
+    // the parked B) -- no EC role and no hand-over.  An index outside [0, K)
+    // is clamped and raises flags[3].
+    uint16_t* tgl = bl + (size_t)CB * a.r_pad * PANEL_N;
+    if (a.r > 0 && a.S) {
+        bool bad = false;
+#pragma unroll 4
+        for (int e = tid; e < M * a.r_pad; e += DEC_THREADS) {
+            const int m = e / a.r_pad, j = e - m * a.r_pad;
+            uint16_t v = 0;
+            if (j < a.r) {
+                int idx = a.S[j];
+                bad |= idx < 0 || idx >= K;
+                idx = min(max(idx, 0), K - 1);
+                v = a.X[(size_t)m * K + idx];
+            }
+            tgl[e] = v;
+        }
+        if (bad)
+            atomic_store_dev(&a.flags[3], 1u);
+    } else if (a.r > 0 && w < CB) {
         const uint64_t* src = sdata + (row * a.r_pad + koff) / 4;
         uint32_t it = 0;
         // read all of them, and again while any has not landed
@@ -687,6 +709,13 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
     }
     __syncthreads();
+    if (a.r > 0 && a.S && w < CB) {
+#pragma unroll
+        for (int rs = 0; rs < 8; ++rs)
+            if (rs < nsteps)
+                af[rs] = xrow ? *reinterpret_cast<const u32x4*>(tgl + (size_t)row * a.r_pad + 32 * rs + koff)
+                              : (u32x4){0u, 0u, 0u, 0u};
+    }
 
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
@@ -722,7 +751,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // The last reader of a slot returns the slot, and its share of the EC
     // partial sums (whose reduction finished before any slot was written),
     // to zero for the next call.
-    if (a.r > 0) {
+    if (a.r > 0 && !a.S) {
         __shared__ int s_last;
         if (tid == 0) {
             const int readers = a.n_main / DEC_NREP + (slot < a.n_main % DEC_NREP ? 1 : 0);
@@ -763,9 +792,10 @@ constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS
 
 bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
 
-static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r)
+static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r, bool gather)
 {
-    return main_b_offset(M, K, p.xlds, p.CB) + (r > 0 ? (size_t)p.CB * p.r_pad * PANEL_N * 2 : 0);
+    return main_b_offset(M, K, p.xlds, p.CB) + (r > 0 ? (size_t)p.CB * p.r_pad * PANEL_N * 2 : 0) +
+           (r > 0 && gather ? (size_t)M * p.r_pad * 2 : 0);
 }
 
 // LDS of the EC role: the staged slice and gate vector, then the final reduction
@@ -789,7 +819,7 @@ template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
 static hipError_t launch_decode_t(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>;
-    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r), ec_lds_bytes(p, k.M, k.r));
+    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr), ec_lds_bytes(p, k.M, k.r));
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
@@ -851,6 +881,7 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.G2 = (const uint16_t*)a.G2; k.c2 = (const uint16_t*)a.c2;
     k.h = a.r > 0 ? a.h : 0;
     k.vg_staged = 0;
+    k.S = a.S;
     if (k.h > 0) {
         // stage the gate parameters when they fit in the EC role's LDS
         const size_t base = ((size_t)2 * p.r_pad + VG_HMAX + VG_THREADS) * 4 + (size_t)p.r_pad / 4 * 8;

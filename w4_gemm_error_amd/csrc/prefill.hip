@@ -300,6 +300,40 @@ void ec_reduce_vgate_kernel(EcReduceKArgs a)
         tg[(size_t)(e / pad) * a.r_pad + r + e % pad] = f32_to_act<ACT>(0.0f);
 }
 
+// ---------------------------------------------------------------- salient channels
+//
+// Single-factor correction over salient input channels (SERQ summary,
+// section 2): T_g is the gather X[:, S] of s channels, laid out like the
+// gated rank-r activations ([rows][r_pad], zero past s and past M), so the
+// GEMM's epilogue adds T_g R unchanged.  An index outside [0, K) is clamped
+// and raises flags[3].
+struct GatherKArgs {
+    const uint16_t* X;
+    const int32_t* S;
+    uint16_t* tg;
+    uint32_t* flags;
+    int M, K, s, r_pad, rows;
+};
+
+__global__ __launch_bounds__(PF_THREADS)
+void serq_gather_kernel(GatherKArgs a)
+{
+    const int e = blockIdx.x * PF_THREADS + threadIdx.x;
+    if (e >= a.rows * a.r_pad)
+        return;
+    const int m = e / a.r_pad, j = e - m * a.r_pad;
+    uint16_t v = 0;
+    if (m < a.M && j < a.s) {
+        int idx = a.S[j];
+        if (idx < 0 || idx >= a.K) {
+            atomic_store_dev(&a.flags[3], 1u);
+            idx = min(max(idx, 0), a.K - 1);
+        }
+        v = a.X[(size_t)m * a.K + idx];
+    }
+    a.tg[e] = v;
+}
+
 // ---------------------------------------------------------------- unfused EC
 //
 // The correction as a kernel of its own, for the unfused and semi-fused
@@ -941,7 +975,29 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
     uint16_t* tg = (uint16_t*)(a.ws + p.off_tg);
     const bool sums = a.act == ACT_BF16 && a.G == a.K;   // the GEMM's bf16 zero-point term
     float* rowsum = (float*)(a.ws + p.off_rowsum);
-    if (a.r > 0 || sums) {
+    if (a.S) {
+        // salient channels: activation sums only if the GEMM needs them
+        // (the prepass without a compensator), then the gather
+        if (sums) {
+            LayerArgs b = a;
+            b.r = 0; b.A = nullptr; b.w_g = nullptr; b.S = nullptr;
+            hipError_t e = launch_prefill_ec_part(b, p, true, st);   // its slices fit r = 0 too
+            if (e != hipSuccess)
+                return e;
+        }
+        GatherKArgs ga;
+        ga.X = (const uint16_t*)a.X;
+        ga.S = a.S;
+        ga.tg = tg;
+        ga.flags = (uint32_t*)(a.ws + p.off_flags);
+        ga.M = a.M; ga.K = a.K; ga.s = a.r; ga.r_pad = p.r_pad;
+        ga.rows = p.pre_mt * 64;
+        const int n = ga.rows * ga.r_pad;
+        hipLaunchKernelGGL(serq_gather_kernel, dim3((n + PF_THREADS - 1) / PF_THREADS), dim3(PF_THREADS), 0, st, ga);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    } else if (a.r > 0 || sums) {
         hipError_t e = launch_prefill_ec_part(a, p, sums, st);
         if (e != hipSuccess)
             return e;

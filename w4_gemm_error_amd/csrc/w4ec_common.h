@@ -378,7 +378,7 @@ struct PrefillPlan {
     int pre_ks;     // prepass split over K
     int pre_kc;     // k per prepass split (multiple of 64, <= 512)
     int r_pad, Mpad;
-    size_t off_gemm_cnt, off_pre_partial, off_tg, off_rowsum, off_gemm_partial, bytes;
+    size_t off_flags, off_gemm_cnt, off_pre_partial, off_tg, off_rowsum, off_gemm_partial, bytes;
 };
 
 }  // namespace w4ec

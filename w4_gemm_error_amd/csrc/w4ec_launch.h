@@ -33,6 +33,9 @@ struct LayerArgs {
     const void* G2;   // act [h][r]
     const void* c2;   // act [r]
     int h;
+    // single-factor correction over salient channels (S non-null): T_g is
+    // the gather X[:, S] (r = s channels), B is the factor R; no gate
+    const int32_t* S; // [s] input-channel indices
 };
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
