@@ -247,6 +247,9 @@ def main():
                     help="prefill only -- fused: the EC inside the GEMM's epilogue (default); unfused: gate "
                          "step, plain W4 GEMM, then a T_g B kernel, on one stream; semi: the gate step on a "
                          "second stream beside the GEMM, then the T_g B kernel")
+    ap.add_argument("--method", choices=["spear", "serq"], default="spear",
+                    help="spear: the input-adaptive EC (default); serq: the single-factor correction over "
+                         "the salient input channels (the config's outlier channels), X[:, S] R")
     ap.add_argument("--lut", action="store_true",
                     help="prefill latency table: time the three paths over a grid of (M, r, N, K) and print "
                          "one JSON line per point (no roofline / CPU legs)")
@@ -296,7 +299,18 @@ def main():
     del Wt, q, s, z
     vector = args.gate == "vector" and r > 0
     h = args.gate_width if vector else 0
-    if r > 0 and vector:
+    serq = args.method == "serq"
+    if serq and (vector or args.path != "fused"):
+        print("bench.py: --method serq takes no --gate vector or --path", file=sys.stderr)
+        sys.exit(2)
+    if serq:
+        S_host = np.asarray(d["outlier_channels"], dtype=np.int32)
+        r = len(S_host)
+        R_bits = synth.to_act_bits(np.random.default_rng(args.seed).normal(0.0, 0.01, (r, N)), act)
+        A0, B0 = torch.from_numpy(S_host).to(dev), dev_act(R_bits)
+        wg0 = None
+        ec_elems = B0.numel() + r * 2          # R, and S as int32 (two halves' worth)
+    elif r > 0 and vector:
         vg = synth.make_vgate(r, h, act, seed=args.seed, t_std=0.02 * K ** 0.5)
         A0, B0 = dev_act(d["A"]), dev_act(d["B"])
         wg0 = tuple(dev_act(vg[k]) for k in ("G1", "c1", "G2", "c2"))
@@ -308,6 +322,9 @@ def main():
         A0 = B0 = wg0 = None
         ec_elems = 0
     nbytes = layer_bytes(M, N, K, r, G, has_gate=r > 0, h=h)
+    if serq:
+        # codes + s/z + X + Y + R [s, N] + S (int32): no A and no gate
+        nbytes = N * K // 2 + N * (K // G) * 4 + M * K * 2 + M * N * 2 + r * N * 2 + r * 4
     weight_bytes = packed0.numel() + ec_elems * 2
     R = max(1, -(-2 * MALL_BYTES // weight_bytes))
     def clone(t):
@@ -321,7 +338,13 @@ def main():
     Y = torch.empty((M, N), dtype=tdt, device=dev)
     ws = torch.zeros(max(w4.w4ec_workspace_bytes(M, N, K, r, G), 256), dtype=torch.uint8, device=dev)
     b_g = d["b_g"]
-    if vector:
+    if serq:
+        fns = w4.w4ec_linear_decode_serq if phase == "decode" else w4.w4ec_linear_prefill_serq
+
+        def step(i):
+            p, Sd, Rd, _ = copies[i % R]
+            fns(X, p, Sd, Rd, N=N, group_size=G, workspace=ws, Y=Y)
+    elif vector:
         fnv = w4.w4ec_linear_decode_vgate if phase == "decode" else w4.w4ec_linear_prefill_vgate
 
         def step(i):
@@ -382,15 +405,20 @@ def main():
     if args.path != "fused" and r > 0:
         kernel_name = (f"prepass_kernel + ec_reduce_kernel, prefill_gemm_kernel (r = 0), ec_apply_kernel "
                        f"({args.path}, per call)")
+    if serq and phase == "prefill":
+        kernel_name = "serq_gather_kernel + prefill_gemm_kernel (per call)"
 
     flops = layer_flops(M, N, K, r, h)
+    if serq:
+        flops = 2 * M * N * K + 2 * M * r * N + 2 * M * N      # main product, X[:, S] R, add
     if phase == "decode":
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
         achieved = nbytes / kdur / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        kernel_key = f"decode_kernel/{args.workload}" + ("/vector_gate" if vector else "")
+        kernel_key = f"decode_kernel/{args.workload}" + ("/vector_gate" if vector else "") + \
+            ("/serq" if serq else "")
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -399,13 +427,13 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4)}
         kernel_key = f"prefill_call/{args.workload}" + ("/vector_gate" if vector else "") + \
-            ("" if args.path == "fused" else f"/{args.path}")
+            ("" if args.path == "fused" else f"/{args.path}") + ("/serq" if serq else "")
     roof["traffic"] = traffic_from_profiles(kernel_key)
     roof["kernel"] = kernel_name
     roof["kernel_us"] = round(kdur * 1e6, 3)
 
     cpu = None
-    if not args.no_cpu and not vector:
+    if not args.no_cpu and not vector and not serq:
         cpu = cpu_baseline(d, phase, args.cpu_budget)
 
     out = {
@@ -422,7 +450,8 @@ def main():
         "dtype": act,
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "r": r, "group_size": G,
-                   "act": act, "phase": phase, "gate": "vector" if vector else "scalar",
+                   "act": act, "phase": phase, "method": args.method,
+                   **({"salient_channels": r} if serq else {"gate": "vector" if vector else "scalar"}),
                    **({"path": args.path} if phase == "prefill" else {}),
                    **({"gate_width": h} if vector else {}), "weight_copies": R,
                    "launch": "hipgraph" if graph is not None else "eager",
