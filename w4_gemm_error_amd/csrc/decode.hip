@@ -462,6 +462,21 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // blocks, 16-byte chunks of 8 columns) are loaded first, so that they do
     // not queue behind the weight stream; they stay in registers during the
     // stream and are parked in LDS after it.
+    // Salient channels with X staged in LDS: the indices are this thread's
+    // first loads (so waiting for them waits for nothing else), and the
+    // gather X[m][S[j]] runs from LDS as soon as X is staged, under the
+    // weight stream, into the operand area past the parked B.
+    constexpr int SG = 4;                            // gather elements per thread (M <= 4, r_pad <= 256)
+    int sg[SG];
+    const bool lds_gather = XLDS && a.S != nullptr && a.r > 0;
+    if (lds_gather) {
+#pragma unroll
+        for (int i = 0; i < SG; ++i) {
+            const int e = tid + DEC_THREADS * i;
+            const int j = e % a.r_pad;
+            sg[i] = (e < M * a.r_pad && j < a.r) ? a.S[j] : 0;
+        }
+    }
     u32x4 bstage[2 * CB];
     {
         const int nbch = CB * a.r_pad * 2;
@@ -521,15 +536,38 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // keep the issue order: the scheduler must not sink these loads below the
     // weight loads (each wait would then cover the whole ring)
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (XLDS && STAGE_FIRST)
+    uint16_t* tgl = reinterpret_cast<uint16_t*>(smem + main_b_offset(M, K, XLDS, CB)) + (size_t)CB * a.r_pad * PANEL_N;
+    auto gather_lds = [&]() {
+        bool bad = false;
+#pragma unroll
+        for (int i = 0; i < SG; ++i) {
+            const int e = tid + DEC_THREADS * i;
+            if (e < M * a.r_pad) {
+                const int m = e / a.r_pad, j = e - m * a.r_pad;
+                int idx = sg[i];
+                bad |= j < a.r && (idx < 0 || idx >= K);
+                idx = min(max(idx, 0), K - 1);
+                tgl[e] = j < a.r ? xs[(size_t)m * K + idx] : (uint16_t)0;
+            }
+        }
+        if (bad)
+            atomic_store_dev(&a.flags[3], 1u);
+    };
+    if constexpr (XLDS && STAGE_FIRST) {
         store_x();
+        if (lds_gather)
+            gather_lds();
+    }
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
         issue(u, u);
         __builtin_amdgcn_sched_barrier(0);   // slot u is issued u-th
     }
-    if constexpr (XLDS && !STAGE_FIRST)
+    if constexpr (XLDS && !STAGE_FIRST) {
         store_x();
+        if (lds_gather)
+            gather_lds();
+    }
 
     floatx4 acc[CB], accg[CB];
     float s_cur[CB];
@@ -662,8 +700,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // X[token][S[j]], made by the whole workgroup into LDS ([M][r_pad], past
     // the parked B) -- no EC role and no hand-over.  An index outside [0, K)
     // is clamped and raises flags[3].
-    uint16_t* tgl = bl + (size_t)CB * a.r_pad * PANEL_N;
-    if (a.r > 0 && a.S) {
+    if (a.r > 0 && a.S && !lds_gather) {
         bool bad = false;
 #pragma unroll 4
         for (int e = tid; e < M * a.r_pad; e += DEC_THREADS) {
@@ -679,7 +716,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
         if (bad)
             atomic_store_dev(&a.flags[3], 1u);
-    } else if (a.r > 0 && w < CB) {
+    } else if (a.r > 0 && w < CB && !a.S) {
         const uint64_t* src = sdata + (row * a.r_pad + koff) / 4;
         uint32_t it = 0;
         // read all of them, and again while any has not landed
