@@ -12,7 +12,9 @@ weight W + B diag(gate) A with a per-token scalar gate sigmoid(x.w_g + b_g)
 (``forward``), or with one gate per rank component from a bottleneck MLP on
 T = X A (``forward_vgate``); the quantizer is the per-channel RTN baseline of
 its results section 3.1.  ``forward_serq`` is the single-factor correction
-over salient input channels of the SERQ summary (section 2).
+over salient input channels of the SERQ summary (section 2); ``forward_xfp``
+the per-channel codebook weights with a sparse outlier residual of the XFP
+summary (section 2).
 """
 from __future__ import annotations
 
@@ -73,6 +75,8 @@ def _load():
         lib.w4o_forward_vgate.restype = I
         lib.w4o_forward_serq.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, P, P, P]
         lib.w4o_forward_serq.restype = I
+        lib.w4o_forward_xfp.argtypes = [I, I, I, I, P, P, P, P, P, P, P, I, P]
+        lib.w4o_forward_xfp.restype = I
         lib.w4o_max_threads.argtypes = []
         lib.w4o_max_threads.restype = I
         _lib = lib
@@ -265,3 +269,31 @@ def forward_serq(X, qc, scale, zero, S, R, *, N, K, group_size, act="fp16", rows
     if want_parts:
         out.update(Y0=Y0, C=C)
     return out
+
+
+def forward_xfp(X, qc, cb, row_ptr, col_idx, val, *, N, K, act="fp16", rows=None):
+    """Y = X Wh^T with Wh[n,k] = cb[n][idx[n,k]] + (sparse residual)[n,k]
+    (see w4o_forward_xfp).  qc: 4-bit indices uint8 [N, K/2]; cb: fp16 bits
+    [N, 16]; row_ptr int32 [N+1], col_idx int32 [nnz], val fp16 bits [nnz]."""
+    lib = _load()
+    X = _c(X, np.uint16)
+    M = X.shape[0]
+    assert X.shape == (M, K)
+    qc, cb = _c(qc, np.uint8), _c(cb, np.uint16)
+    row_ptr, col_idx, val = _c(row_ptr, np.int32), _c(col_idx, np.int32), _c(val, np.uint16)
+    assert qc.shape == (N, K // 2) and cb.shape == (N, 16) and row_ptr.shape == (N + 1,)
+    assert col_idx.shape == val.shape == (int(row_ptr[-1]),)
+    if col_idx.size == 0:
+        col_idx, val = np.zeros(1, np.int32), np.zeros(1, np.uint16)
+    rows_arr = None
+    n_rows = M
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+        n_rows = int(rows_arr.shape[0])
+    Y = np.empty((n_rows, N), np.float64)
+    act_bf16 = {"fp16": 0, "bf16": 1}[act]
+    rc = lib.w4o_forward_xfp(M, N, K, act_bf16, _ptr(X), _ptr(qc), _ptr(cb), _ptr(row_ptr),
+                             _ptr(col_idx), _ptr(val), _ptr(rows_arr), n_rows, _ptr(Y))
+    if rc != 0:
+        raise RuntimeError("oracle forward_xfp failed (bad arguments)")
+    return {"Y": Y}

@@ -516,6 +516,81 @@ int w4o_forward_serq(int M, int N, int K, int s, int G, int act_bf16,
     return bad ? -1 : 0;
 }
 
+/* Codebook weights with a sparse outlier residual (XFP summary, section 2,
+ * "sparse outlier separation" and "adaptive learned codebooks", per-channel
+ * mode): every weight is an index into its output channel's codebook of
+ * 2^4 fp16 entries, plus an fp16 residual at the few outlier positions:
+ *
+ *   Wh[n,k] = cb[n][idx[n,k]] + sum of val[e] over the entries e of row n
+ *             whose column is k (compressed sparse rows: row_ptr, col_idx)
+ *   Y[m,n]  = sum_k X[m,k] * Wh[n,k]
+ *
+ *   idx   canonical 4-bit array [N][K/2] (as the W4 codes)
+ *   cb    fp16 bits [N][16]
+ *   row_ptr int32 [N+1], col_idx int32 [nnz] in [0, K), val fp16 bits [nnz]
+ * rows / n_rows as w4o_forward.  Returns 0, or -1 on bad arguments. */
+int w4o_forward_xfp(int M, int N, int K, int act_bf16,
+                    const uint16_t* X, const uint8_t* qc, const uint16_t* cb,
+                    const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* val,
+                    const int* rows, int n_rows, double* Y)
+{
+    if (M < 0 || N <= 0 || K <= 0 || K % 2 || !Y || !X || !qc || !cb || !row_ptr)
+        return -1;
+    if (row_ptr[0] != 0)
+        return -1;
+    for (int n = 0; n < N; ++n) {
+        if (row_ptr[n + 1] < row_ptr[n])
+            return -1;
+        for (int e = row_ptr[n]; e < row_ptr[n + 1]; ++e)
+            if (col_idx[e] < 0 || col_idx[e] >= K)
+                return -1;
+    }
+    if (!rows)
+        n_rows = M;
+    if (n_rows <= 0)
+        return 0;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)n_rows * K);
+    if (!xd)
+        return -1;
+    for (int i = 0; i < n_rows; ++i) {
+        int m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) {
+            free(xd);
+            return -1;
+        }
+        for (int k = 0; k < K; ++k)
+            xd[(size_t)i * K + k] = act_to_double(X[(size_t)m * K + k], act_bf16);
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!wd) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int n = 0; n < N; ++n) {
+            if (!wd)
+                continue;
+            for (int k = 0; k < K; ++k)
+                wd[k] = w4o_half_to_double(cb[(size_t)n * 16 + code_at(qc, K, n, k)]);
+            for (int e = row_ptr[n]; e < row_ptr[n + 1]; ++e)
+                wd[col_idx[e]] += w4o_half_to_double(val[e]);
+            for (int i = 0; i < n_rows; ++i) {
+                const double* x = xd + (size_t)i * K;
+                double y = 0.0;
+                for (int k = 0; k < K; ++k)
+                    y += x[k] * wd[k];
+                Y[(size_t)i * N + n] = y;
+            }
+        }
+        free(wd);
+    }
+    free(xd);
+    return bad ? -1 : 0;
+}
+
 /* Threads an OpenMP region of this library will use. */
 int w4o_max_threads(void)
 {

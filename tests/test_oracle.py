@@ -447,3 +447,69 @@ def test_serq_rejects_out_of_range_channels():
     L = vg_layer(np.random.default_rng(36))
     with pytest.raises(RuntimeError):
         sq_run(L, np.array([0, L["K"]], np.int32), f16bits(np.zeros((2, L["N"]))))
+
+
+# ---------------------------------------------------------------- codebook weights + sparse outliers
+
+def xfp_dense(idx, cbb, row_ptr, col_idx, valb):
+    """Wh by numpy: fancy indexing into the codebooks, residuals added at their positions."""
+    cb = cbb.view(np.float16).astype(np.float64)
+    Wh = np.take_along_axis(cb, idx.astype(np.int64), axis=1)
+    rows = np.repeat(np.arange(len(row_ptr) - 1), np.diff(row_ptr))
+    np.add.at(Wh, (rows, col_idx), valb.view(np.float16).astype(np.float64))
+    return Wh
+
+
+def test_xfp_linear_codebook_is_the_w4_layer():
+    """cb[n][q] = (q - z_n) s_n with power-of-two scales (exact in fp16) and
+    no outliers: the same weights as the W4 layer, summed in the same order."""
+    rng = np.random.default_rng(41)
+    M, N, K = 5, 24, 256
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    z = rng.integers(0, 16, size=(N, 1)).astype(np.float64)
+    s = np.exp2(rng.integers(-9, -4, size=(N, 1))).astype(np.float64)
+    cb = (np.arange(16)[None, :] - z) * s
+    Xb = f16bits(rng.standard_normal((M, K)))
+    qc = pack_canonical(q)
+    empty = np.zeros(0, np.int32)
+    out = oracle.forward_xfp(Xb, qc, f16bits(cb), np.zeros(N + 1, np.int32), empty, np.zeros(0, np.uint16),
+                             N=N, K=K)
+    w4 = run(M, N, K, 0, K, Xb, qc, f16bits(s), f16bits(z), None, None, None, 0.0)
+    assert np.array_equal(out["Y"], w4["Y"])
+
+
+def test_xfp_against_numpy_dense():
+    rng = np.random.default_rng(42)
+    M, N, K = 6, 40, 512
+    W = rng.standard_normal((N, K)) * 0.02
+    W[rng.random((N, K)) < 0.01] *= 12.0                   # heavy tail: outliers to separate
+    x = synth.make_xfp(W)
+    assert x["row_ptr"][-1] > 0
+    Xb = f16bits(rng.standard_normal((M, K)))
+    out = oracle.forward_xfp(Xb, pack_canonical(x["idx"]), x["cb"], x["row_ptr"], x["col_idx"], x["val"], N=N, K=K)
+    Wh = xfp_dense(x["idx"], x["cb"], x["row_ptr"], x["col_idx"], x["val"])
+    ref = np.matmul(Xb.view(np.float16).astype(np.float64), Wh.T)
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # the residual restores the outliers (to fp16 rounding of the residual)
+    rows = np.repeat(np.arange(N), np.diff(x["row_ptr"]))
+    np.testing.assert_allclose(Wh[rows, x["col_idx"]], W[rows, x["col_idx"]], rtol=0, atol=1e-3)
+
+
+def test_xfp_sparse_only_and_repeated_entries():
+    """An all-zero codebook leaves the sparse part alone; two entries at one
+    position add up."""
+    rng = np.random.default_rng(43)
+    M, N, K = 3, 8, 128
+    Xb = f16bits(rng.standard_normal((M, K)))
+    row_ptr = np.array([0, 2, 2, 5, 5, 5, 6, 6, 8], np.int32)
+    col_idx = np.array([3, 3, 0, 127, 64, 9, 10, 11], np.int32)
+    valb = f16bits(rng.standard_normal(8))
+    idx = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    out = oracle.forward_xfp(Xb, pack_canonical(idx), f16bits(np.zeros((N, 16))), row_ptr, col_idx, valb, N=N, K=K)
+    D = xfp_dense(idx, f16bits(np.zeros((N, 16))), row_ptr, col_idx, valb)
+    ref = np.matmul(Xb.view(np.float16).astype(np.float64), D.T)
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    assert out["Y"][:, 1].tolist() == [0.0] * M
+    with pytest.raises(RuntimeError):
+        bad = col_idx.copy(); bad[0] = K
+        oracle.forward_xfp(Xb, pack_canonical(idx), f16bits(np.zeros((N, 16))), row_ptr, bad, valb, N=N, K=K)

@@ -126,3 +126,43 @@ def make_vgate(r: int, h: int, act: str = "fp16", seed: int = 0, t_std: float = 
     c2 = rng.normal(0.0, 1.0, (r,))
     return {"G1": to_act_bits(G1, act), "c1": to_act_bits(c1, act),
             "G2": to_act_bits(G2, act), "c2": to_act_bits(c2, act), "h": h}
+
+
+def make_xfp(W: np.ndarray, k_sigma: float = 4.0, max_frac: float = 0.02) -> dict:
+    """Synthetic weights in the codebook-plus-outliers format, built from a
+    float32 matrix W [N, K]: per output channel, the weights farther than
+    k_sigma standard deviations from the channel mean (at most max_frac of
+    the channel, the farthest first) are outliers; the rest keep their value,
+    the outlier positions take the channel mean.  The channel's 16 codebook
+    entries are quantiles of those values (fp16, ascending), each weight
+    takes the nearest entry's index, and the outliers carry the fp16 residual
+    w - cb[idx] at their positions (compressed sparse rows).
+    Returns idx (uint8 [N, K], 0..15), cb (fp16 bits [N, 16]), row_ptr,
+    col_idx (int32) and val (fp16 bits)."""
+    W = np.asarray(W, dtype=np.float64)
+    N, K = W.shape
+    mu = W.mean(axis=1, keepdims=True)
+    sd = W.std(axis=1, keepdims=True)
+    dev = np.abs(W - mu)
+    cap = max(0, int(max_frac * K))
+    out = dev > k_sigma * sd
+    if cap < K:
+        # keep only the cap farthest per row
+        kth = -np.partition(-dev, cap, axis=1)[:, cap:cap + 1] if cap > 0 else np.full((N, 1), np.inf)
+        out &= dev > kth
+    block = np.where(out, mu, W)
+    qs = (np.arange(16) + 0.5) / 16.0
+    cb = np.quantile(block, qs, axis=1).T.astype(np.float16)          # [N, 16], ascending
+    cb64 = cb.astype(np.float64)
+    mid = (cb64[:, 1:] + cb64[:, :-1]) / 2.0
+    idx = np.empty((N, K), np.uint8)
+    for n0 in range(0, N, 2048):
+        sl = slice(n0, min(N, n0 + 2048))
+        idx[sl] = (block[sl, :, None] > mid[sl, None, :]).sum(axis=2).astype(np.uint8)
+    rows, cols = np.nonzero(out)
+    resid = W[rows, cols] - cb64[rows, idx[rows, cols]]
+    row_ptr = np.zeros(N + 1, np.int32)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    return {"idx": idx, "cb": cb.view(np.uint16), "row_ptr": row_ptr, "col_idx": cols.astype(np.int32),
+            "val": resid.astype(np.float16).view(np.uint16)}
