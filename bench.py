@@ -224,6 +224,91 @@ def latency_table(torch, w4, synth, dev):
         del pk, packed
 
 
+def xfp_main(args, torch, w4, synth, dev, cfg_id, M):
+    """Codebook decode: Y = X Wh^T, Wh = per-channel 16-entry codebook lookups
+    plus a sparse fp16 outlier residual.  The layer's weights with 0.5 % of
+    them planted as x25 outliers, converted offline (untimed)."""
+    d = synth.make_layer(cfg_id, M, seed=args.seed, r=0)
+    N, K, act = d["N"], d["K"], d["act"]
+    tdt = torch.float16 if act == "fp16" else torch.bfloat16
+    x = synth.make_xfp(synth.plant_outliers(d["W"], seed=args.seed))
+    idx = x["idx"]
+    qc = torch.from_numpy((idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8)).to(dev)
+    packed0 = w4.w4ec_pack(qc, torch.ones((N, 1), dtype=torch.float16, device=dev),
+                           torch.zeros((N, 1), dtype=torch.float16, device=dev), N, K, K)
+    del qc
+    nnz = int(x["row_ptr"][-1])
+    cb0 = torch.from_numpy(x["cb"].view(np.int16)).view(torch.float16).to(dev)
+    rp0 = torch.from_numpy(x["row_ptr"]).to(dev)
+    ci0 = torch.from_numpy(x["col_idx"]).to(dev)
+    val0 = torch.from_numpy(x["val"].view(np.int16)).view(torch.float16).to(dev)
+    # algorithmic bytes: indices, codebooks, the residual (row pointers,
+    # columns, values), X and Y
+    nbytes = N * K // 2 + N * 32 + (N + 1) * 4 + nnz * 6 + M * K * 2 + M * N * 2
+    weight_bytes = packed0.numel() + N * 32 + (N + 1) * 4 + nnz * 6
+    R = max(1, -(-2 * MALL_BYTES // weight_bytes))
+    copies = [(packed0, cb0, rp0, ci0, val0)] + [
+        (packed0.clone(), cb0.clone(), rp0.clone(), ci0.clone(), val0.clone()) for _ in range(R - 1)]
+    X = torch.from_numpy(np.ascontiguousarray(d["X"]).view(np.int16)).view(tdt).to(dev)
+    Y = torch.empty((M, N), dtype=tdt, device=dev)
+
+    def step(i):
+        p, cb, rp, ci, val = copies[i % R]
+        w4.w4ec_linear_decode_xfp(X, p, cb, rp, ci, val, N=N, Y=Y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for i in range(args.steps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(stream)
+        graph.replay()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is None:
+        torch.cuda._sleep(int(100e6))
+    start.record()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kdur = ms_per_step * 1e-3
+    achieved = nbytes / kdur / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profiles(f"decode_kernel/{args.workload}/xfp"),
+            "kernel": "decode_kernel (codebook)", "kernel_us": round(kdur * 1e6, 3)}
+    flops = 2 * M * N * K + 2 * M * nnz
+    out = {
+        "metric": "W4+EC linear: decode HBM GB/s & prefill TFLOP/s, % of MI355X roofline",
+        "value": round(nbytes / kdur / 1e9, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": act, "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "act": act, "phase": "decode",
+                   "method": "xfp", "residual_entries": nnz, "weight_copies": R,
+                   "launch": "hipgraph" if graph is not None else "eager",
+                   "bytes_per_step": nbytes, "flops_per_step": flops},
+        "roofline": roof,
+        "cpu_baseline": None,
+        "wall_s": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,9 +332,11 @@ def main():
                     help="prefill only -- fused: the EC inside the GEMM's epilogue (default); unfused: gate "
                          "step, plain W4 GEMM, then a T_g B kernel, on one stream; semi: the gate step on a "
                          "second stream beside the GEMM, then the T_g B kernel")
-    ap.add_argument("--method", choices=["spear", "serq"], default="spear",
+    ap.add_argument("--method", choices=["spear", "serq", "xfp"], default="spear",
                     help="spear: the input-adaptive EC (default); serq: the single-factor correction over "
-                         "the salient input channels (the config's outlier channels), X[:, S] R")
+                         "the salient input channels (the config's outlier channels), X[:, S] R; xfp "
+                         "(decode workloads): per-channel 16-entry codebooks plus a sparse fp16 outlier "
+                         "residual, no EC")
     ap.add_argument("--lut", action="store_true",
                     help="prefill latency table: time the three paths over a grid of (M, r, N, K) and print "
                          "one JSON line per point (no roofline / CPU legs)")
@@ -285,6 +372,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     cfg_id, M, phase = WORKLOADS[args.workload]
+    if args.method == "xfp":
+        if phase != "decode" or args.gate != "scalar" or args.path != "fused":
+            print("bench.py: --method xfp applies to the decode workloads (no --gate / --path)", file=sys.stderr)
+            sys.exit(2)
+        xfp_main(args, torch, w4, synth, dev, cfg_id, M)
+        return
     d = synth.make_layer(cfg_id, M, seed=args.seed, r=args.rank)
     N, K, r, G, act = d["N"], d["K"], d["r"], d["group_size"], d["act"]
     tdt = torch.float16 if act == "fp16" else torch.bfloat16

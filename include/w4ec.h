@@ -223,6 +223,39 @@ int w4ec_prefill_ec_gate(const void* X, const void* A, const void* w_g, float b_
 int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, int act_dtype,
                           const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Codebook weights with a sparse outlier residual, decode (XFP summary,
+ * "XFP: Quality-Targeted Adaptive Codebook Quantization with Sparse Outlier
+ * Separation for LLM Inference", sections 2 and 3: the outliers kept apart
+ * at full precision, every other weight an index into a learned codebook of
+ * 16 entries), in the W4A16 setting of this library, with one codebook per
+ * output channel (a per-layer codebook is the case of identical rows):
+ *
+ *   Wh[n,k] = codebook[n][idx[n,k]] + (sum of val[e] over the entries e of
+ *             row n with col_idx[e] == k)
+ *   Y[m,n]  = sum_k X[m,k] Wh[n,k]
+ *
+ *   X        device act [M, K], 16-byte aligned; 1 <= M <= 16
+ *   packed   device blob from w4ec_pack of the 4-bit indices idx (as
+ *            q_canon) with group_size = K, scale 1 and zero 0 (the scale
+ *            and zero are not read)
+ *   codebook device fp16 [N][16], 16-byte aligned; with bf16 activations
+ *            each entry is rounded to bf16 before it is multiplied
+ *   row_ptr  device int32 [N + 1]; row n's entries are
+ *            [row_ptr[n], row_ptr[n+1]) (clamped to [0, nnz]; a decreasing
+ *            pair is an empty row)
+ *   col_idx  device int32 [nnz], each in [0, K) (an index outside is
+ *            clamped to that range; the result is then undefined)
+ *   val      device fp16 [nnz], the residual values
+ *   nnz      number of residual entries (>= 0; col_idx and val may be NULL
+ *            when it is 0)
+ *   Y        device act [M, N] (output), 16-byte aligned
+ * K must be a multiple of 128.  No workspace.  Returns W4EC_ERR_UNSUPPORTED
+ * for M > 16; W4EC_ERR_INVALID_ARG for missing or misaligned pointers and
+ * Y aliasing an input.  Asynchronous on stream. */
+int w4ec_linear_decode_xfp(const void* X, const void* packed, const uint16_t* codebook,
+                           const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* val,
+                           int nnz, void* Y, int M, int N, int K, int act_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -195,3 +195,31 @@ def test_serq_argument_errors(name):
     assert c(X=0) == E.W4EC_ERR_INVALID_ARG
     assert c(R=FAKE + 0x500000) == E.W4EC_ERR_INVALID_ARG        # R aliases Y
     assert c(ws=0) == E.W4EC_ERR_WORKSPACE
+
+
+def test_xfp_argument_errors():
+    fn = w4.lib().w4ec_linear_decode_xfp
+    P = ctypes.c_void_p
+    E = w4
+
+    def c(X=FAKE, packed=FAKE + 0x100000, cb=FAKE + 0x200000, rp=FAKE + 0x300000, ci=FAKE + 0x400000,
+          val=FAKE + 0x500000, nnz=10, Y=FAKE + 0x600000, M=1, N=512, K=512, act=0):
+        p = lambda v: P(v) if v else None
+        return fn(p(X), p(packed), p(cb), p(rp), p(ci), p(val), nnz, p(Y), M, N, K, act, None)
+
+    assert c(M=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(M=17) == E.W4EC_ERR_UNSUPPORTED
+    assert c(K=500) == E.W4EC_ERR_UNSUPPORTED
+    assert c(N=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(nnz=-1) == E.W4EC_ERR_INVALID_ARG
+    assert c(act=2) == E.W4EC_ERR_INVALID_ARG
+    assert c(cb=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(rp=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(ci=0) == E.W4EC_ERR_INVALID_ARG                    # entries but no columns
+    assert c(val=0) == E.W4EC_ERR_INVALID_ARG
+    assert c(cb=FAKE + 0x200008) == E.W4EC_ERR_INVALID_ARG      # codebook not 16-byte aligned
+    assert c(rp=FAKE + 0x300002) == E.W4EC_ERR_INVALID_ARG
+    assert c(val=FAKE + 0x500001) == E.W4EC_ERR_INVALID_ARG
+    assert c(packed=FAKE + 0x100010) == E.W4EC_ERR_INVALID_ARG  # blob not 256-byte aligned
+    assert c(Y=FAKE) == E.W4EC_ERR_INVALID_ARG                  # Y aliases X
+    assert c(X=0) == E.W4EC_ERR_INVALID_ARG

@@ -25,6 +25,7 @@ __all__ = [
     "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
     "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
     "w4ec_linear_decode_serq", "w4ec_linear_prefill_serq",
+    "w4ec_linear_decode_xfp",
     "PackedLayer",
 ]
 
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
             fn.restype = I
+        L.w4ec_linear_decode_xfp.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, P]
+        L.w4ec_linear_decode_xfp.restype = I
         for name in ("w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"):
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P, Z, P]
@@ -299,6 +302,35 @@ def w4ec_linear_decode_serq(X, packed, S, R, *, N, group_size, workspace=None, Y
 def w4ec_linear_prefill_serq(X, packed, S, R, *, N, group_size, workspace=None, Y=None, stream=None):
     """Y = X Wd^T + X[:, S] R (salient-channel correction) for any M >= 1."""
     return _layer_call_serq("w4ec_linear_prefill_serq", X, packed, S, R, N, group_size, workspace, Y, stream)
+
+
+def w4ec_linear_decode_xfp(X, packed, codebook, row_ptr, col_idx, val, *, N, Y=None, stream=None):
+    """Y = X Wh^T with Wh[n,k] = codebook[n][idx[n,k]] plus the sparse residual
+    (rows row_ptr, columns col_idx, values val), 1 <= M <= 16.  packed: the
+    indices packed by w4ec_pack with group_size = K (scale 1, zero 0);
+    codebook fp16 [N, 16]; row_ptr int32 [N + 1]; col_idx int32 [nnz]; val fp16 [nnz]."""
+    torch = _torch()
+    _need_cuda(X, "X", (torch.float16, torch.bfloat16))
+    act = X.dtype
+    M, K = X.shape
+    _need_cuda(packed, "packed", torch.uint8)
+    _need_cuda(codebook, "codebook", torch.float16)
+    _need_cuda(row_ptr, "row_ptr", torch.int32)
+    _need_cuda(col_idx, "col_idx", torch.int32)
+    _need_cuda(val, "val", torch.float16)
+    if codebook.shape != (N, 16) or row_ptr.shape != (N + 1,):
+        raise ValueError("codebook must be [N, 16] and row_ptr [N + 1]")
+    nnz = 0 if col_idx is None else int(col_idx.numel())
+    if (val is None and nnz) or (val is not None and int(val.numel()) != nnz):
+        raise ValueError("col_idx and val must have the same length")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=act, device=X.device)
+    _need_cuda(Y, "Y", act)
+    st = lib().w4ec_linear_decode_xfp(_ptr(X), _ptr(packed), _ptr(codebook), _ptr(row_ptr),
+                                      _ptr(col_idx) if nnz else None, _ptr(val) if nnz else None, nnz,
+                                      _ptr(Y), M, N, K, _act_code(act), _stream_handle(stream))
+    _check(st, "w4ec_linear_decode_xfp")
+    return Y
 
 
 def w4ec_prefill_ec_workspace_bytes(M: int, K: int, r: int) -> int:

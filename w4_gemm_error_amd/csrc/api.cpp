@@ -501,4 +501,28 @@ int w4ec_linear_prefill_vgate(const void* X, const void* packed, const void* A, 
                          workspace, workspace_bytes, stream, &vg);
 }
 
+int w4ec_linear_decode_xfp(const void* X, const void* packed, const uint16_t* codebook,
+                           const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* val,
+                           int nnz, void* Y, int M, int N, int K, int act_dtype, void* stream)
+{
+    if (M <= 0 || nnz < 0)
+        return W4EC_ERR_INVALID_ARG;
+    if (M > DECODE_MAX_M)
+        return W4EC_ERR_UNSUPPORTED;
+    int rc = check_weight_shape(N, K, K);
+    if (rc != W4EC_OK)
+        return rc;
+    if (act_dtype != W4EC_FP16 && act_dtype != W4EC_BF16)
+        return W4EC_ERR_INVALID_ARG;
+    if (!X || !packed || !codebook || !row_ptr || !Y || (nnz > 0 && (!col_idx || !val)))
+        return W4EC_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Y, 16) || !aligned(packed, 256) || !aligned(codebook, 16) ||
+        !aligned(row_ptr, 4) || !aligned(col_idx, 4) || !aligned(val, 2))
+        return W4EC_ERR_INVALID_ARG;
+    if (X == Y || packed == Y || codebook == Y)
+        return W4EC_ERR_INVALID_ARG;
+    const XfpArgs x{X, packed, codebook, row_ptr, col_idx, val, nnz, Y, M, N, K, act_dtype};
+    return hip_status(launch_decode_xfp(x, make_decode_plan(M, N, K, 0), (hipStream_t)stream));
+}
+
 }  // extern "C"

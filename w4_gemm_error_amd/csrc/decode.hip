@@ -71,7 +71,34 @@ struct DecodeKArgs {
     int h;
     int vg_staged;       // the gate parameters are copied to LDS (they fit)
     const int32_t* S;    // salient-channel correction: T = X[:, S] (no EC role), or null
+    // codebook weights (codebook kernels only): per-channel codebooks of 16
+    // fp16 entries and the sparse outlier residual in compressed rows
+    const uint16_t* cb;      // [N][16]
+    const int32_t* row_ptr;  // [N + 1]
+    const int32_t* col_idx;  // [nnz]
+    const uint16_t* val;     // [nnz] fp16
+    int nnz;
 };
+
+// Eight codebook entries for the eight 4-bit indices of w, in the MFMA
+// operand order of the affine dequantization (index i of the word is nibble
+// i: pairs (0, 4), (1, 5), (2, 6), (3, 7)); c is the column's 16 entries.
+__device__ inline u32x4 cb_lookup(uint32_t w, const uint16_t* c)
+{
+    auto e = [&](int i) { return (uint32_t)c[(w >> (4 * i)) & 15u]; };
+    return (u32x4){e(0) | (e(4) << 16), e(1) | (e(5) << 16), e(2) | (e(6) << 16), e(3) | (e(7) << 16)};
+}
+
+// eight fp16 values -> bf16 (round to nearest even)
+__device__ inline u32x4 f16x8_to_bf16x8(u32x4 v)
+{
+    auto cv = [](uint32_t p) {
+        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFF));
+        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+        return bf16_pair_from_f32(lo, hi);
+    };
+    return (u32x4){cv(v.x), cv(v.y), cv(v.z), cv(v.w)};
+}
 
 __device__ inline uint32_t* rep_word(const DecodeKArgs& a, int slot, int i)
 {
@@ -392,7 +419,7 @@ __host__ __device__ inline size_t main_b_offset(int M, int K, bool xlds, int CB)
     return (b + 15) / 16 * 16;
 }
 
-template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
 __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 {
     const int tid = threadIdx.x;
@@ -475,6 +502,18 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
             const int e = tid + DEC_THREADS * i;
             const int j = e % a.r_pad;
             sg[i] = (e < M * a.r_pad && j < a.r) ? a.S[j] : 0;
+        }
+    }
+    // Codebook weights (XFP summary, sections 2 and 3): the CB x 16
+    // columns' codebooks (16 entries each, 32 bytes) are loaded before the
+    // weight stream and kept in LDS past the staged activations, in the MFMA
+    // operand format (bf16 for bf16 activations).
+    uint16_t* cbl = reinterpret_cast<uint16_t*>(smem + main_b_offset(M, K, XLDS, CB));
+    u32x4 cbv = (u32x4){0u, 0u, 0u, 0u};
+    if constexpr (CBK) {
+        if (tid < CB * 32) {
+            const int n = min(cb0 * PANEL_N + tid / 2, a.N - 1);
+            cbv = ld16(a.cb + (size_t)n * 16 + 8 * (tid & 1));
         }
     }
     u32x4 bstage[2 * CB];
@@ -568,6 +607,15 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         if (lds_gather)
             gather_lds();
     }
+    if constexpr (CBK) {
+        if (tid < CB * 32) {
+            u32x4 v = cbv;
+            if constexpr (ACT == ACT_BF16)
+                v = f16x8_to_bf16x8(v);
+            st16(cbl + 8 * tid, v);
+        }
+        lds_barrier();
+    }
 
     floatx4 acc[CB], accg[CB];
     float s_cur[CB];
@@ -590,6 +638,11 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         accg[j] = acc[j];
     }
     set_sz(sz0);
+    if constexpr (CBK) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+            s_cur[j] = 1.0f;                         // the codebook entries are the weights
+    }
     int left_in_group = ppg - (kbeg % ppg);          // panels until the group changes
 
     // lanes of absent tokens read token M - 1's row (the same address in all
@@ -648,7 +701,9 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     u32x4 bq;
-                    if constexpr (ACT == ACT_F16)
+                    if constexpr (CBK)
+                        bq = cb_lookup(ws[s], cbl + (j * PANEL_N + (l & 15)) * 16);
+                    else if constexpr (ACT == ACT_F16)
                         bq = dequant_f16(ws[s], dqh[j]);
                     else
                         bq = dequant_bf16(ws[s], dqb[j]);
@@ -669,6 +724,38 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 #pragma unroll
     for (int j = 0; j < CB; ++j)
         acc[j] += s_cur[j] * accg[j];
+
+    if constexpr (CBK) {
+        // sparse outlier residual: wavefront w adds entries w, w + 4, ... of
+        // each of its columns, acc += x[m][k] * val, eight entries' loads at
+        // a time (X from LDS while it is still staged there)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const bool colok = n_l[j] < a.N;
+            const int n = min(n_l[j], a.N - 1);
+            const int e0 = colok ? min(a.row_ptr[n], a.nnz) : 0;
+            const int e1 = colok ? min(a.row_ptr[n + 1], a.nnz) : 0;
+            for (int eb = e0 + w; eb < e1; eb += 32) {
+                int kk[8];
+                float vv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int e = eb + 4 * i;
+                    kk[i] = e < e1 ? min(max(a.col_idx[e], 0), K - 1) : 0;
+                    vv[i] = e < e1 ? (float)__builtin_bit_cast(_Float16, a.val[e]) : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int m = min(4 * (l >> 4) + t, M - 1);
+                        const uint16_t xb = XLDS ? xs[(size_t)m * K + kk[i]] : a.X[(size_t)m * K + kk[i]];
+                        acc[j][t] += act_to_f32<ACT>(xb) * vv[i];
+                    }
+                }
+            }
+        }
+    }
 
     // park B in LDS ([CB][r_pad][16] halves, past the staged activations and
     // the reduction buffer; read after the barrier below)
@@ -812,15 +899,19 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 // Two column blocks per workgroup (activations staged in LDS): the grid
 // holds ~450 workgroups, which fit the CUs in one round at two wavefronts
 // per SIMD, i.e. within 256 registers.
-template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
 __global__ __launch_bounds__(DEC_THREADS, CB == 2 ? 2 : 1)
 void decode_kernel(DecodeKArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
-    if ((int)blockIdx.x < a.P)
-        decode_ec_role<ACT>(a, dsmem);
-    else
-        decode_main_role<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>(a, dsmem);
+    if constexpr (CBK) {
+        decode_main_role<ACT, CB, XCH, DEPTH, false, false, true>(a, dsmem);   // no EC role
+    } else {
+        if ((int)blockIdx.x < a.P)
+            decode_ec_role<ACT>(a, dsmem);
+        else
+            decode_main_role<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>(a, dsmem);
+    }
 }
 
 // activations of at most this many bytes are staged in LDS by the main role
@@ -852,11 +943,12 @@ static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
     return (std::max(at, std::max(fin, vg)) + 15) / 16 * 16;
 }
 
-template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
 static hipError_t launch_decode_t(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
-    auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST>;
-    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr), ec_lds_bytes(p, k.M, k.r));
+    auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST, CBK>;
+    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr) + (CBK ? (size_t)CB * 16 * 16 * 2 : 0),
+                                ec_lds_bytes(p, k.M, k.r));
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
@@ -892,6 +984,40 @@ static hipError_t launch_decode_act(const DecodeKArgs& k, const DecodePlan& p, h
                              : launch_decode_grp<ACT, true, false>(k, p, st);
     return p.stage_first ? launch_decode_grp<ACT, false, true>(k, p, st)
                          : launch_decode_grp<ACT, false, false>(k, p, st);
+}
+
+template <int ACT>
+static hipError_t launch_decode_xfp_act(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
+{
+    if (p.xlds) {
+        const size_t xch = ((size_t)k.M * k.K / 8 + DEC_THREADS - 1) / DEC_THREADS;
+        if (xch <= 2)
+            return launch_decode_t<ACT, 2, 2, 8, false, false, true>(k, p, st);
+        return launch_decode_t<ACT, 2, DEC_XLDS_CHUNKS, 8, false, false, true>(k, p, st);
+    }
+    if (p.CB == 1)
+        return launch_decode_t<ACT, 1, 0, 4, false, false, true>(k, p, st);
+    return launch_decode_t<ACT, 4, 0, 2, false, false, true>(k, p, st);
+}
+
+// Codebook weights with a sparse outlier residual: the main role alone (no
+// EC), the codebook lookup in place of the affine dequantization.
+hipError_t launch_decode_xfp(const XfpArgs& x, const DecodePlan& p, hipStream_t st)
+{
+    BlobGeom g = blob_geom(x.N, x.K, x.K);
+    DecodeKArgs k{};
+    k.X = (const uint16_t*)x.X;
+    k.codes = (const uint8_t*)x.packed + g.codes_off;
+    k.sz = (const uint32_t*)((const char*)x.packed + g.sz_off);
+    k.Y = (uint16_t*)x.Y;
+    k.M = x.M; k.N = x.N; k.K = x.K; k.r = 0; k.r_pad = 0; k.G = x.K;
+    k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;
+    k.P = 0; k.KS = 0; k.RC = 1; k.n_main = p.n_main;
+    k.stage_first = 0;
+    k.cb = x.cb; k.row_ptr = x.row_ptr; k.col_idx = x.col_idx; k.val = x.val; k.nnz = x.nnz;
+    if (x.act == ACT_F16)
+        return launch_decode_xfp_act<ACT_F16>(k, p, st);
+    return launch_decode_xfp_act<ACT_BF16>(k, p, st);
 }
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st)

@@ -50,6 +50,20 @@ struct ApplyArgs {
     char* ws;
 };
 hipError_t launch_prefill_ec_gate(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
+
+// codebook weights with a sparse outlier residual (decode)
+struct XfpArgs {
+    const void* X;
+    const void* packed;       // the 4-bit indices, packed as codes by w4ec_pack
+    const uint16_t* cb;       // [N][16] fp16
+    const int32_t* row_ptr;   // [N + 1]
+    const int32_t* col_idx;   // [nnz]
+    const uint16_t* val;      // [nnz] fp16
+    int nnz;
+    void* Y;
+    int M, N, K, act;
+};
+hipError_t launch_decode_xfp(const XfpArgs& x, const DecodePlan& p, hipStream_t st);
 hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hipStream_t st);
 size_t prepass_lds_bytes(int r, int kc);
 

@@ -128,6 +128,18 @@ def make_vgate(r: int, h: int, act: str = "fp16", seed: int = 0, t_std: float = 
             "G2": to_act_bits(G2, act), "c2": to_act_bits(c2, act), "h": h}
 
 
+def plant_outliers(W: np.ndarray, frac: float = 0.005, scale: float = 25.0, seed: int = 0) -> np.ndarray:
+    """A copy of W [N, K] with frac of its entries (chosen uniformly, seeded)
+    multiplied by scale: the heavy-tailed weights that the codebook format
+    keeps apart."""
+    W = np.array(W, dtype=np.float32, copy=True)
+    n_out = int(frac * W.size)
+    if n_out:
+        pos = np.random.default_rng(900 + seed).choice(W.size, size=n_out, replace=False)
+        W.reshape(-1)[pos] *= np.float32(scale)
+    return W
+
+
 def make_xfp(W: np.ndarray, k_sigma: float = 4.0, max_frac: float = 0.02) -> dict:
     """Synthetic weights in the codebook-plus-outliers format, built from a
     float32 matrix W [N, K]: per output channel, the weights farther than
@@ -152,7 +164,7 @@ def make_xfp(W: np.ndarray, k_sigma: float = 4.0, max_frac: float = 0.02) -> dic
         out &= dev > kth
     block = np.where(out, mu, W)
     qs = (np.arange(16) + 0.5) / 16.0
-    cb = np.quantile(block, qs, axis=1).T.astype(np.float16)          # [N, 16], ascending
+    cb = np.ascontiguousarray(np.quantile(block, qs, axis=1).T.astype(np.float16))   # [N, 16], ascending
     cb64 = cb.astype(np.float64)
     mid = (cb64[:, 1:] + cb64[:, :-1]) / 2.0
     idx = np.empty((N, K), np.uint8)
