@@ -234,8 +234,7 @@ def xfp_main(args, torch, w4, synth, dev, cfg_id, M):
     x = synth.make_xfp(synth.plant_outliers(d["W"], seed=args.seed))
     idx = x["idx"]
     qc = torch.from_numpy((idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8)).to(dev)
-    packed0 = w4.w4ec_pack(qc, torch.ones((N, 1), dtype=torch.float16, device=dev),
-                           torch.zeros((N, 1), dtype=torch.float16, device=dev), N, K, K)
+    packed0 = w4.w4ec_pack_xfp(qc, N, K)
     del qc
     nnz = int(x["row_ptr"][-1])
     cb0 = torch.from_numpy(x["cb"].view(np.int16)).view(torch.float16).to(dev)

@@ -223,6 +223,16 @@ int w4ec_prefill_ec_gate(const void* X, const void* A, const void* w_g, float b_
 int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, int act_dtype,
                           const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Codebook indices, canonical uint8 [N][K/2] (even k in the low nibble,
+ * values 0..15), device -> the blob that w4ec_linear_decode_xfp reads
+ * (w4ec_packed_bytes(N, K, K) bytes, 256-byte aligned): the panel layout of
+ * w4ec_pack with the eight indices of each dword in natural order (byte j
+ * holds those of k = 2j and 2j + 1), so that each byte selects one entry
+ * of a 256-entry table of codebook pairs.  w4ec_unpack does not read it.
+ * Synchronizes the stream.  Returns W4EC_ERR_UNSUPPORTED unless K is a
+ * multiple of 128. */
+int w4ec_pack_xfp(const uint8_t* idx_canon, int N, int K, void* packed, void* stream);
+
 /* Codebook weights with a sparse outlier residual, decode (XFP summary,
  * "XFP: Quality-Targeted Adaptive Codebook Quantization with Sparse Outlier
  * Separation for LLM Inference", sections 2 and 3: the outliers kept apart
@@ -235,9 +245,7 @@ int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, in
  *   Y[m,n]  = sum_k X[m,k] Wh[n,k]
  *
  *   X        device act [M, K], 16-byte aligned; 1 <= M <= 16
- *   packed   device blob from w4ec_pack of the 4-bit indices idx (as
- *            q_canon) with group_size = K, scale 1 and zero 0 (the scale
- *            and zero are not read)
+ *   packed   device blob from w4ec_pack_xfp of the 4-bit indices idx
  *   codebook device fp16 [N][16], 16-byte aligned; with bf16 activations
  *            each entry is rounded to bf16 before it is multiplied
  *   row_ptr  device int32 [N + 1]; row n's entries are

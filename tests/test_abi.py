@@ -223,3 +223,13 @@ def test_xfp_argument_errors():
     assert c(packed=FAKE + 0x100010) == E.W4EC_ERR_INVALID_ARG  # blob not 256-byte aligned
     assert c(Y=FAKE) == E.W4EC_ERR_INVALID_ARG                  # Y aliases X
     assert c(X=0) == E.W4EC_ERR_INVALID_ARG
+
+
+def test_pack_xfp_argument_errors():
+    fn = w4.lib().w4ec_pack_xfp
+    P = ctypes.c_void_p
+    assert fn(None, 512, 512, P(FAKE), None) == w4.W4EC_ERR_INVALID_ARG
+    assert fn(P(FAKE), 512, 512, None, None) == w4.W4EC_ERR_INVALID_ARG
+    assert fn(P(FAKE), 512, 512, P(FAKE + 0x10), None) == w4.W4EC_ERR_INVALID_ARG   # blob alignment
+    assert fn(P(FAKE), 512, 500, P(FAKE), None) == w4.W4EC_ERR_UNSUPPORTED
+    assert fn(P(FAKE), 0, 512, P(FAKE), None) == w4.W4EC_ERR_INVALID_ARG

@@ -22,7 +22,7 @@ def _print(*a):
 
 def pack_nibbles(idx):
     """indices uint8 [N, K] -> [N, K/2], even k in the low nibble (the
-    canonical code layout that w4ec_pack takes)."""
+    canonical layout that w4ec_pack_xfp takes)."""
     idx = np.asarray(idx, dtype=np.uint8)
     return (idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8)
 
@@ -44,9 +44,7 @@ def gpu_xfp(d, x):
     t = torch()
     N, K = d["N"], d["K"]
     qc = t.from_numpy(x["qc"]).cuda()
-    one = t.ones((N, 1), dtype=t.float16, device="cuda")
-    zero = t.zeros((N, 1), dtype=t.float16, device="cuda")
-    packed = w4.w4ec_pack(qc, one, zero, N, K, K)
+    packed = w4.w4ec_pack_xfp(qc, N, K)
     cb = t.from_numpy(x["cb"].view(np.int16)).view(t.float16).cuda()
     rp = t.from_numpy(x["row_ptr"]).cuda()
     nnz = int(x["row_ptr"][-1])

@@ -25,7 +25,7 @@ __all__ = [
     "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
     "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
     "w4ec_linear_decode_serq", "w4ec_linear_prefill_serq",
-    "w4ec_linear_decode_xfp",
+    "w4ec_pack_xfp", "w4ec_linear_decode_xfp",
     "PackedLayer",
 ]
 
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
             fn.restype = I
+        L.w4ec_pack_xfp.argtypes = [P, I, I, P, P]
+        L.w4ec_pack_xfp.restype = I
         L.w4ec_linear_decode_xfp.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, P]
         L.w4ec_linear_decode_xfp.restype = I
         for name in ("w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"):
@@ -304,10 +306,24 @@ def w4ec_linear_prefill_serq(X, packed, S, R, *, N, group_size, workspace=None, 
     return _layer_call_serq("w4ec_linear_prefill_serq", X, packed, S, R, N, group_size, workspace, Y, stream)
 
 
+def w4ec_pack_xfp(idx_canon, N: int, K: int, *, packed=None, stream=None):
+    """Codebook indices, canonical uint8 [N, K/2] (even k in the low nibble)
+    -> the codebook blob that w4ec_linear_decode_xfp reads.  Synchronizes."""
+    torch = _torch()
+    _need_cuda(idx_canon, "idx_canon", torch.uint8)
+    nbytes = w4ec_packed_bytes(N, K, K)
+    if nbytes == 0:
+        raise W4ECError(W4EC_ERR_UNSUPPORTED, "w4ec_packed_bytes")
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=idx_canon.device)
+    _check(lib().w4ec_pack_xfp(_ptr(idx_canon), N, K, _ptr(packed), _stream_handle(stream)), "w4ec_pack_xfp")
+    return packed
+
+
 def w4ec_linear_decode_xfp(X, packed, codebook, row_ptr, col_idx, val, *, N, Y=None, stream=None):
     """Y = X Wh^T with Wh[n,k] = codebook[n][idx[n,k]] plus the sparse residual
     (rows row_ptr, columns col_idx, values val), 1 <= M <= 16.  packed: the
-    indices packed by w4ec_pack with group_size = K (scale 1, zero 0);
+    indices packed by w4ec_pack_xfp;
     codebook fp16 [N, 16]; row_ptr int32 [N + 1]; col_idx int32 [nnz]; val fp16 [nnz]."""
     torch = _torch()
     _need_cuda(X, "X", (torch.float16, torch.bfloat16))

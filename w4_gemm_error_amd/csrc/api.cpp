@@ -241,6 +241,20 @@ int w4ec_pack(const uint8_t* q_canon, const uint16_t* scale, const uint16_t* zer
     return hdr.bad_zero ? W4EC_ERR_INVALID_ARG : W4EC_OK;
 }
 
+int w4ec_pack_xfp(const uint8_t* idx_canon, int N, int K, void* packed, void* stream)
+{
+    int rc = check_weight_shape(N, K, K);
+    if (rc != W4EC_OK)
+        return rc;
+    if (!idx_canon || !packed || !aligned(packed, 256))
+        return W4EC_ERR_INVALID_ARG;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_pack(idx_canon, nullptr, nullptr, N, K, K, packed, st);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(st);
+    return hip_status(e);
+}
+
 int w4ec_unpack(const void* packed, int N, int K, int group_size, uint8_t* q_canon,
                 uint16_t* scale, uint16_t* zero, void* stream)
 {

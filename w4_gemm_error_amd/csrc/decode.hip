@@ -80,13 +80,16 @@ struct DecodeKArgs {
     int nnz;
 };
 
-// Eight codebook entries for the eight 4-bit indices of w, in the MFMA
-// operand order of the affine dequantization (index i of the word is nibble
-// i: pairs (0, 4), (1, 5), (2, 6), (3, 7)); c is the column's 16 entries.
-__device__ inline u32x4 cb_lookup(uint32_t w, const uint16_t* c)
+// Codebook lookup of one dword of indices (natural order: byte j holds the
+// indices of k = 2j and 2j + 1): t points at the column's entry 0 of a pair
+// table laid out [256][16 columns], entry p = cb[p & 15] | cb[p >> 4] << 16,
+// so that each byte of w selects one MFMA operand dword.  A column's
+// entries sit in 4 of the 64 banks, so only the 4 lanes that read the same
+// column's table can conflict.
+__device__ inline u32x4 cb_lookup(uint32_t w, const uint32_t* t)
 {
-    auto e = [&](int i) { return (uint32_t)c[(w >> (4 * i)) & 15u]; };
-    return (u32x4){e(0) | (e(4) << 16), e(1) | (e(5) << 16), e(2) | (e(6) << 16), e(3) | (e(7) << 16)};
+    return (u32x4){t[(w & 0xFFu) * PANEL_N], t[((w >> 8) & 0xFFu) * PANEL_N], t[((w >> 16) & 0xFFu) * PANEL_N],
+                   t[(w >> 24) * PANEL_N]};
 }
 
 // eight fp16 values -> bf16 (round to nearest even)
@@ -505,15 +508,40 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
     }
     // Codebook weights (XFP summary, sections 2 and 3): the CB x 16
-    // columns' codebooks (16 entries each, 32 bytes) are loaded before the
-    // weight stream and kept in LDS past the staged activations, in the MFMA
-    // operand format (bf16 for bf16 activations).
-    uint16_t* cbl = reinterpret_cast<uint16_t*>(smem + main_b_offset(M, K, XLDS, CB));
-    u32x4 cbv = (u32x4){0u, 0u, 0u, 0u};
+    // columns' codebooks are loaded before the weight stream, converted to
+    // the MFMA operand type (bf16 for bf16 activations), and expanded in
+    // LDS, past the staged activations, into pair tables [CB][256][16].
+    // Thread tid writes entries p = tid / 16 + 16 i (i < 16) of column
+    // tid % 16: their low half is codebook entry tid / 16, the high half
+    // entry i, and the stores are contiguous.
+    uint32_t* ptab = reinterpret_cast<uint32_t*>(smem + main_b_offset(M, K, XLDS, CB));
+    u32x4 cbv[CBK ? CB : 1][2];                      // column tid % 16's 16 entries, per block
+    uint32_t cblo[CBK ? CB : 1];                     // its entry tid / 16
+    // The sparse residual is spread over the whole workgroup: thread tid
+    // takes column rc = tid % (CB x 16) of the workgroup and its entries
+    // rsub, rsub + RS, ... (rsub = tid / (CB x 16)).  Its row bounds are
+    // loaded ahead of everything else, its first RB entries after the ring's
+    // first panels, so that the dependent loads run under the weight stream.
+    constexpr int CBN = CB * PANEL_N;                // columns per workgroup
+    constexpr int RS = DEC_THREADS / CBN;            // threads per column
+    constexpr int RB = 4;                            // residual entries per thread and batch
+    const int rc = tid % CBN, rsub = tid / CBN;
+    const bool rcol_ok = cb0 * PANEL_N + rc < a.N;
+    int rb0 = 0, rb1 = 0;
+    int rk[RB];
+    uint32_t rv[RB];
     if constexpr (CBK) {
-        if (tid < CB * 32) {
-            const int n = min(cb0 * PANEL_N + tid / 2, a.N - 1);
-            cbv = ld16(a.cb + (size_t)n * 16 + 8 * (tid & 1));
+        {
+            const int n = min(cb0 * PANEL_N + rc, a.N - 1);
+            rb0 = a.row_ptr[n];
+            rb1 = a.row_ptr[n + 1];
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            const int n = min((cb0 + j) * PANEL_N + (tid & 15), a.N - 1);
+            cbv[j][0] = ld16(a.cb + (size_t)n * 16);
+            cbv[j][1] = ld16(a.cb + (size_t)n * 16 + 8);
+            cblo[j] = a.cb[(size_t)n * 16 + (tid >> 4)];
         }
     }
     u32x4 bstage[2 * CB];
@@ -608,13 +636,35 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
             gather_lds();
     }
     if constexpr (CBK) {
-        if (tid < CB * 32) {
-            u32x4 v = cbv;
-            if constexpr (ACT == ACT_BF16)
-                v = f16x8_to_bf16x8(v);
-            st16(cbl + 8 * tid, v);
+        static_assert(DEC_THREADS == 256, "sixteen pair-table entries per thread and block");
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            u32x4 v0 = cbv[j][0], v1 = cbv[j][1];
+            uint32_t lo = cblo[j];
+            if constexpr (ACT == ACT_BF16) {
+                v0 = f16x8_to_bf16x8(v0);
+                v1 = f16x8_to_bf16x8(v1);
+                lo = f16x8_to_bf16x8((u32x4){lo, 0u, 0u, 0u}).x & 0xFFFFu;
+            }
+            const uint32_t e[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            uint32_t* tj = ptab + j * 256 * PANEL_N + tid;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                tj[256 * i] = lo | ((i & 1) ? (e[i >> 1] & 0xFFFF0000u) : (e[i >> 1] << 16));
         }
         lds_barrier();
+        // row bounds clamped to [0, nnz] (an absent column has none), then
+        // the first batch (indices clamped into the arrays, which the host
+        // makes non-empty; entries past the row are discarded)
+        rb0 = rcol_ok ? min(max(rb0, 0), a.nnz) : 0;
+        rb1 = rcol_ok ? min(max(rb1, 0), a.nnz) : 0;
+        const int elast = max(a.nnz - 1, 0);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int e = min(rb0 + rsub + RS * i, elast);
+            rk[i] = a.col_idx[e];
+            rv[i] = a.val[e];
+        }
     }
 
     floatx4 acc[CB], accg[CB];
@@ -702,7 +752,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
                 for (int s = 0; s < 4; ++s) {
                     u32x4 bq;
                     if constexpr (CBK)
-                        bq = cb_lookup(ws[s], cbl + (j * PANEL_N + (l & 15)) * 16);
+                        bq = cb_lookup(ws[s], ptab + j * 256 * PANEL_N + (l & 15));
                     else if constexpr (ACT == ACT_F16)
                         bq = dequant_f16(ws[s], dqh[j]);
                     else
@@ -725,35 +775,43 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     for (int j = 0; j < CB; ++j)
         acc[j] += s_cur[j] * accg[j];
 
+    // sparse outlier residual: this thread's share of column rc, for every
+    // token, sum x[m][k] * val (X from LDS while it is still staged there)
+    // into rpart[rsub][m][rc] past the pair tables; the prefetched batch,
+    // then any further ones.  Added to the outputs in the final reduction,
+    // in a fixed order.
+    float* rpart = reinterpret_cast<float*>(ptab + CB * 256 * PANEL_N);
     if constexpr (CBK) {
-        // sparse outlier residual: wavefront w adds entries w, w + 4, ... of
-        // each of its columns, acc += x[m][k] * val, eight entries' loads at
-        // a time (X from LDS while it is still staged there)
+        auto add_batch = [&](const int* kk, const uint32_t* vb, int eb, bool first) {
+            int k[RB];
+            float v[RB];
 #pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            const bool colok = n_l[j] < a.N;
-            const int n = min(n_l[j], a.N - 1);
-            const int e0 = colok ? min(a.row_ptr[n], a.nnz) : 0;
-            const int e1 = colok ? min(a.row_ptr[n + 1], a.nnz) : 0;
-            for (int eb = e0 + w; eb < e1; eb += 32) {
-                int kk[8];
-                float vv[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int e = eb + 4 * i;
-                    kk[i] = e < e1 ? min(max(a.col_idx[e], 0), K - 1) : 0;
-                    vv[i] = e < e1 ? (float)__builtin_bit_cast(_Float16, a.val[e]) : 0.0f;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const int m = min(4 * (l >> 4) + t, M - 1);
-                        const uint16_t xb = XLDS ? xs[(size_t)m * K + kk[i]] : a.X[(size_t)m * K + kk[i]];
-                        acc[j][t] += act_to_f32<ACT>(xb) * vv[i];
-                    }
-                }
+            for (int i = 0; i < RB; ++i) {
+                const bool ok = eb + RS * i < rb1;
+                k[i] = ok ? min(max(kk[i], 0), K - 1) : 0;
+                v[i] = ok ? (float)__builtin_bit_cast(_Float16, (uint16_t)vb[i]) : 0.0f;
             }
+            for (int m = 0; m < M; ++m) {
+                float sum = first ? 0.0f : rpart[(rsub * M + m) * CBN + rc];
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    const uint16_t xb = XLDS ? xs[(size_t)m * K + k[i]] : a.X[(size_t)m * K + k[i]];
+                    sum += act_to_f32<ACT>(xb) * v[i];
+                }
+                rpart[(rsub * M + m) * CBN + rc] = sum;
+            }
+        };
+        add_batch(rk, rv, rb0 + rsub, true);
+        for (int eb = rb0 + rsub + RS * RB; eb < rb1; eb += RS * RB) {
+            int kk[RB];
+            uint32_t vb[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int e = min(eb + RS * i, a.nnz - 1);
+                kk[i] = a.col_idx[e];
+                vb[i] = a.val[e];
+            }
+            add_batch(kk, vb, eb, false);
         }
     }
 
@@ -850,6 +908,19 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         tot += red[(2 * CB + j) * 64 + l];
         tot += red[(3 * CB + j) * 64 + l];
         const int n = n_l[j];
+        if constexpr (CBK) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = 4 * (l >> 4) + v;
+                if (m < M) {
+                    float rs = 0.0f;
+#pragma unroll
+                    for (int u = 0; u < RS; ++u)
+                        rs += rpart[(u * M + m) * CBN + j * PANEL_N + (l & 15)];
+                    tot[v] += rs;
+                }
+            }
+        }
         if (a.r > 0) {
             const uint16_t* bj = bl + (size_t)j * a.r_pad * PANEL_N;
             u32x4 bfr[8];
@@ -947,7 +1018,7 @@ template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, b
 static hipError_t launch_decode_t(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST, CBK>;
-    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr) + (CBK ? (size_t)CB * 16 * 16 * 2 : 0),
+    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr) + (CBK ? (size_t)CB * PANEL_N * 256 * 4 + (size_t)DEC_THREADS * k.M * 4 : 0),
                                 ec_lds_bytes(p, k.M, k.r));
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1015,6 +1086,12 @@ hipError_t launch_decode_xfp(const XfpArgs& x, const DecodePlan& p, hipStream_t 
     k.P = 0; k.KS = 0; k.RC = 1; k.n_main = p.n_main;
     k.stage_first = 0;
     k.cb = x.cb; k.row_ptr = x.row_ptr; k.col_idx = x.col_idx; k.val = x.val; k.nnz = x.nnz;
+    if (x.nnz == 0) {
+        // the kernel loads entry 0 unconditionally (and discards it): point
+        // the empty arrays at the row pointers, which always exist
+        k.col_idx = x.row_ptr;
+        k.val = reinterpret_cast<const uint16_t*>(x.row_ptr);
+    }
     if (x.act == ACT_F16)
         return launch_decode_xfp_act<ACT_F16>(k, p, st);
     return launch_decode_xfp_act<ACT_BF16>(k, p, st);

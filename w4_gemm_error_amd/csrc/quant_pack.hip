@@ -121,9 +121,11 @@ void rtn_quantize_kernel(const float* __restrict__ W, int N, int K, int G,
 
 // ---------------------------------------------------------------- pack / unpack
 
-// One thread per blob dword (8 codes).
+// One thread per blob dword (8 codes).  natural: code t of the dword in
+// nibble t (the codebook layout, whose bytes are pairs of consecutive k),
+// else in the nibble that the affine dequantization expects.
 __global__ void pack_codes_kernel(const uint8_t* __restrict__ qc, int N, int K,
-                                  int NB, int KB, uint32_t* __restrict__ codes)
+                                  int NB, int KB, uint32_t* __restrict__ codes, int natural)
 {
     size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     size_t total = (size_t)NB * KB * (PANEL_BYTES / 4);
@@ -142,7 +144,7 @@ __global__ void pack_codes_kernel(const uint8_t* __restrict__ qc, int N, int K,
         for (int t = 0; t < 8; ++t) {
             uint32_t byte = src[t >> 1];
             uint32_t c = (t & 1) ? (byte >> 4) : (byte & 0xF);
-            word |= c << (4 * nibble_of(t));
+            word |= c << (4 * (natural ? t : nibble_of(t)));
         }
     }
     codes[idx] = word;
@@ -158,7 +160,9 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scale, const uint16_
     int gi = (int)(idx / Npad);
     int n = (int)(idx % Npad);
     uint32_t v = 0;
-    if (n < N) {
+    if (n < N && !scale) {
+        v = 0x3C00u;                                 // scale 1, zero 0 (codebook blob)
+    } else if (n < N) {
         uint16_t s = scale[(size_t)n * NG + gi];
         uint16_t z = zero[(size_t)n * NG + gi];
         float zf = (float)__builtin_bit_cast(_Float16, z);
@@ -234,7 +238,7 @@ hipError_t launch_pack(const uint8_t* qc, const uint16_t* scale, const uint16_t*
     hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, st, hdr, N, K, G);
     size_t nw = (size_t)g.NB * g.KB * (PANEL_BYTES / 4);
     hipLaunchKernelGGL(pack_codes_kernel, dim3(blocks_for(nw, 256)), dim3(256), 0, st,
-                       qc, N, K, g.NB, g.KB, (uint32_t*)(base + g.codes_off));
+                       qc, N, K, g.NB, g.KB, (uint32_t*)(base + g.codes_off), scale ? 0 : 1);
     size_t ns = (size_t)g.NG * g.Npad;
     hipLaunchKernelGGL(pack_sz_kernel, dim3(blocks_for(ns, 256)), dim3(256), 0, st,
                        scale, zero, N, g.NG, g.Npad, (uint32_t*)(base + g.sz_off), hdr);

@@ -11,6 +11,8 @@ namespace w4ec {
 
 hipError_t launch_rtn_quantize(const float* W, int N, int K, int G, uint8_t* qc,
                                uint16_t* scale, uint16_t* zero, hipStream_t st);
+// scale == zero == NULL: the codebook blob (indices in natural nibble order,
+// group_size K, scale 1 and zero 0)
 hipError_t launch_pack(const uint8_t* qc, const uint16_t* scale, const uint16_t* zero,
                        int N, int K, int G, void* packed, hipStream_t st);
 hipError_t launch_unpack(const void* packed, int N, int K, int G, uint8_t* qc,
