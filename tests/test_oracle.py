@@ -513,3 +513,22 @@ def test_xfp_sparse_only_and_repeated_entries():
     with pytest.raises(RuntimeError):
         bad = col_idx.copy(); bad[0] = K
         oracle.forward_xfp(Xb, pack_canonical(idx), f16bits(np.zeros((N, 16))), row_ptr, bad, valb, N=N, K=K)
+
+
+def test_xfp_row_subsets_and_malformed_rows():
+    rng = np.random.default_rng(44)
+    M, N, K = 5, 16, 256
+    W = rng.standard_normal((N, K)) * 0.02
+    W[rng.random((N, K)) < 0.02] *= 15.0
+    x = synth.make_xfp(W)
+    Xb = f16bits(rng.standard_normal((M, K)))
+    qc = pack_canonical(x["idx"])
+    full = oracle.forward_xfp(Xb, qc, x["cb"], x["row_ptr"], x["col_idx"], x["val"], N=N, K=K)["Y"]
+    rows = [3, 0, 3]
+    sub = oracle.forward_xfp(Xb, qc, x["cb"], x["row_ptr"], x["col_idx"], x["val"], N=N, K=K, rows=rows)["Y"]
+    assert np.array_equal(sub, full[rows])
+    bad = x["row_ptr"].copy()
+    n = int(np.argmax(np.diff(bad) > 0))                   # a row with entries
+    bad[n + 1] = bad[n] - 1                                 # decreasing pointers
+    with pytest.raises((RuntimeError, AssertionError)):
+        oracle.forward_xfp(Xb, qc, x["cb"], bad, x["col_idx"], x["val"], N=N, K=K)
