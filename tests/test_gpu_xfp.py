@@ -72,6 +72,8 @@ CASES = [
     ("bf16", 2, 272, 384),
     ("bf16", 8, 528, 1280),
     ("bf16", 1, 1024, 8192),
+    ("fp16", 2, 1000, 512),      # N not a multiple of 16: a partial last column block
+    ("bf16", 7, 1000, 640),
 ]
 
 
