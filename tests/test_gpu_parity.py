@@ -81,6 +81,10 @@ SMALL = [
     ("decode", "fp16", 7, 48, 1280, 256, 256),
     ("decode", "fp16", 16, 512, 20480, 256, 20480),    # more K slices than EC workgroups
     ("decode", "bf16", 3, 512, 20480, 256, 1024),
+    # the EC split by column blocks (1-4 tokens, K <= 4096, r a multiple of 16)
+    ("decode", "fp16", 1, 512, 640, 16, 640),          # a partial 512-row round; zero words past r
+    ("decode", "bf16", 4, 528, 4096, 48, 4096),
+    ("decode", "fp16", 2, 272, 1024, 256, 128),
     ("prefill", "fp16", 17, 528, 640, 72, 640),
     ("prefill", "fp16", 300, 512, 512, 8, 512),
     ("prefill", "fp16", 129, 784, 1024, 64, 128),
@@ -108,11 +112,10 @@ def test_small_layer_parity(phase, act, M, N, K, r, G):
     assert_close(Y, ref, act, f"{phase} {act} M={M}")
 
 
-@pytest.mark.parametrize("phase", ["decode", "prefill"])
-def test_special_cases(phase):
-    _print(f"special cases {phase}")
-    M = 9 if phase == "decode" else 40
-    d = small_layer("fp16", M, 528, 512, 24, 512, seed=8)
+@pytest.mark.parametrize("phase,M,r", [("decode", 9, 24), ("decode", 2, 32), ("prefill", 40, 24)])
+def test_special_cases(phase, M, r):
+    _print(f"special cases {phase} M={M} r={r}")
+    d = small_layer("fp16", M, 528, 512, r, 512, seed=8)
     _, _, _, packed = gpu_quantize(d)
     codes = oracle.rtn_quantize(d["W"], 512)
     plain = gpu_layer(d, packed, phase, r=0)
