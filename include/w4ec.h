@@ -168,7 +168,7 @@ int w4ec_linear_prefill_vgate(const void* X, const void* packed, const void* A, 
                               int act_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Single-factor correction over salient input channels (SERQ summary,
- * "Saliency-Aware Error Reconstruction for LLM Low-Bit Quantization",
+ * "SERQ: Saliency-Aware Low-Rank Error Reconstruction for LLM Quantization",
  * section 2): the quantized product plus the activation channels of the
  * salient weight rows times one low-rank factor R,
  *
