@@ -181,18 +181,23 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
         vgate_stage_load(G1, c1, G2, c2, r, h, gv);
     bool staged = false;
     uint32_t it = 0;                                        // bounded wait, shared by all waits
+    // ng thread groups split the P slices (slice q -> group q mod ng), so
+    // that all of them are in flight at once; the groups' sums are added in
+    // group order
+    const int ng = max(1, DEC_THREADS / a.r_pad);
     for (int m = m0; m < M; m += mstep) {
         __syncthreads();                                    // LDS of the previous token is free
-        for (int c = tid; c < a.r_pad; c += DEC_THREADS) {
+        for (int e = tid; e < ng * a.r_pad; e += DEC_THREADS) {
+            const int g = e / a.r_pad, c = e - g * a.r_pad;
             float t = 0.0f;
             if (c < r) {
                 const uint32_t* src = a.partial + (size_t)m * a.RC + c;
-                for (int q = 0; q < a.P; q += 8) {
+                for (int q = g; q < a.P; q += 8 * ng) {
                     // eight slices in flight; those not landed yet are loaded again together
                     uint32_t v[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        v[i] = q + i < a.P ? atomic_load_dev(src + (size_t)(q + i) * qs) : 1u;
+                        v[i] = q + i * ng < a.P ? atomic_load_dev(src + (size_t)(q + i * ng) * qs) : 1u;
                     for (;;) {
                         bool miss = false;
 #pragma unroll
@@ -207,15 +212,22 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
                         }
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
-                            if (v[i] == 0u)
-                                v[i] = atomic_load_dev(src + (size_t)(q + i) * qs);
+                            if (v[i] == 0u)                 // only slices < P can read as zero
+                                v[i] = atomic_load_dev(src + (size_t)(q + i * ng) * qs);
                     }
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        if (q + i < a.P)
+                        if (q + i * ng < a.P)
                             t += hw_dec32(v[i]);
                 }
             }
+            red[e] = t;
+        }
+        __syncthreads();
+        for (int c = tid; c < a.r_pad; c += DEC_THREADS) {
+            float t = red[c];
+            for (int g = 1; g < ng; ++g)
+                t += red[g * a.r_pad + c];
             tT[c] = t;
         }
         if (a.vg_staged && !staged) {
@@ -223,9 +235,19 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
             staged = true;
         }
         __syncthreads();
-        vgate_hidden<ACT>(tT, 0, 1, r, h, G1, c1, tU, red);
-        vgate_gates<ACT>(tU, 1, r, h, G2, c2, 4 * wb, min(r, 4 * we),
-                         [&](int, int c, float g) { tG[c] = g * tT[c]; });
+        // one copy per address space of the parameters (LDS when staged), so
+        // that no access needs a flat (either-space) load
+        auto bottleneck = [&](const uint16_t* g1, const uint16_t* b1, const uint16_t* g2, const uint16_t* b2) {
+            vgate_hidden<ACT>(tT, 0, 1, r, h, g1, b1, tU, red);
+            vgate_gates<ACT>(tU, 1, r, h, g2, b2, 4 * wb, min(r, 4 * we),
+                             [&](int, int c, float g) { tG[c] = g * tT[c]; });
+        };
+        if (staged) {
+            const int n1 = r * h;
+            bottleneck(gst, gst + n1, gst + n1 + h, gst + 2 * n1 + h);
+        } else {
+            bottleneck(a.G1, a.c1, a.G2, a.c2);
+        }
         __syncthreads();
         for (int i = tid; i < we - wb; i += DEC_THREADS) {
             const int c0 = 4 * (wb + i);

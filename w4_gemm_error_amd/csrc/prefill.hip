@@ -290,11 +290,21 @@ void ec_reduce_vgate_kernel(EcReduceKArgs a)
     if (a.vg_staged)
         vgate_stage_store(G1, c1, G2, c2, r, h, gv, gst);
     __syncthreads();
-    vgate_hidden<ACT>(&tT[0][0], VG_RMAX + 1, VG_NT, r, h, G1, c1, tU, red);
     uint16_t* tg = a.tg + (size_t)(16 * rb + 4 * grp) * a.r_pad;
-    vgate_gates<ACT>(tU, VG_NT, r, h, G2, c2, 0, r, [&](int t, int c, float g) {
-        tg[(size_t)t * a.r_pad + c] = f32_to_act<ACT>(g * tT[t][c]);
-    });
+    // one copy per address space of the parameters (LDS when staged), so
+    // that no access needs a flat (either-space) load
+    auto bottleneck = [&](const uint16_t* g1, const uint16_t* b1, const uint16_t* g2, const uint16_t* b2) {
+        vgate_hidden<ACT>(&tT[0][0], VG_RMAX + 1, VG_NT, r, h, g1, b1, tU, red);
+        vgate_gates<ACT>(tU, VG_NT, r, h, g2, b2, 0, r, [&](int t, int c, float g) {
+            tg[(size_t)t * a.r_pad + c] = f32_to_act<ACT>(g * tT[t][c]);
+        });
+    };
+    if (a.vg_staged) {
+        const int n1 = r * h;
+        bottleneck(gst, gst + n1, gst + n1 + h, gst + 2 * n1 + h);
+    } else {
+        bottleneck(a.G1, a.c1, a.G2, a.c2);
+    }
     const int pad = a.r_pad - r;
     for (int e = tid; e < VG_NT * pad; e += PF_THREADS)
         tg[(size_t)(e / pad) * a.r_pad + r + e % pad] = f32_to_act<ACT>(0.0f);
