@@ -159,20 +159,17 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
     uint64_t* tw = reinterpret_cast<uint64_t*>(red + VG_THREADS);      // [w8], 8-byte aligned
     uint16_t* gst = reinterpret_cast<uint16_t*>(tw + w8);   // staged gate parameters (if they fit)
     const int nrep = min(DEC_NREP, a.n_main);               // slots that have readers
-    int m0 = j, mstep = nred, wb = 0, we = w8;
-    if (nred >= M) {
-        m0 = j % M;
-        mstep = M;
-        const int cnt = (nred - 1 - m0) / M + 1, sub = j / M;
-        const int sh = (w8 + cnt - 1) / cnt;
-        wb = min(w8, sub * sh);
-        we = min(w8, wb + sh);
-        // Nothing to publish: read nothing either.  (A slot's last reader
-        // clears the partial sums once the slot is complete, and it is
-        // complete only when every reducer that reads them has written.)
-        if (wb >= we)
-            return;
-    }
+    // Reducer j takes tokens j, j + nred, ...: at most one reducer per
+    // token, which publishes all of the token's words.  Reducers without a
+    // token read nothing.  (A slot's last reader clears the partial sums once
+    // the slot is complete, and it is complete only when every reducer that
+    // reads them has written.)  Splitting a token's words over several
+    // reducers, each of which reads the whole row and runs the bottleneck,
+    // measured slower: every extra reader of the row adds to the traffic
+    // that the row's arrival waits behind.
+    const int m0 = j, mstep = nred, wb = 0, we = w8;
+    if (m0 >= M)
+        return;
     // the gate parameters do not depend on T: their loads go out first and
     // overlap the wait for the partial sums
     const uint16_t *G1 = a.G1, *c1 = a.c1, *G2 = a.G2, *c2 = a.c2;
