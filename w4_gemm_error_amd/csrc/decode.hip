@@ -266,6 +266,34 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
     }
 }
 
+// Scalar-gate reducers: the last nred EC workgroups, each with a share of
+// the M r_pad / 4 words of T_g, for which thread groups split the P slices
+// (slice q -> group q mod ng, eight loads in flight per thread).  nred
+// starts at M (one token's worth of words each) and doubles, up to
+// min(P, DEC_EC_RMAX), while a group would walk more than 16 slices (more
+// than two trips).  Fewer pollers get the partial sums sooner: against
+// every EC workgroup reducing, 10.4 vs 10.7 us at one token (K = 4096,
+// r = 64) and 11.2 vs 11.6 us at four; a single reducer for 16 tokens took
+// 18.0 us.
+__host__ __device__ inline int dec_scalar_groups(int P, int M, int share)
+{
+    const int g = DEC_THREADS / (4 * share + M);
+    return g < 1 ? 1 : (g < P ? g : P);
+}
+__host__ __device__ inline int dec_scalar_reducers(int P, int M, int r_pad)
+{
+    const int cap = P < DEC_EC_RMAX ? P : DEC_EC_RMAX;
+    const int n8 = M * r_pad / 4;
+    int nred = M < cap ? M : cap;
+    for (;;) {
+        const int share = (n8 + nred - 1) / nred;
+        const int ng = dec_scalar_groups(P, M, share);
+        if ((P + ng - 1) / ng <= 16 || nred >= cap)
+            return nred;
+        nred = 2 * nred < cap ? 2 * nred : cap;
+    }
+}
+
 template <int ACT>
 __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 {
@@ -337,9 +365,15 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
         decode_vgate_reduce<ACT>(a, smem, p - red0, a.P - red0);
         return;
     }
+    // With the scalar gate only the last dec_scalar_reducers() of those
+    // reduce: fewer workgroups polling the partial sums get them sooner.
+    const int nred = dec_scalar_reducers(a.P, M, a.r_pad);
+    const int rbeg = a.P - nred;
+    if (p < rbeg)
+        return;
     const int n8 = M * a.r_pad / 4;
-    const int share = (n8 + (a.P - red0) - 1) / (a.P - red0);
-    const int w0 = (p - red0) * share, w1 = min(n8, w0 + share);
+    const int share = (n8 + nred - 1) / nred;
+    const int w0 = (p - rbeg) * share, w1 = min(n8, w0 + share);
     if (w0 >= w1)
         return;
     const int nw = w1 - w0;
@@ -348,7 +382,7 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     // ng thread groups split the P slices (slice q -> group q mod ng); ng
     // depends on the shape only, so every workgroup adds a token's logit in
     // the same order
-    const int ng = max(1, min(a.P, DEC_THREADS / (4 * share + M)));
+    const int ng = dec_scalar_groups(a.P, M, share);
     __syncthreads();                                        // the slice in LDS is no longer read
     const int tsum_off = ng > 1 ? ng * ne : 0;
     float* red = reinterpret_cast<float*>(smem);            // [ng][ne] (ng > 1 only)
@@ -1023,7 +1057,7 @@ static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
         return 0;
     const size_t at = (size_t)ec_slice_bytes(r, p.KS) + (size_t)p.KS * 2;
     // the reduction's share: [ng][ne] sums (<= 256 floats, or none), [ne] totals, [nw] words
-    const int nred = std::min(p.P, DEC_EC_RMAX);
+    const int nred = dec_scalar_reducers(p.P, M, p.r_pad);
     const int share = (M * p.r_pad / 4 + nred - 1) / nred;
     const size_t fin = ((size_t)DEC_THREADS + 4 * share + M + 2) * 4 + (size_t)share * 8;
     // vector gate: [r_pad] T, [r_pad] gated T, [VG_HMAX] bottleneck,
