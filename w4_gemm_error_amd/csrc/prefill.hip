@@ -173,26 +173,32 @@ void ec_reduce_kernel(EcReduceKArgs a)
     const int ne = nb * 64;                          // fragments per slice of this row block
     const floatx4* base = a.partial + ((size_t)mt * a.ks * 4 + w) * ne;
     const size_t zs = (size_t)4 * ne;
-    // wavefront q adds slices q, q + 4, ... of both blocks (fixed order)
+    // wavefront q adds slices q, q + 4, ... of both blocks (fixed order,
+    // ascending); the loads of both blocks for up to eight slices each go
+    // out together, so that a batch costs one trip to memory
+    const floatx4* src0 = base + cb * 64 + l;
+    const floatx4* src1 = base + (nb - 1) * 64 + l;
+    floatx4 t0 = (floatx4){0.f, 0.f, 0.f, 0.f}, t1 = t0;
+    for (int z0 = q; z0 < a.ks; z0 += 32) {
+        floatx4 v0[8], v1[8];
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const floatx4* src = base + (which == 0 ? cb : nb - 1) * 64 + l;
-        floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f};
-        int z = q;
-        for (; z + 28 < a.ks; z += 32) {
-            floatx4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = src[(size_t)(z + 4 * i) * zs];
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                t += v[i];
+        for (int i = 0; i < 8; ++i) {
+            const int z = min(z0 + 4 * i, a.ks - 1);          // past the last slice: re-read it, unused
+            v0[i] = src0[(size_t)z * zs];
+            v1[i] = src1[(size_t)z * zs];
         }
-        for (; z < a.ks; z += 4)
-            t += src[(size_t)z * zs];
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            tl[which][q][l][v] = t[v];
+        for (int i = 0; i < 8; ++i) {
+            if (z0 + 4 * i < a.ks) {
+                t0 += v0[i];
+                t1 += v1[i];
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        tl[0][q][l][v] = t0[v];
+        tl[1][q][l][v] = t1[v];
     }
     __syncthreads();
     // gate logits of the 16 rows: lane column 0 of the gate block (row
