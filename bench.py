@@ -34,16 +34,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0}   # dense fp16 / bf16 MFMA
 MALL_BYTES = 256 << 20
 
-# name -> (config id, tokens, entry point)
+# name -> (synthetic layer, tokens, entry point)
 WORKLOADS = {
-    "decode_up_proj_8b_m1": (2, 1, "decode"),
-    "decode_up_proj_8b_m4": (2, 4, "decode"),
-    "decode_up_proj_8b_m16": (2, 16, "decode"),
-    "tiny_m16": (1, 16, "decode"),
-    "prefill_out_proj_8b_m2048": (3, 2048, "prefill"),
-    "batched_down_proj_8b_g128_m256": (4, 256, "prefill"),
-    "mlp_70b_bf16_m64": (5, 64, "prefill"),
-    "mlp_70b_bf16_m4096": (5, 4096, "prefill"),
+    "decode_up_proj_8b_m1": ("decode_up_proj_8b", 1, "decode"),
+    "decode_up_proj_8b_m4": ("decode_up_proj_8b", 4, "decode"),
+    "decode_up_proj_8b_m16": ("decode_up_proj_8b", 16, "decode"),
+    "tiny_m16": ("tiny", 16, "decode"),
+    "prefill_out_proj_8b_m2048": ("prefill_out_proj_8b", 2048, "prefill"),
+    "batched_down_proj_8b_g128_m256": ("batched_down_proj_8b_g128", 256, "prefill"),
+    "mlp_70b_bf16_m64": ("mlp_70b_bf16", 64, "prefill"),
+    "mlp_70b_bf16_m4096": ("mlp_70b_bf16", 4096, "prefill"),
 }
 DEFAULT_WORKLOAD = "decode_up_proj_8b_m1"
 
@@ -224,11 +224,11 @@ def latency_table(torch, w4, synth, dev):
         del pk, packed
 
 
-def xfp_main(args, torch, w4, synth, dev, cfg_id, M):
+def xfp_main(args, torch, w4, synth, dev, layer, M):
     """Codebook decode: Y = X Wh^T, Wh = per-channel 16-entry codebook lookups
     plus a sparse fp16 outlier residual.  The layer's weights with 0.5 % of
     them planted as x25 outliers, converted offline (untimed)."""
-    d = synth.make_layer(cfg_id, M, seed=args.seed, r=0)
+    d = synth.make_layer(layer, M, seed=args.seed, r=0)
     N, K, act = d["N"], d["K"], d["act"]
     tdt = torch.float16 if act == "fp16" else torch.bfloat16
     x = synth.make_xfp(synth.plant_outliers(d["W"], seed=args.seed))
@@ -342,7 +342,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the layer runs on one MI355X); "
+        print("bench.py: measures one GPU only (the layer runs on one MI355X); "
               "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
@@ -370,14 +370,14 @@ def main():
         print("bench.py: --path unfused/semi applies to the prefill workloads with the scalar gate",
               file=sys.stderr)
         sys.exit(2)
-    cfg_id, M, phase = WORKLOADS[args.workload]
+    layer, M, phase = WORKLOADS[args.workload]
     if args.method == "xfp":
         if phase != "decode" or args.gate != "scalar" or args.path != "fused":
             print("bench.py: --method xfp applies to the decode workloads (no --gate / --path)", file=sys.stderr)
             sys.exit(2)
-        xfp_main(args, torch, w4, synth, dev, cfg_id, M)
+        xfp_main(args, torch, w4, synth, dev, layer, M)
         return
-    d = synth.make_layer(cfg_id, M, seed=args.seed, r=args.rank)
+    d = synth.make_layer(layer, M, seed=args.seed, r=args.rank)
     N, K, r, G, act = d["N"], d["K"], d["r"], d["group_size"], d["act"]
     tdt = torch.float16 if act == "fp16" else torch.bfloat16
 

@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     W4EC_OK = 0,
     W4EC_ERR_INVALID_ARG = -1,  /* null pointer, bad shape, misalignment, bad zero point */
-    W4EC_ERR_UNSUPPORTED = -2,  /* shape outside what this build supports (see above)   */
+    W4EC_ERR_UNSUPPORTED = -2,  /* shape outside what the library supports (see above) */
     W4EC_ERR_WORKSPACE = -3,    /* workspace missing or smaller than w4ec_workspace_bytes */
     W4EC_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed           */
 } w4ec_status;

@@ -29,7 +29,7 @@ def _print(*a):
 @pytest.mark.parametrize("N,K,G", [(512, 512, 512), (300, 1024, 128), (37, 384, 128)])
 def test_quantize_bit_exact(N, K, G):
     _print(f"quantize N={N} K={K} G={G}")
-    d = synth.make_layer(1, 1, seed=3, N=N, K=K, group_size=G)
+    d = synth.make_layer("tiny", 1, seed=3, N=N, K=K, group_size=G)
     q, s, z, _ = gpu_quantize(d)
     oq, os_, oz = oracle.rtn_quantize(d["W"], G)
     assert np.array_equal(q.cpu().numpy(), oq)
@@ -96,7 +96,7 @@ SMALL = [
 
 
 def small_layer(act, M, N, K, r, G, seed=5):
-    cfg = synth.CONFIGS[5] if act == "bf16" else synth.CONFIGS[1]
+    cfg = synth.LAYERS["mlp_70b_bf16"] if act == "bf16" else synth.LAYERS["tiny"]
     return synth.make_layer(cfg, M, seed=seed, N=N, K=K, r=r, group_size=G)
 
 
@@ -145,7 +145,7 @@ def test_bf16_prefill_plain_w4(M, K, G):
 def test_deterministic_and_workspace_reuse(phase, M):
     _print(f"determinism {phase} M={M}")
     t = torch()
-    d = synth.make_layer(4, M, seed=2, N=1024, K=2048)   # group 128, split-K in prefill
+    d = synth.make_layer("batched_down_proj_8b_g128", M, seed=2, N=1024, K=2048)   # group 128, split-K in prefill
     _, _, _, packed = gpu_quantize(d)
     ws = t.zeros(w4.w4ec_workspace_bytes(M, d["N"], d["K"], d["r"], d["group_size"]),
                  dtype=t.uint8, device="cuda")
@@ -173,20 +173,20 @@ def test_phase_dispatch_agrees():
 
 FULL = [
     # cfg, M, phase, sampled rows (None = all)
-    (1, 16, "decode", None),
-    (2, 1, "decode", None),
-    (2, 4, "decode", None),
-    (2, 16, "decode", None),
-    (3, 2048, "prefill", [0, 1, 77, 1023, 1500, 2047]),
-    (4, 256, "prefill", [0, 5, 128, 255]),
-    (5, 64, "prefill", [0, 31, 63]),
-    (5, 4096, "prefill", [0, 2049, 4095]),
+    ("tiny", 16, "decode", None),
+    ("decode_up_proj_8b", 1, "decode", None),
+    ("decode_up_proj_8b", 4, "decode", None),
+    ("decode_up_proj_8b", 16, "decode", None),
+    ("prefill_out_proj_8b", 2048, "prefill", [0, 1, 77, 1023, 1500, 2047]),
+    ("batched_down_proj_8b_g128", 256, "prefill", [0, 5, 128, 255]),
+    ("mlp_70b_bf16", 64, "prefill", [0, 31, 63]),
+    ("mlp_70b_bf16", 4096, "prefill", [0, 2049, 4095]),
 ]
 
 
 @pytest.mark.parametrize("cfg,M,phase,rows", FULL)
 def test_full_size_parity(cfg, M, phase, rows):
-    _print(f"full cfg{cfg} M={M} {phase}")
+    _print(f"full {cfg} M={M} {phase}")
     d = synth.make_layer(cfg, M, seed=0)
     q, s, z, packed = gpu_quantize(d)
     codes = oracle.rtn_quantize(d["W"], d["group_size"])
@@ -196,7 +196,7 @@ def test_full_size_parity(cfg, M, phase, rows):
     Y = gpu_layer(d, packed, phase)
     ref = oracle_layer(d, codes, rows=rows)
     Ysub = Y if rows is None else Y[rows]
-    worst = assert_close(Ysub, ref, d["act"], f"cfg{cfg} M={M}")
+    worst = assert_close(Ysub, ref, d["act"], f"{cfg} M={M}")
     _print(f"  worst err/tol {worst:.3f}")
 
 

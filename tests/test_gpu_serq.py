@@ -58,7 +58,7 @@ def oracle_serq(d, codes, S, R, rows=None):
 
 
 def small_layer(act, M, N, K, G, seed=5):
-    cfg = synth.CONFIGS[5] if act == "bf16" else synth.CONFIGS[1]
+    cfg = synth.LAYERS["mlp_70b_bf16"] if act == "bf16" else synth.LAYERS["tiny"]
     return synth.make_layer(cfg, M, seed=seed, N=N, K=K, r=8, group_size=G)
 
 
@@ -116,10 +116,10 @@ def test_serq_out_of_range_index_is_flagged(phase):
 
 FULL = [
     # cfg, M, phase, sampled rows (None = all)
-    (2, 1, "decode", None),
-    (2, 16, "decode", None),
-    (3, 2048, "prefill", [0, 1, 77, 1023, 2047]),
-    (5, 64, "prefill", [0, 31, 63]),
+    ("decode_up_proj_8b", 1, "decode", None),
+    ("decode_up_proj_8b", 16, "decode", None),
+    ("prefill_out_proj_8b", 2048, "prefill", [0, 1, 77, 1023, 2047]),
+    ("mlp_70b_bf16", 64, "prefill", [0, 31, 63]),
 ]
 
 
@@ -127,13 +127,13 @@ FULL = [
 def test_serq_full_size_parity(cfg, M, phase, rows):
     """The salient channels are the configs' outlier channels (the ones whose
     activation scale marks them), as an offline permutation would gather."""
-    _print(f"serq full cfg{cfg} M={M} {phase}")
+    _print(f"serq full {cfg} M={M} {phase}")
     d = synth.make_layer(cfg, M, seed=0)
     S = np.asarray(d["outlier_channels"], dtype=np.int32)
-    R = synth.to_act_bits(np.random.default_rng(cfg).normal(0.0, 0.01, (len(S), d["N"])), d["act"])
+    R = synth.to_act_bits(np.random.default_rng(synth.SEEDS[cfg]).normal(0.0, 0.01, (len(S), d["N"])), d["act"])
     _, _, _, packed = gpu_quantize(d)
     codes = oracle.rtn_quantize(d["W"], d["group_size"])
     Y, _ = gpu_serq(d, packed, phase, S, R)
     ref = oracle_serq(d, codes, S, R, rows=rows)
-    worst = assert_close(Y if rows is None else Y[rows], ref, d["act"], f"serq cfg{cfg} M={M}")
+    worst = assert_close(Y if rows is None else Y[rows], ref, d["act"], f"serq {cfg} M={M}")
     _print(f"  worst err/tol {worst:.3f}")

@@ -23,7 +23,7 @@ def _print(*a):
 
 
 def small_layer(act, M, N, K, r, G, seed=5):
-    cfg = synth.CONFIGS[5] if act == "bf16" else synth.CONFIGS[1]
+    cfg = synth.LAYERS["mlp_70b_bf16"] if act == "bf16" else synth.LAYERS["tiny"]
     return synth.make_layer(cfg, M, seed=seed, N=N, K=K, r=r, group_size=G)
 
 
@@ -78,7 +78,7 @@ def test_unfused_prefill_parity(act, M, N, K, r, G):
 
 def test_unfused_matches_fused_at_full_size():
     _print("unfused vs fused, 2048 x 4096 x 4096")
-    d = synth.make_layer(3, 2048, seed=0)
+    d = synth.make_layer("prefill_out_proj_8b", 2048, seed=0)
     _, _, _, packed = gpu_quantize(d)
     Yu = unfused(d, packed, two_streams=True)
     Yf = gpu_layer(d, packed, "prefill")

@@ -57,7 +57,7 @@ def oracle_vgate(d, codes, p, *, rows=None, c2=None, G2=None):
 
 
 def small_layer(act, M, N, K, r, G, seed=5):
-    cfg = synth.CONFIGS[5] if act == "bf16" else synth.CONFIGS[1]
+    cfg = synth.LAYERS["mlp_70b_bf16"] if act == "bf16" else synth.LAYERS["tiny"]
     return synth.make_layer(cfg, M, seed=seed, N=N, K=K, r=r, group_size=G)
 
 
@@ -111,18 +111,18 @@ def test_vgate_closed_and_open(phase):
 
 FULL = [
     # cfg, M, phase, sampled rows (None = all), h
-    (2, 1, "decode", None, 16),
-    (2, 16, "decode", None, 16),
-    (3, 2048, "prefill", [0, 1, 77, 1023, 2047], 16),
-    (5, 64, "prefill", [0, 31, 63], 32),
+    ("decode_up_proj_8b", 1, "decode", None, 16),
+    ("decode_up_proj_8b", 16, "decode", None, 16),
+    ("prefill_out_proj_8b", 2048, "prefill", [0, 1, 77, 1023, 2047], 16),
+    ("mlp_70b_bf16", 64, "prefill", [0, 31, 63], 32),
 ]
 
 
 @pytest.mark.parametrize("cfg,M,phase,rows,h", FULL)
 def test_vgate_full_size_parity(cfg, M, phase, rows, h):
-    _print(f"vgate full cfg{cfg} M={M} {phase}")
+    _print(f"vgate full {cfg} M={M} {phase}")
     d = synth.make_layer(cfg, M, seed=0)
-    p = vg_params(d, h, seed=cfg)
+    p = vg_params(d, h, seed=synth.SEEDS[cfg])
     q, s, z, packed = gpu_quantize(d)
     codes = oracle.rtn_quantize(d["W"], d["group_size"])
     del q, s, z
@@ -133,7 +133,7 @@ def test_vgate_full_size_parity(cfg, M, phase, rows, h):
                                  act=d["act"], rows=rows)
     g = parts["gamma"]
     assert np.mean((g > 0.05) & (g < 0.95)) > 0.5, "gates saturated: the case would not test them"
-    worst = assert_close(Y if rows is None else Y[rows], parts["Y"], d["act"], f"vgate cfg{cfg} M={M}")
+    worst = assert_close(Y if rows is None else Y[rows], parts["Y"], d["act"], f"vgate {cfg} M={M}")
     _print(f"  worst err/tol {worst:.3f}")
 
 

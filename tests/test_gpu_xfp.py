@@ -28,7 +28,7 @@ def pack_nibbles(idx):
 
 
 def xfp_layer(act, M, N, K, seed=0, frac=0.005, dense_row=None, k_sigma=4.0):
-    cfg = 5 if act == "bf16" else 1
+    cfg = "mlp_70b_bf16" if act == "bf16" else "tiny"
     d = synth.make_layer(cfg, M, seed=seed, N=N, K=K, r=8, group_size=K)
     W = synth.plant_outliers(d["W"], frac=frac, seed=seed)
     max_frac = 0.02

@@ -203,7 +203,7 @@ def test_on_grid_weights_reproduce_matmul(G):
 
 
 def cfg1_inputs(seed=0, M=16):
-    d = synth.make_layer(1, M, seed)
+    d = synth.make_layer("tiny", M, seed)
     qc, s, z = oracle.rtn_quantize(d["W"], d["group_size"])
     return d, qc, s, z
 
@@ -287,12 +287,12 @@ def test_equivariance_and_row_subsets():
 
 
 def test_synth_shapes_and_outliers():
-    d = synth.make_layer(2, 4, seed=0)
+    d = synth.make_layer("decode_up_proj_8b", 4, seed=0)
     assert d["X"].shape == (4, 4096) and d["W"].shape == (14336, 4096)
     assert len(d["outlier_channels"]) == 41
-    d5 = synth.make_layer(5, 2, seed=0, N=256)
+    d5 = synth.make_layer("mlp_70b_bf16", 2, seed=0, N=256)
     assert d5["act"] == "bf16" and len(d5["outlier_channels"]) == 41
-    d3 = synth.make_layer(3, 256, seed=0, N=64)
+    d3 = synth.make_layer("prefill_out_proj_8b", 256, seed=0, N=64)
     g = expit(synth.act_bits_to_f64(d3["X"], "fp16") @ synth.act_bits_to_f64(d3["w_g"], "fp16") + d3["b_g"])
     inside = np.mean((g > 0.05) & (g < 0.95))
     assert inside > 0.9

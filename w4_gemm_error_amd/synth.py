@@ -38,13 +38,17 @@ class LayerConfig:
     wg_std: float = 0.05
 
 
-CONFIGS = {
-    1: LayerConfig("tiny", (16,), 512, 512, 8, 512, "fp16", 0.01, 20.0, "plain"),
-    2: LayerConfig("decode_up_proj_8b", (1, 4, 16), 4096, 14336, 64, 4096, "fp16", 0.01, 20.0, "plain"),
-    3: LayerConfig("prefill_out_proj_8b", (2048,), 4096, 4096, 64, 4096, "fp16", 0.01, 20.0, "calibrated"),
-    4: LayerConfig("batched_down_proj_8b_g128", (256,), 14336, 4096, 128, 128, "fp16", 0.01, 20.0, "plain"),
-    5: LayerConfig("mlp_70b_bf16", (64, 4096), 8192, 28672, 128, 8192, "bf16", 0.005, 30.0, "plain"),
-}
+# the synthetic layers, by name; SEEDS gives each a small integer for the
+# generators of its extra inputs
+LAYERS = {c.name: c for c in (
+    LayerConfig("tiny", (16,), 512, 512, 8, 512, "fp16", 0.01, 20.0, "plain"),
+    LayerConfig("decode_up_proj_8b", (1, 4, 16), 4096, 14336, 64, 4096, "fp16", 0.01, 20.0, "plain"),
+    LayerConfig("prefill_out_proj_8b", (2048,), 4096, 4096, 64, 4096, "fp16", 0.01, 20.0, "calibrated"),
+    LayerConfig("batched_down_proj_8b_g128", (256,), 14336, 4096, 128, 128, "fp16", 0.01, 20.0, "plain"),
+    LayerConfig("mlp_70b_bf16", (64, 4096), 8192, 28672, 128, 8192, "bf16", 0.005, 30.0, "plain"),
+)}
+SEEDS = {"tiny": 1, "decode_up_proj_8b": 2, "prefill_out_proj_8b": 3, "batched_down_proj_8b_g128": 4,
+         "mlp_70b_bf16": 5}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -79,7 +83,7 @@ def make_layer(cfg, M: int, seed: int = 0, *, K=None, N=None, r=None,
     [K, r]), B (act bits [r, N]), w_g (act bits [K]), b_g (float), the shape,
     ``act`` and the outlier channel indices.
     """
-    c = CONFIGS[cfg] if isinstance(cfg, int) else cfg
+    c = LAYERS[cfg] if isinstance(cfg, str) else cfg
     K = c.K if K is None else int(K)
     N = c.N if N is None else int(N)
     r = c.r if r is None else int(r)
