@@ -169,6 +169,22 @@ def test_phase_dispatch_agrees():
     assert (np.abs(a - b) <= 2 * bound).all()
 
 
+def test_special_cases_full_size_decode():
+    """The 8B up-projection at one token (N 14336, K 4096, r 64): the plain
+    W4 layer (r = 0), a closed gate (b_g = -inf: the plain layer, bitwise),
+    and a fully open gate with no gate vector (the static compensation)."""
+    _print("special cases, decode_up_proj_8b M=1")
+    d = synth.make_layer("decode_up_proj_8b", 1, seed=0)
+    _, _, _, packed = gpu_quantize(d)
+    codes = oracle.rtn_quantize(d["W"], d["group_size"])
+    plain = gpu_layer(d, packed, "decode", r=0)
+    assert_close(plain, oracle_layer(d, codes, r=0), "fp16", "r=0")
+    closed = gpu_layer(d, packed, "decode", b_g=-math.inf)
+    assert np.array_equal(synth.act_bits_to_f64(closed, "fp16"), synth.act_bits_to_f64(plain, "fp16"))
+    opened = gpu_layer(d, packed, "decode", b_g=math.inf, with_gate=False)
+    assert_close(opened, oracle_layer(d, codes, b_g=math.inf, with_gate=False), "fp16", "g=1")
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 FULL = [
