@@ -103,6 +103,18 @@ def traffic_from_profiles(kernel_key):
     return e.get("bytes_per_launch")
 
 
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, phase, budget_s):
     """The float64 oracle on the host, on a bounded sample of the workload."""
     import oracle
@@ -132,7 +144,8 @@ def cpu_baseline(d, phase, budget_s):
         value = layer_flops(rows_per_call, N, K, r) / per_call / 1e12
         unit = "TFLOP/s"
     sample = (f"{n} oracle call(s) of {rows_per_call} of {M} token(s) "
-              f"({frac:.3g} of the batch), {el:.1f} s total, weights quantized beforehand")
+              f"({frac:.3g} of the batch), {el:.1f} s total, weights quantized beforehand, "
+              f"host CPU: {host_cpu_model()}")
     return {"value": round(value, 6), "unit": unit, "cores": int(oracle.max_threads()),
             "kind": "oracle", "sample": sample}
 
