@@ -71,8 +71,8 @@ def layer_flops(M, N, K, r, h=0):
 # the sources each measured kernel is built from (its counters stay valid
 # while these are unchanged)
 KERNEL_SOURCES = {
-    "decode_kernel": ["decode.hip", "ec_tile.h", "w4ec_common.h", "w4ec_launch.h"],
-    "prefill_call": ["prefill.hip", "ec_tile.h", "w4ec_common.h", "w4ec_launch.h"],
+    "decode_kernel": ["decode.hip", "ec_tile.h", "w4ec_common.h", "w4ec_launch.h", "api.cpp"],
+    "prefill_call": ["prefill.hip", "ec_tile.h", "w4ec_common.h", "w4ec_launch.h", "api.cpp"],
 }
 
 
