@@ -525,9 +525,10 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     // then a ring of DEPTH weight panels, consumed one by one as they arrive
     // and refilled unconditionally (indices clamped to the wavefront's last
     // panel, extra panels multiplied by zero) so that the ring's waits stay
-    // exact.  With an EC to wait for, the activations are staged completely
-    // before the first weight load, which lets the EC workgroups' loads reach
-    // memory ahead of the weight stream.
+    // exact.  STAGE_FIRST stages the activations completely before the first
+    // weight load (so that EC loads reach memory ahead of the weight stream);
+    // the launch plan currently issues the ring first in every case, which
+    // measured faster once the EC reduction ran on few workgroups.
     // (Every load below is issued unconditionally -- indices are clamped and
     // unwanted values zeroed afterwards -- so that the compiler can count the
     // loads in flight and wait for exactly the one it needs.)
