@@ -12,9 +12,12 @@ EC parameters are replicated R times (R x layer bytes >= 512 MB, twice the
 step streams its weights from HBM.
 
 Prints one JSON line: the whole-job rate (decode: algorithmic HBM GB/s;
-prefill: TFLOP/s), the dominant kernel's roofline from the HIP events that
-bracket the timed region, and the float64 CPU oracle timed on a bounded
-sample on the host.
+prefill: TFLOP/s), the roofline that binds the call (HBM or MFMA, whichever
+takes longer at its peak) from the HIP events that bracket the timed region,
+and the float64 CPU oracle timed on a bounded sample on the host.  Without
+--workload the line is the one-token decode of the 8B up-projection, and its
+"prefill" object times the 2048-token prefill of the 8B out-projection in
+the same run: the metric's two halves.
 """
 from __future__ import annotations
 
@@ -46,6 +49,7 @@ WORKLOADS = {
     "mlp_70b_bf16_m4096": ("mlp_70b_bf16", 4096, "prefill"),
 }
 DEFAULT_WORKLOAD = "decode_up_proj_8b_m1"
+PREFILL_WORKLOAD = "prefill_out_proj_8b_m2048"   # the prefill half of the default line
 
 
 def layer_bytes(M, N, K, r, G, has_gate=True, h=0):
@@ -66,6 +70,22 @@ def layer_flops(M, N, K, r, h=0):
     gating/add."""
     gate = 2 * M * K * r + 4 * M * r * h if h else 2 * M * K * (r + 1)
     return 2 * M * N * K + gate + 2 * M * r * N + 2 * M * N
+
+
+def roofline(nbytes, flops, seconds, act):
+    """The binding roofline of one call: HBM if moving its algorithmic bytes
+    at 8 TB/s takes longer than its algorithmic flops at the dense MFMA
+    peak, else MFMA; `achieved` is the rate in that roofline's unit."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[act] * 1e12)
+    if t_hbm >= t_mfma:
+        achieved = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = flops / seconds / 1e12
+    peak = MFMA_PEAK_TFLOPS[act]
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4)}
 
 
 # the sources each measured kernel is built from (its counters stay valid
@@ -286,8 +306,7 @@ def xfp_main(args, torch, w4, synth, dev, layer, M):
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if graph is None:
-        torch.cuda._sleep(int(100e6))
+    torch.cuda._sleep(int(100e6) if graph is None else int(20e6))
     start.record()
     if graph is not None:
         graph.replay()
@@ -326,7 +345,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help=f"one workload only (default: {DEFAULT_WORKLOAD}, with {PREFILL_WORKLOAD} "
+                         "timed in the same run as the line's prefill half)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work on the host")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -353,6 +374,9 @@ def main():
                     help="prefill latency table: time the three paths over a grid of (M, r, N, K) and print "
                          "one JSON line per point (no roofline / CPU legs)")
     args = ap.parse_args()
+    args.default_workload = args.workload is None
+    if args.workload is None:
+        args.workload = DEFAULT_WORKLOAD
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only (the layer runs on one MI355X); "
@@ -390,6 +414,19 @@ def main():
             sys.exit(2)
         xfp_main(args, torch, w4, synth, dev, layer, M)
         return
+    out = measure_layer(args, args.workload, torch, w4, synth, dev)
+    if args.default_workload and args.method == "spear" and args.gate == "scalar" and args.rank is None:
+        # the metric has two halves: decode HBM GB/s (the line's value) and
+        # prefill TFLOP/s, timed in the same run on the 2048-token prefill
+        pf = measure_layer(args, PREFILL_WORKLOAD, torch, w4, synth, dev)
+        out["prefill"] = {k: pf[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                             "roofline", "cpu_baseline")}
+    print(json.dumps(out), flush=True)
+
+
+def measure_layer(args, workload, torch, w4, synth, dev):
+    """Time one workload of the W4 + EC layer; returns the JSON record."""
+    layer, M, phase = WORKLOADS[workload]
     d = synth.make_layer(layer, M, seed=args.seed, r=args.rank)
     N, K, r, G, act = d["N"], d["K"], d["r"], d["group_size"], d["act"]
     tdt = torch.float16 if act == "fp16" else torch.bfloat16
@@ -432,6 +469,7 @@ def main():
         nbytes = N * K // 2 + N * (K // G) * 4 + M * K * 2 + M * N * 2 + r * N * 2 + r * 4
     weight_bytes = packed0.numel() + ec_elems * 2
     R = max(1, -(-2 * MALL_BYTES // weight_bytes))
+
     def clone(t):
         if isinstance(t, tuple):
             return tuple(x.clone() for x in t)
@@ -485,8 +523,9 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if graph is None:
-        torch.cuda._sleep(int(100e6))   # hold the stream while the host queues the eager launches
+    # hold the stream while the host submits the work, so that the timed
+    # region starts with the first kernel, not with the host's submission
+    torch.cuda._sleep(int(100e6) if graph is None else int(20e6))
     start.record()
     if graph is not None:
         graph.replay()
@@ -516,23 +555,19 @@ def main():
     flops = layer_flops(M, N, K, r, h)
     if serq:
         flops = 2 * M * N * K + 2 * M * r * N + 2 * M * N      # main product, X[:, S] R, add
+    # the line's value: decode in algorithmic HBM GB/s, prefill in TFLOP/s
+    # (the metric's two halves); the roofline takes whichever bound binds
     if phase == "decode":
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
-        achieved = nbytes / kdur / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        kernel_key = f"decode_kernel/{args.workload}" + ("/vector_gate" if vector else "") + \
+        kernel_key = f"decode_kernel/{workload}" + ("/vector_gate" if vector else "") + \
             ("/serq" if serq else "")
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        achieved = flops / kdur / 1e12
-        peak = MFMA_PEAK_TFLOPS[act]
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-        kernel_key = f"prefill_call/{args.workload}" + ("/vector_gate" if vector else "") + \
+        kernel_key = f"prefill_call/{workload}" + ("/vector_gate" if vector else "") + \
             ("" if args.path == "fused" else f"/{args.path}") + ("/serq" if serq else "")
+    roof = roofline(nbytes, flops, kdur, act)
     roof["traffic"] = traffic_from_profiles(kernel_key)
     roof["kernel"] = kernel_name
     roof["kernel_us"] = round(kdur * 1e6, 3)
@@ -541,7 +576,7 @@ def main():
     if not args.no_cpu and not vector and not serq:
         cpu = cpu_baseline(d, phase, args.cpu_budget)
 
-    out = {
+    return {
         "metric": "W4+EC linear: decode HBM GB/s & prefill TFLOP/s, % of MI355X roofline",
         "value": round(value, 3),
         "unit": unit,
@@ -554,7 +589,7 @@ def main():
         "vs_baseline": None,
         "dtype": act,
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "r": r, "group_size": G,
+        "config": {"workload": workload, "M": M, "N": N, "K": K, "r": r, "group_size": G,
                    "act": act, "phase": phase, "method": args.method,
                    **({"salient_channels": r} if serq else {"gate": "vector" if vector else "scalar"}),
                    **({"path": args.path} if phase == "prefill" else {}),
@@ -565,7 +600,6 @@ def main():
         "cpu_baseline": cpu,
         "wall_s": round(wall, 4),
     }
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -55,7 +55,10 @@ typedef enum {
     W4EC_ERR_INVALID_ARG = -1,  /* null pointer, bad shape, misalignment, bad zero point */
     W4EC_ERR_UNSUPPORTED = -2,  /* shape outside what the library supports (see above) */
     W4EC_ERR_WORKSPACE = -3,    /* workspace missing or smaller than w4ec_workspace_bytes */
-    W4EC_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed           */
+    W4EC_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed           */
+    W4EC_ERR_TIMED_OUT = -5,    /* w4ec_workspace_status: a bounded wait gave up        */
+    W4EC_ERR_BAD_INDEX = -6     /* w4ec_workspace_status: a salient-channel index was   */
+                                /* outside [0, K) and was clamped                       */
 } w4ec_status;
 
 typedef enum { W4EC_FP16 = 0, W4EC_BF16 = 1 } w4ec_dtype;
@@ -102,14 +105,50 @@ int w4ec_unpack(const void* packed, int N, int K, int group_size,
  * this shape (the larger of the two when both apply; at least
  * W4EC_WS_STATE_BYTES when r > 0).  The workspace holds the gated rank-r
  * activations, partial sums and the counters through which workgroups hand
- * over partial results.  It must be zero-filled once when allocated.  Its
- * first W4EC_WS_STATE_BYTES bytes hold hand-over state that every call
- * returns to zero (a nonzero byte there after a call has completed means a
- * bounded wait inside a kernel timed out), so the workspace can be reused by
- * later calls on the same stream, of any shape and either phase, without
- * clearing.  Two calls that overlap in time must not share a workspace. */
+ * over partial results.  It must be zero-filled once when allocated (or
+ * passed to w4ec_workspace_reset).  Its first W4EC_WS_STATE_BYTES bytes hold
+ * hand-over state that every call returns to zero, so the workspace can be
+ * reused by later calls on the same stream, of any shape and either phase,
+ * without clearing.  Two calls that overlap in time must not share a
+ * workspace.
+ *
+ * Failures inside a call.  The decode kernel's workgroups hand partial
+ * results to each other and wait for them with bounded waits (a wait gives
+ * up after w4ec_wait_limit() polls, about a second by default), so a broken
+ * hand-over can never hang the GPU.  A wait that gives up records it in the
+ * workspace and turns the outputs that depend on it into NaN; the call
+ * itself has already returned W4EC_OK.  From then on the decode hand-over
+ * state in the workspace is not to be trusted: every later decode call that
+ * uses it writes NaN into all of Y, until w4ec_workspace_reset (the prefill
+ * calls wait for nothing and stay correct).  A salient-channel index outside [0, K)
+ * (w4ec_linear_*_serq) is also recorded, without the NaN outputs.
+ * w4ec_workspace_status reports both. */
 #define W4EC_WS_STATE_BYTES ((size_t)16 << 20)
 size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size);
+
+/* What the calls so far on this workspace recorded: W4EC_OK,
+ * W4EC_ERR_TIMED_OUT (a bounded wait gave up: the results of that call
+ * where they depend on it, and of every later decode call on this
+ * workspace, are NaN) or
+ * W4EC_ERR_BAD_INDEX (a salient-channel index was clamped).  Synchronizes
+ * `stream` and reads 16 bytes of the workspace.  W4EC_ERR_WORKSPACE for a
+ * missing or misaligned (256 B) workspace. */
+int w4ec_workspace_status(const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Zero the workspace's state region (its first W4EC_WS_STATE_BYTES bytes,
+ * or all of it when smaller) with a kernel on `stream` (asynchronous; no
+ * memset node in a captured graph): the recovery after a recorded failure,
+ * and an alternative to zero-filling a new workspace.  workspace_bytes must
+ * be a multiple of 16. */
+int w4ec_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Polls a bounded wait makes before it gives up, for every later launch in
+ * this process (default 4194304, about a second).  0 makes every wait give
+ * up at once, as if it had timed out: a way to exercise the failure path
+ * above from the host, with every kernel still exiting normally.  Not
+ * thread-safe with respect to launches already being prepared. */
+void w4ec_set_wait_limit(uint32_t polls);
+uint32_t w4ec_wait_limit(void);
 
 /* The layer, decode phase: 1 <= M <= 16 tokens, one kernel launch.
  *   X     device act [M, K]          packed  device blob from w4ec_pack

@@ -28,7 +28,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "w4ec_oracle.c")
 _BUILD_DIR = os.path.join(_HERE, "_build")
-_LIB_PATH = os.path.join(_BUILD_DIR, "libw4ec_oracle.so")
+# W4EC_ORACLE_SANITIZE=1 builds and loads a copy instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must then
+# preload the ASan runtime; tests/test_sanitizers.py runs the pins that way)
+_SANITIZE = os.environ.get("W4EC_ORACLE_SANITIZE") == "1"
+_LIB_PATH = os.path.join(_BUILD_DIR, "libw4ec_oracle_san.so" if _SANITIZE else "libw4ec_oracle.so")
 
 _lock = threading.Lock()
 _lib = None
@@ -42,6 +46,9 @@ def build(force: bool = True) -> str:
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
+    if _SANITIZE:
+        cmd[1:2] = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH

@@ -43,6 +43,57 @@ def gpu_quantize(d):
     return q, s, z, packed
 
 
+def nan_y(M, N, act):
+    """An output buffer filled with NaN, so that an element the kernels never
+    write cannot pass as a result left over from an earlier call."""
+    t = torch()
+    return t.full((M, N), float("nan"), dtype=t.float16 if act == "fp16" else t.bfloat16, device="cuda")
+
+
+def poison_workspace(ws):
+    """Fill the per-call part of a workspace (past the hand-over state,
+    which must stay zero between calls) with 0xFF bytes: NaN as fp16, bf16
+    and fp32, so that data a kernel reads before writing it shows up."""
+    if ws.numel() > w4.W4EC_WS_STATE_BYTES:
+        ws[w4.W4EC_WS_STATE_BYTES:].fill_(0xFF)
+    return ws
+
+
+def new_workspace(nbytes):
+    t = torch()
+    return poison_workspace(t.zeros(max(nbytes, 256), dtype=t.uint8, device="cuda"))
+
+
+def assert_all_finite(Y, what=""):
+    """Every element of Y (device tensor) is finite: no tile left unwritten."""
+    t = torch()
+    bad = int((~t.isfinite(Y.float())).sum().item())
+    assert bad == 0, f"{what}: {bad} non-finite output elements"
+
+
+def sample_rows(M):
+    """Tokens compared against the oracle at full size: every token up to 64;
+    one per 16-token MFMA block up to 256; beyond that one per 64 (M <= 2048)
+    or 128 tokens -- a token in every GEMM row tile -- placed so that the
+    16-token block hit inside a 128-token tile cycles through all eight from
+    tile to tile, at a lane row that moves too; plus the last token."""
+    if M <= 64:
+        return None
+    if M <= 256:
+        rows = [16 * b + (b * 5) % 16 for b in range((M + 15) // 16)]
+    else:
+        span = 64 if M <= 2048 else 128
+        per = 128 // span
+        nb = span // 16
+        rows = []
+        for T in range((M + 127) // 128):
+            for h in range(per):
+                blk = h * nb + (T + 2 * h) % nb
+                rows.append(T * 128 + 16 * blk + (7 * T + 3 * h) % 16)
+    rows.append(M - 1)
+    return sorted(set(min(x, M - 1) for x in rows))
+
+
 def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=None):
     act = d["act"]
     r = d["r"] if r is None else r
@@ -53,11 +104,13 @@ def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=N
     bg = d["b_g"] if b_g is None else b_g
     fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
     if workspace is None:
-        t = torch()
-        need = w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], r, d["group_size"])
-        workspace = t.zeros(max(need, 256), dtype=t.uint8, device="cuda")
-    Y = fn(X, packed, A, B, wg, bg, N=d["N"], group_size=d["group_size"], workspace=workspace)
+        workspace = new_workspace(w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], r, d["group_size"]))
+    else:
+        poison_workspace(workspace)
+    Y = nan_y(d["M"], d["N"], act)
+    fn(X, packed, A, B, wg, bg, N=d["N"], group_size=d["group_size"], workspace=workspace, Y=Y)
     torch().cuda.synchronize()
+    assert_all_finite(Y, f"{phase} M={d['M']}")
     # every call leaves the hand-over state at zero; a nonzero byte there
     # would mean that a bounded wait timed out
     state = workspace[: w4.W4EC_WS_STATE_BYTES]

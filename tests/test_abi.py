@@ -23,8 +23,28 @@ def test_library_exports_every_header_symbol():
 
 def test_status_strings():
     for code, name in [(0, "W4EC_OK"), (-1, "W4EC_ERR_INVALID_ARG"), (-2, "W4EC_ERR_UNSUPPORTED"),
-                       (-3, "W4EC_ERR_WORKSPACE"), (-4, "W4EC_ERR_HIP"), (7, "W4EC_UNKNOWN_STATUS")]:
+                       (-3, "W4EC_ERR_WORKSPACE"), (-4, "W4EC_ERR_HIP"), (-5, "W4EC_ERR_TIMED_OUT"),
+                       (-6, "W4EC_ERR_BAD_INDEX"), (7, "W4EC_UNKNOWN_STATUS")]:
         assert w4.w4ec_status_str(code) == name
+
+
+def test_wait_limit_round_trip_and_workspace_checks():
+    old = w4.w4ec_wait_limit()
+    assert old == 1 << 22
+    try:
+        w4.w4ec_set_wait_limit(0)
+        assert w4.w4ec_wait_limit() == 0
+        w4.w4ec_set_wait_limit(123)
+        assert w4.w4ec_wait_limit() == 123
+    finally:
+        w4.w4ec_set_wait_limit(old)
+    L = w4.lib()
+    P = ctypes.c_void_p
+    # no or a misaligned workspace is rejected before any HIP call
+    assert L.w4ec_workspace_status(None, 1 << 20, None) == w4.W4EC_ERR_WORKSPACE
+    assert L.w4ec_workspace_status(P(FAKE + 16), 1 << 20, None) == w4.W4EC_ERR_WORKSPACE
+    assert L.w4ec_workspace_reset(None, 1 << 20, None) == w4.W4EC_ERR_WORKSPACE
+    assert L.w4ec_workspace_reset(P(FAKE), 100, None) == w4.W4EC_ERR_WORKSPACE
 
 
 def test_packed_bytes():

@@ -15,7 +15,7 @@ import w4_gemm_error_amd as w4
 from w4_gemm_error_amd import synth
 
 from gpu_util import (assert_close, dev_act, gpu_layer, gpu_quantize, host_bits, oracle_layer,
-                      torch)
+                      sample_rows, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,20 +53,6 @@ def test_pack_unpack_round_trip(N, K, G):
     assert np.array_equal(q2.cpu().numpy(), qc)
     assert np.array_equal(s2.cpu().numpy().view(np.uint16), s.view(np.uint16))
     assert np.array_equal(z2.cpu().numpy().view(np.uint16), z.view(np.uint16))
-
-
-def test_pack_rejects_non_integer_zero():
-    t = torch()
-    N, K = 16, 128
-    q = t.zeros((N, K // 2), dtype=t.uint8, device="cuda")
-    s = t.ones((N, 1), dtype=t.float16, device="cuda")
-    z = t.full((N, 1), 7.5, dtype=t.float16, device="cuda")
-    with pytest.raises(w4.W4ECError) as e:
-        w4.w4ec_pack(q, s, z, N, K, K)
-    assert e.value.status == w4.W4EC_ERR_INVALID_ARG
-    z = t.full((N, 1), 16.0, dtype=t.float16, device="cuda")
-    with pytest.raises(w4.W4ECError):
-        w4.w4ec_pack(q, s, z, N, K, K)
 
 
 # ---------------------------------------------------------------- small layers
@@ -153,9 +139,8 @@ def test_deterministic_and_workspace_reuse(phase, M):
     for _ in range(5):
         again = gpu_layer(d, packed, phase, workspace=ws)
         assert np.array_equal(again, first)
-    if phase == "decode":
-        # decode hand-over state (flags, counters, data) is back at zero, no wait timed out
-        assert int(t.count_nonzero(ws).item()) == 0
+    # hand-over state (flags, counters, data) is back at zero, no wait timed out
+    assert int(t.count_nonzero(ws[: w4.W4EC_WS_STATE_BYTES]).item()) == 0
 
 
 def test_phase_dispatch_agrees():
@@ -188,21 +173,23 @@ def test_special_cases_full_size_decode():
 # ---------------------------------------------------------------- full-size workloads
 
 FULL = [
-    # cfg, M, phase, sampled rows (None = all)
-    ("tiny", 16, "decode", None),
-    ("decode_up_proj_8b", 1, "decode", None),
-    ("decode_up_proj_8b", 4, "decode", None),
-    ("decode_up_proj_8b", 16, "decode", None),
-    ("prefill_out_proj_8b", 2048, "prefill", [0, 1, 77, 1023, 1500, 2047]),
-    ("batched_down_proj_8b_g128", 256, "prefill", [0, 5, 128, 255]),
-    ("mlp_70b_bf16", 64, "prefill", [0, 31, 63]),
-    ("mlp_70b_bf16", 4096, "prefill", [0, 2049, 4095]),
+    # cfg, M, phase (every token of Y must be finite; the oracle checks all
+    # tokens up to 64 and a token in every row tile beyond: sample_rows)
+    ("tiny", 16, "decode"),
+    ("decode_up_proj_8b", 1, "decode"),
+    ("decode_up_proj_8b", 4, "decode"),
+    ("decode_up_proj_8b", 16, "decode"),
+    ("prefill_out_proj_8b", 2048, "prefill"),
+    ("batched_down_proj_8b_g128", 256, "prefill"),
+    ("mlp_70b_bf16", 64, "prefill"),
+    ("mlp_70b_bf16", 4096, "prefill"),
 ]
 
 
-@pytest.mark.parametrize("cfg,M,phase,rows", FULL)
-def test_full_size_parity(cfg, M, phase, rows):
-    _print(f"full {cfg} M={M} {phase}")
+@pytest.mark.parametrize("cfg,M,phase", FULL)
+def test_full_size_parity(cfg, M, phase):
+    rows = sample_rows(M)
+    _print(f"full {cfg} M={M} {phase} rows={'all' if rows is None else len(rows)}")
     d = synth.make_layer(cfg, M, seed=0)
     q, s, z, packed = gpu_quantize(d)
     codes = oracle.rtn_quantize(d["W"], d["group_size"])

@@ -10,7 +10,8 @@ import oracle
 import w4_gemm_error_amd as w4
 from w4_gemm_error_amd import synth
 
-from gpu_util import assert_close, dev_act, gpu_quantize, host_bits, torch
+from gpu_util import (assert_all_finite, assert_close, dev_act, gpu_quantize, host_bits, nan_y,
+                      new_workspace, poison_workspace, sample_rows, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,11 +40,14 @@ def gpu_serq(d, packed, phase, S, R, *, workspace=None, check_state=True):
     Sd = t.from_numpy(S).cuda() if s else None
     Rd = dev_act(R, act) if s else None
     if workspace is None:
-        need = w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], s, d["group_size"])
-        workspace = t.zeros(max(need, 256), dtype=t.uint8, device="cuda")
+        workspace = new_workspace(w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], s, d["group_size"]))
+    else:
+        poison_workspace(workspace)
     fn = w4.w4ec_linear_decode_serq if phase == "decode" else w4.w4ec_linear_prefill_serq
-    Y = fn(X, packed, Sd, Rd, N=d["N"], group_size=d["group_size"], workspace=workspace)
+    Y = nan_y(d["M"], d["N"], act)
+    fn(X, packed, Sd, Rd, N=d["N"], group_size=d["group_size"], workspace=workspace, Y=Y)
     t.cuda.synchronize()
+    assert_all_finite(Y, f"serq {phase} M={d['M']}")
     if check_state:
         state = workspace[: w4.W4EC_WS_STATE_BYTES]
         assert int(t.count_nonzero(state).item()) == 0, f"{phase}: state not at zero after the call"
@@ -115,19 +119,20 @@ def test_serq_out_of_range_index_is_flagged(phase):
 
 
 FULL = [
-    # cfg, M, phase, sampled rows (None = all)
-    ("decode_up_proj_8b", 1, "decode", None),
-    ("decode_up_proj_8b", 16, "decode", None),
-    ("prefill_out_proj_8b", 2048, "prefill", [0, 1, 77, 1023, 2047]),
-    ("mlp_70b_bf16", 64, "prefill", [0, 31, 63]),
+    # cfg, M, phase (oracle rows: sample_rows)
+    ("decode_up_proj_8b", 1, "decode"),
+    ("decode_up_proj_8b", 16, "decode"),
+    ("prefill_out_proj_8b", 2048, "prefill"),
+    ("mlp_70b_bf16", 64, "prefill"),
 ]
 
 
-@pytest.mark.parametrize("cfg,M,phase,rows", FULL)
-def test_serq_full_size_parity(cfg, M, phase, rows):
+@pytest.mark.parametrize("cfg,M,phase", FULL)
+def test_serq_full_size_parity(cfg, M, phase):
     """The salient channels are the configs' outlier channels (the ones whose
     activation scale marks them), as an offline permutation would gather."""
-    _print(f"serq full {cfg} M={M} {phase}")
+    rows = sample_rows(M)
+    _print(f"serq full {cfg} M={M} {phase} rows={'all' if rows is None else len(rows)}")
     d = synth.make_layer(cfg, M, seed=0)
     S = np.asarray(d["outlier_channels"], dtype=np.int32)
     R = synth.to_act_bits(np.random.default_rng(synth.SEEDS[cfg]).normal(0.0, 0.01, (len(S), d["N"])), d["act"])

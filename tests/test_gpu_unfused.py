@@ -13,7 +13,8 @@ import oracle
 import w4_gemm_error_amd as w4
 from w4_gemm_error_amd import synth
 
-from gpu_util import assert_close, dev_act, gpu_layer, gpu_quantize, host_bits, oracle_layer, torch
+from gpu_util import (assert_all_finite, assert_close, dev_act, gpu_layer, gpu_quantize, host_bits, nan_y,
+                      new_workspace, oracle_layer, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,9 +33,10 @@ def unfused(d, packed, *, two_streams=False):
     act = d["act"]
     M, N, K, r, G = d["M"], d["N"], d["K"], d["r"], d["group_size"]
     X, A, B, wg = (dev_act(d[k], act) for k in ("X", "A", "B", "w_g"))
-    ws_ec = t.zeros(w4.w4ec_prefill_ec_workspace_bytes(M, K, r), dtype=t.uint8, device="cuda")
-    ws_mm = t.zeros(max(w4.w4ec_workspace_bytes(M, N, K, 0, G), 256), dtype=t.uint8, device="cuda")
-    Y = t.empty((M, N), dtype=X.dtype, device="cuda")
+    # the EC workspace holds only per-call data (no hand-over state): all of it poisoned
+    ws_ec = t.full((w4.w4ec_prefill_ec_workspace_bytes(M, K, r),), 0xFF, dtype=t.uint8, device="cuda")
+    ws_mm = new_workspace(w4.w4ec_workspace_bytes(M, N, K, 0, G))
+    Y = nan_y(M, N, act)
     main = t.cuda.current_stream()
     if two_streams:
         side = t.cuda.Stream()
@@ -49,6 +51,7 @@ def unfused(d, packed, *, two_streams=False):
     w4.w4ec_prefill_ec_apply(Y, B, K=K, workspace=ws_ec)
     t.cuda.synchronize()
     assert int(t.count_nonzero(ws_mm[: w4.W4EC_WS_STATE_BYTES]).item()) == 0
+    assert_all_finite(Y, f"unfused M={M}")
     return host_bits(Y)
 
 

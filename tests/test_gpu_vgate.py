@@ -14,7 +14,8 @@ import oracle
 import w4_gemm_error_amd as w4
 from w4_gemm_error_amd import synth
 
-from gpu_util import assert_close, dev_act, gpu_quantize, host_bits, torch
+from gpu_util import (assert_all_finite, assert_close, dev_act, gpu_quantize, host_bits, nan_y,
+                      new_workspace, poison_workspace, sample_rows, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,12 +38,14 @@ def gpu_vgate(d, packed, phase, p, *, workspace=None, c2=None, G2=None):
     G2d = dev_act(p["G2"] if G2 is None else G2, act)
     c2d = dev_act(p["c2"] if c2 is None else c2, act)
     if workspace is None:
-        t = torch()
-        need = w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], d["r"], d["group_size"])
-        workspace = t.zeros(max(need, 256), dtype=t.uint8, device="cuda")
+        workspace = new_workspace(w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], d["r"], d["group_size"]))
+    else:
+        poison_workspace(workspace)
     fn = w4.w4ec_linear_decode_vgate if phase == "decode" else w4.w4ec_linear_prefill_vgate
-    Y = fn(X, packed, A, B, G1, c1, G2d, c2d, N=d["N"], group_size=d["group_size"], workspace=workspace)
+    Y = nan_y(d["M"], d["N"], act)
+    fn(X, packed, A, B, G1, c1, G2d, c2d, N=d["N"], group_size=d["group_size"], workspace=workspace, Y=Y)
     torch().cuda.synchronize()
+    assert_all_finite(Y, f"vgate {phase} M={d['M']}")
     state = workspace[: w4.W4EC_WS_STATE_BYTES]
     assert int(torch().count_nonzero(state).item()) == 0, f"{phase}: hand-over state not at zero after the call"
     return host_bits(Y)
@@ -110,17 +113,18 @@ def test_vgate_closed_and_open(phase):
 
 
 FULL = [
-    # cfg, M, phase, sampled rows (None = all), h
-    ("decode_up_proj_8b", 1, "decode", None, 16),
-    ("decode_up_proj_8b", 16, "decode", None, 16),
-    ("prefill_out_proj_8b", 2048, "prefill", [0, 1, 77, 1023, 2047], 16),
-    ("mlp_70b_bf16", 64, "prefill", [0, 31, 63], 32),
+    # cfg, M, phase, h (oracle rows: sample_rows)
+    ("decode_up_proj_8b", 1, "decode", 16),
+    ("decode_up_proj_8b", 16, "decode", 16),
+    ("prefill_out_proj_8b", 2048, "prefill", 16),
+    ("mlp_70b_bf16", 64, "prefill", 32),
 ]
 
 
-@pytest.mark.parametrize("cfg,M,phase,rows,h", FULL)
-def test_vgate_full_size_parity(cfg, M, phase, rows, h):
-    _print(f"vgate full {cfg} M={M} {phase}")
+@pytest.mark.parametrize("cfg,M,phase,h", FULL)
+def test_vgate_full_size_parity(cfg, M, phase, h):
+    rows = sample_rows(M)
+    _print(f"vgate full {cfg} M={M} {phase} rows={'all' if rows is None else len(rows)}")
     d = synth.make_layer(cfg, M, seed=0)
     p = vg_params(d, h, seed=synth.SEEDS[cfg])
     q, s, z, packed = gpu_quantize(d)

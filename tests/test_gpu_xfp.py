@@ -11,7 +11,7 @@ import oracle
 import w4_gemm_error_amd as w4
 from w4_gemm_error_amd import synth
 
-from gpu_util import assert_close, dev_act, host_bits, torch
+from gpu_util import assert_all_finite, assert_close, dev_act, host_bits, nan_y, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -51,8 +51,10 @@ def gpu_xfp(d, x):
     ci = t.from_numpy(x["col_idx"]).cuda() if nnz else None
     val = t.from_numpy(x["val"].view(np.int16)).view(t.float16).cuda() if nnz else None
     X = dev_act(d["X"], d["act"])
-    Y = w4.w4ec_linear_decode_xfp(X, packed, cb, rp, ci, val, N=N)
+    Y = nan_y(d["M"], N, d["act"])
+    w4.w4ec_linear_decode_xfp(X, packed, cb, rp, ci, val, N=N, Y=Y)
     t.cuda.synchronize()
+    assert_all_finite(Y, f"xfp M={d['M']}")
     return host_bits(Y)
 
 

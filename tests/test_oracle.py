@@ -190,6 +190,37 @@ def test_tiny_exact_rational(act):
             assert out["Y"][m, n] == pytest.approx(y, rel=1e-12, abs=1e-12)
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_fractional_zero_points_exact_rational(G):
+    """Zero points need not be integers (quantizers other than RTN may learn
+    them): with arbitrary fp16 zero points -- fractional, negative, above 15
+    -- the plain product matches exact rational arithmetic, and moving every
+    zero point of a group by d moves each output by exactly -d s times the
+    group's activation sum (the dequantization is affine in z)."""
+    rng = np.random.default_rng(17)
+    M, N, K = 3, 5, 8
+    q, s, _, _ = on_grid_layer(rng, N, K, G)
+    z = np.array(rng.choice([-3.5, -0.125, 0.375, 7.25, 7.3125, 15.0, 17.75, 2.0], size=(N, K // G)),
+                 np.float16).view(np.uint16)
+    Xb = f16bits(rng.standard_normal((M, K)) * 2)
+    out = run(M, N, K, 0, G, Xb, pack_canonical(q), s, z, None, None, None, 0.0)
+    X = [[Fraction(float(v)) for v in row] for row in Xb.view(np.float16).astype(np.float64)]
+    sv = s.view(np.float16).astype(np.float64)
+    zv = z.view(np.float16).astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            y0 = sum(X[m][k] * (int(q[n, k]) - Fraction(zv[n, k // G])) * Fraction(sv[n, k // G])
+                     for k in range(K))
+            assert out["Y0"][m, n] == pytest.approx(float(y0), rel=1e-13, abs=1e-300)
+    d = 0.25
+    z2 = (zv + d).astype(np.float16)
+    assert np.array_equal(z2.astype(np.float64), zv + d)        # exact shift
+    out2 = run(M, N, K, 0, G, Xb, pack_canonical(q), s, z2.view(np.uint16), None, None, None, 0.0)
+    xs = Xb.view(np.float16).astype(np.float64).reshape(M, K // G, G).sum(axis=2)   # [M][groups]
+    expect = out["Y0"] - d * xs @ sv.T
+    np.testing.assert_allclose(out2["Y0"], expect, rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("G", [128, 512])
 def test_on_grid_weights_reproduce_matmul(G):
     rng = np.random.default_rng(5)

@@ -18,6 +18,8 @@ import threading
 __all__ = [
     "W4ECError", "lib", "exported_symbols", "header_symbols",
     "W4EC_OK", "W4EC_ERR_INVALID_ARG", "W4EC_ERR_UNSUPPORTED", "W4EC_ERR_WORKSPACE", "W4EC_ERR_HIP",
+    "W4EC_ERR_TIMED_OUT", "W4EC_ERR_BAD_INDEX",
+    "w4ec_workspace_status", "w4ec_workspace_reset", "w4ec_set_wait_limit", "w4ec_wait_limit",
     "W4EC_FP16", "W4EC_BF16", "DECODE_MAX_M", "W4EC_WS_STATE_BYTES",
     "w4ec_status_str", "w4ec_packed_bytes", "w4ec_workspace_bytes",
     "w4ec_quantize_rtn", "w4ec_pack", "w4ec_unpack",
@@ -38,6 +40,8 @@ W4EC_ERR_INVALID_ARG = -1
 W4EC_ERR_UNSUPPORTED = -2
 W4EC_ERR_WORKSPACE = -3
 W4EC_ERR_HIP = -4
+W4EC_ERR_TIMED_OUT = -5
+W4EC_ERR_BAD_INDEX = -6
 W4EC_FP16 = 0
 W4EC_BF16 = 1
 DECODE_MAX_M = 16
@@ -69,6 +73,14 @@ def lib() -> ctypes.CDLL:
         L.w4ec_packed_bytes.restype = Z
         L.w4ec_workspace_bytes.argtypes = [I, I, I, I, I]
         L.w4ec_workspace_bytes.restype = Z
+        L.w4ec_workspace_status.argtypes = [P, Z, P]
+        L.w4ec_workspace_status.restype = I
+        L.w4ec_workspace_reset.argtypes = [P, Z, P]
+        L.w4ec_workspace_reset.restype = I
+        L.w4ec_set_wait_limit.argtypes = [ctypes.c_uint32]
+        L.w4ec_set_wait_limit.restype = None
+        L.w4ec_wait_limit.argtypes = []
+        L.w4ec_wait_limit.restype = ctypes.c_uint32
         L.w4ec_quantize_rtn.argtypes = [P, I, I, I, P, P, P, P]
         L.w4ec_quantize_rtn.restype = I
         L.w4ec_pack.argtypes = [P, P, P, I, I, I, P, P]
@@ -127,6 +139,16 @@ def w4ec_workspace_bytes(M: int, N: int, K: int, r: int, group_size: int) -> int
     return int(lib().w4ec_workspace_bytes(M, N, K, r, group_size))
 
 
+def w4ec_set_wait_limit(polls: int) -> None:
+    """Polls a bounded wait makes before it gives up (0: every wait gives up
+    at once, for exercising the failure path)."""
+    lib().w4ec_set_wait_limit(int(polls))
+
+
+def w4ec_wait_limit() -> int:
+    return int(lib().w4ec_wait_limit())
+
+
 # ---------------------------------------------------------------- device calls
 
 def _torch():
@@ -167,6 +189,24 @@ def _act_code(dtype) -> int:
     if dtype == torch.bfloat16:
         return W4EC_BF16
     raise ValueError(f"activation dtype {dtype} is not fp16/bf16")
+
+
+def w4ec_workspace_status(workspace, *, stream=None) -> int:
+    """W4EC_OK, W4EC_ERR_TIMED_OUT or W4EC_ERR_BAD_INDEX: what the calls so
+    far on this workspace recorded (synchronizes the stream)."""
+    _need_cuda(workspace, "workspace")
+    st = lib().w4ec_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream_handle(stream))
+    if st not in (W4EC_OK, W4EC_ERR_TIMED_OUT, W4EC_ERR_BAD_INDEX):
+        raise W4ECError(st, "w4ec_workspace_status")
+    return int(st)
+
+
+def w4ec_workspace_reset(workspace, *, stream=None) -> None:
+    """Zero the workspace's hand-over state (asynchronous, a kernel)."""
+    _need_cuda(workspace, "workspace")
+    _check(lib().w4ec_workspace_reset(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream_handle(stream)), "w4ec_workspace_reset")
 
 
 def w4ec_quantize_rtn(W, group_size: int, *, stream=None):

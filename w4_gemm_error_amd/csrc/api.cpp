@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <new>
 
 #include "w4ec_common.h"
@@ -183,6 +184,9 @@ int check_layer_args(const void* X, const void* packed, const void* A, const voi
 
 int hip_status(hipError_t e) { return e == hipSuccess ? W4EC_OK : W4EC_ERR_HIP; }
 
+// polls a bounded wait makes before it gives up (w4ec_set_wait_limit)
+std::atomic<uint32_t> g_wait_limit{SPIN_LIMIT};
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +199,8 @@ const char* w4ec_status_str(int status)
     case W4EC_ERR_UNSUPPORTED: return "W4EC_ERR_UNSUPPORTED";
     case W4EC_ERR_WORKSPACE: return "W4EC_ERR_WORKSPACE";
     case W4EC_ERR_HIP: return "W4EC_ERR_HIP";
+    case W4EC_ERR_TIMED_OUT: return "W4EC_ERR_TIMED_OUT";
+    case W4EC_ERR_BAD_INDEX: return "W4EC_ERR_BAD_INDEX";
     default: return "W4EC_UNKNOWN_STATUS";
     }
 }
@@ -232,17 +238,7 @@ int w4ec_pack(const uint8_t* q_canon, const uint16_t* scale, const uint16_t* zer
         return W4EC_ERR_INVALID_ARG;
     if (!aligned(packed, 256) || !aligned(scale, 2) || !aligned(zero, 2))
         return W4EC_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_pack(q_canon, scale, zero, N, K, group_size, packed, st);
-    if (e != hipSuccess)
-        return W4EC_ERR_HIP;
-    BlobHeader hdr;
-    e = hipMemcpyAsync(&hdr, packed, sizeof hdr, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(st);
-    if (e != hipSuccess)
-        return W4EC_ERR_HIP;
-    return hdr.bad_zero ? W4EC_ERR_INVALID_ARG : W4EC_OK;
+    return hip_status(launch_pack(q_canon, scale, zero, N, K, group_size, packed, (hipStream_t)stream));
 }
 
 int w4ec_pack_xfp(const uint8_t* idx_canon, int N, int K, void* packed, void* stream)
@@ -252,11 +248,7 @@ int w4ec_pack_xfp(const uint8_t* idx_canon, int N, int K, void* packed, void* st
         return rc;
     if (!idx_canon || !packed || !aligned(packed, 256))
         return W4EC_ERR_INVALID_ARG;
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_pack(idx_canon, nullptr, nullptr, N, K, K, packed, st);
-    if (e == hipSuccess)
-        e = hipStreamSynchronize(st);
-    return hip_status(e);
+    return hip_status(launch_pack(idx_canon, nullptr, nullptr, N, K, K, packed, (hipStream_t)stream));
 }
 
 int w4ec_unpack(const void* packed, int N, int K, int group_size, uint8_t* q_canon,
@@ -321,6 +313,7 @@ LayerArgs layer_args(const void* X, const void* packed, const void* A, const voi
 {
     LayerArgs a{X, packed, r > 0 ? A : nullptr, r > 0 ? B : nullptr, r > 0 ? w_g : nullptr,
                 b_g, Y, M, N, K, r, group_size, act_dtype, (char*)workspace};
+    a.spin = g_wait_limit.load(std::memory_order_relaxed);
     if (vg && r > 0) {
         a.w_g = nullptr;                 // the vector gate replaces the scalar one
         a.G1 = vg->G1; a.c1 = vg->c1; a.G2 = vg->G2; a.c2 = vg->c2;
@@ -354,7 +347,7 @@ int decode_entry(const void* X, const void* packed, const void* A, const void* B
     if (!vg && w_g && !((uintptr_t)w_g % 2 == 0))
         return W4EC_ERR_INVALID_ARG;
     LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
-                             workspace, vg);
+                             need > 0 ? workspace : nullptr, vg);
     if (S && r > 0) {
         // salient channels: the main workgroups gather their own operand,
         // no EC workgroups and no hand-over
@@ -389,7 +382,7 @@ int prefill_entry(const void* X, const void* packed, const void* A, const void* 
     if (!vg && w_g && !((uintptr_t)w_g % 2 == 0))
         return W4EC_ERR_INVALID_ARG;
     LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
-                             workspace, vg);
+                             need > 0 ? workspace : nullptr, vg);
     if (S && r > 0) {
         a.S = S;
         a.A = nullptr;
@@ -541,6 +534,42 @@ int w4ec_linear_decode_xfp(const void* X, const void* packed, const uint16_t* co
         return W4EC_ERR_INVALID_ARG;
     const XfpArgs x{X, packed, codebook, row_ptr, col_idx, val, nnz, Y, M, N, K, act_dtype};
     return hip_status(launch_decode_xfp(x, make_decode_plan(M, N, K, 0), (hipStream_t)stream));
+}
+
+void w4ec_set_wait_limit(uint32_t polls)
+{
+    g_wait_limit.store(polls, std::memory_order_relaxed);
+}
+
+uint32_t w4ec_wait_limit(void)
+{
+    return g_wait_limit.load(std::memory_order_relaxed);
+}
+
+int w4ec_workspace_status(const void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!workspace || workspace_bytes < OFF_DEC_FLAGS + 16 || !aligned(workspace, 256))
+        return W4EC_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t f[4] = {0, 0, 0, 0};
+    hipError_t e = hipMemcpyAsync(f, (const char*)workspace + OFF_DEC_FLAGS, sizeof f, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(st);
+    if (e != hipSuccess)
+        return W4EC_ERR_HIP;
+    if (f[2])
+        return W4EC_ERR_TIMED_OUT;
+    if (f[3])
+        return W4EC_ERR_BAD_INDEX;
+    return W4EC_OK;
+}
+
+int w4ec_workspace_reset(void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes % 16 != 0)
+        return W4EC_ERR_WORKSPACE;
+    const size_t n = std::min(workspace_bytes, CTRL_BYTES);
+    return hip_status(launch_zero_fill(workspace, n, (hipStream_t)stream));
 }
 
 }  // extern "C"

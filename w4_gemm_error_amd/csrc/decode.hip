@@ -41,9 +41,7 @@
 
 namespace w4ec {
 
-constexpr int DEC_THREADS = 256;
 constexpr int DEC_EC_MAXI = 5;     // column blocks per wavefront in the EC role (17 / 4)
-constexpr int DEC_XLDS_CHUNKS = 8; // 16-byte chunks of staged activations per thread
 constexpr int DEC_EC_KSMAX = 256;  // k per EC slice (at most)
 
 
@@ -59,7 +57,9 @@ struct DecodeKArgs {
     int M, N, K, r, r_pad, G, NB, KB, Npad;
     int P, KS, RC, n_main;
     int stage_first;     // main workgroups stage X before issuing weight loads
-    uint32_t* flags;     // [2]: a wait timed out
+    uint32_t* flags;     // [2]: a wait timed out (sticky: every later call's Y is NaN)
+    uint32_t spin;       // polls before a bounded wait gives up (0: give up at once)
+    const uint32_t* zflags;  // the blob's zero-point flags (ZF_*), or null
     uint32_t* partial;   // [P][M][RC] hand-over words
     uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [1] readers done
     uint8_t* rep_data;   // DEC_NREP slots of DEC_REP_DATA_STRIDE bytes: T_g [M][r_pad] as hand-over words
@@ -178,6 +178,9 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
         vgate_stage_load(G1, c1, G2, c2, r, h, gv);
     bool staged = false;
     uint32_t it = 0;                                        // bounded wait, shared by all waits
+    // a wait that gave up (or a wait limit of 0) publishes NaN for the
+    // token instead of sums of partials that had not all landed
+    bool lost = a.spin == 0;
     // ng thread groups split the P slices (slice q -> group q mod ng), so
     // that all of them are in flight at once; the groups' sums are added in
     // group order
@@ -200,13 +203,14 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
                             miss |= v[i] == 0u;
-                        if (!miss)
+                        if (!miss || lost)
                             break;
-                        __builtin_amdgcn_s_sleep(1);
-                        if (++it >= SPIN_LIMIT) {
-                            atomic_store_dev(&a.flags[2], 1u);
+                        if (it >= a.spin) {
+                            lost = true;
                             break;
                         }
+                        ++it;
+                        __builtin_amdgcn_s_sleep(1);
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
                             if (v[i] == 0u)                 // only slices < P can read as zero
@@ -220,12 +224,14 @@ __device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, 
             }
             red[e] = t;
         }
-        __syncthreads();
+        const bool lost_any = __syncthreads_or(lost) != 0;
+        if (lost_any && tid == 0)
+            atomic_store_dev(&a.flags[2], 1u);
         for (int c = tid; c < a.r_pad; c += DEC_THREADS) {
             float t = red[c];
             for (int g = 1; g < ng; ++g)
                 t += red[g * a.r_pad + c];
-            tT[c] = t;
+            tT[c] = lost_any ? __builtin_nanf("") : t;
         }
         if (a.vg_staged && !staged) {
             vgate_stage_store(G1, c1, G2, c2, r, h, gv, gst);
@@ -341,7 +347,10 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     for (int i = 0; i < DEC_EC_MAXI; ++i) {
         const int cb = w + 4 * i;
         const int c = cb < ec_blocks(r) ? ec_col(r, cb, l & 15) : -1;
-        if (c >= 0) {
+        // the vector gate reads only the columns of T: the logit column is
+        // not stored (a word no reducer waits for could land after the slot's
+        // last reader has cleared the partial sums)
+        if (c >= 0 && !(a.h > 0 && c == r)) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = 4 * (l >> 4) + v;
@@ -389,6 +398,9 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
     float* tsum = red + tsum_off;                           // [ne]
     uint64_t* tw = reinterpret_cast<uint64_t*>(red + ((tsum_off + ne + 1) & ~1));   // [nw], 8-byte aligned
     uint32_t it = 0;                                        // bounded wait, shared by all of this thread's waits
+    // a wait that gave up (or a wait limit of 0) publishes NaN for this
+    // share instead of sums of partials that had not all landed
+    bool lost = a.spin == 0;
     for (int e0 = tid; e0 < ne * ng; e0 += DEC_THREADS) {
         const int g = e0 / ne, e = e0 - g * ne;
         int pe = (e - nv) * a.RC + r;                       // a logit ...
@@ -411,13 +423,14 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
                         miss |= v[i] == 0u;
-                    if (!miss)
+                    if (!miss || lost)
                         break;
-                    __builtin_amdgcn_s_sleep(1);
-                    if (++it >= SPIN_LIMIT) {
-                        atomic_store_dev(&a.flags[2], 1u);
+                    if (it >= a.spin) {
+                        lost = true;
                         break;
                     }
+                    ++it;
+                    __builtin_amdgcn_s_sleep(1);
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
                         if (v[i] == 0u)                     // only slices < P can read as zero
@@ -434,8 +447,10 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
         else
             tsum[e] = t;
     }
+    const bool lost_any = __syncthreads_or(lost) != 0;
+    if (lost_any && tid == 0)
+        atomic_store_dev(&a.flags[2], 1u);
     if (ng > 1) {
-        __syncthreads();
         for (int e = tid; e < ne; e += DEC_THREADS) {
             float t = red[e];
             for (int g = 1; g < ng; ++g)
@@ -443,6 +458,9 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
             tsum[e] = t;
         }
     }
+    if (lost_any)
+        for (int e = tid; e < ne; e += DEC_THREADS)
+            tsum[e] = __builtin_nanf("");
     __syncthreads();
     // gate, round to the activation format, pack four values per word
     for (int i = tid; i < nw; i += DEC_THREADS) {
@@ -491,6 +509,11 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     const int M = a.M;
     const int K = a.K;
     const int KB = a.KB;
+    // a wait that timed out in an earlier call on this workspace (issued
+    // first, needed only at the stores; no workspace without a rank), and a
+    // blob whose zero points are out of range (both make the outputs NaN)
+    const uint32_t sticky = (a.r > 0 ? atomic_load_dev(&a.flags[2]) : 0u) |
+                            (a.zflags ? (*a.zflags & ZF_BAD) : 0u);
 
     const int per = KB >> 2, rem = KB & 3;
     const int kcnt = per + (w < rem ? 1 : 0);
@@ -721,8 +744,14 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
     }
 
-    floatx4 acc[CB], accg[CB];
-    float s_cur[CB];
+    // Zero points: the codes are offset by the integer part zi = floor(z)
+    // exactly (the exponent trick); a fractional part zf = z - zi leaves
+    // -zf * s * (sum of the group's activations), for which accx keeps the
+    // token's activation sum over the current group (one more MFMA per
+    // k-step, against a column of ones).  With integer zero points zf = 0
+    // and the correction adds nothing.
+    floatx4 acc[CB], accg[CB], accx;
+    float s_cur[CB], szf[CB];
     DqF16 dqh[CB];
     float dqb[CB];
     auto set_sz = [&](const uint32_t* v) {
@@ -730,12 +759,17 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         for (int j = 0; j < CB; ++j) {
             s_cur[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
             const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
+            const float zi = floorf(z);
+            szf[j] = s_cur[j] * (z - zi);
             if constexpr (ACT == ACT_F16)
-                dqh[j] = dq_f16_consts(z);
+                dqh[j] = dq_f16_consts(zi);
             else
-                dqb[j] = -(8388608.0f + z);
+                dqb[j] = -(8388608.0f + zi);
         }
     };
+    constexpr uint32_t ONE2 = ACT == ACT_F16 ? 0x3C003C00u : 0x3F803F80u;   // two ones
+    const u32x4 ones = (u32x4){ONE2, ONE2, ONE2, ONE2};
+    accx = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
         acc[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -792,9 +826,10 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
                 if (valid && left_in_group == ppg && i > 0) {
 #pragma unroll
                     for (int j = 0; j < CB; ++j) {
-                        acc[j] += s_cur[j] * accg[j];
+                        acc[j] += s_cur[j] * accg[j] - szf[j] * accx;
                         accg[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
                     }
+                    accx = (floatx4){0.f, 0.f, 0.f, 0.f};
                     set_sz(szv);
                 }
             }
@@ -814,6 +849,11 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
                     accg[j] = mfma16x16x32<ACT>(xf[s], bq, accg[j]);
                 }
             }
+            if constexpr (!CBK) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    accx = mfma16x16x32<ACT>(xf[s], ones, accx);
+            }
             if constexpr (GROUPED) {
                 if (--left_in_group == 0)
                     left_in_group = ppg;
@@ -827,7 +867,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 
 #pragma unroll
     for (int j = 0; j < CB; ++j)
-        acc[j] += s_cur[j] * accg[j];
+        acc[j] += s_cur[j] * accg[j] - (CBK ? 0.0f : szf[j]) * accx;
 
     // sparse outlier residual: this thread's share of column rc, for every
     // token, sum x[m][k] * val (X from LDS while it is still staged there)
@@ -895,6 +935,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     const int slot = mb % DEC_NREP;
     uint64_t* sdata = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * DEC_REP_DATA_STRIDE);
     u32x4 af[8];
+    bool lost = false;      // this wavefront's wait for T_g gave up: its outputs are NaN
     // salient channels (SERQ summary, section 2): the operand is the gather
     // X[token][S[j]], made by the whole workgroup into LDS ([M][r_pad], past
     // the parked B) -- no EC role and no hand-over.  An index outside [0, K)
@@ -918,8 +959,10 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     } else if (a.r > 0 && w < CB && !a.S) {
         const uint64_t* src = sdata + (row * a.r_pad + koff) / 4;
         uint32_t it = 0;
-        // read all of them, and again while any has not landed
-        for (;;) {
+        lost = a.spin == 0;
+        // read all of them, and again while any has not landed (a wait limit
+        // of 0 gives up at once)
+        for (; !lost;) {
             bool miss = false;
 #pragma unroll
             for (int rs = 0; rs < 8; ++rs) {
@@ -937,12 +980,15 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
             }
             if (__builtin_amdgcn_ballot_w64(miss) == 0)
                 break;
-            __builtin_amdgcn_s_sleep(1);
-            if (++it >= SPIN_LIMIT) {
-                atomic_store_dev(&a.flags[2], 1u);
+            if (it >= a.spin) {
+                lost = true;
                 break;
             }
+            ++it;
+            __builtin_amdgcn_s_sleep(1);
         }
+        if (lost && l == 0)
+            atomic_store_dev(&a.flags[2], 1u);
     }
     __syncthreads();
     if (a.r > 0 && a.S && w < CB) {
@@ -988,11 +1034,15 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
                     tot = mfma16x16x32<ACT>(af[rs], bfr[rs], tot);
         }
         if (n < a.N) {
+            // a wait that gave up here, or one that did in an earlier call on
+            // this workspace (whose hand-over state is then not to be
+            // trusted), turns the outputs into NaN rather than wrong numbers
+            const bool poison = lost || sticky != 0u;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = 4 * (l >> 4) + v;
                 if (m < M)
-                    a.Y[(size_t)m * a.N + n] = f32_to_act<ACT>(tot[v]);
+                    a.Y[(size_t)m * a.N + n] = poison ? act_nan<ACT>() : f32_to_act<ACT>(tot[v]);
             }
         }
     }
@@ -1039,11 +1089,6 @@ void decode_kernel(DecodeKArgs a)
     }
 }
 
-// activations of at most this many bytes are staged in LDS by the main role
-// (8 chunks of 16 bytes per thread)
-constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS;
-
-bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
 
 static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r, bool gather)
 {
@@ -1104,11 +1149,10 @@ static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, h
 template <int ACT>
 static hipError_t launch_decode_act(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
+    // (the plan always issues the weight ring before staging X)
     if (k.G != k.K)
-        return p.stage_first ? launch_decode_grp<ACT, true, true>(k, p, st)
-                             : launch_decode_grp<ACT, true, false>(k, p, st);
-    return p.stage_first ? launch_decode_grp<ACT, false, true>(k, p, st)
-                         : launch_decode_grp<ACT, false, false>(k, p, st);
+        return launch_decode_grp<ACT, true, false>(k, p, st);
+    return launch_decode_grp<ACT, false, false>(k, p, st);
 }
 
 template <int ACT>
@@ -1168,6 +1212,8 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.P = p.P; k.KS = p.KS; k.RC = p.RC; k.n_main = p.n_main;
     k.stage_first = p.stage_first;
     k.flags = (uint32_t*)(a.ws + p.off_flags);
+    k.spin = a.spin;
+    k.zflags = &reinterpret_cast<const BlobHeader*>(a.packed)->zflags;
     k.partial = (uint32_t*)(a.ws + p.off_partial);
     k.rep_ctrl = (uint8_t*)(a.ws + p.off_rep_ctrl);
     k.rep_data = (uint8_t*)(a.ws + p.off_rep_data);

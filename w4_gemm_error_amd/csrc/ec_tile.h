@@ -27,14 +27,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) short4_t lds_short4;
 
-// halves per LDS row of an A slice (the transpose read needs 8-byte aligned rows)
-__host__ __device__ inline int ec_pitch(int r) { return (r + 3) & ~3; }
-// column blocks of A, and the total including the gate block
-__host__ __device__ inline int ec_a_blocks(int r) { return (r + 15) >> 4; }
-__host__ __device__ inline int ec_blocks(int r) { return ec_a_blocks(r) + 1; }
-// LDS bytes of a staged slice of kc rows (plus slack for the last block's
-// over-read) and of its gate vector
-__host__ __device__ inline int ec_slice_bytes(int r, int kc) { return (kc * ec_pitch(r) + 16) * 2; }
+// (slice geometry: ec_pitch, ec_a_blocks, ec_blocks, ec_slice_bytes in w4ec_common.h)
 
 // 16 bytes from global memory into LDS; lds_base is wavefront-uniform and
 // lane l's bytes land at lds_base + 16 l

@@ -445,6 +445,7 @@ struct GemmKArgs {
     uint16_t* Y;
     floatx4* partial;  // [tile][ksplit][NW][RB][JW][64] fragments
     uint32_t* cnt;     // [mt*nt]
+    const uint32_t* zflags;  // the blob's zero-point flags (ZF_*)
     int M, N, K, r, r_pad, G, NB, KB, Npad, mt, nt, ksplit, Mpad;
 };
 
@@ -502,6 +503,10 @@ void prefill_gemm_kernel(GemmKArgs a)
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // zero-point flags of the blob: out-of-range zero points make the
+    // outputs NaN; fractional ones need a correction in the fp16 per-channel
+    // epilogue (the other forms handle them in the dequantization)
+    const uint32_t zfl = *a.zflags;
     int tm, tn;
     tile_of(blockIdx.x, a.mt, a.nt, tm, tn);
     const int kz = blockIdx.y;
@@ -545,22 +550,28 @@ void prefill_gemm_kernel(GemmKArgs a)
         for (int j = 0; j < JW; ++j)
             acc[i][j] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-    // scale/zero of the current group
+    // scale/zero of the current group: fp16 codes are offset by the integer
+    // part zi = floor(z) exactly; the fractional part z - zi enters as
+    // -(z - zi) s in the fp16 grouped dequantization, and as a correction by
+    // the tokens' activation sums in the fp16 per-channel epilogue; bf16
+    // grouped weights are q s - z s (exact operands, one rounding), and the
+    // bf16 per-channel epilogue subtracts (128 + z) times the sums
     DqF16 dqh[JW];
-    float dqb[JW];
-    half2_t sh2[JW];
+    half2_t sh2[JW], ch2[JW];   // fp16 grouped: s and -(z - zi) s
     float sf[JW];
-    float zf[JW];
+    float zf[JW];        // bf16 per-channel: z; bf16 grouped: -z s
     auto set_sz = [&](const uint32_t* v) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < JW; ++j) {
             const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
             const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
+            const float zi = floorf(z);
+            const _Float16 ch = (_Float16)(-(z - zi) * (float)sv);
             sf[j] = (float)sv;
-            zf[j] = z;
+            zf[j] = GROUPED ? -z * (float)sv : z;
             sh2[j] = (half2_t){sv, sv};
-            dqh[j] = dq_f16_consts(z);
-            dqb[j] = -(8388608.0f + z);
+            ch2[j] = (half2_t){ch, ch};
+            dqh[j] = dq_f16_consts(zi);
         }
     };
 
@@ -652,12 +663,12 @@ void prefill_gemm_kernel(GemmKArgs a)
                 u32x4 bq;
                 if constexpr (ACT == ACT_F16) {
                     if constexpr (GROUPED)
-                        bq = dequant_f16_scaled(q, dqh[j], sh2[j]);
+                        bq = dequant_f16_scaled(q, dqh[j], sh2[j], ch2[j]);
                     else
                         bq = dequant_f16(q, dqh[j]);
                 } else {
                     if constexpr (GROUPED)
-                        bq = dequant_bf16_scaled(q, dqb[j], sf[j]);
+                        bq = dequant_bf16_scaled(q, sf[j], zf[j]);
                     else
                         bq = bf16_biased(q);
                 }
@@ -796,6 +807,58 @@ void prefill_gemm_kernel(GemmKArgs a)
             }
         }
     }
+    if constexpr (ACT == ACT_F16 && !GROUPED) {
+        if (zfl & ZF_FRAC) {
+            // fractional zero points (a slower path): subtract (z - zi) times
+            // each token's sum of activations over K, computed here from X
+            // (TPR threads per token, each a contiguous share of K, added in
+            // a fixed order)
+            constexpr int TPR = GEMM_THREADS / BM;
+            float* rs = reinterpret_cast<float*>(smem);          // [TPR][BM], then [BM]
+            {
+                const int row = tid / TPR, part = tid - row * TPR;
+                const int len = a.K / TPR;                       // a multiple of 16
+                const uint16_t* xs = a.X + (size_t)min(m0 + row, a.M - 1) * a.K + (size_t)part * len;
+                float t = 0.0f;
+#pragma unroll 1
+                for (int k = 0; k < len; k += 8) {
+                    const u32x4 v = ld16(xs + k);
+                    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const half2_t h = h2_of(u[i]);
+                        t += (float)h.x;
+                        t += (float)h.y;
+                    }
+                }
+                rs[part * BM + row] = t;
+            }
+            __syncthreads();
+            if (tid < BM) {
+                float t = rs[tid];
+                for (int q = 1; q < TPR; ++q)
+                    t += rs[q * BM + tid];
+                rs[TPR * BM + tid] = t;
+            }
+            __syncthreads();
+            float zfr[JW];                              // z - floor(z) of this lane's columns
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+                const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(*szsrc[j] >> 16));
+                zfr[j] = z - floorf(z);
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sx = rs[TPR * BM + rb * 16 + 4 * (l >> 4) + v];
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        acc[rb][j][v] -= zfr[j] * sx;
+                }
+            __syncthreads();                            // before the epilogue reuses the LDS
+        }
+    }
     if constexpr (!GROUPED) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -882,6 +945,14 @@ void prefill_gemm_kernel(GemmKArgs a)
         }
     }
 
+    if (zfl & ZF_BAD) {
+        // zero points out of the supported range: NaN rather than wrong numbers
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                acc[rb][j] = (floatx4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
     // ---- store: round to the activation format into an LDS tile, then
     // write whole rows of the tile with 16-byte stores
     uint16_t* yt = reinterpret_cast<uint16_t*>(smem);   // [BM][YT_PITCH]; the last step's barrier freed it
@@ -927,10 +998,6 @@ static hipError_t launch_gemm_act(const GemmKArgs& k, int BM, bool grouped, hipS
     return grouped ? launch_gemm_t<ACT, 128, true>(k, st) : launch_gemm_t<ACT, 128, false>(k, st);
 }
 
-size_t prepass_lds_bytes(int r, int kc)
-{
-    return (size_t)ec_slice_bytes(r, kc) + (size_t)kc * 2;
-}
 
 // The gate / X A prepass and its reduction: T_g (and, for the GEMM's bf16
 // per-channel zero-point term, each token's activation sum) in the workspace.
@@ -1028,6 +1095,7 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
     k.Y = (uint16_t*)a.Y;
     k.partial = (floatx4*)(a.ws + p.off_gemm_partial);
     k.cnt = (uint32_t*)(a.ws + p.off_gemm_cnt);
+    k.zflags = &reinterpret_cast<const BlobHeader*>(a.packed)->zflags;
     k.M = a.M; k.N = a.N; k.K = a.K; k.r = a.r; k.r_pad = p.r_pad; k.G = a.G;
     k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;
     k.mt = p.mt; k.nt = p.nt; k.ksplit = p.ksplit; k.Mpad = p.Mpad;

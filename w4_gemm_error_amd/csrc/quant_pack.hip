@@ -1,5 +1,7 @@
 // quant_pack.hip -- offline weight preparation on the GPU: RTN int4
 // quantization into canonical codes, and the canonical <-> blob re-layout.
+#include <algorithm>
+
 #include "w4ec_common.h"
 #include "w4ec_launch.h"
 
@@ -166,9 +168,11 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scale, const uint16_
         uint16_t s = scale[(size_t)n * NG + gi];
         uint16_t z = zero[(size_t)n * NG + gi];
         float zf = (float)__builtin_bit_cast(_Float16, z);
-        bool ok = (zf >= 0.0f) && (zf <= 15.0f) && (zf == rintf(zf));
-        if (!ok)
-            atomicOr(&hdr->bad_zero, 1u);
+        // any zero point is accepted; the kernels take its integer part
+        // exactly and correct for a fractional part, which needs |z| <= ZMAX
+        const uint32_t f = !(fabsf(zf) <= ZMAX) ? ZF_BAD : (zf != floorf(zf) ? ZF_FRAC : 0u);
+        if (f)
+            atomicOr(&hdr->zflags, f);
         v = (uint32_t)s | ((uint32_t)z << 16);
     }
     sz[idx] = v;
@@ -181,7 +185,7 @@ __global__ void write_header_kernel(BlobHeader* hdr, int N, int K, int G)
         hdr->N = N;
         hdr->K = K;
         hdr->G = G;
-        hdr->bad_zero = 0;
+        hdr->zflags = 0;
     }
 }
 
@@ -256,6 +260,25 @@ hipError_t launch_unpack(const void* packed, int N, int K, int G, uint8_t* qc,
     size_t ns = (size_t)N * g.NG;
     hipLaunchKernelGGL(unpack_sz_kernel, dim3(blocks_for(ns, 256)), dim3(256), 0, st,
                        (const uint32_t*)(base + g.sz_off), N, g.NG, g.Npad, scale, zero);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- workspace reset
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* p, size_t n16)
+{
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+        p[i] = (u32x4){0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st)
+{
+    const size_t n16 = bytes / 16;
+    if (n16 == 0)
+        return hipSuccess;
+    const size_t wgs = std::min<size_t>((n16 + 255) / 256, 2048);
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)wgs), dim3(256), 0, st, (u32x4*)p, n16);
     return hipGetLastError();
 }
 

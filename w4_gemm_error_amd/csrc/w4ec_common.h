@@ -40,10 +40,15 @@ constexpr int PANEL_BYTES = 1024;
 constexpr size_t HEADER_BYTES = 256;
 constexpr uint32_t BLOB_MAGIC = 0x43453457u;  // "W4EC"
 
+// zero-point flags of a blob (set by the pack kernel)
+constexpr uint32_t ZF_FRAC = 1u;   // some zero point is not an integer
+constexpr uint32_t ZF_BAD = 2u;    // some zero point is not finite or |z| > ZMAX: the layer's outputs are NaN
+constexpr float ZMAX = 1024.0f;    // the exact integer offsets hold for |z| <= ZMAX
+
 struct BlobHeader {
     uint32_t magic;
     int32_t N, K, G;
-    uint32_t bad_zero;   // set by the pack kernel when a zero point is not an integer in 0..15
+    uint32_t zflags;     // ZF_FRAC | ZF_BAD
 };
 
 __host__ __device__ inline int nibble_of(int t) { return (t & 1) ? 4 + (t >> 1) : (t >> 1); }
@@ -86,6 +91,9 @@ template <int ACT> __device__ inline float act_to_f32(uint16_t v)
         return __uint_as_float((uint32_t)v << 16);
     }
 }
+
+// A quiet NaN in the activation format.
+template <int ACT> __device__ inline uint16_t act_nan() { return ACT == ACT_F16 ? 0x7E00u : 0x7FC0u; }
 
 // float -> act bits, round to nearest even.
 template <int ACT> __device__ inline uint16_t f32_to_act(float f)
@@ -168,17 +176,20 @@ __device__ inline u32x4 dequant_f16(uint32_t w, const DqF16& c)
     return r;
 }
 
-// Same, multiplied by the scale s (rounded once, to fp16).
+// Same, times the scale s, plus c2 = -(z - zi) s for a zero point z with
+// integer part zi (the consts hold zi): (q - zi) s - (z - zi) s in one fused
+// multiply-add, rounded once to fp16.  With an integer zero point c2 = -0
+// and this is the rounded product (q - z) s.  sc holds {s, c2}.
 
-__device__ inline u32x4 dequant_f16_scaled(uint32_t w, const DqF16& c, half2_t s2)
+__device__ inline u32x4 dequant_f16_scaled(uint32_t w, const DqF16& c, half2_t s2, half2_t c2)
 {
     const u32x4 q = dequant_f16(w, c);
     const uint32_t q0 = q.x, q1 = q.y, q2 = q.z, q3 = q.w;
     u32x4 r;
-    r.x = u32_of(h2_of(q0) * s2);
-    r.y = u32_of(h2_of(q1) * s2);
-    r.z = u32_of(h2_of(q2) * s2);
-    r.w = u32_of(h2_of(q3) * s2);
+    r.x = u32_of(__builtin_elementwise_fma(h2_of(q0), s2, c2));
+    r.y = u32_of(__builtin_elementwise_fma(h2_of(q1), s2, c2));
+    r.z = u32_of(__builtin_elementwise_fma(h2_of(q2), s2, c2));
+    r.w = u32_of(__builtin_elementwise_fma(h2_of(q3), s2, c2));
     return r;
 }
 
@@ -224,13 +235,18 @@ __device__ inline u32x4 bf16_biased(uint32_t w)
     return r;
 }
 
-__device__ inline u32x4 dequant_bf16_scaled(uint32_t w, float off, float s)
+// q s + c in fp32 with c = -z s, then rounded to bf16.  z s is exact in fp32
+// (two fp16 values carry at most 22 significant bits), so the fused
+// multiply-add rounds (q - z) s once, for any fp16 zero point z.
+__device__ inline float nib_val(uint32_t w, int p) { return (float)((w >> (4 * p)) & 0xFu); }
+
+__device__ inline u32x4 dequant_bf16_scaled(uint32_t w, float s, float c)
 {
     u32x4 r;
-    r.x = bf16_pair_from_f32(nib_f32(w, 0, off) * s, nib_f32(w, 4, off) * s);
-    r.y = bf16_pair_from_f32(nib_f32(w, 1, off) * s, nib_f32(w, 5, off) * s);
-    r.z = bf16_pair_from_f32(nib_f32(w, 2, off) * s, nib_f32(w, 6, off) * s);
-    r.w = bf16_pair_from_f32(nib_f32(w, 3, off) * s, nib_f32(w, 7, off) * s);
+    r.x = bf16_pair_from_f32(fmaf(nib_val(w, 0), s, c), fmaf(nib_val(w, 4), s, c));
+    r.y = bf16_pair_from_f32(fmaf(nib_val(w, 1), s, c), fmaf(nib_val(w, 5), s, c));
+    r.z = bf16_pair_from_f32(fmaf(nib_val(w, 2), s, c), fmaf(nib_val(w, 6), s, c));
+    r.w = bf16_pair_from_f32(fmaf(nib_val(w, 3), s, c), fmaf(nib_val(w, 7), s, c));
     return r;
 }
 
@@ -343,12 +359,31 @@ __device__ inline void atomic_store_dev(uint32_t* p, uint32_t v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A bounded wait: every waiter gives up after roughly a second so that a
-// broken hand-over can never hang the GPU; it then records the failure.
+// A bounded wait: every waiter gives up after this many polls (roughly a
+// second) so that a broken hand-over can never hang the GPU; it then records
+// the failure in the workspace and its results become NaN.  The host can
+// lower the limit (w4ec_set_wait_limit); 0 makes every wait give up at once.
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
 // ------------------------------------------------------------ launch plans
 // (shared by the host dispatch and the workspace sizing)
+
+// Geometry of a staged [A | w_g] slice (the decode EC role and the prefill
+// prepass): halves per LDS row of an A slice (the transpose read needs 8-byte
+// aligned rows); column blocks of A, and the total with the gate block; LDS
+// bytes of a slice of kc rows (plus slack for the last block's over-read).
+__host__ __device__ inline int ec_pitch(int r) { return (r + 3) & ~3; }
+__host__ __device__ inline int ec_a_blocks(int r) { return (r + 15) >> 4; }
+__host__ __device__ inline int ec_blocks(int r) { return ec_a_blocks(r) + 1; }
+__host__ __device__ inline int ec_slice_bytes(int r, int kc) { return (kc * ec_pitch(r) + 16) * 2; }
+// LDS of a prepass workgroup: the slice and its gate vector
+inline size_t prepass_lds_bytes(int r, int kc) { return (size_t)ec_slice_bytes(r, kc) + (size_t)kc * 2; }
+
+constexpr int DEC_THREADS = 256;     // threads per decode workgroup
+constexpr int DEC_XLDS_CHUNKS = 8;   // 16-byte chunks of staged activations per decode thread
+// the decode main role stages X in LDS for at most 4 tokens and this many bytes
+constexpr size_t DEC_XLDS_MAX_BYTES = (size_t)DEC_XLDS_CHUNKS * 16 * DEC_THREADS;
+inline bool decode_use_xlds(int M, int K) { return M <= 4 && (size_t)M * K * 2 <= DEC_XLDS_MAX_BYTES; }
 
 constexpr int DEC_EC_KS = 256;   // at most this many k per decode EC workgroup
 constexpr int DEC_EC_RMAX = 128; // at most this many decode EC workgroups reduce (half the CUs)

@@ -38,10 +38,10 @@ struct LayerArgs {
     // single-factor correction over salient channels (S non-null): T_g is
     // the gather X[:, S] (r = s channels), B is the factor R; no gate
     const int32_t* S; // [s] input-channel indices
+    uint32_t spin;    // polls before a bounded wait gives up (0: at once)
 };
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st);
-bool decode_use_xlds(int M, int K);
 hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st);
 
 // unfused / semi-fused prefill pieces: T_g into the workspace, then Y += T_g B
@@ -67,6 +67,8 @@ struct XfpArgs {
 };
 hipError_t launch_decode_xfp(const XfpArgs& x, const DecodePlan& p, hipStream_t st);
 hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hipStream_t st);
-size_t prepass_lds_bytes(int r, int kc);
+// bytes (a multiple of 16, 16-byte aligned) set to zero by a kernel (no
+// hipMemsetAsync node when a caller captures the stream into a graph)
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace w4ec
