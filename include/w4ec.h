@@ -86,18 +86,24 @@ int w4ec_quantize_rtn(const float* W, int N, int K, int group_size,
                       uint8_t* q_canon, uint16_t* scale, uint16_t* zero,
                       void* stream);
 
-/* Re-lay canonical codes and fp16 scale/zero into the device blob (an
- * offline step; weights are prepared once).  `zero` must hold integers in
- * 0..15.  This call synchronizes `stream` to check the zero points and
- * returns W4EC_ERR_INVALID_ARG if one is not such an integer (the blob is
- * then unusable).
+/* Re-lay canonical codes and fp16 scale/zero into the device blob.  Weights
+ * are prepared once, offline (the 2:4-sparsity-versus-quantization summary,
+ * "Is 2:4 Sparsity Still Worth It?", chiosa.app, section on space and
+ * compute parity, counts index and scale bytes with the weights and prepares
+ * them offline).  Zero points need not be integers: the SPEAR summary's
+ * results (section 3.1) cover quantizers beside RTN (GPTQ, AWQ, OmniQuant)
+ * whose zero points are arbitrary; any fp16 z with |z| <= 1024 is exact (the
+ * kernels take floor(z) exactly and correct for the fraction).  A zero point
+ * that is not finite or lies beyond +-1024 is stored as NaN: the outputs that
+ * use it are NaN, and w4ec_unpack returns NaN for it.  Asynchronous.
  *   q_canon device uint8 [N, K/2]; scale, zero device fp16 bits [N, K/G];
  *   packed  device, w4ec_packed_bytes(N, K, G) bytes, 256-byte aligned.   */
 int w4ec_pack(const uint8_t* q_canon, const uint16_t* scale, const uint16_t* zero,
               int N, int K, int group_size, void* packed, void* stream);
 
-/* Exact inverse of w4ec_pack (a test hook): blob -> canonical codes and
- * fp16 scale/zero, same layouts as w4ec_pack's inputs.  Asynchronous. */
+/* Inverse of w4ec_pack (a test hook): blob -> canonical codes and fp16
+ * scale/zero, same layouts as w4ec_pack's inputs; exact except for zero
+ * points that w4ec_pack stored as NaN.  Asynchronous. */
 int w4ec_unpack(const void* packed, int N, int K, int group_size,
                 uint8_t* q_canon, uint16_t* scale, uint16_t* zero, void* stream);
 
@@ -268,8 +274,8 @@ int w4ec_prefill_ec_apply(void* Y, const void* B, int M, int N, int K, int r, in
  * w4ec_pack with the eight indices of each dword in natural order (byte j
  * holds those of k = 2j and 2j + 1), so that each byte selects one entry
  * of a 256-entry table of codebook pairs.  w4ec_unpack does not read it.
- * Synchronizes the stream.  Returns W4EC_ERR_UNSUPPORTED unless K is a
- * multiple of 128. */
+ * Asynchronous.  Returns W4EC_ERR_UNSUPPORTED unless K is a multiple of
+ * 128. */
 int w4ec_pack_xfp(const uint8_t* idx_canon, int N, int K, void* packed, void* stream);
 
 /* Codebook weights with a sparse outlier residual, decode (XFP summary,

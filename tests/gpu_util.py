@@ -94,7 +94,7 @@ def sample_rows(M):
     return sorted(set(min(x, M - 1) for x in rows))
 
 
-def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=None):
+def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=None, expect_nan=False):
     act = d["act"]
     r = d["r"] if r is None else r
     X = dev_act(d["X"], act)
@@ -110,7 +110,8 @@ def gpu_layer(d, packed, phase, *, r=None, b_g=None, with_gate=True, workspace=N
     Y = nan_y(d["M"], d["N"], act)
     fn(X, packed, A, B, wg, bg, N=d["N"], group_size=d["group_size"], workspace=workspace, Y=Y)
     torch().cuda.synchronize()
-    assert_all_finite(Y, f"{phase} M={d['M']}")
+    if not expect_nan:
+        assert_all_finite(Y, f"{phase} M={d['M']}")
     # every call leaves the hand-over state at zero; a nonzero byte there
     # would mean that a bounded wait timed out
     state = workspace[: w4.W4EC_WS_STATE_BYTES]

@@ -7,7 +7,8 @@ correct for the fractional part (an activation-sum term, or a fused
 multiply-add in the grouped dequantization).  A zero point that is not
 finite or lies outside that range makes the layer's outputs NaN.
 Same tolerance as the layer; every path: decode and prefill, fp16 and bf16,
-per channel and grouped, with and without the compensator.
+per channel and grouped, with and without the compensator.  An out-of-range
+zero point is stored as NaN, so the column that uses it comes out NaN.
 """
 import numpy as np
 import pytest
@@ -76,20 +77,29 @@ def test_fractional_zero_point_parity(phase, act, M, N, K, r, G):
 
 
 @pytest.mark.parametrize("phase,act,G", [("decode", "fp16", 512), ("prefill", "fp16", 128),
-                                         ("prefill", "bf16", 512), ("decode", "bf16", 128)])
+                                         ("prefill", "bf16", 512), ("decode", "bf16", 128),
+                                         ("prefill", "fp16", 512), ("decode", "fp16", 128)])
 def test_out_of_range_zero_point_gives_nan(phase, act, G):
+    """A zero point beyond +-1024 (or not finite) is stored as NaN: the
+    output column that uses it is NaN for every token, the others are right."""
     _print(f"out-of-range z {phase} {act} G={G}")
     t = torch()
     M = 3 if phase == "decode" else 80
     cfg = synth.LAYERS["mlp_70b_bf16"] if act == "bf16" else synth.LAYERS["tiny"]
     d = synth.make_layer(cfg, M, seed=5, N=272, K=512, r=8, group_size=G)
     qc, s, z = oracle.rtn_quantize(d["W"], G)
-    z = z.copy()
-    z.reshape(-1)[7] = np.float16(4096.0).view(np.uint16)
-    packed = pack_host(qc, s, z, d["N"], d["K"], G)          # accepted, flagged in the blob
-    fn = w4.w4ec_linear_decode if phase == "decode" else w4.w4ec_linear_prefill
-    X = dev_act(d["X"], act)
-    ws = t.zeros(max(w4.w4ec_workspace_bytes(M, d["N"], d["K"], 0, G), 256), dtype=t.uint8, device="cuda")
-    Y = fn(X, packed, None, None, None, 0.0, N=d["N"], group_size=G, workspace=ws)
-    t.cuda.synchronize()
-    assert bool(t.isnan(Y.float()).all())
+    ng = d["K"] // G
+    bad_col = 7 // ng
+    z2 = z.copy()
+    z2.reshape(-1)[7] = np.float16(4096.0).view(np.uint16)
+    z2.reshape(-1)[ng * 20] = np.float16(np.inf).view(np.uint16)     # column 20, group 0
+    packed = pack_host(qc, s, z2, d["N"], d["K"], G)
+    _, _, zu = w4.w4ec_unpack(packed, d["N"], d["K"], G)
+    zu = host_bits(zu)
+    assert np.isnan(zu.view(np.float16).astype(np.float32).reshape(-1)[[7, ng * 20]]).all()
+    Y = gpu_layer(dict(d, M=M), packed, phase, r=0, expect_nan=True)
+    Yf = synth.act_bits_to_f64(Y, act)
+    assert np.isnan(Yf[:, [bad_col, 20]]).all()
+    good = [n for n in range(d["N"]) if n not in (bad_col, 20)]
+    ref = oracle_layer(d, (qc, s, z), r=0)
+    assert_close(Y[:, good], ref[:, good], act, "columns with valid zero points")

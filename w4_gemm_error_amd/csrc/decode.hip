@@ -59,7 +59,6 @@ struct DecodeKArgs {
     int stage_first;     // main workgroups stage X before issuing weight loads
     uint32_t* flags;     // [2]: a wait timed out (sticky: every later call's Y is NaN)
     uint32_t spin;       // polls before a bounded wait gives up (0: give up at once)
-    const uint32_t* zflags;  // the blob's zero-point flags (ZF_*), or null
     uint32_t* partial;   // [P][M][RC] hand-over words
     uint8_t* rep_ctrl;   // DEC_NREP slots of DEC_REP_CTRL_STRIDE bytes: [1] readers done
     uint8_t* rep_data;   // DEC_NREP slots of DEC_REP_DATA_STRIDE bytes: T_g [M][r_pad] as hand-over words
@@ -146,7 +145,7 @@ __device__ inline void dec_ec_mfma(const u32x4 (&xf)[DEC_EC_KSMAX / 32], const u
 // Every reducer of a token adds the P slices of the row in slice order and
 // runs the bottleneck in fp32, so all of them compute the same gates.
 template <int ACT>
-__device__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, int nred)
+__device__ __forceinline__ void decode_vgate_reduce(const DecodeKArgs& a, uint8_t* smem, int j, int nred)
 {
     const int tid = threadIdx.x;
     const int M = a.M, r = a.r, h = a.h;
@@ -301,7 +300,7 @@ __host__ __device__ inline int dec_scalar_reducers(int P, int M, int r_pad)
 }
 
 template <int ACT>
-__device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
+__device__ __forceinline__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 {
     const int tid = threadIdx.x;
     const int l = tid & 63;
@@ -484,7 +483,10 @@ __device__ void decode_ec_role(const DecodeKArgs& a, uint8_t* smem)
 }
 
 // LDS of the main role: the staged activations (during the stream), the
-// wavefront reduction (after it) at the same offset, then the B columns
+// wavefront reduction (after it) at the same offset, then the B columns,
+// the salient-channel operand, and for fractional zero points the chunk
+// sums of the activations ([M][K / 128] floats) and the correction
+// ([M][CB x 16] floats)
 __host__ __device__ inline size_t main_b_offset(int M, int K, bool xlds, int CB)
 {
     size_t b = (size_t)4 * CB * 64 * 16;
@@ -493,8 +495,15 @@ __host__ __device__ inline size_t main_b_offset(int M, int K, bool xlds, int CB)
     return (b + 15) / 16 * 16;
 }
 
+__host__ __device__ inline size_t main_frac_offset(int M, int K, bool xlds, int CB, int r_pad, bool ec, bool gather)
+{
+    const size_t b = main_b_offset(M, K, xlds, CB) + (ec ? (size_t)CB * r_pad * PANEL_N * 2 : 0) +
+                     (gather ? (size_t)M * r_pad * 2 : 0);
+    return (b + 15) / 16 * 16;
+}
+
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
-__device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
+__device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 {
     const int tid = threadIdx.x;
     const int l = tid & 63;
@@ -509,12 +518,6 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     const int M = a.M;
     const int K = a.K;
     const int KB = a.KB;
-    // a wait that timed out in an earlier call on this workspace (issued
-    // first, needed only at the stores; no workspace without a rank), and a
-    // blob whose zero points are out of range (both make the outputs NaN)
-    const uint32_t sticky = (a.r > 0 ? atomic_load_dev(&a.flags[2]) : 0u) |
-                            (a.zflags ? (*a.zflags & ZF_BAD) : 0u);
-
     const int per = KB >> 2, rem = KB & 3;
     const int kcnt = per + (w < rem ? 1 : 0);
     // a wavefront without panels (K < 512) still issues its (clamped) loads,
@@ -745,31 +748,28 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     }
 
     // Zero points: the codes are offset by the integer part zi = floor(z)
-    // exactly (the exponent trick); a fractional part zf = z - zi leaves
-    // -zf * s * (sum of the group's activations), for which accx keeps the
-    // token's activation sum over the current group (one more MFMA per
-    // k-step, against a column of ones).  With integer zero points zf = 0
-    // and the correction adds nothing.
-    floatx4 acc[CB], accg[CB], accx;
-    float s_cur[CB], szf[CB];
+    // exactly (the exponent trick).  A fractional part zf = z - zi leaves
+    // -zf * s * (the group's activation sum) per output, which the epilogue
+    // subtracts when the blob records a fractional zero point (a slower
+    // path; with integer zero points nothing is added).
+    floatx4 acc[CB], accg[CB];
+    float s_cur[CB];
     DqF16 dqh[CB];
     float dqb[CB];
+    bool fz = false;        // a zero point this lane has seen is fractional
     auto set_sz = [&](const uint32_t* v) {
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
             s_cur[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
             const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
             const float zi = floorf(z);
-            szf[j] = s_cur[j] * (z - zi);
+            fz |= z != zi;
             if constexpr (ACT == ACT_F16)
                 dqh[j] = dq_f16_consts(zi);
             else
                 dqb[j] = -(8388608.0f + zi);
         }
     };
-    constexpr uint32_t ONE2 = ACT == ACT_F16 ? 0x3C003C00u : 0x3F803F80u;   // two ones
-    const u32x4 ones = (u32x4){ONE2, ONE2, ONE2, ONE2};
-    accx = (floatx4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
         acc[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -826,10 +826,9 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
                 if (valid && left_in_group == ppg && i > 0) {
 #pragma unroll
                     for (int j = 0; j < CB; ++j) {
-                        acc[j] += s_cur[j] * accg[j] - szf[j] * accx;
+                        acc[j] += s_cur[j] * accg[j];
                         accg[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
                     }
-                    accx = (floatx4){0.f, 0.f, 0.f, 0.f};
                     set_sz(szv);
                 }
             }
@@ -849,11 +848,6 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
                     accg[j] = mfma16x16x32<ACT>(xf[s], bq, accg[j]);
                 }
             }
-            if constexpr (!CBK) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    accx = mfma16x16x32<ACT>(xf[s], ones, accx);
-            }
             if constexpr (GROUPED) {
                 if (--left_in_group == 0)
                     left_in_group = ppg;
@@ -867,7 +861,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 
 #pragma unroll
     for (int j = 0; j < CB; ++j)
-        acc[j] += s_cur[j] * accg[j] - (CBK ? 0.0f : szf[j]) * accx;
+        acc[j] += s_cur[j] * accg[j];
 
     // sparse outlier residual: this thread's share of column rc, for every
     // token, sum x[m][k] * val (X from LDS while it is still staged there)
@@ -921,12 +915,71 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         }
     }
 
-    // ---- reduce the four K shares (fixed order); LDS is reused from here on
-    __syncthreads();
+    // ---- reduce the four K shares (fixed order); LDS is reused from here on.
+    // The barrier also tells whether some lane of the workgroup saw a
+    // fractional zero point.
+    bool anyfrac = false;
+    if constexpr (CBK)
+        __syncthreads();
+    else
+        anyfrac = __syncthreads_or(fz) != 0;
     floatx4* red = reinterpret_cast<floatx4*>(smem);                       // [4][CB][64]
 #pragma unroll
     for (int j = 0; j < CB; ++j)
         red[(w * CB + j) * 64 + l] = acc[j];
+
+    // Fractional zero points (a slower path, taken once the partial sums are
+    // parked and few registers are live): each token's activation sums over
+    // 128-k chunks, xck[m][kb] (from global memory: the staged copy is being
+    // overwritten), then for this workgroup's columns the correction
+    // corr[m][c] = sum_g s_g (z_g - floor z_g) sum_{k in g} x[m][k], groups and
+    // chunks added in order; the epilogue subtracts it (zero without a
+    // fractional zero point).
+    float* xck = reinterpret_cast<float*>(smem + main_frac_offset(M, K, XLDS, CB, a.r_pad,
+                                                                  a.r > 0, a.r > 0 && a.S != nullptr));
+    float* corr = xck + M * KB;                                            // [M][CB x 16]
+    if (anyfrac) {
+#pragma unroll 1
+        for (int e = tid; e < M * KB; e += DEC_THREADS) {
+            const int m = e / KB, kb = e - m * KB;
+            const uint16_t* src = a.X + (size_t)m * K + kb * PANEL_K;
+            float t = 0.0f;
+#pragma unroll 1
+            for (int c = 0; c < PANEL_K; c += 8) {
+                const u32x4 v = ld16(src + c);
+                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    t += act_to_f32<ACT>((uint16_t)(u[i] & 0xFFFF));
+                    t += act_to_f32<ACT>((uint16_t)(u[i] >> 16));
+                }
+            }
+            xck[e] = t;
+        }
+        __syncthreads();                                    // uniform: anyfrac is the workgroup's
+        const int cpg = a.G / PANEL_K;                       // chunks per group
+#pragma unroll 1
+        for (int e = tid; e < M * CB * PANEL_N; e += DEC_THREADS) {
+            const int m = e / (CB * PANEL_N), c = e - m * (CB * PANEL_N);
+            const int nc = min(cb0 * PANEL_N + c, a.Npad - 1);
+            float t = 0.0f;
+#pragma unroll 1
+            for (int g = 0; g < K / a.G; ++g) {
+                const uint32_t v = a.sz[(size_t)g * a.Npad + nc];
+                const float sg = (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFF));
+                const float zg = (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+                float xsum = 0.0f;
+#pragma unroll 1
+                for (int q = 0; q < cpg; ++q)
+                    xsum += xck[m * KB + g * cpg + q];
+                t += sg * (zg - floorf(zg)) * xsum;
+            }
+            corr[e] = t;
+        }
+    } else if constexpr (!CBK) {
+        for (int e = tid; e < M * CB * PANEL_N; e += DEC_THREADS)
+            corr[e] = 0.0f;
+    }
 
     // ---- gated rank-r activations from this workgroup's replica slot, in
     // the MFMA A-operand layout (row = token l & 15, ranks 32 rs + koff + t),
@@ -936,6 +989,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     uint64_t* sdata = reinterpret_cast<uint64_t*>(a.rep_data + (size_t)slot * DEC_REP_DATA_STRIDE);
     u32x4 af[8];
     bool lost = false;      // this wavefront's wait for T_g gave up: its outputs are NaN
+    uint32_t sticky = 0;    // a wait gave up in an earlier call on this workspace: NaN too
     // salient channels (SERQ summary, section 2): the operand is the gather
     // X[token][S[j]], made by the whole workgroup into LDS ([M][r_pad], past
     // the parked B) -- no EC role and no hand-over.  An index outside [0, K)
@@ -959,6 +1013,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
     } else if (a.r > 0 && w < CB && !a.S) {
         const uint64_t* src = sdata + (row * a.r_pad + koff) / 4;
         uint32_t it = 0;
+        sticky = atomic_load_dev(&a.flags[2]);            // alongside the first poll
         lost = a.spin == 0;
         // read all of them, and again while any has not landed (a wait limit
         // of 0 gives up at once)
@@ -1008,6 +1063,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
         tot += red[(2 * CB + j) * 64 + l];
         tot += red[(3 * CB + j) * 64 + l];
         const int n = n_l[j];
+
         if constexpr (CBK) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -1032,6 +1088,13 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
             for (int rs = 0; rs < 8; ++rs)
                 if (rs < nsteps)
                     tot = mfma16x16x32<ACT>(af[rs], bfr[rs], tot);
+        }
+        if constexpr (!CBK) {
+            // fractional zero points (zero otherwise: read unconditionally,
+            // so that the compiler keeps one copy of this loop)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                tot[v] -= corr[min(4 * (l >> 4) + v, M - 1) * (CB * PANEL_N) + j * PANEL_N + (l & 15)];
         }
         if (n < a.N) {
             // a wait that gave up here, or one that did in an earlier call on
@@ -1075,7 +1138,7 @@ __device__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 // holds ~450 workgroups, which fit the CUs in one round at two wavefronts
 // per SIMD, i.e. within 256 registers.
 template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
-__global__ __launch_bounds__(DEC_THREADS, CB == 2 ? 2 : 1)
+__global__ __launch_bounds__(DEC_THREADS, 2)
 void decode_kernel(DecodeKArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
@@ -1092,8 +1155,8 @@ void decode_kernel(DecodeKArgs a)
 
 static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r, bool gather)
 {
-    return main_b_offset(M, K, p.xlds, p.CB) + (r > 0 ? (size_t)p.CB * p.r_pad * PANEL_N * 2 : 0) +
-           (r > 0 && gather ? (size_t)M * p.r_pad * 2 : 0);
+    return main_frac_offset(M, K, p.xlds, p.CB, p.r_pad, r > 0, r > 0 && gather) +
+           (size_t)M * (K / PANEL_K + p.CB * PANEL_N) * sizeof(float);
 }
 
 // LDS of the EC role: the staged slice and gate vector, then the final reduction
@@ -1213,7 +1276,6 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     k.stage_first = p.stage_first;
     k.flags = (uint32_t*)(a.ws + p.off_flags);
     k.spin = a.spin;
-    k.zflags = &reinterpret_cast<const BlobHeader*>(a.packed)->zflags;
     k.partial = (uint32_t*)(a.ws + p.off_partial);
     k.rep_ctrl = (uint8_t*)(a.ws + p.off_rep_ctrl);
     k.rep_data = (uint8_t*)(a.ws + p.off_rep_data);

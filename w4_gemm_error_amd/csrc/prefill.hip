@@ -445,7 +445,6 @@ struct GemmKArgs {
     uint16_t* Y;
     floatx4* partial;  // [tile][ksplit][NW][RB][JW][64] fragments
     uint32_t* cnt;     // [mt*nt]
-    const uint32_t* zflags;  // the blob's zero-point flags (ZF_*)
     int M, N, K, r, r_pad, G, NB, KB, Npad, mt, nt, ksplit, Mpad;
 };
 
@@ -473,6 +472,281 @@ template <int BM>
 constexpr int gemm_lds_bytes()
 {
     return (2 * BM * PANEL_K * 2 > BM * YT_PITCH * 2) ? 2 * BM * PANEL_K * 2 : BM * YT_PITCH * 2;
+}
+
+// The end of a GEMM tile: the split-K hand-over (the last workgroup of a
+// tile adds the partial sums), the zero-point terms and scales, the gated
+// rank-r correction, and the store.  NWV wavefronts, each owning 16 / NWV
+// column blocks of the 256-column tile for all BM rows; `smem` is an LDS
+// region of LDSB bytes that the main loop no longer uses.
+template <int ACT, int BM, bool GROUPED, int NWV, int LDSB>
+__device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM / 16][16 / NWV], const float (&sf)[16 / NWV],
+                                          const float (&zf)[16 / NWV], const uint32_t* const (&szsrc)[16 / NWV], int tm,
+                                          int tn, int kz, int m0, int n0, uint8_t* smem, uint32_t& s_old)
+{
+    constexpr int GEMM_THREADS = 64 * NWV;
+    constexpr int NW = NWV;
+    constexpr int JW = 16 / NWV;
+    constexpr int RB = BM / 16;
+    constexpr bool BIAS = ACT == ACT_BF16 && !GROUPED;
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // ---- split-K hand-over: the last workgroup of the tile sums the partials
+    // (fragment layout [tile][split][wavefront][RB][JW][64 lanes], 16 bytes per lane)
+    if (a.ksplit > 1) {
+        const int tile = tm * a.nt + tn;
+        // byte offset of a fragment, within the region of all tiles' partials
+        auto frag = [&](int z, int rb, int j) -> uint32_t {
+            return (uint32_t)(((((size_t)tile * a.ksplit + z) * NW + w) * RB * JW + rb * JW + j) * 64 + l) * 16u;
+        };
+        const __amdgpu_buffer_rsrc_t prs =
+            dev_rsrc(a.partial, (uint32_t)((size_t)a.mt * a.nt * a.ksplit * NW * RB * JW * 64 * 16));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                st16_sc1(prs, frag(kz, rb, j), acc[rb][j]);
+        wait_all_mem();
+        __syncthreads();
+        if (tid == 0)
+            s_old = atomic_add_dev(&a.cnt[tile], 1u);
+        __syncthreads();
+        if (s_old != (uint32_t)(a.ksplit - 1))
+            return;
+        if (tid == 0)
+            atomic_store_dev(&a.cnt[tile], 0u);
+        // splits added in order; all fragments of one split are in flight at once
+        floatx4 sum[RB][JW];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                sum[rb][j] = (floatx4){0.f, 0.f, 0.f, 0.f};
+        for (int z = 0; z < a.ksplit; ++z) {
+            if (z == kz) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        sum[rb][j] += acc[rb][j];
+            } else {
+                floatx4 t[RB][JW];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        t[rb][j] = ld16_sc1(prs, frag(z, rb, j));
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        sum[rb][j] += t[rb][j];
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                acc[rb][j] = sum[rb][j];
+    }
+
+    // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r correction
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float sx = a.rowsum[m0 + rb * 16 + 4 * (l >> 4) + v];
+#pragma unroll
+                for (int j = 0; j < JW; ++j)
+                    acc[rb][j][v] -= (128.0f + zf[j]) * sx;
+            }
+        }
+    }
+    if constexpr (ACT == ACT_F16 && !GROUPED) {
+        // a fractional zero point among the tile's columns (the other forms
+        // take it in the dequantization or the bf16 zero-point term)
+        bool fz = false;
+#pragma unroll
+        for (int j = 0; j < JW; ++j) {
+            const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(*szsrc[j] >> 16));
+            fz |= z != floorf(z);
+        }
+        if (__syncthreads_or(fz)) {
+            // fractional zero points (a slower path): subtract (z - zi) times
+            // each token's sum of activations over K, computed here from X
+            // (TPR threads per token, each a contiguous share of K, added in
+            // a fixed order)
+            constexpr int TPR = GEMM_THREADS / BM;
+            float* rs = reinterpret_cast<float*>(smem);          // [TPR][BM], then [BM]
+            {
+                const int row = tid / TPR, part = tid - row * TPR;
+                const int len = a.K / TPR;                       // a multiple of 16
+                const uint16_t* xs = a.X + (size_t)min(m0 + row, a.M - 1) * a.K + (size_t)part * len;
+                float t = 0.0f;
+#pragma unroll 1
+                for (int k = 0; k < len; k += 8) {
+                    const u32x4 v = ld16(xs + k);
+                    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const half2_t h = h2_of(u[i]);
+                        t += (float)h.x;
+                        t += (float)h.y;
+                    }
+                }
+                rs[part * BM + row] = t;
+            }
+            __syncthreads();
+            if (tid < BM) {
+                float t = rs[tid];
+                for (int q = 1; q < TPR; ++q)
+                    t += rs[q * BM + tid];
+                rs[TPR * BM + tid] = t;
+            }
+            __syncthreads();
+            float zfr[JW];                              // z - floor(z) of this lane's columns
+#pragma unroll
+            for (int j = 0; j < JW; ++j) {
+                const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(*szsrc[j] >> 16));
+                zfr[j] = z - floorf(z);
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float sx = rs[TPR * BM + rb * 16 + 4 * (l >> 4) + v];
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        acc[rb][j][v] -= zfr[j] * sx;
+                }
+            __syncthreads();                            // before the epilogue reuses the LDS
+        }
+    }
+    if constexpr (!GROUPED) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+                acc[rb][j] *= sf[j];
+    }
+    if (a.r > 0) {
+        // The rank dimension in chunks of RCH: B rows [c0, c0 + RCH) of the
+        // tile's 256 columns and the same ranks of T_g for the tile's BM
+        // tokens are loaded with every load of the chunk in flight, parked in
+        // LDS, and read back as MFMA operands (B through the transpose read;
+        // its rows are padded to 272 halves so that the read is free of bank
+        // conflicts).  The last main-loop barrier freed the LDS.
+        constexpr int BP = PF_BN + 16;                  // halves per LDS row of B
+        // 64 ranks per chunk where they fit (and BM = 128), else 32
+        constexpr int RCH = BM == 128 && 64 * BP * 2 + BM * 72 * 2 <= LDSB ? 64 : 32;
+        constexpr int TP = RCH + 8;                     // halves per LDS row of T_g
+        constexpr int BCH = RCH * (PF_BN / 8) / GEMM_THREADS;             // 16-byte B chunks per thread
+        constexpr int TCH = (BM * (RCH / 8) + GEMM_THREADS - 1) / GEMM_THREADS;
+        static_assert(RCH * BP * 2 + BM * TP * 2 <= LDSB, "EC staging fits the LDS");
+        uint16_t* bl = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* tl = bl + RCH * BP;
+        const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
+        const int koff = 8 * (l >> 4);
+        for (int c0 = 0; c0 < a.r_pad; c0 += RCH) {
+            u32x4 bv[BCH], tv[TCH];
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) {
+                const int ch = tid + GEMM_THREADS * i;
+                const int jr = c0 + (ch >> 5), n = n0 + 8 * (ch & 31);
+                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+                if (jr < a.r) {
+                    const uint16_t* src = a.B + (size_t)jr * a.N + n;
+                    if (bvec && n + 8 <= a.N) {
+                        v = ld16(src);
+                    } else {
+                        uint32_t hv[8];
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            hv[t] = n + t < a.N ? (uint32_t)src[t] : 0u;
+                        v = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                    hv[6] | (hv[7] << 16)};
+                    }
+                }
+                bv[i] = v;
+            }
+#pragma unroll
+            for (int i = 0; i < TCH; ++i) {
+                const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
+                const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                // ranks past r_pad (a last chunk wider than the rest) are not loaded and not used
+                tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
+                                              : (u32x4){0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) {
+                const int ch = tid + GEMM_THREADS * i;
+                st16(bl + (ch >> 5) * BP + 8 * (ch & 31), bv[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < TCH; ++i) {
+                const int ch = tid + GEMM_THREADS * i;
+                if (ch < BM * (RCH / 8)) {
+                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                    st16(tl + rr * TP + 8 * cc, tv[i]);
+                }
+            }
+            __syncthreads();
+            const int ns = min(RCH, a.r_pad - c0) >> 5;
+            for (int rs = 0; rs < ns; ++rs) {
+                u32x4 bfr[JW];
+#pragma unroll
+                for (int j = 0; j < JW; ++j)
+                    bfr[j] = lds_bfrag(bl, BP, 16 * (JW * w + j), 32 * rs);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const u32x4 af = *reinterpret_cast<const u32x4*>(tl + (rb * 16 + (l & 15)) * TP + 32 * rs + koff);
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
+                }
+            }
+            __syncthreads();                            // before the next chunk or the output tile reuses the LDS
+        }
+    }
+
+    // ---- store: round to the activation format into an LDS tile, then
+    // write whole rows of the tile with 16-byte stores (in passes of RBP
+    // row blocks when the region holds fewer than BM rows)
+    constexpr int RBP = LDSB / (16 * YT_PITCH * 2) < RB ? LDSB / (16 * YT_PITCH * 2) : RB;
+    static_assert(RBP >= 1, "one row block of the output tile fits the LDS");
+    uint16_t* yt = reinterpret_cast<uint16_t*>(smem);   // [RBP * 16][YT_PITCH]
+    const bool vec = (a.N & 7) == 0;
+#pragma unroll
+    for (int rp = 0; rp < RB; rp += RBP) {
+        if (rp > 0)
+            __syncthreads();                            // the previous pass has read its rows
+#pragma unroll
+        for (int rb = rp; rb < rp + RBP && rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < JW; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    yt[((rb - rp) * 16 + 4 * (l >> 4) + v) * YT_PITCH + 16 * JW * w + 16 * j + (l & 15)] =
+                        f32_to_act<ACT>(acc[rb][j][v]);
+        __syncthreads();
+        const int nrow = (rp + RBP <= RB ? RBP : RB - rp) * 16;
+        for (int e = tid; e < nrow * (PF_BN / 8); e += GEMM_THREADS) {
+            const int row = e >> 5, c8 = (e & 31) * 8;
+            const int m = m0 + rp * 16 + row, n = n0 + c8;
+            if (m >= a.M || n >= a.N)
+                continue;
+            const uint16_t* src = yt + row * YT_PITCH + c8;
+            uint16_t* dst = a.Y + (size_t)m * a.N + n;
+            if (vec) {
+                st16(dst, *reinterpret_cast<const u32x4*>(src));
+            } else {
+                for (int t = 0; t < 8 && n + t < a.N; ++t)
+                    dst[t] = src[t];
+            }
+        }
+    }
 }
 
 template <int ACT, int BM, bool GROUPED>
@@ -503,10 +777,6 @@ void prefill_gemm_kernel(GemmKArgs a)
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // zero-point flags of the blob: out-of-range zero points make the
-    // outputs NaN; fractional ones need a correction in the fp16 per-channel
-    // epilogue (the other forms handle them in the dequantization)
-    const uint32_t zfl = *a.zflags;
     int tm, tn;
     tile_of(blockIdx.x, a.mt, a.nt, tm, tn);
     const int kz = blockIdx.y;
@@ -560,18 +830,29 @@ void prefill_gemm_kernel(GemmKArgs a)
     half2_t sh2[JW], ch2[JW];   // fp16 grouped: s and -(z - zi) s
     float sf[JW];
     float zf[JW];        // bf16 per-channel: z; bf16 grouped: -z s
+    // The constants are formed in fp16 from the packed dword: zi = floor(z)
+    // exactly, -(1024 + zi) and -(64 + zi) exactly (|z| <= 1024), and
+    // (zi - z) s rounded once (zi - z is exact) -- -0 for an integer zero
+    // point, so that those products are unchanged.
     auto set_sz = [&](const uint32_t* v) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < JW; ++j) {
             const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
-            const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
-            const float zi = floorf(z);
-            const _Float16 ch = (_Float16)(-(z - zi) * (float)sv);
-            sf[j] = (float)sv;
-            zf[j] = GROUPED ? -z * (float)sv : z;
+            const _Float16 zh = __builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
+            const _Float16 zi = __builtin_floorf16(zh);
+            const _Float16 ch = (zi - zh) * sv;
+            const _Float16 a = (_Float16)-1024.0f - zi, b = (_Float16)-64.0f - zi;
             sh2[j] = (half2_t){sv, sv};
             ch2[j] = (half2_t){ch, ch};
-            dqh[j] = dq_f16_consts(zi);
+            dqh[j].off_lo = (half2_t){a, a};
+            dqh[j].off_hi = (half2_t){b, b};
+            if constexpr (ACT == ACT_BF16) {
+                const float z = (float)zh;
+                sf[j] = (float)sv;
+                zf[j] = GROUPED ? -z * (float)sv : z;
+            } else {
+                sf[j] = (float)sv;
+            }
         }
     };
 
@@ -738,248 +1019,7 @@ void prefill_gemm_kernel(GemmKArgs a)
         chunk(i0, std::true_type{});
     chunk(i0, std::false_type{});
 
-    // ---- split-K hand-over: the last workgroup of the tile sums the partials
-    // (fragment layout [tile][split][wavefront][RB][JW][64 lanes], 16 bytes per lane)
-    if (a.ksplit > 1) {
-        const int tile = tm * a.nt + tn;
-        auto frag = [&](int z, int rb, int j) -> size_t {
-            return ((((size_t)tile * a.ksplit + z) * NW + w) * RB * JW + rb * JW + j) * 64 + l;
-        };
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int j = 0; j < JW; ++j)
-                st16_dev(a.partial + frag(kz, rb, j), acc[rb][j]);
-        wait_all_mem();
-        __syncthreads();
-        if (tid == 0)
-            s_old = atomic_add_dev(&a.cnt[tile], 1u);
-        __syncthreads();
-        if (s_old != (uint32_t)(a.ksplit - 1))
-            return;
-        if (tid == 0)
-            atomic_store_dev(&a.cnt[tile], 0u);
-        // splits added in order; all fragments of one split are in flight at once
-        floatx4 sum[RB][JW];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int j = 0; j < JW; ++j)
-                sum[rb][j] = (floatx4){0.f, 0.f, 0.f, 0.f};
-        for (int z = 0; z < a.ksplit; ++z) {
-            if (z == kz) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        sum[rb][j] += acc[rb][j];
-            } else {
-                floatx4 t[RB][JW];
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        t[rb][j] = ld16_dev(a.partial + frag(z, rb, j));
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        sum[rb][j] += t[rb][j];
-            }
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int j = 0; j < JW; ++j)
-                acc[rb][j] = sum[rb][j];
-    }
-
-    // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r correction
-    if constexpr (BIAS) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float sx = a.rowsum[m0 + rb * 16 + 4 * (l >> 4) + v];
-#pragma unroll
-                for (int j = 0; j < JW; ++j)
-                    acc[rb][j][v] -= (128.0f + zf[j]) * sx;
-            }
-        }
-    }
-    if constexpr (ACT == ACT_F16 && !GROUPED) {
-        if (zfl & ZF_FRAC) {
-            // fractional zero points (a slower path): subtract (z - zi) times
-            // each token's sum of activations over K, computed here from X
-            // (TPR threads per token, each a contiguous share of K, added in
-            // a fixed order)
-            constexpr int TPR = GEMM_THREADS / BM;
-            float* rs = reinterpret_cast<float*>(smem);          // [TPR][BM], then [BM]
-            {
-                const int row = tid / TPR, part = tid - row * TPR;
-                const int len = a.K / TPR;                       // a multiple of 16
-                const uint16_t* xs = a.X + (size_t)min(m0 + row, a.M - 1) * a.K + (size_t)part * len;
-                float t = 0.0f;
-#pragma unroll 1
-                for (int k = 0; k < len; k += 8) {
-                    const u32x4 v = ld16(xs + k);
-                    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const half2_t h = h2_of(u[i]);
-                        t += (float)h.x;
-                        t += (float)h.y;
-                    }
-                }
-                rs[part * BM + row] = t;
-            }
-            __syncthreads();
-            if (tid < BM) {
-                float t = rs[tid];
-                for (int q = 1; q < TPR; ++q)
-                    t += rs[q * BM + tid];
-                rs[TPR * BM + tid] = t;
-            }
-            __syncthreads();
-            float zfr[JW];                              // z - floor(z) of this lane's columns
-#pragma unroll
-            for (int j = 0; j < JW; ++j) {
-                const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(*szsrc[j] >> 16));
-                zfr[j] = z - floorf(z);
-            }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float sx = rs[TPR * BM + rb * 16 + 4 * (l >> 4) + v];
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        acc[rb][j][v] -= zfr[j] * sx;
-                }
-            __syncthreads();                            // before the epilogue reuses the LDS
-        }
-    }
-    if constexpr (!GROUPED) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int j = 0; j < JW; ++j)
-                acc[rb][j] *= sf[j];
-    }
-    if (a.r > 0) {
-        // The rank dimension in chunks of RCH: B rows [c0, c0 + RCH) of the
-        // tile's 256 columns and the same ranks of T_g for the tile's BM
-        // tokens are loaded with every load of the chunk in flight, parked in
-        // LDS, and read back as MFMA operands (B through the transpose read;
-        // its rows are padded to 272 halves so that the read is free of bank
-        // conflicts).  The last main-loop barrier freed the LDS.
-        constexpr int RCH = BM == 64 ? 32 : 64;
-        constexpr int BP = PF_BN + 16;                  // halves per LDS row of B
-        constexpr int TP = RCH + 8;                     // halves per LDS row of T_g
-        constexpr int BCH = RCH * (PF_BN / 8) / GEMM_THREADS;             // 16-byte B chunks per thread
-        constexpr int TCH = (BM * (RCH / 8) + GEMM_THREADS - 1) / GEMM_THREADS;
-        static_assert(RCH * BP * 2 + BM * TP * 2 <= gemm_lds_bytes<BM>(), "EC staging fits the LDS");
-        uint16_t* bl = reinterpret_cast<uint16_t*>(smem);
-        uint16_t* tl = bl + RCH * BP;
-        const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
-        const int koff = 8 * (l >> 4);
-        for (int c0 = 0; c0 < a.r_pad; c0 += RCH) {
-            u32x4 bv[BCH], tv[TCH];
-#pragma unroll
-            for (int i = 0; i < BCH; ++i) {
-                const int ch = tid + GEMM_THREADS * i;
-                const int jr = c0 + (ch >> 5), n = n0 + 8 * (ch & 31);
-                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-                if (jr < a.r) {
-                    const uint16_t* src = a.B + (size_t)jr * a.N + n;
-                    if (bvec && n + 8 <= a.N) {
-                        v = ld16(src);
-                    } else {
-                        uint32_t hv[8];
-#pragma unroll
-                        for (int t = 0; t < 8; ++t)
-                            hv[t] = n + t < a.N ? (uint32_t)src[t] : 0u;
-                        v = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
-                                    hv[6] | (hv[7] << 16)};
-                    }
-                }
-                bv[i] = v;
-            }
-#pragma unroll
-            for (int i = 0; i < TCH; ++i) {
-                const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
-                const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
-                // ranks past r_pad (a last chunk wider than the rest) are not loaded and not used
-                tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
-                                              : (u32x4){0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int i = 0; i < BCH; ++i) {
-                const int ch = tid + GEMM_THREADS * i;
-                st16(bl + (ch >> 5) * BP + 8 * (ch & 31), bv[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < TCH; ++i) {
-                const int ch = tid + GEMM_THREADS * i;
-                if (ch < BM * (RCH / 8)) {
-                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
-                    st16(tl + rr * TP + 8 * cc, tv[i]);
-                }
-            }
-            __syncthreads();
-            const int ns = min(RCH, a.r_pad - c0) >> 5;
-            for (int rs = 0; rs < ns; ++rs) {
-                u32x4 bfr[JW];
-#pragma unroll
-                for (int j = 0; j < JW; ++j)
-                    bfr[j] = lds_bfrag(bl, BP, 16 * (JW * w + j), 32 * rs);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const u32x4 af = *reinterpret_cast<const u32x4*>(tl + (rb * 16 + (l & 15)) * TP + 32 * rs + koff);
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
-                }
-            }
-            __syncthreads();                            // before the next chunk or the output tile reuses the LDS
-        }
-    }
-
-    if (zfl & ZF_BAD) {
-        // zero points out of the supported range: NaN rather than wrong numbers
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int j = 0; j < JW; ++j)
-                acc[rb][j] = (floatx4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-    }
-    // ---- store: round to the activation format into an LDS tile, then
-    // write whole rows of the tile with 16-byte stores
-    uint16_t* yt = reinterpret_cast<uint16_t*>(smem);   // [BM][YT_PITCH]; the last step's barrier freed it
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int j = 0; j < JW; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                yt[(rb * 16 + 4 * (l >> 4) + v) * YT_PITCH + 16 * JW * w + 16 * j + (l & 15)] =
-                    f32_to_act<ACT>(acc[rb][j][v]);
-    __syncthreads();
-    const bool vec = (a.N & 7) == 0;
-    for (int e = tid; e < BM * (PF_BN / 8); e += GEMM_THREADS) {
-        const int row = e >> 5, c8 = (e & 31) * 8;
-        const int m = m0 + row, n = n0 + c8;
-        if (m >= a.M || n >= a.N)
-            continue;
-        const uint16_t* src = yt + row * YT_PITCH + c8;
-        uint16_t* dst = a.Y + (size_t)m * a.N + n;
-        if (vec) {
-            st16(dst, *reinterpret_cast<const u32x4*>(src));
-        } else {
-            for (int t = 0; t < 8 && n + t < a.N; ++t)
-                dst[t] = src[t];
-        }
-    }
+    gemm_tail<ACT, BM, GROUPED, 8, gemm_lds_bytes<BM>()>(a, acc, sf, zf, szsrc, tm, tn, kz, m0, n0, smem, s_old);
 }
 
 template <int ACT, int BM, bool GROUPED>
@@ -1095,7 +1135,6 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
     k.Y = (uint16_t*)a.Y;
     k.partial = (floatx4*)(a.ws + p.off_gemm_partial);
     k.cnt = (uint32_t*)(a.ws + p.off_gemm_cnt);
-    k.zflags = &reinterpret_cast<const BlobHeader*>(a.packed)->zflags;
     k.M = a.M; k.N = a.N; k.K = a.K; k.r = a.r; k.r_pad = p.r_pad; k.G = a.G;
     k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;
     k.mt = p.mt; k.nt = p.nt; k.ksplit = p.ksplit; k.Mpad = p.Mpad;

@@ -169,10 +169,14 @@ __global__ void pack_sz_kernel(const uint16_t* __restrict__ scale, const uint16_
         uint16_t z = zero[(size_t)n * NG + gi];
         float zf = (float)__builtin_bit_cast(_Float16, z);
         // any zero point is accepted; the kernels take its integer part
-        // exactly and correct for a fractional part, which needs |z| <= ZMAX
+        // exactly and correct for a fractional part, which needs |z| <= ZMAX.
+        // One outside that range (or not finite) is stored as NaN, which
+        // turns the outputs that use it into NaN.
         const uint32_t f = !(fabsf(zf) <= ZMAX) ? ZF_BAD : (zf != floorf(zf) ? ZF_FRAC : 0u);
         if (f)
             atomicOr(&hdr->zflags, f);
+        if (f & ZF_BAD)
+            z = 0x7E00u;
         v = (uint32_t)s | ((uint32_t)z << 16);
     }
     sz[idx] = v;

@@ -40,9 +40,10 @@ constexpr int PANEL_BYTES = 1024;
 constexpr size_t HEADER_BYTES = 256;
 constexpr uint32_t BLOB_MAGIC = 0x43453457u;  // "W4EC"
 
-// zero-point flags of a blob (set by the pack kernel)
+// zero-point flags of a blob, recorded by the pack kernel (the kernels
+// read the zero points themselves)
 constexpr uint32_t ZF_FRAC = 1u;   // some zero point is not an integer
-constexpr uint32_t ZF_BAD = 2u;    // some zero point is not finite or |z| > ZMAX: the layer's outputs are NaN
+constexpr uint32_t ZF_BAD = 2u;    // some zero point is not finite or |z| > ZMAX: stored as NaN
 constexpr float ZMAX = 1024.0f;    // the exact integer offsets hold for |z| <= ZMAX
 
 struct BlobHeader {
@@ -299,6 +300,26 @@ __device__ inline floatx4 ld16_dev(const floatx4* p)
     const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return (floatx4){__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
                      __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
+}
+
+// 16-byte device-coherent accesses through a buffer resource (base and size
+// wave-uniform, byte offset per lane): sc1 stores write through to memory and
+// sc1 loads read past this XCD's L2, like the relaxed agent-scope atomics
+// above, but as one contiguous 16-byte access per lane (two strided 8-byte
+// accesses write whole 32-byte sectors for 8 bytes each).  Offsets at or
+// past `bytes` read as zero and are not written.
+__device__ inline __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr int CPOL_SC1 = 16;
+__device__ inline void st16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off, floatx4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, CPOL_SC1);
+}
+__device__ inline floatx4 ld16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_SC1));
 }
 
 // Self-announcing hand-over words.  A value is stored as the bit complement
