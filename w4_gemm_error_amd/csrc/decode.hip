@@ -559,6 +559,12 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     // unwanted values zeroed afterwards -- so that the compiler can count the
     // loads in flight and wait for exactly the one it needs.)
     constexpr bool XLDS = XCH > 0;
+    // With the activations in LDS the weights enter the MFMAs with their
+    // exponent-trick offsets (one AND-OR per pair); the offsets and the zero
+    // point come off per group through the activations' sums.  (fp16 with
+    // groups keeps the exact offset subtraction: a group of one panel would
+    // pay the sums' transposition on every panel.)
+    constexpr bool BIAS = XLDS && !CBK && (ACT == ACT_BF16 || !GROUPED);
     u32x4 wring[DEPTH][CB];
     u32x4 xring[XLDS ? 1 : DEPTH][4];
     uint32_t szring[GROUPED ? DEPTH : 1][CB];
@@ -747,27 +753,78 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
         }
     }
 
-    // Zero points: the codes are offset by the integer part zi = floor(z)
-    // exactly (the exponent trick).  A fractional part zf = z - zi leaves
-    // -zf * s * (the group's activation sum) per output, which the epilogue
-    // subtracts when the blob records a fractional zero point (a slower
-    // path; with integer zero points nothing is added).
+    // Zero points.  Offset codes (BIAS): a group adds s (accg - (oL + z) xL -
+    // (oH + z) xH), xL and xH this wavefront's activation sums over the
+    // group's panels and the two kinds of k position -- exact in z, any fp16
+    // zero point.  Otherwise the codes are offset by the integer part
+    // zi = floor(z) exactly (the exponent trick), and a fractional part
+    // zf = z - zi leaves -zf * s * (the group's activation sum) per output,
+    // which the epilogue subtracts when some zero point is fractional (a
+    // slower path; with integer zero points nothing is added).
     floatx4 acc[CB], accg[CB];
     float s_cur[CB];
     DqF16 dqh[CB];
     float dqb[CB];
+    float cL[CB], cH[CB];   // BIAS: s (oL + z), s (oH + z)
+    // BIAS: this lane's activation sums over the group so far (token l & 15,
+    // the lane's k chunks), at the two kinds of k position (offset 1024 /
+    // 64 for fp16, both 128 for bf16)
+    float plo = 0.0f, phi = 0.0f;
+    // ... and their transposition through LDS at a group's end: [4 chunk
+    // groups][16 tokens][2] per wavefront
+    float* tsum = reinterpret_cast<float*>(smem + main_frac_offset(M, K, XLDS, CB, a.r_pad, a.r > 0,
+                                                                   a.r > 0 && a.S != nullptr)) + w * 128;
     bool fz = false;        // a zero point this lane has seen is fractional
     auto set_sz = [&](const uint32_t* v) {
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
             s_cur[j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] & 0xFFFF));
             const float z = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[j] >> 16));
-            const float zi = floorf(z);
-            fz |= z != zi;
-            if constexpr (ACT == ACT_F16)
-                dqh[j] = dq_f16_consts(zi);
-            else
-                dqb[j] = -(8388608.0f + zi);
+            if constexpr (BIAS) {
+                cL[j] = s_cur[j] * ((ACT == ACT_F16 ? 1024.0f : 128.0f) + z);
+                cH[j] = s_cur[j] * ((ACT == ACT_F16 ? 64.0f : 128.0f) + z);
+            } else {
+                const float zi = floorf(z);
+                fz |= z != zi;
+                if constexpr (ACT == ACT_F16)
+                    dqh[j] = dq_f16_consts(zi);
+                else
+                    dqb[j] = -(8388608.0f + zi);
+            }
+        }
+    };
+    // the end of a group: its partial sums, scaled, into acc.  With offset
+    // codes the activation sums go through LDS from the lanes that hold them
+    // (token l & 15) to those whose accumulator rows they are (tokens
+    // 4 (l >> 4) + v), the four chunk groups added in order; only this
+    // wavefront touches its area, and its LDS accesses complete in order.
+    auto flush = [&]() {
+        float sxl[4] = {0.f, 0.f, 0.f, 0.f}, sxh[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BIAS) {
+            tsum[((l >> 4) * 16 + (l & 15)) * 2] = plo;
+            tsum[((l >> 4) * 16 + (l & 15)) * 2 + 1] = phi;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const floatx4 t0 = *reinterpret_cast<const floatx4*>(tsum + (g * 16 + 4 * (l >> 4)) * 2);
+                const floatx4 t1 = *reinterpret_cast<const floatx4*>(tsum + (g * 16 + 4 * (l >> 4)) * 2 + 4);
+                sxl[0] += t0[0]; sxh[0] += t0[1];
+                sxl[1] += t0[2]; sxh[1] += t0[3];
+                sxl[2] += t1[0]; sxh[2] += t1[1];
+                sxl[3] += t1[2]; sxh[3] += t1[3];
+            }
+            plo = 0.0f;
+            phi = 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+            if constexpr (BIAS) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[j][v] += s_cur[j] * accg[j][v] - (cL[j] * sxl[v] + cH[j] * sxh[v]);
+            } else {
+                acc[j] += s_cur[j] * accg[j];
+            }
+            accg[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
         }
     };
 #pragma unroll
@@ -824,12 +881,18 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
             }
             if constexpr (GROUPED) {
                 if (valid && left_in_group == ppg && i > 0) {
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) {
-                        acc[j] += s_cur[j] * accg[j];
-                        accg[j] = (floatx4){0.f, 0.f, 0.f, 0.f};
-                    }
+                    flush();
                     set_sz(szv);
+                }
+            }
+            if constexpr (BIAS) {
+                // (zero for a panel past the wavefront's last and for absent tokens)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    plo = act_dot2_ones<ACT>(xf[s].x, plo);
+                    plo = act_dot2_ones<ACT>(xf[s].z, plo);
+                    phi = act_dot2_ones<ACT>(xf[s].y, phi);
+                    phi = act_dot2_ones<ACT>(xf[s].w, phi);
                 }
             }
 #pragma unroll
@@ -841,6 +904,8 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
                     u32x4 bq;
                     if constexpr (CBK)
                         bq = cb_lookup(ws[s], ptab + j * 256 * PANEL_N + (l & 15));
+                    else if constexpr (BIAS)
+                        bq = ACT == ACT_F16 ? dequant_f16_biased(ws[s]) : bf16_biased(ws[s]);
                     else if constexpr (ACT == ACT_F16)
                         bq = dequant_f16(ws[s], dqh[j]);
                     else
@@ -858,10 +923,7 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     for (; i0 + DEPTH < kcnt; i0 += DEPTH)
         chunk(i0, std::true_type{});
     chunk(i0, std::false_type{});
-
-#pragma unroll
-    for (int j = 0; j < CB; ++j)
-        acc[j] += s_cur[j] * accg[j];
+    flush();
 
     // sparse outlier residual: this thread's share of column rc, for every
     // token, sum x[m][k] * val (X from LDS while it is still staged there)
@@ -919,7 +981,7 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     // The barrier also tells whether some lane of the workgroup saw a
     // fractional zero point.
     bool anyfrac = false;
-    if constexpr (CBK)
+    if constexpr (CBK || BIAS)
         __syncthreads();
     else
         anyfrac = __syncthreads_or(fz) != 0;
@@ -976,7 +1038,7 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
             }
             corr[e] = t;
         }
-    } else if constexpr (!CBK) {
+    } else if constexpr (!CBK && !BIAS) {
         for (int e = tid; e < M * CB * PANEL_N; e += DEC_THREADS)
             corr[e] = 0.0f;
     }
@@ -1089,7 +1151,7 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
                 if (rs < nsteps)
                     tot = mfma16x16x32<ACT>(af[rs], bfr[rs], tot);
         }
-        if constexpr (!CBK) {
+        if constexpr (!CBK && !BIAS) {
             // fractional zero points (zero otherwise: read unconditionally,
             // so that the compiler keeps one copy of this loop)
 #pragma unroll
@@ -1155,8 +1217,10 @@ void decode_kernel(DecodeKArgs a)
 
 static size_t main_lds_bytes(const DecodePlan& p, int M, int K, int r, bool gather)
 {
+    // past the other regions: the fractional-zero-point sums and correction,
+    // or (offset codes) the transposition areas of the four wavefronts
     return main_frac_offset(M, K, p.xlds, p.CB, p.r_pad, r > 0, r > 0 && gather) +
-           (size_t)M * (K / PANEL_K + p.CB * PANEL_N) * sizeof(float);
+           std::max((size_t)M * (K / PANEL_K + p.CB * PANEL_N) * sizeof(float), (size_t)4 * 128 * sizeof(float));
 }
 
 // LDS of the EC role: the staged slice and gate vector, then the final reduction

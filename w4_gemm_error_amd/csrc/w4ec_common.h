@@ -194,6 +194,42 @@ __device__ inline u32x4 dequant_f16_scaled(uint32_t w, const DqF16& c, half2_t s
     return r;
 }
 
+// The codes with their exponent-trick offsets left in: 1024 + c for the
+// codes at bits 0-3 and 8-11 of each half of the dword (MFMA k positions 0,
+// 1, 4, 5 of the eight), 64 + c for those at bits 4-7 and 12-15 (positions
+// 2, 3, 6, 7).  Exact, one AND-OR per pair; the caller takes the offsets and
+// the zero point off afterwards, as (offset + z) times the activations'
+// sums over those positions.
+// A constant the compiler keeps in a register (an empty asm hides its
+// value): with both operands in registers, (a & m) | b is one v_and_or_b32,
+// where two literals would take an AND and an OR.
+__device__ inline uint32_t reg_const(uint32_t c)
+{
+    asm("" : "+v"(c));
+    return c;
+}
+
+__device__ inline u32x4 dequant_f16_biased(uint32_t w)
+{
+    const uint32_t w8 = w >> 8;
+    const uint32_t m0 = reg_const(0x000F000Fu), m1 = reg_const(0x00F000F0u);
+    const uint32_t b0 = reg_const(0x64006400u), b1 = reg_const(0x54005400u);
+    return (u32x4){(w & m0) | b0, (w & m1) | b1, (w8 & m0) | b0, (w8 & m1) | b1};
+}
+
+// c + a.lo + a.hi in fp32 (a pair of activations; products with one are exact)
+template <int ACT>
+__device__ inline float act_dot2_ones(uint32_t a, float c)
+{
+    if constexpr (ACT == ACT_F16) {
+        return __builtin_amdgcn_fdot2(h2_of(a), (half2_t){(_Float16)1.0f, (_Float16)1.0f}, c, false);
+    } else {
+        typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, 0x3F803F80u),
+                                               c, false);
+    }
+}
+
 // bf16: build 2^23 + c as a float (0x4B000000 | c), subtract 2^23 + z
 // exactly, and keep the upper half of the float -- exact for the small
 // integer c - z (and for (c - z) * s the bf16 conversion rounds to nearest
@@ -228,11 +264,12 @@ __device__ inline u32x4 dequant_bf16(uint32_t w, float off)
 __device__ inline u32x4 bf16_biased(uint32_t w)
 {
     const uint32_t w8 = w >> 8;
+    const uint32_t m = reg_const(0x000F000Fu), b = reg_const(0x43004300u);
     u32x4 r;
-    r.x = (w & 0x000F000Fu) | 0x43004300u;
-    r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-    r.z = (w8 & 0x000F000Fu) | 0x43004300u;
-    r.w = ((w8 >> 4) & 0x000F000Fu) | 0x43004300u;
+    r.x = (w & m) | b;
+    r.y = ((w >> 4) & m) | b;
+    r.z = (w8 & m) | b;
+    r.w = ((w8 >> 4) & m) | b;
     return r;
 }
 
