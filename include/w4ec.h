@@ -172,6 +172,29 @@ int w4ec_linear_decode(const void* X, const void* packed, const void* A, const v
                        int M, int N, int K, int r, int group_size, int act_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* w4ec_linear_decode without a workspace argument and without allocating:
+ * for callers that cannot call hipMalloc (code under HIP graph capture,
+ * serving loops, harnesses that forbid allocation).  The decode hand-over
+ * state lives in a static device array of W4EC_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on each GPU it runs on until the process ends.
+ * The first call on a device (with that device current) looks up the
+ * array's address and clears it with a kernel on `stream`; later calls
+ * reuse it, each returning the state to zero as with a workspace.
+ * Arguments, results and errors as for w4ec_linear_decode, plus
+ * W4EC_ERR_UNSUPPORTED when the shape's state would exceed the array
+ * (512 KiB + 4 * ceil(K / KS) * M * (r + 1) bytes, KS <= 256 the EC slice
+ * width: with K = 4096 any M <= 16 and r <= 256 fits).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must not be issued.  A bounded wait
+ * that gives up is recorded in the array as in a workspace, and every later
+ * call of this entry point on that GPU then writes NaN into all of Y (there
+ * is no reset for the array).  r == 0 touches no state at all. */
+#define W4EC_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int w4ec_linear_decode_noalloc(const void* X, const void* packed, const void* A, const void* B,
+                               const void* w_g, float b_g, void* Y,
+                               int M, int N, int K, int r, int group_size, int act_dtype,
+                               void* stream);
+
 /* The layer, prefill phase: any M >= 1 (tiled MFMA GEMM, three launches:
  * the gate / X A prepass over K slices, the reduction of its slices with the
  * gate, then the GEMM with the gated correction in its epilogue; for bf16

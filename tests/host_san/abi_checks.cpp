@@ -25,6 +25,8 @@ int g_fail = 0;
 long g_calls = 0;
 long g_launches = 0;
 size_t g_ws_bytes = 0;     // workspace bytes the current call was given
+bool g_noalloc = false;    // the current call uses the static state array
+long g_scratch_lookups = 0;
 
 #define CHECK(cond, ...)                                                  \
     do {                                                                  \
@@ -75,11 +77,13 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t)
     CHECK((p.n_main - 1) * p.CB * PANEL_N < a.N, "decode: a workgroup with no column");
     CHECK(!p.xlds || (a.M <= 4 && (size_t)a.M * a.K * 2 <= DEC_XLDS_MAX_BYTES), "decode xlds M=%d K=%d", a.M, a.K);
     if (a.r > 0) {
-        CHECK(a.ws != nullptr && g_ws_bytes >= STATE, "decode r=%d without a state region", a.r);
+        CHECK(a.ws != nullptr && g_ws_bytes >= (g_noalloc ? W4EC_NOALLOC_SCRATCH_BYTES : STATE),
+              "decode r=%d without a state region", a.r);
         if (a.S == nullptr) {
             CHECK(p.P >= 1 && p.KS % 64 == 0 && (long)p.P * p.KS >= a.K && (long)(p.P - 1) * p.KS < a.K,
                   "decode EC slices P=%d KS=%d K=%d", p.P, p.KS, a.K);
-            CHECK(p.off_partial + (size_t)p.P * a.M * p.RC * 4 <= STATE, "decode partials outside the state region");
+            CHECK(p.off_partial + (size_t)p.P * a.M * p.RC * 4 <= (g_noalloc ? W4EC_NOALLOC_SCRATCH_BYTES : STATE),
+                  "decode partials outside the state region");
         }
         CHECK(p.r_pad >= a.r && p.r_pad % 32 == 0 && (size_t)a.M * p.r_pad * 2 <= DEC_REP_DATA_STRIDE,
               "decode T_g slot r_pad=%d M=%d", p.r_pad, a.M);
@@ -147,6 +151,14 @@ hipError_t launch_zero_fill(void*, size_t bytes, hipStream_t)
 {
     ++g_launches;
     CHECK(bytes % 16 == 0 && bytes <= g_ws_bytes && bytes <= STATE, "zero fill %zu", bytes);
+    return hipSuccess;
+}
+
+hipError_t noalloc_scratch(void** out, hipStream_t)
+{
+    ++g_scratch_lookups;
+    CHECK(g_noalloc, "state array looked up outside a noalloc call");
+    *out = reinterpret_cast<void*>(uintptr_t(0x78000000));
     return hipSuccess;
 }
 
@@ -244,6 +256,27 @@ int main()
                             }
                         }
                     }
+    // ---- the no-allocation decode: same argument checks, the state array
+    // only for r > 0, and shapes whose state would not fit it refused
+    g_noalloc = true;
+    g_ws_bytes = W4EC_NOALLOC_SCRATCH_BYTES;
+    {
+        const long l1 = g_launches, s1 = g_scratch_lookups;
+        ++g_calls;
+        expect(w4ec_linear_decode_noalloc(fake(X), fake(PK), fake(A), fake(B), fake(WG), 0.f, fake(Y), 17, 512, 512,
+                                          8, 512, 0, nullptr), W4EC_ERR_UNSUPPORTED, "noalloc M = 17");
+        expect(w4ec_linear_decode_noalloc(fake(X + 2), fake(PK), fake(A), fake(B), fake(WG), 0.f, fake(Y), 4, 512, 512,
+                                          8, 512, 0, nullptr), W4EC_ERR_INVALID_ARG, "noalloc misaligned X");
+        expect(w4ec_linear_decode_noalloc(fake(X), fake(PK), fake(A), fake(B), fake(WG), 0.f, fake(Y), 16, 256, 16384,
+                                          256, 16384, 0, nullptr), W4EC_ERR_UNSUPPORTED, "noalloc state too large");
+        CHECK(g_launches == l1 && g_scratch_lookups == s1, "a refused noalloc call launched or looked up the array");
+        expect(w4ec_linear_decode_noalloc(fake(X), fake(PK), fake(A), fake(B), fake(WG), 0.f, fake(Y), 16, 14336, 4096,
+                                          256, 4096, 1, nullptr), W4EC_OK, "noalloc 16 tokens rank 256");
+        expect(w4ec_linear_decode_noalloc(fake(X), fake(PK), nullptr, nullptr, nullptr, 0.f, fake(Y), 1, 4096, 4096,
+                                          0, 128, 0, nullptr), W4EC_OK, "noalloc without rank");
+        CHECK(g_scratch_lookups == s1 + 1, "the state array is looked up only with a rank");
+    }
+    g_noalloc = false;
     g_ws_bytes = STATE;
     expect(w4ec_workspace_reset(fake(WS), STATE, nullptr), W4EC_OK, "reset");
     if (g_fail) {

@@ -24,6 +24,7 @@ __all__ = [
     "w4ec_status_str", "w4ec_packed_bytes", "w4ec_workspace_bytes",
     "w4ec_quantize_rtn", "w4ec_pack", "w4ec_unpack",
     "w4ec_linear_decode", "w4ec_linear_prefill", "w4ec_linear",
+    "w4ec_linear_decode_noalloc", "W4EC_NOALLOC_SCRATCH_BYTES",
     "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
     "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
     "w4ec_linear_decode_serq", "w4ec_linear_prefill_serq",
@@ -46,6 +47,7 @@ W4EC_FP16 = 0
 W4EC_BF16 = 1
 DECODE_MAX_M = 16
 W4EC_WS_STATE_BYTES = 16 << 20   # leading workspace bytes every call returns to zero
+W4EC_NOALLOC_SCRATCH_BYTES = 4 << 20   # the static device array of w4ec_linear_decode_noalloc
 
 _lock = threading.Lock()
 _lib = None
@@ -91,6 +93,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, P, Z, P]
             fn.restype = I
+        L.w4ec_linear_decode_noalloc.argtypes = [P, P, P, P, P, F, P, I, I, I, I, I, I, P]
+        L.w4ec_linear_decode_noalloc.restype = I
         L.w4ec_prefill_ec_workspace_bytes.argtypes = [I, I, I]
         L.w4ec_prefill_ec_workspace_bytes.restype = Z
         L.w4ec_prefill_ec_gate.argtypes = [P, P, P, F, I, I, I, I, P, Z, P]
@@ -421,6 +425,27 @@ def w4ec_prefill_ec_apply(Y, B, *, K, workspace, stream=None):
 def w4ec_linear_decode(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):
     """Y = X Wd^T + g (X A) B for 1 <= M <= 16 tokens (one kernel launch)."""
     return _layer_call("w4ec_linear_decode", X, packed, A, B, w_g, b_g, N, group_size, workspace, Y, stream)
+
+
+def w4ec_linear_decode_noalloc(X, packed, A, B, w_g, b_g, *, N, group_size, Y=None, stream=None):
+    """w4ec_linear_decode with no workspace and no allocation in the library
+    (its state in a static device array; calls on one GPU must not overlap)."""
+    torch = _torch()
+    acts = (torch.float16, torch.bfloat16)
+    _need_cuda(X, "X", acts)
+    act = X.dtype
+    M, K = X.shape
+    r = 0 if A is None else int(A.shape[1])
+    for t, nm in ((A, "A"), (B, "B"), (w_g, "w_g")):
+        _need_cuda(t, nm, act)
+    _need_cuda(packed, "packed", torch.uint8)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=act, device=X.device)
+    _need_cuda(Y, "Y", act)
+    st = lib().w4ec_linear_decode_noalloc(_ptr(X), _ptr(packed), _ptr(A), _ptr(B), _ptr(w_g), float(b_g), _ptr(Y),
+                                          M, N, K, r, int(group_size), _act_code(act), _stream_handle(stream))
+    _check(st, "w4ec_linear_decode_noalloc")
+    return Y
 
 
 def w4ec_linear_prefill(X, packed, A, B, w_g, b_g, *, N, group_size, workspace=None, Y=None, stream=None):

@@ -325,7 +325,7 @@ LayerArgs layer_args(const void* X, const void* packed, const void* A, const voi
 int decode_entry(const void* X, const void* packed, const void* A, const void* B,
                  const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
                  int group_size, int act_dtype, void* workspace, size_t workspace_bytes,
-                 void* stream, const VGate* vg, const int32_t* S = nullptr)
+                 void* stream, const VGate* vg, const int32_t* S = nullptr, bool noalloc = false)
 {
     if (M > DECODE_MAX_M)
         return W4EC_ERR_UNSUPPORTED;
@@ -335,10 +335,13 @@ int decode_entry(const void* X, const void* packed, const void* A, const void* B
         p = make_decode_plan(M, N, K, r);
         if (!p.ok)
             return W4EC_ERR_UNSUPPORTED;
-        need = r > 0 ? p.bytes : 0;
+        // a caller's workspace must hold the whole state region; the static
+        // area (noalloc) only the bytes this shape touches: the control
+        // words and replica slots, then the EC partial sums
+        need = r == 0 ? 0 : noalloc ? OFF_DEC_PARTIAL + (size_t)p.P * M * p.RC * sizeof(uint32_t) : p.bytes;
     }
     int rc = check_layer_args(X, packed, A, B, vg ? nullptr : w_g, Y, M, N, K, r, group_size,
-                              act_dtype, workspace, workspace_bytes, need);
+                              act_dtype, workspace, workspace_bytes, noalloc ? 0 : need);
     if (rc != W4EC_OK)
         return rc;
     rc = check_vgate(vg, r);
@@ -346,6 +349,15 @@ int decode_entry(const void* X, const void* packed, const void* A, const void* B
         return rc;
     if (!vg && w_g && !((uintptr_t)w_g % 2 == 0))
         return W4EC_ERR_INVALID_ARG;
+    if (noalloc && need > 0) {
+        if (need > W4EC_NOALLOC_SCRATCH_BYTES)
+            return W4EC_ERR_UNSUPPORTED;
+        const hipError_t e = noalloc_scratch(&workspace, (hipStream_t)stream);
+        if (e == hipErrorInvalidDevice)
+            return W4EC_ERR_UNSUPPORTED;
+        if (e != hipSuccess)
+            return W4EC_ERR_HIP;
+    }
     LayerArgs a = layer_args(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
                              need > 0 ? workspace : nullptr, vg);
     if (S && r > 0) {
@@ -402,6 +414,14 @@ int w4ec_linear_decode(const void* X, const void* packed, const void* A, const v
 {
     return decode_entry(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype,
                         workspace, workspace_bytes, stream, nullptr);
+}
+
+int w4ec_linear_decode_noalloc(const void* X, const void* packed, const void* A, const void* B,
+                               const void* w_g, float b_g, void* Y, int M, int N, int K, int r,
+                               int group_size, int act_dtype, void* stream)
+{
+    return decode_entry(X, packed, A, B, w_g, b_g, Y, M, N, K, r, group_size, act_dtype, nullptr, 0,
+                        stream, nullptr, nullptr, true);
 }
 
 int w4ec_linear_prefill(const void* X, const void* packed, const void* A, const void* B,

@@ -33,9 +33,11 @@
 // are bounded.  Hand-over data moves with device-coherent accesses (see
 // w4ec_common.h), so no cache-wide write-back or invalidate is needed.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "ec_tile.h"
+#include "w4ec.h"
 #include "w4ec_common.h"
 #include "w4ec_launch.h"
 
@@ -1357,6 +1359,50 @@ hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st
     if (a.act == ACT_F16)
         return launch_decode_act<ACT_F16>(k, p, st);
     return launch_decode_act<ACT_BF16>(k, p, st);
+}
+
+
+// ---------------------------------------------------------------- no-allocation state
+//
+// The decode hand-over state of w4ec_linear_decode_noalloc: a static device
+// array, one copy per GPU, held until the process ends.  On the host the
+// array's name is a stand-in, never a device address, so it is not passed
+// to any kernel: the first call on a device, with that device current, takes
+// the address with hipGetSymbolAddress, clears the array with a fill kernel
+// on the caller's stream (capturable: no memset node), and keeps the address
+// for every later call on that device.  Calls that overlap in time on one
+// device share the array and race.
+static __device__ __align__(256) uint8_t scratch[W4EC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+}  // namespace
+
+hipError_t noalloc_scratch(void** out, hipStream_t st)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        if (!ptr)
+            return hipErrorInvalidSymbol;
+        e = launch_zero_fill(ptr, W4EC_NOALLOC_SCRATCH_BYTES, st);
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace w4ec

@@ -70,5 +70,10 @@ hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hip
 // bytes (a multiple of 16, 16-byte aligned) set to zero by a kernel (no
 // hipMemsetAsync node when a caller captures the stream into a graph)
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
+// The static state array of w4ec_linear_decode_noalloc on the current
+// device (W4EC_NOALLOC_SCRATCH_BYTES bytes): its device address, looked up
+// and cleared (a fill kernel on `st`) by the first call on each device.
+// hipErrorInvalidDevice beyond the devices it keeps addresses for.
+hipError_t noalloc_scratch(void** out, hipStream_t st);
 
 }  // namespace w4ec
