@@ -78,6 +78,9 @@ SMALL = [
     ("prefill", "bf16", 200, 512, 768, 16, 128),
     ("prefill", "fp16", 2, 512, 512, 8, 512),
     ("prefill", "fp16", 64, 1024, 2048, 130, 2048),
+    # many tiles, ragged in M and N
+    ("prefill", "fp16", 1000, 8000, 256, 16, 256),
+    ("prefill", "bf16", 1030, 8008, 384, 24, 384),
 ]
 
 
