@@ -448,15 +448,21 @@ struct GemmKArgs {
     int M, N, K, r, r_pad, G, NB, KB, Npad, mt, nt, ksplit, Mpad;
 };
 
-__device__ inline void tile_of(int bid, int mt, int nt, int& tm, int& tn)
+// Work item of a workgroup: its tile (tm, tn) and K split kz.  Workgroups
+// whose linear ids are congruent mod 8 run on one XCD; each XCD gets a
+// contiguous run of the work items in split-major order, so that with a K
+// split it holds one split's K range of many tiles (its L2 then fetches
+// that range of X and of the weights once, instead of every range of the
+// tiles it holds); the tiles of a split run in a grouped raster (GM M tiles
+// by all N tiles), so that neighbouring items share activations and weights.
+__device__ inline void work_of(int mt, int nt, int ksplit, int& tm, int& tn, int& kz)
 {
     const int T = mt * nt;
-    int t = bid;
-    if ((T & 7) == 0) {
-        // block ids congruent mod 8 land on one XCD: give each XCD a
-        // contiguous run of the grouped raster below
-        t = (bid & 7) * (T >> 3) + (bid >> 3);
-    }
+    const int W = T * ksplit;
+    const int bid = blockIdx.x + blockIdx.y * gridDim.x;
+    const int wi = (W & 7) == 0 ? (bid & 7) * (W >> 3) + (bid >> 3) : bid;
+    kz = wi / T;
+    const int t = wi - kz * T;
     const int GM = 4;  // M tiles per raster group
     const int group = t / (GM * nt);
     const int first = group * GM;
@@ -777,9 +783,8 @@ void prefill_gemm_kernel(GemmKArgs a)
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int tm, tn;
-    tile_of(blockIdx.x, a.mt, a.nt, tm, tn);
-    const int kz = blockIdx.y;
+    int tm, tn, kz;
+    work_of(a.mt, a.nt, a.ksplit, tm, tn, kz);
     const int m0 = tm * BM;
     const int n0 = tn * PF_BN;
     const int cbw = n0 / PANEL_N + JW * w;  // first column block of this wavefront
