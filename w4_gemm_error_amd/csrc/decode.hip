@@ -561,12 +561,12 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     // unwanted values zeroed afterwards -- so that the compiler can count the
     // loads in flight and wait for exactly the one it needs.)
     constexpr bool XLDS = XCH > 0;
-    // With the activations in LDS the weights enter the MFMAs with their
-    // exponent-trick offsets (one AND-OR per pair); the offsets and the zero
-    // point come off per group through the activations' sums.  (fp16 with
-    // groups keeps the exact offset subtraction: a group of one panel would
-    // pay the sums' transposition on every panel.)
-    constexpr bool BIAS = XLDS && !CBK && (ACT == ACT_BF16 || !GROUPED);
+    // The weights enter the MFMAs with their exponent-trick offsets (one
+    // AND-OR per pair); the offsets and the zero point come off per group
+    // through the activations' sums.  (fp16 with groups keeps the exact
+    // offset subtraction: a group of one panel would pay the sums'
+    // transposition on every panel.)
+    constexpr bool BIAS = !CBK && (ACT == ACT_BF16 || !GROUPED);
     u32x4 wring[DEPTH][CB];
     u32x4 xring[XLDS ? 1 : DEPTH][4];
     uint32_t szring[GROUPED ? DEPTH : 1][CB];
