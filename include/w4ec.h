@@ -121,21 +121,24 @@ int w4ec_unpack(const void* packed, int N, int K, int group_size,
  * Failures inside a call.  The decode kernel's workgroups hand partial
  * results to each other and wait for them with bounded waits (a wait gives
  * up after w4ec_wait_limit() polls, about a second by default), so a broken
- * hand-over can never hang the GPU.  A wait that gives up records it in the
- * workspace and turns the outputs that depend on it into NaN; the call
- * itself has already returned W4EC_OK.  From then on the decode hand-over
- * state in the workspace is not to be trusted: every later decode call that
- * uses it writes NaN into all of Y, until w4ec_workspace_reset (the prefill
- * calls wait for nothing and stay correct).  A salient-channel index outside [0, K)
- * (w4ec_linear_*_serq) is also recorded, without the NaN outputs.
- * w4ec_workspace_status reports both. */
+ * hand-over can never hang the GPU.  So do the prefill GEMM's workgroups
+ * when they compute the gated rank-r activations themselves (at most 64
+ * tokens, when all of them fit on the device at once).  A wait that gives
+ * up records it in the workspace and turns the outputs that depend on it
+ * into NaN; the call itself has already returned W4EC_OK.  From then on
+ * that phase's hand-over state in the workspace is not to be trusted:
+ * every later call of that phase that waits on it writes NaN into the
+ * outputs that depend on it, until w4ec_workspace_reset; the other phase
+ * stays correct.  A
+ * salient-channel index outside [0, K) (w4ec_linear_*_serq) is also
+ * recorded, without the NaN outputs.  w4ec_workspace_status reports both. */
 #define W4EC_WS_STATE_BYTES ((size_t)16 << 20)
 size_t w4ec_workspace_bytes(int M, int N, int K, int r, int group_size);
 
 /* What the calls so far on this workspace recorded: W4EC_OK,
  * W4EC_ERR_TIMED_OUT (a bounded wait gave up: the results of that call
- * where they depend on it, and of every later decode call on this
- * workspace, are NaN) or
+ * where they depend on it, and of every later call of that phase that waits
+ * on this workspace, are NaN) or
  * W4EC_ERR_BAD_INDEX (a salient-channel index was clamped).  Synchronizes
  * `stream` and reads 16 bytes of the workspace.  W4EC_ERR_WORKSPACE for a
  * missing or misaligned (256 B) workspace. */

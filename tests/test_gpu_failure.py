@@ -8,8 +8,12 @@ every kernel still exits normally.  Then:
   * w4ec_workspace_status reports W4EC_ERR_TIMED_OUT;
   * later decode calls on that workspace, with the normal limit, write NaN
     into all of Y: its hand-over state is no longer trusted (the prefill
-    kernels, which hand nothing over through waits, stay correct);
+    kernels keep their own hand-over state and stay correct);
   * after w4ec_workspace_reset the same calls match the oracle again.
+The same holds, phase for phase, for a prefill call of at most 64 tokens,
+whose GEMM workgroups compute the gated rank-r activations themselves and
+wait for each other's pieces (a decode call on the workspace stays correct
+meanwhile).
 A salient-channel index outside [0, K) is reported as W4EC_ERR_BAD_INDEX.
 """
 import numpy as np
@@ -61,8 +65,8 @@ def test_forced_timeout_is_visible_sticky_and_reset():
     # sticky: the normal limit, same workspace -> decode writes NaN everywhere
     Y = _call(d, packed, "decode", ws)
     assert bool(t.isnan(Y.float()).all())
-    # the prefill kernels hand nothing over through waits: their part of the
-    # state is untouched, and they stay correct on that workspace
+    # the prefill kernels keep their own hand-over state: untouched, and they
+    # stay correct on that workspace
     d40 = synth.make_layer("tiny", 40, seed=21, N=784, K=2048, r=64, group_size=2048)
     Y = _call(d40, packed, "prefill", ws)
     assert_close(host_bits(Y), oracle_layer(d40, oracle.rtn_quantize(d40["W"], 2048)), "fp16", "prefill")
@@ -72,6 +76,41 @@ def test_forced_timeout_is_visible_sticky_and_reset():
     assert w4.w4ec_workspace_status(ws) == w4.W4EC_OK
     Y = _call(d, packed, "decode", ws)
     assert_close(host_bits(Y), ref, "fp16", "after reset")
+    assert w4.w4ec_workspace_status(ws) == w4.W4EC_OK
+    assert int(t.count_nonzero(ws[: w4.W4EC_WS_STATE_BYTES]).item()) == 0
+
+
+def test_forced_prefill_fused_ec_timeout_is_visible_sticky_and_reset():
+    # M=40, N=784, K=2048: one row of 64-token tiles (4 column tiles, K split
+    # in 4): the fused EC
+    _print("forced timeout: prefill M=40 N=784 K=2048 r=64 (fused EC)")
+    t = torch()
+    d = synth.make_layer("tiny", 40, seed=23, N=784, K=2048, r=64, group_size=2048)
+    _, _, _, packed = gpu_quantize(d)
+    ref = oracle_layer(d, oracle.rtn_quantize(d["W"], d["group_size"]))
+    need = max(w4.w4ec_workspace_bytes(4, d["N"], d["K"], d["r"], d["group_size"]),
+               w4.w4ec_workspace_bytes(40, d["N"], d["K"], d["r"], d["group_size"]))
+    ws = t.zeros(need, dtype=t.uint8, device="cuda")
+    old = w4.w4ec_wait_limit()
+    try:
+        w4.w4ec_set_wait_limit(0)
+        Y = _call(d, packed, "prefill", ws)            # returns normally
+    finally:
+        w4.w4ec_set_wait_limit(old)
+    assert bool(t.isnan(Y.float()).all()), "outputs of a wait that gave up must be NaN"
+    assert w4.w4ec_workspace_status(ws) == w4.W4EC_ERR_TIMED_OUT
+    # sticky for the prefill hand-over
+    Y = _call(d, packed, "prefill", ws)
+    assert bool(t.isnan(Y.float()).all())
+    # the decode hand-over state is separate: decode stays correct
+    d4 = synth.make_layer("tiny", 4, seed=23, N=784, K=2048, r=64, group_size=2048)
+    Y = _call(d4, packed, "decode", ws)
+    assert_close(host_bits(Y), oracle_layer(d4, oracle.rtn_quantize(d4["W"], 2048)), "fp16", "decode")
+    # reset: correct again, state back at zero after the call
+    w4.w4ec_workspace_reset(ws)
+    assert w4.w4ec_workspace_status(ws) == w4.W4EC_OK
+    Y = _call(d, packed, "prefill", ws)
+    assert_close(host_bits(Y), ref, "fp16", "prefill after reset")
     assert w4.w4ec_workspace_status(ws) == w4.W4EC_OK
     assert int(t.count_nonzero(ws[: w4.W4EC_WS_STATE_BYTES]).item()) == 0
 

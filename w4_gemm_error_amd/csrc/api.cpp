@@ -52,9 +52,11 @@ constexpr size_t CTRL_BYTES = W4EC_WS_STATE_BYTES;
 
 constexpr size_t OFF_DEC_FLAGS = 0;           // 256 B
 constexpr size_t OFF_GEMM_CNT = 256 + 1024;   // split-K tile counters, <= 256 of them
+constexpr size_t OFF_EC_CNT = 4 << 10;        // fused-EC counters, 4 per row of tiles, <= 256 rows
 constexpr size_t OFF_DEC_REP = 64 << 10;      // DEC_NREP decode slots of DEC_REP_CTRL_STRIDE bytes
 constexpr size_t OFF_DEC_REP_DATA = 256 << 10;  // DEC_NREP slots of DEC_REP_DATA_STRIDE bytes
 constexpr size_t OFF_DEC_PARTIAL = 512 << 10;   // decode EC partial sums, up to CTRL_BYTES
+static_assert(OFF_GEMM_CNT + 256 * 4 <= OFF_EC_CNT && OFF_EC_CNT + 4 * 256 * 4 <= OFF_DEC_REP, "control region");
 static_assert(OFF_DEC_REP + DEC_NREP * DEC_REP_CTRL_STRIDE <= OFF_DEC_REP_DATA, "control region");
 static_assert(OFF_DEC_REP_DATA + DEC_NREP * DEC_REP_DATA_STRIDE <= OFF_DEC_PARTIAL, "control region");
 
@@ -137,11 +139,34 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
     // tile counters exist only for split work, which is chosen only while the
     // workgroup count is below TARGET_WGS: at most 256 of them
     p.off_gemm_cnt = OFF_GEMM_CNT;
+    p.off_ec_cnt = OFF_EC_CNT;
     p.off_flags = OFF_DEC_FLAGS;
+    // Fused EC for a single row of 64-token tiles (M <= 64), when every
+    // workgroup is resident at once: the prepass would have one workgroup
+    // per K slice only, so the GEMM's workgroups do it instead.  Each of the
+    // first ec_q workgroups computes [T | l] for the row's tokens over about
+    // K / ec_q of K, a range whose rows of [A | w_g] fit the GEMM's LDS at
+    // once (at most ec_kc of them).  (With more rows of tiles the prepass
+    // kernels measured faster: the pieces' reduction, a chain of trips to
+    // memory after the main loop, then costs more than the launches.)
+    p.ec_q = 0;
+    {
+        p.ec_kc = 512;
+        while (p.ec_kc > 64 && prepass_lds_bytes(r, p.ec_kc) > (size_t)GEMM_EC_LDS)
+            p.ec_kc -= 64;
+        const long long W = (long long)p.mt * p.nt * p.ksplit;
+        const int K64 = K / 64;
+        const int q = std::min(p.nt * p.ksplit, K64);
+        const int piece = 64 * ((K64 + q - 1) / q);
+        if (M <= 64 && p.BM == 64 && W <= TARGET_WGS && piece <= p.ec_kc)
+            p.ec_q = q;
+    }
 
     size_t off = CTRL_BYTES;
-    p.off_pre_partial = off;
-    off = align_up(off + (size_t)p.pre_mt * p.pre_ks * 4 * ((r + 15) / 16 + 1) * 64 * 16, 256);
+    p.off_pre_partial = off;   // the prepass's partial sums, or the fused EC's pieces
+    off = align_up(off + std::max((size_t)p.pre_mt * p.pre_ks * 4, (size_t)p.mt * p.ec_q * (p.BM / 16)) *
+                             ((r + 15) / 16 + 1) * 64 * 16,
+                   256);
     p.off_tg = off;
     if (r > 0)
         off = align_up(off + (size_t)p.Mpad * p.r_pad * 2, 256);
@@ -577,7 +602,7 @@ int w4ec_workspace_status(const void* workspace, size_t workspace_bytes, void* s
         e = hipStreamSynchronize(st);
     if (e != hipSuccess)
         return W4EC_ERR_HIP;
-    if (f[2])
+    if (f[1] || f[2])
         return W4EC_ERR_TIMED_OUT;
     if (f[3])
         return W4EC_ERR_BAD_INDEX;

@@ -29,6 +29,21 @@ typedef __attribute__((address_space(3))) short4_t lds_short4;
 
 // (slice geometry: ec_pitch, ec_a_blocks, ec_blocks, ec_slice_bytes in w4ec_common.h)
 
+// Bank swizzle of a staged slice.  A fragment read takes, per group of 16
+// lanes, 32 bytes (16 columns) from each of four consecutive rows.  When a
+// row is a multiple of 128 bytes (r a multiple of 64) those four 32-byte
+// pieces would fall on the same eight of the 32 banks; so row k stores its
+// 32-byte column pairs in the order p ^ ec_swz(k): then the four rows of a
+// read land on four different groups of eight banks (rows of 64 + 128 j
+// bytes take (k >> 1) & 1; other pitches are left as they are).  Applies
+// to pitches (halves) that are multiples of 32.
+__host__ __device__ inline int ec_swz(int k, int pitch)
+{
+    if (pitch & 31)
+        return 0;
+    return ((pitch >> 4) & 3) == 0 ? (k & 3) : ((k >> 1) & 1);
+}
+
 // 16 bytes from global memory into LDS; lds_base is wavefront-uniform and
 // lane l's bytes land at lds_base + 16 l
 __device__ inline void copy16_to_lds(const void* src, void* lds_base)
@@ -37,9 +52,10 @@ __device__ inline void copy16_to_lds(const void* src, void* lds_base)
 }
 
 // Stage rows [k0, k0 + kc) of A into at[kc][ec_pitch(r)] and w_g[k0, k0 + kc)
-// into wgl[kc] (kc a multiple of 64, <= 512; k0 a multiple of 64).  Every
-// thread of the 256 calls; the caller waits for the loads (s_waitcnt
-// vmcnt) and synchronizes before reading.
+// into wgl[kc] (kc a multiple of 64, <= 512; k0 a multiple of 64), swizzled
+// (ec_swz) when SWZ.  Every thread of the NT calls; the caller waits for
+// the loads (s_waitcnt vmcnt) and synchronizes before reading.
+template <int NT = 256, bool SWZ = false>
 __device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* __restrict__ w_g, int r,
                                 int k0, int kc, uint16_t* at, uint16_t* wgl)
 {
@@ -47,18 +63,33 @@ __device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* 
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     if ((r & 3) == 0) {
-        // pitch == r: the LDS slice is a byte copy of the global one (16-byte
-        // aligned: k0 r 2 is a multiple of 128)
+        // pitch == r: the LDS slice is the global one, 16-byte chunk by chunk
+        // (16-byte aligned: k0 r 2 is a multiple of 128), with each row's
+        // 32-byte pairs in swizzled order: LDS chunk j of row k holds global
+        // chunk 2 ((j >> 1) ^ ec_swz(k)) + (j & 1)
         const int bytes = kc * r * 2;
+        const int cpr = r >> 3;                         // 16-byte chunks per row
+        const bool pow2 = (cpr & (cpr - 1)) == 0;
+        const int sh = __builtin_ctz(cpr);
         const char* src = reinterpret_cast<const char*>(A + (size_t)k0 * r);
-        for (int off = w * 1024; off < bytes; off += 4096)
-            if (off + 16 * l < bytes)
-                copy16_to_lds(src + off + 16 * l, reinterpret_cast<char*>(at) + off);
+        for (int off = w * 1024; off < bytes; off += NT * 16) {
+            const int c = (off >> 4) + l;
+            if (16 * c < bytes) {
+                if constexpr (SWZ) {
+                    const int k = pow2 ? c >> sh : c / cpr, j = c - k * cpr;
+                    const int jg = 2 * ((j >> 1) ^ ec_swz(k, r)) + (j & 1);
+                    copy16_to_lds(src + 16 * (k * cpr + jg), reinterpret_cast<char*>(at) + off);
+                } else {
+                    copy16_to_lds(src + 16 * c, reinterpret_cast<char*>(at) + off);
+                }
+            }
+        }
     } else {
         const int pitch = ec_pitch(r);
-        for (int idx = tid; idx < kc * r; idx += 256) {
+        for (int idx = tid; idx < kc * r; idx += NT) {
             const int kk = idx / r, c = idx - kk * r;
-            at[kk * pitch + c] = A[(size_t)(k0 + kk) * r + c];
+            const int cs = SWZ ? (((c >> 4) ^ ec_swz(kk, pitch)) << 4) + (c & 15) : c;
+            at[kk * pitch + cs] = A[(size_t)(k0 + kk) * r + c];
         }
     }
     if (w_g && w == 0 && 8 * l < kc)
@@ -69,12 +100,10 @@ __device__ inline void ec_stage(const uint16_t* __restrict__ A, const uint16_t* 
 // values (pitch halves per row, a multiple of 4), columns c0 .. c0 + 15,
 // rows krow .. krow + 31: lane l gets column c0 + (l & 15) at rows
 // krow + 8 (l >> 4) + t, t = 0..7.
-__device__ inline u32x4 lds_bfrag(const uint16_t* base, int pitch, int c0, int krow)
+// the transpose reads of a B fragment, lane l at p (its row and column
+// chosen by the caller), the second four rows 4 pitch halves further on
+__device__ inline u32x4 tr_bfrag(const uint16_t* p, int pitch)
 {
-    const int l = threadIdx.x & 63;
-    const int g = l >> 4;
-    const int s = l & 15;
-    const uint16_t* p = base + (krow + 8 * g + (s >> 2)) * pitch + c0 + 4 * (s & 3);
     const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
     const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * pitch));
     return (u32x4){(uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16),
@@ -83,10 +112,23 @@ __device__ inline u32x4 lds_bfrag(const uint16_t* base, int pitch, int c0, int k
                    (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16)};
 }
 
-// B fragment for column block cb < ec_a_blocks(r) of the staged slice
+__device__ inline u32x4 lds_bfrag(const uint16_t* base, int pitch, int c0, int krow)
+{
+    const int l = threadIdx.x & 63;
+    return tr_bfrag(base + (krow + 8 * (l >> 4) + ((l & 15) >> 2)) * pitch + c0 + 4 * (l & 3), pitch);
+}
+
+// B fragment for column block cb < ec_a_blocks(r) of the staged slice (rows
+// krow .. krow + 31, krow a multiple of 8; the swizzle, when SWZ, is the
+// same for rows k and k + 4)
+template <bool SWZ = false>
 __device__ inline u32x4 ec_bfrag_a(const uint16_t* at, int r, int cb, int krow)
 {
-    return lds_bfrag(at, ec_pitch(r), 16 * cb, krow);
+    const int l = threadIdx.x & 63;
+    const int pitch = ec_pitch(r);
+    const int row = krow + 8 * (l >> 4) + ((l & 15) >> 2);
+    const int cbs = SWZ ? cb ^ ec_swz(row, pitch) : cb;
+    return tr_bfrag(at + row * pitch + 16 * cbs + 4 * (l & 3), pitch);
 }
 
 // B fragment of the gate block (column block ec_a_blocks(r)), same rows:

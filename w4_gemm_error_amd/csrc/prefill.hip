@@ -30,6 +30,7 @@
 //    them in a fixed order, then runs the epilogue;
 //  * tile ids are remapped so that the workgroups an XCD receives (block ids
 //    congruent mod 8) share rows of X and columns of W in that XCD's L2.
+#include <atomic>
 #include <type_traits>
 
 #include "ec_tile.h"
@@ -74,7 +75,7 @@ __device__ inline void prepass_mfma(const u32x4 (&xf)[PRE_MAXS], const uint16_t*
             if (cb < nba) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
-                    bf[s] = ec_bfrag_a(at, r, cb, 32 * s);
+                    bf[s] = ec_bfrag_a<true>(at, r, cb, 32 * s);
             } else {
 #pragma unroll
                 for (int s = 0; s < NS; ++s)
@@ -115,7 +116,7 @@ void prepass_kernel(PrepassKArgs a)
 #pragma unroll
     for (int s = 0; s < PRE_MAXS; ++s)                // steps past the slice are never used
         xf[s] = ld16(xp + 32 * min(s, (len >> 5) - 1));
-    ec_stage(a.A, a.w_g, a.r, kbeg, len, at, wgl);
+    ec_stage<PF_THREADS, true>(a.A, a.w_g, a.r, kbeg, len, at, wgl);
     wait_all_mem();
     __syncthreads();
 
@@ -440,11 +441,26 @@ struct GemmKArgs {
     const uint8_t* codes;
     const uint32_t* sz;
     const uint16_t* B;
-    const uint16_t* tg;
-    const float* rowsum;  // bf16 per-channel: sums of each token's activations over K
+    uint16_t* tg;      // [Mpad][r_pad] T_g, activation format
+    float* rowsum;     // bf16 per-channel: sums of each token's activations over K
     uint16_t* Y;
     floatx4* partial;  // [tile][ksplit][NW][RB][JW][64] fragments
     uint32_t* cnt;     // [mt*nt]
+    // Fused EC (ec_q > 0): the workgroups make T_g (and the activation sums)
+    // themselves.  Every workgroup is resident at once; the first ec_q of
+    // each row of tiles compute a K range of [T | l] = X [A | w_g] for the
+    // row's tokens before their main loop, and after it they hand out the
+    // reduction of those pieces among themselves, 16 tokens x 16 ranks at a
+    // time; the epilogue waits (bounded) for all of its row's units.
+    const uint16_t* A;
+    const uint16_t* w_g;
+    float b_g;
+    uint32_t one2;     // two ones in the activation format: also sum the activations (else 0)
+    floatx4* ecp;      // [mt][ec_q][BM / 16][ec_blocks(r)][64] fragments
+    uint32_t* eccnt;   // [4][mt]: pieces done, units handed out, units done, workgroups done
+    uint32_t* flags;   // workspace flags: [1] a fused-EC wait gave up (sticky until reset)
+    uint32_t spin;     // polls before a bounded wait gives up
+    int ec_q, ec_kc;   // pieces per row of tiles; k per LDS slice of [A | w_g]
     int M, N, K, r, r_pad, G, NB, KB, Npad, mt, nt, ksplit, Mpad;
 };
 
@@ -472,12 +488,230 @@ __device__ inline void work_of(int mt, int nt, int ksplit, int& tm, int& tn, int
     tn = in / gm;
 }
 
-constexpr int YT_PITCH = 264;    // halves per LDS row of the output tile (256 + 8: staggered banks)
+// ---------------------------------------------------------------- fused EC
+//
+// SPEAR (gist.science technical summary, section 2.1A): the gate logit
+// x w_g and the rank-r projection X A come from one pass over X; the
+// correction g (X A) B is added in the epilogue.  Here the pass over X is
+// spread over the GEMM's own workgroups (all resident: a plan of at most
+// one workgroup per CU), so that no separate launch precedes the GEMM.
+
+__device__ inline float ld_dev_f32(const float* p)
+{
+    return __uint_as_float(atomic_load_dev(reinterpret_cast<const uint32_t*>(p)));
+}
+
+// byte offset of piece q's fragment (row block rb, column block cb) of tile row tm
+__device__ inline uint32_t ecp_off(const GemmKArgs& a, int rbk, int tm, int q, int rb, int cb)
+{
+    const int l = threadIdx.x & 63;
+    return (uint32_t)(((((size_t)tm * a.ec_q + q) * rbk + rb) * ec_blocks(a.r) + cb) * 64 + l) * 16u;
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t ecp_rsrc(const GemmKArgs& a, int rbk)
+{
+    return dev_rsrc(a.ecp, (uint32_t)((size_t)a.mt * a.ec_q * rbk * ec_blocks(a.r) * 64 * 16));
+}
+
+// Bounded wait (thread 0 of the workgroup) until *p >= target; true when it
+// gave up (at once with a wait limit of 0, or after an earlier wait of the
+// fused EC gave up on this workspace: flags[1], sticky until reset).
+__device__ inline bool ec_wait_ge(const GemmKArgs& a, const uint32_t* p, uint32_t target)
+{
+    bool lost = a.spin == 0 || atomic_load_dev(&a.flags[1]) != 0;
+    for (uint32_t it = 0; !lost && atomic_load_dev(p) < target; ++it) {
+        if (it >= a.spin)
+            lost = true;
+        else
+            __builtin_amdgcn_s_sleep(1);
+    }
+    if (lost)
+        atomic_store_dev(&a.flags[1], 1u);
+    return lost;
+}
+
+// Producer: piece q of tile row tm, rows m0 .. m0 + BM - 1 of [T | l] over
+// the K range [k0, k1) (64-multiples, about K / ec_q, at most ec_kc), with
+// that range of [A | w_g] in LDS.  Wavefront w takes row block w mod (BM /
+// 16) and, with two wavefronts per row block, every other column block;
+// each block is one chain of MFMAs, stored as soon as it is done.  The LDS
+// is not in use yet, nor are the main loop's registers.
+template <int ACT, int NS>
+__device__ __forceinline__ void ec_piece_blocks(const GemmKArgs& a, const u32x4 (&xf)[PRE_MAXS], const uint16_t* at,
+                                                const uint16_t* wgl, int cb0, int cbstep, __amdgpu_buffer_rsrc_t rs,
+                                                uint32_t off0)
+{
+    const int nb = ec_blocks(a.r), nba = ec_a_blocks(a.r);
+    const bool gate = a.w_g != nullptr;
+#pragma unroll 1
+    for (int cb = cb0; cb < nb; cb += cbstep) {        // wavefront-uniform
+        u32x4 bf[NS];
+        if (cb < nba) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                bf[s] = ec_bfrag_a<true>(at, a.r, cb, 32 * s);
+        } else {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                bf[s] = ec_bfrag_gate(wgl, gate, a.one2, 32 * s);
+        }
+        floatx4 acc = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            acc = mfma16x16x32<ACT>(xf[s], bf[s], acc);
+        st16_sc1(rs, off0 + (uint32_t)cb * 1024u, acc);
+    }
+}
+
+template <int ACT, int BM>
+__device__ __forceinline__ void ec_produce(const GemmKArgs& a, int tm, int q, int m0, uint8_t* smem)
+{
+    constexpr int RBK = BM / 16;
+    constexpr int WPR = NW / RBK;
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb = w % RBK, part = w / RBK;
+    const int K64 = a.K >> 6;
+    const int k0 = 64 * (int)((long long)q * K64 / a.ec_q);
+    const int k1 = 64 * (int)((long long)(q + 1) * K64 / a.ec_q);
+    const int ns = (k1 - k0) >> 5;                     // 32-k steps (even, 2 .. 16)
+    uint16_t* at = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* wgl = at + (k1 - k0) * ec_pitch(a.r) + 16;
+    const uint16_t* xp = a.X + (size_t)min(m0 + 16 * rb + (l & 15), a.M - 1) * a.K + k0 + 8 * (l >> 4);
+    u32x4 xf[PRE_MAXS];
+#pragma unroll
+    for (int s = 0; s < PRE_MAXS; ++s)                 // steps past the range are never used
+        xf[s] = ld16(xp + 32 * min(s, ns - 1));
+    ec_stage<GEMM_THREADS, true>(a.A, a.w_g, a.r, k0, k1 - k0, at, wgl);
+    wait_all_mem();
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rs = ecp_rsrc(a, RBK);
+    const uint32_t off0 = ecp_off(a, RBK, tm, q, rb, 0);
+    switch (ns >> 1) {
+    case 1: ec_piece_blocks<ACT, 2>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    case 2: ec_piece_blocks<ACT, 4>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    case 3: ec_piece_blocks<ACT, 6>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    case 4: ec_piece_blocks<ACT, 8>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    case 5: ec_piece_blocks<ACT, 10>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    case 6: ec_piece_blocks<ACT, 12>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    case 7: ec_piece_blocks<ACT, 14>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    default: ec_piece_blocks<ACT, 16>(a, xf, at, wgl, part, WPR, rs, off0); break;
+    }
+}
+
+// Reducer: after its main loop a workgroup takes units (row block, column
+// block of T) of its tile row from the row's dispenser until none is left,
+// so that the workgroups that finish first do the work.  A unit adds the
+// pieces' fragments of its block and of the gate block in a fixed order
+// (wavefront w adds pieces w, w + 8, ...; then wavefront 0 adds the eight
+// sums in order), applies the gate and stores 16 tokens x 16 ranks of T_g
+// (and, for the first column block, the tokens' activation sums) with
+// device-coherent stores; then it counts the unit as done.
+template <int ACT, int BM>
+__device__ __forceinline__ void ec_reduce_units(const GemmKArgs& a, int tm, int m0, uint8_t* smem, uint32_t& s_u)
+{
+    constexpr int RBK = BM / 16;
+    const int tid = threadIdx.x;
+    const int l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nb = ec_blocks(a.r), nba = ec_a_blocks(a.r);
+    const int ucb = nba > 0 ? nba : 1;                 // units per row block (r = 0: the sums alone)
+    const uint32_t U = (uint32_t)(RBK * ucb);
+    uint32_t* cnt_piece = a.eccnt;
+    uint32_t* cnt_grab = a.eccnt + a.mt;
+    uint32_t* cnt_unit = a.eccnt + 2 * a.mt;
+    floatx4* red = reinterpret_cast<floatx4*>(smem);  // [NW][2][64]
+    uint16_t* tgl = reinterpret_cast<uint16_t*>(red + NW * 2 * 64);   // [16][16]
+    const __amdgpu_buffer_rsrc_t rs = ecp_rsrc(a, RBK);
+    const __amdgpu_buffer_rsrc_t tgs = dev_rsrc(a.tg, (uint32_t)((size_t)a.Mpad * a.r_pad * 2));
+    bool waited = false, lost = false;
+    for (;;) {
+        if (tid == 0)
+            s_u = atomic_add_dev(&cnt_grab[tm], 1u);
+        __syncthreads();
+        const uint32_t u = s_u;
+        if (u >= U)
+            break;
+        if (!waited) {
+            // every piece of the row has been stored (long done in practice)
+            __syncthreads();
+            if (tid == 0)
+                s_u = ec_wait_ge(a, &cnt_piece[tm], (uint32_t)a.ec_q) ? 1u : 0u;
+            __syncthreads();
+            lost = s_u != 0;
+            waited = true;
+        }
+        const int rb = (int)u / ucb;
+        const int cbt = nba > 0 ? (int)u - rb * ucb : nb - 1;
+        floatx4 t = (floatx4){0.f, 0.f, 0.f, 0.f}, gsum = t;
+        for (int q0 = w; q0 < a.ec_q; q0 += 4 * NW) {
+            floatx4 vt[4], vg[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = min(q0 + NW * i, a.ec_q - 1);   // past the last piece: re-read it, unused
+                vt[i] = ld16_sc1(rs, ecp_off(a, RBK, tm, q, rb, cbt));
+                vg[i] = ld16_sc1(rs, ecp_off(a, RBK, tm, q, rb, nb - 1));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (q0 + NW * i < a.ec_q) {
+                    t += vt[i];
+                    gsum += vg[i];
+                }
+            }
+        }
+        red[(w * 2) * 64 + l] = t;
+        red[(w * 2 + 1) * 64 + l] = gsum;
+        __syncthreads();
+        if (w == 0) {
+            floatx4 T = red[l], Gb = red[64 + l];
+#pragma unroll
+            for (int v = 1; v < NW; ++v) {
+                T += red[(v * 2) * 64 + l];
+                Gb += red[(v * 2 + 1) * 64 + l];
+            }
+            // lane l: column l & 15 of the block, rows 4 (l >> 4) + v; the
+            // gate logits of those rows sit in lane 16 (l >> 4) (column 0),
+            // their activation sums in lane 16 (l >> 4) + 1
+            const float nan = __builtin_nanf("");
+            if (nba > 0) {
+                const int c = 16 * cbt + (l & 15);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float lg = __shfl(Gb[v], l & 48);
+                    const float g = sigmoid_f32(lg + a.b_g);
+                    tgl[(4 * (l >> 4) + v) * 16 + (l & 15)] = f32_to_act<ACT>(lost ? nan : c < a.r ? g * T[v] : 0.0f);
+                }
+                if (l < 32) {
+                    const int row = l >> 1, c8 = 8 * (l & 1);
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(tgl + row * 16 + c8);
+                    const uint32_t off = (uint32_t)(((size_t)(m0 + 16 * rb + row) * a.r_pad) * 2);
+                    st16_sc1(tgs, off + (16 * cbt + c8) * 2, __builtin_bit_cast(floatx4, val));
+                    // ranks of r_pad past the last block of A: zero
+                    if (cbt == nba - 1 && 16 * nba < a.r_pad)
+                        st16_sc1(tgs, off + (16 * nba + c8) * 2, (floatx4){0.f, 0.f, 0.f, 0.f});
+                }
+            }
+            if (a.one2 != 0 && cbt == (nba > 0 ? 0 : nb - 1) && (l & 15) == 1) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    atomic_store_dev(reinterpret_cast<uint32_t*>(a.rowsum + m0 + 16 * rb + 4 * (l >> 4) + v),
+                                     __float_as_uint(lost ? nan : Gb[v]));
+            }
+            wait_all_mem();
+            if (l == 0)
+                atomic_add_dev(&cnt_unit[tm], 1u);
+        }
+    }
+}
+
+constexpr int YT_PITCH = GEMM_YT_PITCH;   // halves per LDS row of the output tile (256 + 8: staggered banks)
 
 template <int BM>
 constexpr int gemm_lds_bytes()
 {
-    return (2 * BM * PANEL_K * 2 > BM * YT_PITCH * 2) ? 2 * BM * PANEL_K * 2 : BM * YT_PITCH * 2;
+    return gemm_lds_bytes_of(BM);
 }
 
 // The end of a GEMM tile: the split-K hand-over (the last workgroup of a
@@ -488,7 +722,7 @@ constexpr int gemm_lds_bytes()
 template <int ACT, int BM, bool GROUPED, int NWV, int LDSB>
 __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM / 16][16 / NWV], const float (&sf)[16 / NWV],
                                           const float (&zf)[16 / NWV], const uint32_t* const (&szsrc)[16 / NWV], int tm,
-                                          int tn, int kz, int m0, int n0, uint8_t* smem, uint32_t& s_old)
+                                          int tn, int kz, int m0, int n0, uint8_t* smem, uint32_t& s_old, uint32_t& s_ec)
 {
     constexpr int GEMM_THREADS = 64 * NWV;
     constexpr int NW = NWV;
@@ -557,13 +791,27 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
                 acc[rb][j] = sum[rb][j];
     }
 
+    // ---- fused EC: wait (bounded) until every unit of this tile row is done;
+    // a wait that gave up stores NaN
+    bool eclost = false;
+    if (BM == 64 && a.ec_q > 0) {
+        const int ucb = ec_a_blocks(a.r) > 0 ? ec_a_blocks(a.r) : 1;
+        if (tid == 0)
+            s_ec = ec_wait_ge(a, a.eccnt + 2 * a.mt + tm, (uint32_t)(RB * ucb)) ? 1u : 0u;
+        __syncthreads();
+        eclost = s_ec != 0;
+    }
+
     // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r correction
+    // (with the fused EC, T_g and the activation sums are read past this
+    // XCD's L2: they were written during this kernel)
     if constexpr (BIAS) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float sx = a.rowsum[m0 + rb * 16 + 4 * (l >> 4) + v];
+                const float* ps = a.rowsum + m0 + rb * 16 + 4 * (l >> 4) + v;
+                const float sx = BM == 64 && a.ec_q > 0 ? ld_dev_f32(ps) : *ps;
 #pragma unroll
                 for (int j = 0; j < JW; ++j)
                     acc[rb][j][v] -= (128.0f + zf[j]) * sx;
@@ -655,6 +903,7 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
         uint16_t* tl = bl + RCH * BP;
         const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
         const int koff = 8 * (l >> 4);
+        const __amdgpu_buffer_rsrc_t tgs = dev_rsrc(a.tg, (uint32_t)((size_t)a.Mpad * a.r_pad * 2));
         for (int c0 = 0; c0 < a.r_pad; c0 += RCH) {
             u32x4 bv[BCH], tv[TCH];
 #pragma unroll
@@ -677,13 +926,24 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
                 }
                 bv[i] = v;
             }
+            // (ranks past r_pad -- a last chunk wider than the rest -- are not
+            // loaded and not used)
+            if (BM == 64 && a.ec_q > 0) {
 #pragma unroll
-            for (int i = 0; i < TCH; ++i) {
-                const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
-                const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
-                // ranks past r_pad (a last chunk wider than the rest) are not loaded and not used
-                tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
-                                              : (u32x4){0u, 0u, 0u, 0u};
+                for (int i = 0; i < TCH; ++i) {
+                    const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
+                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                    tv[i] = c0 + 8 * cc < a.r_pad ? __builtin_bit_cast(u32x4, ld16_sc1(tgs, (uint32_t)(((size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc) * 2)))
+                                                  : (u32x4){0u, 0u, 0u, 0u};
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < TCH; ++i) {
+                    const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
+                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                    tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
+                                                  : (u32x4){0u, 0u, 0u, 0u};
+                }
             }
 #pragma unroll
             for (int i = 0; i < BCH; ++i) {
@@ -735,7 +995,7 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
                     yt[((rb - rp) * 16 + 4 * (l >> 4) + v) * YT_PITCH + 16 * JW * w + 16 * j + (l & 15)] =
-                        f32_to_act<ACT>(acc[rb][j][v]);
+                        f32_to_act<ACT>(eclost ? __builtin_nanf("") : acc[rb][j][v]);
         __syncthreads();
         const int nrow = (rp + RBP <= RB ? RBP : RB - rp) * 16;
         for (int e = tid; e < nrow * (PF_BN / 8); e += GEMM_THREADS) {
@@ -777,8 +1037,8 @@ void prefill_gemm_kernel(GemmKArgs a)
     // registers allow.
     constexpr int XS = BM == 64 ? 4 : 2;
     static_assert(D % XS == 0, "activation sets must divide the ring");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[gemm_lds_bytes<BM>()];
-    __shared__ uint32_t s_old;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[BM == 64 ? gemm_smem_bytes_of(BM) : gemm_lds_bytes<BM>()];
+    __shared__ uint32_t s_old, s_ec;
 
     const int tid = threadIdx.x;
     const int l = tid & 63;
@@ -898,6 +1158,20 @@ void prefill_gemm_kernel(GemmKArgs a)
             st16(dst + xdst[x], xr[set][x]);
     };
 
+    // fused EC (64-token tiles only, a single row of them): this
+    // workgroup's piece, stored and counted before the main loop's first
+    // loads go out (its registers are free then)
+    constexpr bool FUSED = BM == 64;
+    if (FUSED && a.ec_q > 0) {
+        const int q = kz * a.nt + tn;
+        if (q < a.ec_q) {
+            ec_produce<ACT, BM>(a, tm, q, m0, smem);
+            wait_all_mem();
+            __syncthreads();
+            if (tid == 0)
+                atomic_add_dev(&a.eccnt[tm], 1u);
+        }
+    }
     if constexpr (!GROUPED) {
         uint32_t v[JW];
 #pragma unroll
@@ -1024,7 +1298,18 @@ void prefill_gemm_kernel(GemmKArgs a)
         chunk(i0, std::true_type{});
     chunk(i0, std::false_type{});
 
-    gemm_tail<ACT, BM, GROUPED, 8, gemm_lds_bytes<BM>()>(a, acc, sf, zf, szsrc, tm, tn, kz, m0, n0, smem, s_old);
+    if (FUSED && a.ec_q > 0)
+        ec_reduce_units<ACT, BM>(a, tm, m0, smem, s_ec);
+    gemm_tail<ACT, BM, GROUPED, 8, gemm_lds_bytes<BM>()>(a, acc, sf, zf, szsrc, tm, tn, kz, m0, n0, smem, s_old, s_ec);
+    // fused EC: the last workgroup of the tile row to be done with the
+    // counters returns them to zero
+    if (FUSED && a.ec_q > 0 && tid == 0) {
+        if (atomic_add_dev(&a.eccnt[3 * a.mt + tm], 1u) == (uint32_t)(a.nt * a.ksplit - 1)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                atomic_store_dev(&a.eccnt[c * a.mt + tm], 0u);
+        }
+    }
 }
 
 template <int ACT, int BM, bool GROUPED>
@@ -1097,6 +1382,26 @@ hipError_t launch_prefill_ec_gate(const LayerArgs& a, const PrefillPlan& p, hipS
     return launch_prefill_ec_part(a, p, false, st);
 }
 
+// Compute units of the current device (looked up once per device).
+static hipError_t resident_cus(int* out)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    int n = dev < 64 ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        if (dev < 64)
+            cache[dev].store(n, std::memory_order_relaxed);
+    }
+    *out = n;
+    return hipSuccess;
+}
+
 hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t st)
 {
     BlobGeom g = blob_geom(a.N, a.K, a.G);
@@ -1125,7 +1430,18 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
-    } else if (a.r > 0 || sums) {
+    }
+    // the fused EC needs every workgroup resident at once (one per CU: the
+    // GEMM's workgroups hold a CU's registers)
+    bool fused = false;
+    if (!a.S && a.h == 0 && (a.r > 0 || sums) && p.ec_q > 0) {
+        int cus = 0;
+        hipError_t e = resident_cus(&cus);
+        if (e != hipSuccess)
+            return e;
+        fused = (long long)p.mt * p.nt * p.ksplit <= cus;
+    }
+    if (!a.S && !fused && (a.r > 0 || sums)) {
         hipError_t e = launch_prefill_ec_part(a, p, sums, st);
         if (e != hipSuccess)
             return e;
@@ -1140,6 +1456,16 @@ hipError_t launch_prefill(const LayerArgs& a, const PrefillPlan& p, hipStream_t 
     k.Y = (uint16_t*)a.Y;
     k.partial = (floatx4*)(a.ws + p.off_gemm_partial);
     k.cnt = (uint32_t*)(a.ws + p.off_gemm_cnt);
+    k.A = (const uint16_t*)a.A;
+    k.w_g = (const uint16_t*)a.w_g;
+    k.b_g = a.b_g;
+    k.one2 = !sums ? 0u : 0x3F803F80u;                   // bf16 ones
+    k.ecp = (floatx4*)(a.ws + p.off_pre_partial);
+    k.eccnt = (uint32_t*)(a.ws + p.off_ec_cnt);
+    k.flags = (uint32_t*)(a.ws + p.off_flags);
+    k.spin = a.spin;
+    k.ec_q = fused ? p.ec_q : 0;
+    k.ec_kc = p.ec_kc;
     k.M = a.M; k.N = a.N; k.K = a.K; k.r = a.r; k.r_pad = p.r_pad; k.G = a.G;
     k.NB = g.NB; k.KB = g.KB; k.Npad = g.Npad;
     k.mt = p.mt; k.nt = p.nt; k.ksplit = p.ksplit; k.Mpad = p.Mpad;

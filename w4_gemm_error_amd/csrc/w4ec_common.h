@@ -436,6 +436,22 @@ __host__ __device__ inline int ec_blocks(int r) { return ec_a_blocks(r) + 1; }
 __host__ __device__ inline int ec_slice_bytes(int r, int kc) { return (kc * ec_pitch(r) + 16) * 2; }
 // LDS of a prepass workgroup: the slice and its gate vector
 inline size_t prepass_lds_bytes(int r, int kc) { return (size_t)ec_slice_bytes(r, kc) + (size_t)kc * 2; }
+// LDS of a prefill GEMM workgroup of BM tokens: two staged 128-k steps of X,
+// or the rounded output tile (rows of GEMM_YT_PITCH halves), whichever is
+// larger
+constexpr int GEMM_YT_PITCH = 264;
+__host__ __device__ constexpr int gemm_lds_bytes_of(int BM)
+{
+    return (2 * BM * PANEL_K * 2 > BM * GEMM_YT_PITCH * 2) ? 2 * BM * PANEL_K * 2 : BM * GEMM_YT_PITCH * 2;
+}
+// LDS array of a 64-token GEMM workgroup: at least the main loop's and the
+// epilogue's, and room for a fused-EC slice of [A | w_g] (a workgroup holds
+// a CU's registers, so its LDS costs no occupancy)
+constexpr int GEMM_EC_LDS = 128 << 10;
+__host__ __device__ constexpr int gemm_smem_bytes_of(int BM)
+{
+    return gemm_lds_bytes_of(BM) > GEMM_EC_LDS ? gemm_lds_bytes_of(BM) : GEMM_EC_LDS;
+}
 
 constexpr int DEC_THREADS = 256;     // threads per decode workgroup
 constexpr int DEC_XLDS_CHUNKS = 8;   // 16-byte chunks of staged activations per decode thread
@@ -471,7 +487,9 @@ struct PrefillPlan {
     int pre_ks;     // prepass split over K
     int pre_kc;     // k per prepass split (multiple of 64, <= 512)
     int r_pad, Mpad;
-    size_t off_flags, off_gemm_cnt, off_pre_partial, off_tg, off_rowsum, off_gemm_partial, bytes;
+    int ec_q;       // fused EC: pieces of [T | l] per row of tiles (0: the prepass kernels instead)
+    int ec_kc;      // fused EC: k per LDS slice of [A | w_g] (multiple of 64, <= 512)
+    size_t off_flags, off_gemm_cnt, off_ec_cnt, off_pre_partial, off_tg, off_rowsum, off_gemm_partial, bytes;
 };
 
 }  // namespace w4ec
