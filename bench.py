@@ -195,9 +195,10 @@ def split_prefill_step(torch, w4, path, X, Y, copies, R, b_g, M, N, K, r, G):
     return step
 
 
-def graph_time_us(torch, step, steps, warmup):
+def graph_time_us(torch, step, steps, warmup, reps=1):
     """Microseconds per step of `steps` calls captured in one graph (after
-    `warmup` eager calls and one untimed replay)."""
+    `warmup` eager calls and one untimed replay; the best of `reps` timed
+    replays)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -211,12 +212,16 @@ def graph_time_us(torch, step, steps, warmup):
     torch.cuda.current_stream().wait_stream(stream)
     graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / steps
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e3 / steps
+        best = t if best is None else min(best, t)
+    return best
 
 
 def latency_table(torch, w4, synth, dev):
@@ -340,6 +345,41 @@ def xfp_main(args, torch, w4, synth, dev, layer, M):
     print(json.dumps(out), flush=True)
 
 
+def stream_read_time_us(torch, w4, nbytes, steps, warmup, dev):
+    """Microseconds per launch of the library's streaming-read reference
+    kernel over nbytes, the launches cycling through copies that together
+    exceed twice the 256 MB Infinity Cache (graph replay, events)."""
+    nb = -(-nbytes // 256) * 256
+    R = max(2, -(-2 * MALL_BYTES // nb))
+    buf = torch.ones(R * nb, dtype=torch.uint8, device=dev)
+    sink = torch.empty(512, dtype=torch.int32, device=dev)
+
+    def step(i):
+        w4.w4ec_stream_read(buf[(i % R) * nb:(i % R) * nb + nbytes // 16 * 16], sink)
+
+    # the attainable time: the best of three timed replays (one that a
+    # stall of the machine interrupts says nothing about the read)
+    us = graph_time_us(torch, step, steps, warmup, reps=3)
+    del buf
+    return us, R
+
+
+def stream_read_main(args, torch, w4, synth, dev):
+    """Only the streaming-read reference, over the algorithmic bytes of the
+    workload's call: the HBM read time attainable for that byte count."""
+    layer, M, phase = WORKLOADS[args.workload]
+    c = synth.LAYERS[layer]
+    r = c.r if args.rank is None else args.rank
+    nbytes = layer_bytes(M, c.N, c.K, r, c.group_size, has_gate=r > 0) // 16 * 16
+    us, R = stream_read_time_us(torch, w4, nbytes, args.steps, args.warmup, dev)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({"metric": "streaming-read reference (stream_read_kernel)", "value": round(achieved, 2),
+                      "unit": "GB/s", "us_per_launch": round(us, 3), "bytes": nbytes, "copies": R,
+                      "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4), "steps": args.steps,
+                      "config": {"workload": args.workload, "bytes_of": "one call's algorithmic bytes"}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +410,9 @@ def main():
                          "the salient input channels (the config's outlier channels), X[:, S] R; xfp "
                          "(decode workloads): per-channel 16-entry codebooks plus a sparse fp16 outlier "
                          "residual, no EC")
+    ap.add_argument("--stream-read", action="store_true",
+                    help="only time the library's streaming-read reference kernel over the workload's "
+                         "algorithmic bytes (the attainable HBM read time for that byte count)")
     ap.add_argument("--lut", action="store_true",
                     help="prefill latency table: time the three paths over a grid of (M, r, N, K) and print "
                          "one JSON line per point (no roofline / CPU legs)")
@@ -402,6 +445,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.lut:
         latency_table(torch, w4, synth, dev)
+        return
+    if args.stream_read:
+        stream_read_main(args, torch, w4, synth, dev)
         return
     if args.path != "fused" and (WORKLOADS[args.workload][2] != "prefill" or args.gate != "scalar"):
         print("bench.py: --path unfused/semi applies to the prefill workloads with the scalar gate",
@@ -546,6 +592,10 @@ def measure_layer(args, workload, torch, w4, synth, dev):
     kdur = elapsed_ms * 1e-3 / args.steps
     reduce_name = "ec_reduce_vgate_kernel" if vector else "ec_reduce_kernel"
     kernel_name = "decode_kernel" if phase == "decode" else f"prepass_kernel + {reduce_name} + prefill_gemm_kernel (per call)"
+    if phase == "prefill" and M <= 64 and r > 0 and not vector and not serq and args.path == "fused" \
+            and -(-N // 256) <= 256:
+        # one row of 64-token tiles: the GEMM's workgroups make T_g themselves
+        kernel_name = "prefill_gemm_kernel (EC inside; per call)"
     if args.path != "fused" and r > 0:
         kernel_name = (f"prepass_kernel + ec_reduce_kernel, prefill_gemm_kernel (r = 0), ec_apply_kernel "
                        f"({args.path}, per call)")
@@ -571,6 +621,14 @@ def measure_layer(args, workload, torch, w4, synth, dev):
     roof["traffic"] = traffic_from_profiles(kernel_key)
     roof["kernel"] = kernel_name
     roof["kernel_us"] = round(kdur * 1e6, 3)
+    if phase == "decode" and roof["bound"] == "hbm":
+        # the attainable read time for the same bytes, timed in this run:
+        # the library's plain streaming-read kernel
+        sus, _ = stream_read_time_us(torch, w4, nbytes // 16 * 16, min(args.steps, 200), 10, dev)
+        roof["stream_read"] = {"kernel": "stream_read_kernel", "us": round(sus, 3),
+                               "achieved": round(nbytes / (sus * 1e-6) / 1e9, 2),
+                               "frac": round(nbytes / (sus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                               "call_over_read": round(kdur * 1e6 / sus, 3)}
 
     cpu = None
     if not args.no_cpu and not vector and not serq:

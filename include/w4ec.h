@@ -335,6 +335,22 @@ int w4ec_linear_decode_xfp(const void* X, const void* packed, const uint16_t* co
                            const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* val,
                            int nnz, void* Y, int M, int N, int K, int act_dtype, void* stream);
 
+/* Streaming-read reference (a measurement hook, not part of the layer):
+ * reads `bytes` from `src` with the plainest access pattern the library
+ * knows for HBM -- 512 workgroups of 256 threads, workgroup w reading the
+ * 16-byte chunks [w c, (w + 1) c) with c = ceil(bytes / 16 / 512), sixteen
+ * non-temporal 16-byte loads in flight per thread -- and writes one 32-bit
+ * XOR of its chunks' words per workgroup into sink[0 .. 511], so that no
+ * load can be dropped.  The duration of this kernel for a byte count is the HBM
+ * read time actually attainable on the device, against which the decode's
+ * fraction of the 8 TB/s roofline can be read (the decode streams the same
+ * packed weights in one pass).
+ *   src   device, 16-byte aligned; bytes a multiple of 16 (0 launches nothing)
+ *   sink  device uint32 [512], 4-byte aligned (output)
+ * W4EC_ERR_INVALID_ARG for a missing or misaligned pointer or a byte count
+ * that is not a multiple of 16.  Asynchronous on stream. */
+int w4ec_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

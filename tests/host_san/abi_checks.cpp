@@ -154,6 +154,13 @@ hipError_t launch_zero_fill(void*, size_t bytes, hipStream_t)
     return hipSuccess;
 }
 
+hipError_t launch_stream_read(const void*, size_t bytes, uint32_t*, hipStream_t)
+{
+    ++g_launches;
+    CHECK(bytes % 16 == 0 && bytes > 0, "stream read %zu", bytes);
+    return hipSuccess;
+}
+
 hipError_t noalloc_scratch(void** out, hipStream_t)
 {
     ++g_scratch_lookups;
@@ -209,6 +216,11 @@ int main()
     expect(w4ec_pack(nullptr, nullptr, nullptr, 16, 128, 128, fake(PK), nullptr), W4EC_ERR_INVALID_ARG, "pack nulls");
     expect(w4ec_workspace_status(nullptr, 0, nullptr), W4EC_ERR_WORKSPACE, "status without workspace");
     expect(w4ec_workspace_reset(fake(WS + 16), 256, nullptr), W4EC_ERR_WORKSPACE, "reset misaligned");
+    expect(w4ec_stream_read(fake(WS), 24, reinterpret_cast<uint32_t*>(fake(WS)), nullptr), W4EC_ERR_INVALID_ARG,
+           "stream read of a partial chunk");
+    expect(w4ec_stream_read(fake(WS + 8), 256, reinterpret_cast<uint32_t*>(fake(WS)), nullptr),
+           W4EC_ERR_INVALID_ARG, "stream read misaligned");
+    expect(w4ec_stream_read(fake(WS), 256, nullptr, nullptr), W4EC_ERR_INVALID_ARG, "stream read without sink");
     expect(w4ec_linear_decode_vgate(fake(X), fake(PK), fake(A), fake(B), fake(WG), fake(WG + 4096), fake(WG + 8192),
                                     fake(WG + 12288), 65, fake(Y), 1, 512, 512, 32, 512, 0, fake(WS), 1 << 26, nullptr),
            W4EC_ERR_UNSUPPORTED, "vgate h = 65");
@@ -216,6 +228,10 @@ int main()
                                   fake(Y), 1, 512, 512, 0,
                                   nullptr), W4EC_ERR_INVALID_ARG, "xfp without codebooks");
     CHECK(g_launches == l0, "an invalid call launched");
+    expect(w4ec_stream_read(fake(WS), 256, reinterpret_cast<uint32_t*>(fake(WS)), nullptr), W4EC_OK, "stream read");
+    CHECK(g_launches == l0 + 1, "stream read launches once");
+    expect(w4ec_stream_read(fake(WS), 0, reinterpret_cast<uint32_t*>(fake(WS)), nullptr), W4EC_OK, "empty stream read");
+    CHECK(g_launches == l0 + 1, "an empty stream read launches nothing");
 
     // ---- wait limit round trip
     const uint32_t lim = w4ec_wait_limit();

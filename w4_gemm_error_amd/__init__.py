@@ -29,6 +29,7 @@ __all__ = [
     "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
     "w4ec_linear_decode_serq", "w4ec_linear_prefill_serq",
     "w4ec_pack_xfp", "w4ec_linear_decode_xfp",
+    "w4ec_stream_read",
     "PackedLayer",
 ]
 
@@ -79,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.w4ec_workspace_status.restype = I
         L.w4ec_workspace_reset.argtypes = [P, Z, P]
         L.w4ec_workspace_reset.restype = I
+        L.w4ec_stream_read.argtypes = [P, Z, P, P]
+        L.w4ec_stream_read.restype = I
         L.w4ec_set_wait_limit.argtypes = [ctypes.c_uint32]
         L.w4ec_set_wait_limit.restype = None
         L.w4ec_wait_limit.argtypes = []
@@ -211,6 +214,18 @@ def w4ec_workspace_reset(workspace, *, stream=None) -> None:
     _need_cuda(workspace, "workspace")
     _check(lib().w4ec_workspace_reset(_ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream_handle(stream)), "w4ec_workspace_reset")
+
+
+def w4ec_stream_read(src, sink, *, nbytes=None, stream=None) -> None:
+    """The library's streaming-read reference kernel over the first nbytes
+    (default: all) of src; one XOR word per workgroup into sink (uint32 or
+    int32, 512 elements).  A measurement hook: the attainable HBM read time."""
+    _need_cuda(src, "src")
+    _need_cuda(sink, "sink")
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    if sink.numel() * sink.element_size() < 512 * 4:
+        raise ValueError("sink holds 512 32-bit words")
+    _check(lib().w4ec_stream_read(_ptr(src), n, _ptr(sink), _stream_handle(stream)), "w4ec_stream_read")
 
 
 def w4ec_quantize_rtn(W, group_size: int, *, stream=None):

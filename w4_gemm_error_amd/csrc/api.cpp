@@ -609,6 +609,15 @@ int w4ec_workspace_status(const void* workspace, size_t workspace_bytes, void* s
     return W4EC_OK;
 }
 
+int w4ec_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream)
+{
+    if (!src || !sink || !aligned(src, 16) || !aligned(sink, 4) || bytes % 16 != 0)
+        return W4EC_ERR_INVALID_ARG;
+    if (bytes == 0)
+        return W4EC_OK;
+    return hip_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));
+}
+
 int w4ec_workspace_reset(void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!workspace || !aligned(workspace, 256) || workspace_bytes % 16 != 0)

@@ -276,6 +276,54 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* p, size_t n16)
         p[i] = (u32x4){0u, 0u, 0u, 0u};
 }
 
+// ---------------------------------------------------------------- streaming-read reference
+//
+// The plainest read of a buffer: STREAM_WGS workgroups of 256 threads, each
+// workgroup a contiguous share of the 16-byte chunks (ceil(n / STREAM_WGS)),
+// each thread with STREAM_BATCH 16-byte non-temporal loads in flight at once
+// (one round trip for a ~32 MB buffer), folding the data into one XOR word
+// per workgroup so that no load can be dropped.  Its duration is the
+// attainable HBM read time for a byte count, the reference for the decode's
+// fraction of the roofline.
+constexpr int STREAM_WGS = 512;
+constexpr int STREAM_BATCH = 16;
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, size_t n16, uint32_t* sink)
+{
+    __shared__ uint32_t part[4];
+    const size_t per = (n16 + STREAM_WGS - 1) / STREAM_WGS;
+    const size_t lo = (size_t)blockIdx.x * per;
+    const size_t hi = lo + per < n16 ? lo + per : n16;
+    u32x4 acc = (u32x4){0u, 0u, 0u, 0u};
+    for (size_t b = lo + threadIdx.x; b < hi; b += 256 * STREAM_BATCH) {
+        u32x4 v[STREAM_BATCH];
+#pragma unroll
+        for (int u = 0; u < STREAM_BATCH; ++u) {         // past the share: re-read its last chunk, unused
+            const size_t i = b + 256 * (size_t)u;
+            v[u] = ld16_stream(src + (i < hi ? i : hi - 1));
+        }
+#pragma unroll
+        for (int u = 0; u < STREAM_BATCH; ++u)
+            if (b + 256 * (size_t)u < hi)
+                acc ^= v[u];
+    }
+    uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x ^= (uint32_t)__shfl_xor((int)x, o);
+    if ((threadIdx.x & 63) == 0)
+        part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st)
+{
+    hipLaunchKernelGGL(stream_read_kernel, dim3(STREAM_WGS), dim3(256), 0, st, (const u32x4*)src, bytes / 16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st)
 {
     const size_t n16 = bytes / 16;

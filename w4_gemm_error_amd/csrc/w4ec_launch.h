@@ -70,6 +70,9 @@ hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hip
 // bytes (a multiple of 16, 16-byte aligned) set to zero by a kernel (no
 // hipMemsetAsync node when a caller captures the stream into a graph)
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t st);
+// the streaming-read reference: bytes (a multiple of 16) from src, one XOR
+// word per workgroup (512 of them) into sink
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 // The static state array of w4ec_linear_decode_noalloc on the current
 // device (W4EC_NOALLOC_SCRATCH_BYTES bytes): its device address, looked up
 // and cleared (a fill kernel on `st`) by the first call on each device.
