@@ -14,7 +14,8 @@ T = X A (``forward_vgate``); the quantizer is the per-channel RTN baseline of
 its results section 3.1.  ``forward_serq`` is the single-factor correction
 over salient input channels of the SERQ summary (section 2); ``forward_xfp``
 the per-channel codebook weights with a sparse outlier residual of the XFP
-summary (section 2).
+summary (section 2), and ``forward_xfp_lib`` its shared-library mode (one
+library of codebooks per layer, an entry per group of 128 weights).
 """
 from __future__ import annotations
 
@@ -84,6 +85,8 @@ def _load():
         lib.w4o_forward_serq.restype = I
         lib.w4o_forward_xfp.argtypes = [I, I, I, I, P, P, P, P, P, P, P, I, P]
         lib.w4o_forward_xfp.restype = I
+        lib.w4o_forward_xfp_lib.argtypes = [I, I, I, I, P, P, P, I, P, P, P, P, P, I, P]
+        lib.w4o_forward_xfp_lib.restype = I
         lib.w4o_max_threads.argtypes = []
         lib.w4o_max_threads.restype = I
         _lib = lib
@@ -303,4 +306,34 @@ def forward_xfp(X, qc, cb, row_ptr, col_idx, val, *, N, K, act="fp16", rows=None
                              _ptr(col_idx), _ptr(val), _ptr(rows_arr), n_rows, _ptr(Y))
     if rc != 0:
         raise RuntimeError("oracle forward_xfp failed (bad arguments)")
+    return {"Y": Y}
+
+
+def forward_xfp_lib(X, qc, library, libid, row_ptr, col_idx, val, *, N, K, act="fp16", rows=None):
+    """Y = X Wh^T with Wh[n,k] = library[libid[n, k // 128]][idx[n,k]] +
+    (sparse residual)[n,k] (see w4o_forward_xfp_lib).  qc: 4-bit indices
+    uint8 [N, K/2]; library: fp16 bits [L, 16]; libid: uint8 [N, K/128];
+    row_ptr, col_idx, val as forward_xfp."""
+    lib = _load()
+    X = _c(X, np.uint16)
+    M = X.shape[0]
+    assert X.shape == (M, K) and K % 128 == 0
+    qc, library, libid = _c(qc, np.uint8), _c(library, np.uint16), _c(libid, np.uint8)
+    row_ptr, col_idx, val = _c(row_ptr, np.int32), _c(col_idx, np.int32), _c(val, np.uint16)
+    L = int(library.shape[0])
+    assert qc.shape == (N, K // 2) and library.shape == (L, 16) and libid.shape == (N, K // 128)
+    assert row_ptr.shape == (N + 1,) and col_idx.shape == val.shape == (int(row_ptr[-1]),)
+    if col_idx.size == 0:
+        col_idx, val = np.zeros(1, np.int32), np.zeros(1, np.uint16)
+    rows_arr = None
+    n_rows = M
+    if rows is not None:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int32)
+        n_rows = int(rows_arr.shape[0])
+    Y = np.empty((n_rows, N), np.float64)
+    act_bf16 = {"fp16": 0, "bf16": 1}[act]
+    rc = lib.w4o_forward_xfp_lib(M, N, K, act_bf16, _ptr(X), _ptr(qc), _ptr(library), L, _ptr(libid),
+                                 _ptr(row_ptr), _ptr(col_idx), _ptr(val), _ptr(rows_arr), n_rows, _ptr(Y))
+    if rc != 0:
+        raise RuntimeError("oracle forward_xfp_lib failed (bad arguments)")
     return {"Y": Y}

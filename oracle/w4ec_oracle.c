@@ -591,6 +591,89 @@ int w4o_forward_xfp(int M, int N, int K, int act_bf16,
     return bad ? -1 : 0;
 }
 
+/* Codebook weights from a shared library (XFP summary, section 2, "adaptive
+ * learned codebooks", shared-library mode): the layer keeps L codebooks of
+ * 2^4 fp16 entries, and each group of 128 consecutive weights of an output
+ * channel (along K) names the library entry it uses; the sparse fp16
+ * residual is as in w4o_forward_xfp:
+ *
+ *   Wh[n,k] = lib[libid[n][k / 128]][idx[n,k]] + sum of val[e] over the
+ *             entries e of row n whose column is k
+ *   Y[m,n]  = sum_k X[m,k] * Wh[n,k]
+ *
+ *   idx    canonical 4-bit array [N][K/2]
+ *   lib    fp16 bits [L][16], 1 <= L <= 256
+ *   libid  uint8 [N][K/128], each < L
+ *   row_ptr, col_idx, val, rows, n_rows as w4o_forward_xfp.
+ * K a multiple of 128.  Returns 0, or -1 on bad arguments. */
+int w4o_forward_xfp_lib(int M, int N, int K, int act_bf16,
+                        const uint16_t* X, const uint8_t* qc, const uint16_t* lib, int L,
+                        const uint8_t* libid, const int32_t* row_ptr, const int32_t* col_idx,
+                        const uint16_t* val, const int* rows, int n_rows, double* Y)
+{
+    if (M < 0 || N <= 0 || K <= 0 || K % 128 || !Y || !X || !qc || !lib || !libid || !row_ptr)
+        return -1;
+    if (L < 1 || L > 256 || row_ptr[0] != 0)
+        return -1;
+    const int ng = K / 128;
+    for (int n = 0; n < N; ++n) {
+        if (row_ptr[n + 1] < row_ptr[n])
+            return -1;
+        for (int e = row_ptr[n]; e < row_ptr[n + 1]; ++e)
+            if (col_idx[e] < 0 || col_idx[e] >= K)
+                return -1;
+        for (int g = 0; g < ng; ++g)
+            if (libid[(size_t)n * ng + g] >= L)
+                return -1;
+    }
+    if (!rows)
+        n_rows = M;
+    if (n_rows <= 0)
+        return 0;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)n_rows * K);
+    if (!xd)
+        return -1;
+    for (int i = 0; i < n_rows; ++i) {
+        int m = rows ? rows[i] : i;
+        if (m < 0 || m >= M) {
+            free(xd);
+            return -1;
+        }
+        for (int k = 0; k < K; ++k)
+            xd[(size_t)i * K + k] = act_to_double(X[(size_t)m * K + k], act_bf16);
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* wd = (double*)malloc(sizeof(double) * (size_t)K);
+        if (!wd) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 8)
+        for (int n = 0; n < N; ++n) {
+            if (!wd)
+                continue;
+            for (int k = 0; k < K; ++k) {
+                const int entry = libid[(size_t)n * ng + k / 128];
+                wd[k] = w4o_half_to_double(lib[(size_t)entry * 16 + code_at(qc, K, n, k)]);
+            }
+            for (int e = row_ptr[n]; e < row_ptr[n + 1]; ++e)
+                wd[col_idx[e]] += w4o_half_to_double(val[e]);
+            for (int i = 0; i < n_rows; ++i) {
+                const double* x = xd + (size_t)i * K;
+                double y = 0.0;
+                for (int k = 0; k < K; ++k)
+                    y += x[k] * wd[k];
+                Y[(size_t)i * N + n] = y;
+            }
+        }
+        free(wd);
+    }
+    free(xd);
+    return bad ? -1 : 0;
+}
+
 /* Threads an OpenMP region of this library will use. */
 int w4o_max_threads(void)
 {

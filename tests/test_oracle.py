@@ -563,3 +563,91 @@ def test_xfp_row_subsets_and_malformed_rows():
     bad[n + 1] = bad[n] - 1                                 # decreasing pointers
     with pytest.raises((RuntimeError, AssertionError)):
         oracle.forward_xfp(Xb, qc, x["cb"], bad, x["col_idx"], x["val"], N=N, K=K)
+
+
+# ---------------------------------------------------------------- codebook weights from a shared library
+
+def xfp_lib_dense(idx, libb, libid, row_ptr, col_idx, valb):
+    """Wh by numpy: each group of 128 weights indexes its library entry."""
+    lib = libb.view(np.float16).astype(np.float64)
+    N, K = idx.shape
+    ent = np.repeat(libid.astype(np.int64), 128, axis=1)                 # [N, K] library entry per weight
+    Wh = lib[ent, idx.astype(np.int64)]
+    rows = np.repeat(np.arange(N), np.diff(row_ptr))
+    np.add.at(Wh, (rows, col_idx), valb.view(np.float16).astype(np.float64))
+    return Wh
+
+
+def test_xfp_lib_with_a_library_entry_per_channel_is_the_per_channel_mode():
+    """L = N and every group of channel n naming entry n: the per-channel
+    codebooks exactly (same weights, same order)."""
+    rng = np.random.default_rng(51)
+    M, N, K = 4, 24, 384
+    W = rng.standard_normal((N, K)) * 0.02
+    W[rng.random((N, K)) < 0.01] *= 10.0
+    x = synth.make_xfp(W)
+    Xb = f16bits(rng.standard_normal((M, K)))
+    qc = pack_canonical(x["idx"])
+    libid = np.repeat(np.arange(N, dtype=np.uint8)[:, None], K // 128, axis=1)
+    per_ch = oracle.forward_xfp(Xb, qc, x["cb"], x["row_ptr"], x["col_idx"], x["val"], N=N, K=K)["Y"]
+    lib = oracle.forward_xfp_lib(Xb, qc, x["cb"], libid, x["row_ptr"], x["col_idx"], x["val"], N=N, K=K)["Y"]
+    assert np.array_equal(lib, per_ch)
+
+
+def test_xfp_lib_against_numpy_dense():
+    rng = np.random.default_rng(52)
+    M, N, K = 6, 40, 640
+    W = rng.standard_normal((N, K)) * 0.02 * np.exp(rng.standard_normal((N, 1)))
+    W[rng.random((N, K)) < 0.01] *= 12.0
+    x = synth.make_xfp_lib(W, L=32)
+    assert len(np.unique(x["libid"])) > 4 and x["row_ptr"][-1] > 0
+    Xb = f16bits(rng.standard_normal((M, K)))
+    out = oracle.forward_xfp_lib(Xb, pack_canonical(x["idx"]), x["lib"], x["libid"], x["row_ptr"],
+                                 x["col_idx"], x["val"], N=N, K=K)
+    Wh = xfp_lib_dense(x["idx"], x["lib"], x["libid"], x["row_ptr"], x["col_idx"], x["val"])
+    ref = np.matmul(Xb.view(np.float16).astype(np.float64), Wh.T)
+    np.testing.assert_allclose(out["Y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # the weights it encodes are close to W (4-bit library codebooks; outliers restored)
+    rel = np.abs(Wh - W).mean() / np.abs(W).mean()
+    assert rel < 0.15, rel
+
+
+def test_xfp_lib_group_boundaries():
+    """Entry 1 holds 1.0 at index 3, entry 0 zero: with every index 3 and
+    the groups' entries alternating, each output sums exactly the inputs of
+    the groups (128 consecutive k) that name entry 1."""
+    rng = np.random.default_rng(53)
+    M, N, K = 3, 5, 768
+    libv = np.zeros((2, 16))
+    libv[1, 3] = 1.0
+    idx = np.full((N, K), 3, np.uint8)
+    libid = rng.integers(0, 2, size=(N, K // 128)).astype(np.uint8)
+    X = rng.integers(-8, 9, size=(M, K)).astype(np.float64)           # small integers: exact sums
+    out = oracle.forward_xfp_lib(f16bits(X), pack_canonical(idx), f16bits(libv), libid,
+                                 np.zeros(N + 1, np.int32), np.zeros(0, np.int32), np.zeros(0, np.uint16),
+                                 N=N, K=K)["Y"]
+    for n in range(N):
+        want = sum(X[:, g * 128:(g + 1) * 128].sum(axis=1) for g in range(K // 128) if libid[n, g] == 1)
+        want = np.zeros(M) if isinstance(want, int) else want
+        assert np.array_equal(out[:, n], want)
+
+
+def test_xfp_lib_relabelled_library_and_bad_ids():
+    """Permuting the library and relabelling the groups' entries leaves Y
+    unchanged; an entry id past the library is rejected."""
+    rng = np.random.default_rng(54)
+    M, N, K = 4, 16, 256
+    W = rng.standard_normal((N, K)) * 0.02
+    x = synth.make_xfp_lib(W, L=8)
+    Xb = f16bits(rng.standard_normal((M, K)))
+    qc = pack_canonical(x["idx"])
+    args = (x["row_ptr"], x["col_idx"], x["val"])
+    base = oracle.forward_xfp_lib(Xb, qc, x["lib"], x["libid"], *args, N=N, K=K)["Y"]
+    perm = rng.permutation(8)                                           # new entry j holds old entry perm[j]
+    inv = np.argsort(perm).astype(np.uint8)
+    again = oracle.forward_xfp_lib(Xb, qc, np.ascontiguousarray(x["lib"][perm]), inv[x["libid"]], *args, N=N, K=K)["Y"]
+    assert np.array_equal(again, base)
+    bad = x["libid"].copy()
+    bad[2, 1] = 8
+    with pytest.raises(RuntimeError):
+        oracle.forward_xfp_lib(Xb, qc, x["lib"], bad, *args, N=N, K=K)

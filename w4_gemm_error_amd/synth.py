@@ -182,3 +182,57 @@ def make_xfp(W: np.ndarray, k_sigma: float = 4.0, max_frac: float = 0.02) -> dic
     row_ptr = np.cumsum(row_ptr).astype(np.int32)
     return {"idx": idx, "cb": cb.view(np.uint16), "row_ptr": row_ptr, "col_idx": cols.astype(np.int32),
             "val": resid.astype(np.float16).view(np.uint16)}
+
+
+def make_xfp_lib(W: np.ndarray, L: int = 32, k_sigma: float = 4.0, max_frac: float = 0.02) -> dict:
+    """Synthetic weights in the shared-library codebook format, built from a
+    float32 matrix W [N, K] (K a multiple of 128): the outliers are separated
+    as in make_xfp; the library holds L codebooks, the 16 quantiles of a
+    standard normal scaled by L scales spaced geometrically over the range
+    of the groups' standard deviations (fp16); each group of 128 weights of
+    a channel takes the entry whose scale is nearest its own (in log), each
+    weight the nearest value of that entry, and the outliers carry the fp16
+    residual w - entry[idx] at their positions.
+    Returns idx (uint8 [N, K]), lib (fp16 bits [L, 16]), libid (uint8
+    [N, K/128]), row_ptr, col_idx (int32) and val (fp16 bits)."""
+    from math import erf, sqrt
+    W = np.asarray(W, dtype=np.float64)
+    N, K = W.shape
+    assert K % 128 == 0 and 1 <= L <= 256
+    mu = W.mean(axis=1, keepdims=True)
+    sd = W.std(axis=1, keepdims=True)
+    dev = np.abs(W - mu)
+    cap = max(0, int(max_frac * K))
+    out = dev > k_sigma * sd
+    if cap < K:
+        kth = -np.partition(-dev, cap, axis=1)[:, cap:cap + 1] if cap > 0 else np.full((N, 1), np.inf)
+        out &= dev > kth
+    block = np.where(out, mu, W)
+    ng = K // 128
+    gsd = np.maximum(block.reshape(N, ng, 128).std(axis=2), 1e-8)          # [N, ng]
+    lo, hi = np.log(gsd.min()), np.log(gsd.max())
+    scales = np.exp(np.linspace(lo, hi, L)) if L > 1 else np.exp(np.array([(lo + hi) / 2]))
+    # the 16 quantiles (t + 1/2) / 16 of a standard normal, by bisection on erf
+    z = np.empty(16)
+    for t in range(16):
+        p, a, b = (t + 0.5) / 16.0, -8.0, 8.0
+        for _ in range(80):
+            m = (a + b) / 2
+            a, b = (m, b) if 0.5 * (1 + erf(m / sqrt(2))) < p else (a, m)
+        z[t] = (a + b) / 2
+    lib = (scales[:, None] * z[None, :]).astype(np.float16)                  # [L, 16], ascending
+    libid = np.abs(np.log(gsd)[:, :, None] - np.log(scales)[None, None, :]).argmin(axis=2).astype(np.uint8)
+    ent = lib.astype(np.float64)[libid]                                      # [N, ng, 16]
+    mid = (ent[:, :, 1:] + ent[:, :, :-1]) / 2.0
+    idx = np.empty((N, K), np.uint8)
+    for n0 in range(0, N, 1024):
+        sl = slice(n0, min(N, n0 + 1024))
+        bl = block[sl].reshape(-1, ng, 128)
+        idx[sl] = (bl[:, :, :, None] > mid[sl][:, :, None, :]).sum(axis=3).astype(np.uint8).reshape(-1, K)
+    rows, cols = np.nonzero(out)
+    resid = W[rows, cols] - ent[rows, cols // 128, idx[rows, cols]]
+    row_ptr = np.zeros(N + 1, np.int32)
+    np.add.at(row_ptr, rows + 1, 1)
+    row_ptr = np.cumsum(row_ptr).astype(np.int32)
+    return {"idx": idx, "lib": np.ascontiguousarray(lib).view(np.uint16), "libid": libid,
+            "row_ptr": row_ptr, "col_idx": cols.astype(np.int32), "val": resid.astype(np.float16).view(np.uint16)}
