@@ -42,8 +42,8 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, no fast-math, no FMA contraction)."""
     os.makedirs(_BUILD_DIR, exist_ok=True)
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH   # built from the current source
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
            "-fno-fast-math", "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"]
@@ -60,8 +60,7 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB_PATH):
-            build(force=False)
+        build(force=False)    # (only when missing or older than the source)
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         I = ctypes.c_int
