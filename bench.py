@@ -269,29 +269,51 @@ def xfp_main(args, torch, w4, synth, dev, layer, M):
     d = synth.make_layer(layer, M, seed=args.seed, r=0)
     N, K, act = d["N"], d["K"], d["act"]
     tdt = torch.float16 if act == "fp16" else torch.bfloat16
-    x = synth.make_xfp(synth.plant_outliers(d["W"], seed=args.seed))
+    L = args.xfp_lib
+    W = synth.plant_outliers(d["W"], seed=args.seed)
+    if L:
+        # shared-library mode: channels of different spreads (so that the
+        # groups name many of the L entries)
+        W = W * np.exp(np.random.default_rng(args.seed + 1).normal(0.0, 0.5, (N, 1))).astype(np.float32)
+        x = synth.make_xfp_lib(W, L=L)
+    else:
+        x = synth.make_xfp(W)
     idx = x["idx"]
     qc = torch.from_numpy((idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8)).to(dev)
     packed0 = w4.w4ec_pack_xfp(qc, N, K)
     del qc
     nnz = int(x["row_ptr"][-1])
-    cb0 = torch.from_numpy(x["cb"].view(np.int16)).view(torch.float16).to(dev)
+    if L:
+        cb0 = torch.from_numpy(x["lib"].view(np.int16)).view(torch.float16).to(dev)
+        id0 = torch.from_numpy(x["libid"]).to(dev)
+        table_bytes = L * 32 + N * (K // 128)
+    else:
+        cb0 = torch.from_numpy(x["cb"].view(np.int16)).view(torch.float16).to(dev)
+        id0 = None
+        table_bytes = N * 32
     rp0 = torch.from_numpy(x["row_ptr"]).to(dev)
     ci0 = torch.from_numpy(x["col_idx"]).to(dev)
     val0 = torch.from_numpy(x["val"].view(np.int16)).view(torch.float16).to(dev)
-    # algorithmic bytes: indices, codebooks, the residual (row pointers,
-    # columns, values), X and Y
-    nbytes = N * K // 2 + N * 32 + (N + 1) * 4 + nnz * 6 + M * K * 2 + M * N * 2
-    weight_bytes = packed0.numel() + N * 32 + (N + 1) * 4 + nnz * 6
+    # algorithmic bytes: indices, codebooks (per channel; or the library and
+    # the groups' entry ids), the residual (row pointers, columns, values), X and Y
+    nbytes = N * K // 2 + table_bytes + (N + 1) * 4 + nnz * 6 + M * K * 2 + M * N * 2
+    weight_bytes = packed0.numel() + table_bytes + (N + 1) * 4 + nnz * 6
     R = max(1, -(-2 * MALL_BYTES // weight_bytes))
-    copies = [(packed0, cb0, rp0, ci0, val0)] + [
-        (packed0.clone(), cb0.clone(), rp0.clone(), ci0.clone(), val0.clone()) for _ in range(R - 1)]
+
+    def clone(t):
+        return None if t is None else t.clone()
+
+    copies = [(packed0, cb0, id0, rp0, ci0, val0)] + [
+        (packed0.clone(), cb0.clone(), clone(id0), rp0.clone(), ci0.clone(), val0.clone()) for _ in range(R - 1)]
     X = torch.from_numpy(np.ascontiguousarray(d["X"]).view(np.int16)).view(tdt).to(dev)
     Y = torch.empty((M, N), dtype=tdt, device=dev)
 
     def step(i):
-        p, cb, rp, ci, val = copies[i % R]
-        w4.w4ec_linear_decode_xfp(X, p, cb, rp, ci, val, N=N, Y=Y)
+        p, cb, lid, rp, ci, val = copies[i % R]
+        if L:
+            w4.w4ec_linear_decode_xfp_lib(X, p, cb, lid, rp, ci, val, N=N, Y=Y)
+        else:
+            w4.w4ec_linear_decode_xfp(X, p, cb, rp, ci, val, N=N, Y=Y)
 
     for i in range(args.warmup):
         step(i)
@@ -326,8 +348,8 @@ def xfp_main(args, torch, w4, synth, dev, layer, M):
     achieved = nbytes / kdur / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profiles(f"decode_kernel/{args.workload}/xfp"),
-            "kernel": "decode_kernel (codebook)", "kernel_us": round(kdur * 1e6, 3)}
+            "traffic": traffic_from_profiles(f"decode_kernel/{args.workload}/xfp" + (f"_lib{L}" if L else "")),
+            "kernel": "decode_kernel (codebook" + (", shared library)" if L else ")"), "kernel_us": round(kdur * 1e6, 3)}
     flops = 2 * M * N * K + 2 * M * nnz
     out = {
         "metric": "W4+EC linear: decode HBM GB/s & prefill TFLOP/s, % of MI355X roofline",
@@ -335,7 +357,8 @@ def xfp_main(args, torch, w4, synth, dev, layer, M):
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": act, "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "act": act, "phase": "decode",
-                   "method": "xfp", "residual_entries": nnz, "weight_copies": R,
+                   "method": "xfp", **({"library_entries": L} if L else {}), "residual_entries": nnz,
+                   "weight_copies": R,
                    "launch": "hipgraph" if graph is not None else "eager",
                    "bytes_per_step": nbytes, "flops_per_step": flops},
         "roofline": roof,
@@ -413,6 +436,9 @@ def main():
     ap.add_argument("--stream-read", action="store_true",
                     help="only time the library's streaming-read reference kernel over the workload's "
                          "algorithmic bytes (the attainable HBM read time for that byte count)")
+    ap.add_argument("--xfp-lib", type=int, default=0, metavar="L",
+                    help="with --method xfp: the shared-library mode with L codebooks (1..32) instead of "
+                         "per-channel codebooks")
     ap.add_argument("--lut", action="store_true",
                     help="prefill latency table: time the three paths over a grid of (M, r, N, K) and print "
                          "one JSON line per point (no roofline / CPU legs)")

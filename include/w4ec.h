@@ -335,6 +335,35 @@ int w4ec_linear_decode_xfp(const void* X, const void* packed, const uint16_t* co
                            const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* val,
                            int nnz, void* Y, int M, int N, int K, int act_dtype, void* stream);
 
+/* Codebook weights from a shared library (XFP summary, section 2,
+ * "adaptive learned codebooks", shared-library mode): the layer keeps L
+ * codebooks of 16 fp16 entries, and each group of 128 consecutive weights of
+ * an output channel (along K) names the entry it uses; the sparse fp16
+ * outlier residual is as in w4ec_linear_decode_xfp:
+ *
+ *   Wh[n,k] = library[libid[n][k / 128]][idx[n,k]] + (sum of val[e] over the
+ *             entries e of row n with col_idx[e] == k)
+ *   Y[m,n]  = sum_k X[m,k] Wh[n,k]
+ *
+ *   X        device act [M, K], 16-byte aligned; 1 <= M <= 16
+ *   packed   device blob from w4ec_pack_xfp of the 4-bit indices idx
+ *   library  device fp16 [L][16], 16-byte aligned, 1 <= L <= W4EC_XFP_LIB_MAX;
+ *            with bf16 activations each entry is rounded to bf16 before it
+ *            is multiplied
+ *   libid    device uint8 [N][K/128], each group's entry (one past the
+ *            library is clamped to entry L - 1; the result is then undefined)
+ *   row_ptr, col_idx, val, nnz, Y as w4ec_linear_decode_xfp.
+ * The workgroups hold the whole library's pair tables in LDS (32 KB for 32
+ * entries) instead of one table per output channel.  K must be a multiple
+ * of 128.  No workspace.  Returns W4EC_ERR_UNSUPPORTED for M > 16 or
+ * L > W4EC_XFP_LIB_MAX; W4EC_ERR_INVALID_ARG for L < 1, missing or
+ * misaligned pointers and Y aliasing an input.  Asynchronous on stream. */
+#define W4EC_XFP_LIB_MAX 32
+int w4ec_linear_decode_xfp_lib(const void* X, const void* packed, const uint16_t* library, int L,
+                               const uint8_t* libid, const int32_t* row_ptr, const int32_t* col_idx,
+                               const uint16_t* val, int nnz, void* Y, int M, int N, int K, int act_dtype,
+                               void* stream);
+
 /* Streaming-read reference (a measurement hook, not part of the layer):
  * reads `bytes` from `src` with the plainest access pattern the library
  * knows for HBM -- 512 workgroups of 256 threads, workgroup w reading the

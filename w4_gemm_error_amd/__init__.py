@@ -28,7 +28,7 @@ __all__ = [
     "w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate",
     "w4ec_prefill_ec_workspace_bytes", "w4ec_prefill_ec_gate", "w4ec_prefill_ec_apply",
     "w4ec_linear_decode_serq", "w4ec_linear_prefill_serq",
-    "w4ec_pack_xfp", "w4ec_linear_decode_xfp",
+    "w4ec_pack_xfp", "w4ec_linear_decode_xfp", "w4ec_linear_decode_xfp_lib", "W4EC_XFP_LIB_MAX",
     "w4ec_stream_read",
     "PackedLayer",
 ]
@@ -112,6 +112,8 @@ def lib() -> ctypes.CDLL:
         L.w4ec_pack_xfp.restype = I
         L.w4ec_linear_decode_xfp.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, P]
         L.w4ec_linear_decode_xfp.restype = I
+        L.w4ec_linear_decode_xfp_lib.argtypes = [P, P, P, I, P, P, P, P, I, P, I, I, I, I, P]
+        L.w4ec_linear_decode_xfp_lib.restype = I
         for name in ("w4ec_linear_decode_vgate", "w4ec_linear_prefill_vgate"):
             fn = getattr(L, name)
             fn.argtypes = [P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, P, Z, P]
@@ -405,6 +407,40 @@ def w4ec_linear_decode_xfp(X, packed, codebook, row_ptr, col_idx, val, *, N, Y=N
                                       _ptr(col_idx) if nnz else None, _ptr(val) if nnz else None, nnz,
                                       _ptr(Y), M, N, K, _act_code(act), _stream_handle(stream))
     _check(st, "w4ec_linear_decode_xfp")
+    return Y
+
+
+W4EC_XFP_LIB_MAX = 32
+
+
+def w4ec_linear_decode_xfp_lib(X, packed, library, libid, row_ptr, col_idx, val, *, N, Y=None, stream=None):
+    """Y = X Wh^T with Wh[n,k] = library[libid[n, k // 128]][idx[n,k]] plus the
+    sparse residual, 1 <= M <= 16.  packed: the indices packed by
+    w4ec_pack_xfp; library fp16 [L, 16] (1 <= L <= 32); libid uint8 [N, K/128];
+    row_ptr int32 [N + 1]; col_idx int32 [nnz]; val fp16 [nnz]."""
+    torch = _torch()
+    _need_cuda(X, "X", (torch.float16, torch.bfloat16))
+    act = X.dtype
+    M, K = X.shape
+    _need_cuda(packed, "packed", torch.uint8)
+    _need_cuda(library, "library", torch.float16)
+    _need_cuda(libid, "libid", torch.uint8)
+    _need_cuda(row_ptr, "row_ptr", torch.int32)
+    _need_cuda(col_idx, "col_idx", torch.int32)
+    _need_cuda(val, "val", torch.float16)
+    L = int(library.shape[0])
+    if library.dim() != 2 or library.shape[1] != 16 or libid.shape != (N, K // 128) or row_ptr.shape != (N + 1,):
+        raise ValueError("library must be [L, 16], libid [N, K/128] and row_ptr [N + 1]")
+    nnz = 0 if col_idx is None else int(col_idx.numel())
+    if (val is None and nnz) or (val is not None and int(val.numel()) != nnz):
+        raise ValueError("col_idx and val must have the same length")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=act, device=X.device)
+    _need_cuda(Y, "Y", act)
+    st = lib().w4ec_linear_decode_xfp_lib(_ptr(X), _ptr(packed), _ptr(library), L, _ptr(libid), _ptr(row_ptr),
+                                          _ptr(col_idx) if nnz else None, _ptr(val) if nnz else None, nnz,
+                                          _ptr(Y), M, N, K, _act_code(act), _stream_handle(stream))
+    _check(st, "w4ec_linear_decode_xfp_lib")
     return Y
 
 

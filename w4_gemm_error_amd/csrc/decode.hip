@@ -74,12 +74,18 @@ struct DecodeKArgs {
     const int32_t* S;    // salient-channel correction: T = X[:, S] (no EC role), or null
     // codebook weights (codebook kernels only): per-channel codebooks of 16
     // fp16 entries and the sparse outlier residual in compressed rows
-    const uint16_t* cb;      // [N][16]
+    const uint16_t* cb;      // [N][16] (per channel), or the library [L][16]
     const int32_t* row_ptr;  // [N + 1]
     const int32_t* col_idx;  // [nnz]
     const uint16_t* val;     // [nnz] fp16
     int nnz;
+    const uint8_t* libid;    // library mode: [N][K / 128] each group's entry
+    int L;                   // library mode: entries (1 .. CBK_LIB_MAX)
 };
+
+// Codebook modes of the decode main role (template parameter CBK)
+constexpr int CBK_NONE = 0, CBK_CHANNEL = 1, CBK_LIBRARY = 2;
+constexpr int CBK_LIB_MAX = W4EC_XFP_LIB_MAX;   // library entries a workgroup's tables hold
 
 // Codebook lookup of one dword of indices (natural order: byte j holds the
 // indices of k = 2j and 2j + 1): t points at the column's entry 0 of a pair
@@ -87,11 +93,15 @@ struct DecodeKArgs {
 // so that each byte of w selects one MFMA operand dword.  A column's
 // entries sit in 4 of the 64 banks, so only the 4 lanes that read the same
 // column's table can conflict.
+template <int STRIDE = PANEL_N>
 __device__ inline u32x4 cb_lookup(uint32_t w, const uint32_t* t)
 {
-    return (u32x4){t[(w & 0xFFu) * PANEL_N], t[((w >> 8) & 0xFFu) * PANEL_N], t[((w >> 16) & 0xFFu) * PANEL_N],
-                   t[(w >> 24) * PANEL_N]};
+    return (u32x4){t[(w & 0xFFu) * STRIDE], t[((w >> 8) & 0xFFu) * STRIDE], t[((w >> 16) & 0xFFu) * STRIDE],
+                   t[(w >> 24) * STRIDE]};
 }
+// Library mode: the tables of all the library's entries are laid out
+// [entry][256] (t = the group's entry's table, stride 1), so that a read's
+// bank follows the index byte alone: many lanes may name one entry.
 
 // eight fp16 values -> bf16 (round to nearest even)
 __device__ inline u32x4 f16x8_to_bf16x8(u32x4 v)
@@ -504,7 +514,7 @@ __host__ __device__ inline size_t main_frac_offset(int M, int K, bool xlds, int 
     return (b + 15) / 16 * 16;
 }
 
-template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, int CBK = CBK_NONE>
 __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* smem)
 {
     const int tid = threadIdx.x;
@@ -547,6 +557,12 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
         const int n = min(n_l[j], a.Npad - 1);
         szp[j] = a.sz + (size_t)((kbeg * PANEL_K) / a.G) * a.Npad + n;
     }
+    const uint8_t* idp[CB];     // library mode: column n_l[j]'s group entries, from panel kbeg
+    if constexpr (CBK == CBK_LIBRARY) {
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+            idp[j] = a.libid + (size_t)min(n_l[j], a.N - 1) * KB + kbeg;
+    }
 
     // Loads retire in issue order, so everything consumed before the first
     // panel (scale/zero, the activations staged in LDS) is issued first;
@@ -570,6 +586,7 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     u32x4 wring[DEPTH][CB];
     u32x4 xring[XLDS ? 1 : DEPTH][4];
     uint32_t szring[GROUPED ? DEPTH : 1][CB];
+    uint32_t idring[CBK == CBK_LIBRARY ? DEPTH : 1][CB];   // library mode: the panels' group entries
     uint32_t sz0[CB];
 #pragma unroll
     for (int j = 0; j < CB; ++j)
@@ -618,18 +635,24 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     int rb0 = 0, rb1 = 0;
     int rk[RB];
     uint32_t rv[RB];
+    u32x4 libv = (u32x4){0u, 0u, 0u, 0u};            // library mode: 16 bytes of the library
     if constexpr (CBK) {
         {
             const int n = min(cb0 * PANEL_N + rc, a.N - 1);
             rb0 = a.row_ptr[n];
             rb1 = a.row_ptr[n + 1];
         }
+        if constexpr (CBK == CBK_LIBRARY) {
+            if (tid < 2 * a.L)
+                libv = ld16(a.cb + (size_t)tid * 8);
+        } else {
 #pragma unroll
-        for (int j = 0; j < CB; ++j) {
-            const int n = min((cb0 + j) * PANEL_N + (tid & 15), a.N - 1);
-            cbv[j][0] = ld16(a.cb + (size_t)n * 16);
-            cbv[j][1] = ld16(a.cb + (size_t)n * 16 + 8);
-            cblo[j] = a.cb[(size_t)n * 16 + (tid >> 4)];
+            for (int j = 0; j < CB; ++j) {
+                const int n = min((cb0 + j) * PANEL_N + (tid & 15), a.N - 1);
+                cbv[j][0] = ld16(a.cb + (size_t)n * 16);
+                cbv[j][1] = ld16(a.cb + (size_t)n * 16 + 8);
+                cblo[j] = a.cb[(size_t)n * 16 + (tid >> 4)];
+            }
         }
     }
     u32x4 bstage[2 * CB];
@@ -662,6 +685,11 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     const uint16_t* xg = a.X + (size_t)(xrow ? row : 0) * K + (size_t)kbeg * PANEL_K + koff;
     auto issue = [&](int u, int i) {                 // panel i (clamped) into ring slot u
         const int ic = min(i, klast);
+        if constexpr (CBK == CBK_LIBRARY) {
+#pragma unroll
+            for (int j = 0; j < CB; ++j)
+                idring[u][j] = idp[j][ic];
+        }
         if constexpr (GROUPED) {
             const int gi = ((kbeg + ic) * PANEL_K) / a.G - (kbeg * PANEL_K) / a.G;
 #pragma unroll
@@ -723,7 +751,20 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
         if (lds_gather)
             gather_lds();
     }
-    if constexpr (CBK) {
+    if constexpr (CBK == CBK_LIBRARY) {
+        // the library, staged in LDS past the tables (rounded to bf16 for
+        // bf16 activations), then every entry's table: thread tid writes
+        // entry byte tid of each, cb[tid & 15] | cb[tid >> 4] << 16
+        static_assert(DEC_THREADS == 256, "one table entry per thread and library entry");
+        uint16_t* libl = reinterpret_cast<uint16_t*>(ptab + CBK_LIB_MAX * 256);
+        if (tid < 2 * a.L)
+            st16(libl + tid * 8, ACT == ACT_BF16 ? f16x8_to_bf16x8(libv) : libv);
+        lds_barrier();
+#pragma unroll 4
+        for (int e = 0; e < a.L; ++e)
+            ptab[e * 256 + tid] = (uint32_t)libl[e * 16 + (tid & 15)] | ((uint32_t)libl[e * 16 + (tid >> 4)] << 16);
+        lds_barrier();
+    } else if constexpr (CBK) {
         static_assert(DEC_THREADS == 256, "sixteen pair-table entries per thread and block");
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
@@ -741,6 +782,8 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
                 tj[256 * i] = lo | ((i & 1) ? (e[i >> 1] & 0xFFFF0000u) : (e[i >> 1] << 16));
         }
         lds_barrier();
+    }
+    if constexpr (CBK) {
         // row bounds clamped to [0, nnz] (an absent column has none), then
         // the first batch (indices clamped into the arrays, which the host
         // makes non-empty; entries past the row are discarded)
@@ -864,6 +907,13 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
                 for (int j = 0; j < CB; ++j)
                     szv[j] = szring[u][j];
             }
+            uint32_t tl[CB];                            // library mode: the panel's entries' tables
+            if constexpr (CBK == CBK_LIBRARY) {
+                // (an entry past the library is clamped to its last)
+#pragma unroll
+                for (int j = 0; j < CB; ++j)
+                    tl[j] = min(idring[u][j], (uint32_t)(a.L - 1)) << 8;
+            }
             if constexpr (XLDS) {
                 const int ic = min(i, klast);
 #pragma unroll
@@ -904,7 +954,9 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     u32x4 bq;
-                    if constexpr (CBK)
+                    if constexpr (CBK == CBK_LIBRARY)
+                        bq = cb_lookup<1>(ws[s], ptab + tl[j]);
+                    else if constexpr (CBK)
                         bq = cb_lookup(ws[s], ptab + j * 256 * PANEL_N + (l & 15));
                     else if constexpr (BIAS)
                         bq = ACT == ACT_F16 ? dequant_f16_biased(ws[s]) : bf16_biased(ws[s]);
@@ -932,7 +984,7 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
     // into rpart[rsub][m][rc] past the pair tables; the prefetched batch,
     // then any further ones.  Added to the outputs in the final reduction,
     // in a fixed order.
-    float* rpart = reinterpret_cast<float*>(ptab + CB * 256 * PANEL_N);
+    float* rpart = reinterpret_cast<float*>(ptab + (CBK == CBK_LIBRARY ? CBK_LIB_MAX * 256 + 256 : CB * 256 * PANEL_N));
     if constexpr (CBK) {
         auto add_batch = [&](const int* kk, const uint32_t* vb, int eb, bool first) {
             int k[RB];
@@ -1201,13 +1253,13 @@ __device__ __forceinline__ void decode_main_role(const DecodeKArgs& a, uint8_t* 
 // Two column blocks per workgroup (activations staged in LDS): the grid
 // holds ~450 workgroups, which fit the CUs in one round at two wavefronts
 // per SIMD, i.e. within 256 registers.
-template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, int CBK = CBK_NONE>
 __global__ __launch_bounds__(DEC_THREADS, 2)
 void decode_kernel(DecodeKArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t dsmem[];
     if constexpr (CBK) {
-        decode_main_role<ACT, CB, XCH, DEPTH, false, false, true>(a, dsmem);   // no EC role
+        decode_main_role<ACT, CB, XCH, DEPTH, false, false, CBK>(a, dsmem);   // no EC role
     } else {
         if ((int)blockIdx.x < a.P)
             decode_ec_role<ACT>(a, dsmem);
@@ -1242,11 +1294,14 @@ static size_t ec_lds_bytes(const DecodePlan& p, int M, int r)
     return (std::max(at, std::max(fin, vg)) + 15) / 16 * 16;
 }
 
-template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, bool CBK = false>
+template <int ACT, int CB, int XCH, int DEPTH, bool GROUPED, bool STAGE_FIRST, int CBK = CBK_NONE>
 static hipError_t launch_decode_t(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     auto kern = decode_kernel<ACT, CB, XCH, DEPTH, GROUPED, STAGE_FIRST, CBK>;
-    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr) + (CBK ? (size_t)CB * PANEL_N * 256 * 4 + (size_t)DEC_THREADS * k.M * 4 : 0),
+    // codebook tables (per channel [CB][256][16], or the library's
+    // [CBK_LIB_MAX][256] and the staged library) and the residual's sums
+    const size_t tables = CBK == CBK_LIBRARY ? (size_t)CBK_LIB_MAX * 256 * 4 + 1024 : (size_t)CB * PANEL_N * 256 * 4;
+    const size_t lds = std::max(main_lds_bytes(p, k.M, k.K, k.r, k.S != nullptr) + (CBK ? tables + (size_t)DEC_THREADS * k.M * 4 : 0),
                                 ec_lds_bytes(p, k.M, k.r));
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1284,18 +1339,29 @@ static hipError_t launch_decode_act(const DecodeKArgs& k, const DecodePlan& p, h
     return launch_decode_grp<ACT, false, false>(k, p, st);
 }
 
-template <int ACT>
+template <int ACT, int MODE>
 static hipError_t launch_decode_xfp_act(const DecodeKArgs& k, const DecodePlan& p, hipStream_t st)
 {
     if (p.xlds) {
         const size_t xch = ((size_t)k.M * k.K / 8 + DEC_THREADS - 1) / DEC_THREADS;
         if (xch <= 2)
-            return launch_decode_t<ACT, 2, 2, 8, false, false, true>(k, p, st);
-        return launch_decode_t<ACT, 2, DEC_XLDS_CHUNKS, 8, false, false, true>(k, p, st);
+            return launch_decode_t<ACT, 2, 2, 8, false, false, MODE>(k, p, st);
+        return launch_decode_t<ACT, 2, DEC_XLDS_CHUNKS, 8, false, false, MODE>(k, p, st);
     }
     if (p.CB == 1)
-        return launch_decode_t<ACT, 1, 0, 4, false, false, true>(k, p, st);
-    return launch_decode_t<ACT, 4, 0, 2, false, false, true>(k, p, st);
+        return launch_decode_t<ACT, 1, 0, 4, false, false, MODE>(k, p, st);
+    if constexpr (MODE == CBK_LIBRARY) {
+        // the panels' entry ids take the registers of two more column blocks:
+        // two blocks per workgroup, a ring of four steps
+        DecodePlan q = p;
+        q.CB = 2;
+        q.n_main = (k.NB + 1) / 2;
+        DecodeKArgs kq = k;
+        kq.n_main = q.n_main;
+        return launch_decode_t<ACT, 2, 0, 4, false, false, MODE>(kq, q, st);
+    } else {
+        return launch_decode_t<ACT, 4, 0, 2, false, false, MODE>(k, p, st);
+    }
 }
 
 // Codebook weights with a sparse outlier residual: the main role alone (no
@@ -1313,15 +1379,21 @@ hipError_t launch_decode_xfp(const XfpArgs& x, const DecodePlan& p, hipStream_t 
     k.P = 0; k.KS = 0; k.RC = 1; k.n_main = p.n_main;
     k.stage_first = 0;
     k.cb = x.cb; k.row_ptr = x.row_ptr; k.col_idx = x.col_idx; k.val = x.val; k.nnz = x.nnz;
+    k.libid = x.libid; k.L = x.L;
     if (x.nnz == 0) {
         // the kernel loads entry 0 unconditionally (and discards it): point
         // the empty arrays at the row pointers, which always exist
         k.col_idx = x.row_ptr;
         k.val = reinterpret_cast<const uint16_t*>(x.row_ptr);
     }
+    if (x.libid) {
+        if (x.act == ACT_F16)
+            return launch_decode_xfp_act<ACT_F16, CBK_LIBRARY>(k, p, st);
+        return launch_decode_xfp_act<ACT_BF16, CBK_LIBRARY>(k, p, st);
+    }
     if (x.act == ACT_F16)
-        return launch_decode_xfp_act<ACT_F16>(k, p, st);
-    return launch_decode_xfp_act<ACT_BF16>(k, p, st);
+        return launch_decode_xfp_act<ACT_F16, CBK_CHANNEL>(k, p, st);
+    return launch_decode_xfp_act<ACT_BF16, CBK_CHANNEL>(k, p, st);
 }
 
 hipError_t launch_decode(const LayerArgs& a, const DecodePlan& p, hipStream_t st)

@@ -64,6 +64,10 @@ struct XfpArgs {
     int nnz;
     void* Y;
     int M, N, K, act;
+    // shared-library mode (libid non-null): cb is the library [L][16] and
+    // libid [N][K / 128] names each group's entry
+    const uint8_t* libid = nullptr;
+    int L = 0;
 };
 hipError_t launch_decode_xfp(const XfpArgs& x, const DecodePlan& p, hipStream_t st);
 hipError_t launch_prefill_ec_apply(const ApplyArgs& a, const PrefillPlan& p, hipStream_t st);
