@@ -78,10 +78,13 @@ DecodePlan make_decode_plan(int M, int N, int K, int r)
     }
     p.xlds = decode_use_xlds(M, K);
     // column blocks per workgroup: two when X is staged in LDS (X staged once
-    // for twice the weights); one for a few tokens with a long K; four for
-    // more tokens, so that each activation fragment loaded from L2 feeds
-    // four blocks' MFMAs
-    p.CB = p.xlds ? 2 : (M <= 4 ? 1 : 4);
+    // for twice the weights); one for a few tokens with a long K; for more
+    // tokens four, so that each activation fragment loaded from L2 feeds
+    // four blocks' MFMAs -- unless that leaves too few workgroups: below 512
+    // column blocks (N < 8192) two (N = 4096, 12 tokens, K = 14336, G = 128:
+    // 27.8 -> 22.6 us; 8 tokens at K = 4096: 10.1 -> 9.5 us; from N = 8192
+    // on, four measured faster)
+    p.CB = p.xlds ? 2 : (M <= 4 ? 1 : (NB >= 512 ? 4 : 2));
     p.n_main = (NB + p.CB - 1) / p.CB;
     // X is staged after the weight ring is issued, also with an EC: since the
     // EC reduction runs on few reducers its chain no longer gains from

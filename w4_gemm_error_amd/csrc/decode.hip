@@ -1324,6 +1324,8 @@ static hipError_t launch_decode_grp(const DecodeKArgs& k, const DecodePlan& p, h
             return launch_decode_t<ACT, 2, 2, 8, GROUPED, STAGE_FIRST>(k, p, st);
         return launch_decode_t<ACT, 2, DEC_XLDS_CHUNKS, 8, GROUPED, STAGE_FIRST>(k, p, st);
     }
+    if (p.CB == 2)
+        return launch_decode_t<ACT, 2, 0, 4, GROUPED, false>(k, p, st);
     if (p.CB == 1)
         return launch_decode_t<ACT, 1, 0, 4, GROUPED, false>(k, p, st);
     // four column blocks: a ring of two steps keeps the registers at two waves per SIMD
@@ -1350,6 +1352,8 @@ static hipError_t launch_decode_xfp_act(const DecodeKArgs& k, const DecodePlan& 
     }
     if (p.CB == 1)
         return launch_decode_t<ACT, 1, 0, 4, false, false, MODE>(k, p, st);
+    if (p.CB == 2)
+        return launch_decode_t<ACT, 2, 0, 4, false, false, MODE>(k, p, st);
     if constexpr (MODE == CBK_LIBRARY) {
         // the panels' entry ids take the registers of two more column blocks:
         // two blocks per workgroup, a ring of four steps
