@@ -103,3 +103,30 @@ def test_out_of_range_zero_point_gives_nan(phase, act, G):
     good = [n for n in range(d["N"]) if n not in (bad_col, 20)]
     ref = oracle_layer(d, (qc, s, z), r=0)
     assert_close(Y[:, good], ref[:, good], act, "columns with valid zero points")
+
+
+@pytest.mark.parametrize("act,M,N,K,r", [
+    ("fp16", 200, 528, 640, 16),       # 64-token tiles, K in one piece
+    ("bf16", 100, 528, 512, 40),
+    ("fp16", 96, 512, 4096, 64),       # 64-token tiles, K split in eight
+    ("bf16", 1280, 2048, 1024, 32),    # 128-token tiles, K split in two
+])
+def test_zero_scale_columns_prefill(act, M, N, K, r):
+    """A zero scale (a constant weight row, or a quantizer's choice) in a few
+    columns: those weights are zero and the correction still applies, so
+    those output columns hold the gated rank-r term alone.  Per-channel
+    prefill tiles in one piece and split in K, 64- and 128-token tiles."""
+    _print(f"zero scales prefill {act} M={M} N={N} K={K} r={r}")
+    cfg = synth.LAYERS["mlp_70b_bf16"] if act == "bf16" else synth.LAYERS["tiny"]
+    d = synth.make_layer(cfg, M, seed=17, N=N, K=K, r=r, group_size=K)
+    qc, s, z = oracle.rtn_quantize(d["W"], K)
+    s = s.copy()
+    s[[5, 300, N - 1], :] = 0                  # tiles 0 and 1 and the last one
+    packed = pack_host(qc, s, z, N, K, K)
+    Y = gpu_layer(d, packed, "prefill", r=r)
+    rows = sample_rows(M)
+    ref = oracle_layer(d, (qc, s, z), r=r, rows=rows)
+    Ys = Y if rows is None else Y[rows]
+    assert_close(Ys, ref, act, f"zero scales {act} M={M}")
+    # the zero-scale columns hold the correction alone
+    assert np.abs(synth.act_bits_to_f64(Ys, act)[:, [5, 300, N - 1]]).max() > 0

@@ -479,7 +479,7 @@ __device__ inline void work_of(int mt, int nt, int ksplit, int& tm, int& tn, int
     const int wi = (W & 7) == 0 ? (bid & 7) * (W >> 3) + (bid >> 3) : bid;
     kz = wi / T;
     const int t = wi - kz * T;
-    const int GM = 4;  // M tiles per raster group
+    const int GM = 8;  // M tiles per raster group (2, 4, 16 measured slower at 4096 tokens)
     const int group = t / (GM * nt);
     const int first = group * GM;
     const int gm = min(GM, mt - first);
@@ -719,10 +719,142 @@ constexpr int gemm_lds_bytes()
 // rank-r correction, and the store.  NWV wavefronts, each owning 16 / NWV
 // column blocks of the 256-column tile for all BM rows; `smem` is an LDS
 // region of LDSB bytes that the main loop no longer uses.
+// The gated rank-r correction as r more terms of a tile's reduction:
+// acc += T_g[m0, m0 + BM) B[:, n0, n0 + 256).  The rank dimension goes in
+// chunks of RCH ranks, as many as the LDS region of LDSB bytes holds: B rows
+// padded to 272 halves, so that their transpose read is free of bank
+// conflicts, T_g rows to RCH + 8.  load() sends the loads of 128 ranks (NCH
+// chunks) out together into registers; apply() parks each chunk in LDS and
+// reads it back as MFMA operands (loading ranks past 128 itself).  `fused`:
+// T_g was written during this kernel, so it is read past this XCD's L2.
+template <int ACT, int BM, int NWV, int LDSB>
+struct GemmEc {
+    static constexpr int GEMM_THREADS = 64 * NWV;
+    static constexpr int JW = 16 / NWV;
+    static constexpr int RB = BM / 16;
+    static constexpr int BP = PF_BN + 16;               // halves per LDS row of B
+    static constexpr int RCH = 128 * BP * 2 + BM * 136 * 2 <= LDSB ? 128 : 64 * BP * 2 + BM * 72 * 2 <= LDSB ? 64 : 32;
+    static constexpr int TP = RCH + 8;                  // halves per LDS row of T_g
+    static constexpr int BCH = RCH * (PF_BN / 8) / GEMM_THREADS;      // 16-byte B chunks per thread
+    static constexpr int TCH = (BM * (RCH / 8) + GEMM_THREADS - 1) / GEMM_THREADS;
+    static constexpr int NCH = 128 / RCH;               // chunks loaded together
+    static_assert(RCH * BP * 2 + BM * TP * 2 <= LDSB, "EC staging fits the LDS");
+    u32x4 bva[NCH][BCH], tva[NCH][TCH];
+
+    // chunk [c0, c0 + RCH) of B's rows for the tile's 256 columns and of
+    // T_g's columns for its BM tokens (zero past r and past r_pad, where
+    // nothing is loaded)
+    __device__ __forceinline__ void load_chunk(const GemmKArgs& a, int c0, int m0, int n0, bool fused,
+                                               u32x4 (&bv)[BCH], u32x4 (&tv)[TCH])
+    {
+        const int tid = threadIdx.x;
+        const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int ch = tid + GEMM_THREADS * i;
+            const int jr = c0 + (ch >> 5), n = n0 + 8 * (ch & 31);
+            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+            if (jr < a.r) {
+                const uint16_t* src = a.B + (size_t)jr * a.N + n;
+                if (bvec && n + 8 <= a.N) {
+                    v = ld16(src);
+                } else {
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        hv[t] = n + t < a.N ? (uint32_t)src[t] : 0u;
+                    v = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
+                                hv[6] | (hv[7] << 16)};
+                }
+            }
+            bv[i] = v;
+        }
+        if (fused) {
+            const __amdgpu_buffer_rsrc_t tgs = dev_rsrc(a.tg, (uint32_t)((size_t)a.Mpad * a.r_pad * 2));
+#pragma unroll
+            for (int i = 0; i < TCH; ++i) {
+                const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
+                const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                tv[i] = c0 + 8 * cc < a.r_pad ? __builtin_bit_cast(u32x4, ld16_sc1(tgs, (uint32_t)(((size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc) * 2)))
+                                              : (u32x4){0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < TCH; ++i) {
+                const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
+                const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
+                                              : (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    }
+
+    // ranks [g0, g0 + 128)
+    __device__ __forceinline__ void load(const GemmKArgs& a, int g0, int m0, int n0, bool fused)
+    {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            load_chunk(a, g0 + c * RCH, m0, n0, fused, bva[c], tva[c]);
+    }
+
+    // after load(a, 0, ...): every rank into acc (LDSB bytes of LDS at smem
+    // free for it; a barrier ends each chunk)
+    __device__ __forceinline__ void apply(const GemmKArgs& a, floatx4 (&acc)[RB][JW], int m0, int n0, uint8_t* smem,
+                                          bool fused)
+    {
+        const int tid = threadIdx.x;
+        const int l = tid & 63;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        uint16_t* bl = reinterpret_cast<uint16_t*>(smem);
+        uint16_t* tl = bl + RCH * BP;
+        const int koff = 8 * (l >> 4);
+        for (int g0 = 0; g0 < a.r_pad; g0 += NCH * RCH) {
+            if (g0 > 0)
+                load(a, g0, m0, n0, fused);
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int c0 = g0 + c * RCH;
+                if (c0 >= a.r_pad)
+                    break;
+#pragma unroll
+                for (int i = 0; i < BCH; ++i) {
+                    const int ch = tid + GEMM_THREADS * i;
+                    st16(bl + (ch >> 5) * BP + 8 * (ch & 31), bva[c][i]);
+                }
+#pragma unroll
+                for (int i = 0; i < TCH; ++i) {
+                    const int ch = tid + GEMM_THREADS * i;
+                    if (ch < BM * (RCH / 8)) {
+                        const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
+                        st16(tl + rr * TP + 8 * cc, tva[c][i]);
+                    }
+                }
+                __syncthreads();
+                const int ns = min(RCH, a.r_pad - c0) >> 5;
+                for (int rs = 0; rs < ns; ++rs) {
+                    u32x4 bfr[JW];
+#pragma unroll
+                    for (int j = 0; j < JW; ++j)
+                        bfr[j] = lds_bfrag(bl, BP, 16 * (JW * w + j), 32 * rs);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const u32x4 af = *reinterpret_cast<const u32x4*>(tl + (rb * 16 + (l & 15)) * TP + 32 * rs + koff);
+#pragma unroll
+                        for (int j = 0; j < JW; ++j)
+                            acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
+                    }
+                }
+                __syncthreads();                        // before the next chunk or another use of the LDS
+            }
+        }
+    }
+};
+
 template <int ACT, int BM, bool GROUPED, int NWV, int LDSB>
 __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM / 16][16 / NWV], const float (&sf)[16 / NWV],
                                           const float (&zf)[16 / NWV], const uint32_t* const (&szsrc)[16 / NWV], int tm,
-                                          int tn, int kz, int m0, int n0, uint8_t* smem, uint32_t& s_old, uint32_t& s_ec)
+                                          int tn, int kz, int m0, int n0, uint8_t* smem, uint32_t& s_old, uint32_t& s_ec,
+                                          const float* rsl)
 {
     constexpr int GEMM_THREADS = 64 * NWV;
     constexpr int NW = NWV;
@@ -732,6 +864,18 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
     const int tid = threadIdx.x;
     const int l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool fused = BM == 64 && a.ec_q > 0;
+    // The gated rank-r correction's operands (its first 128 ranks) are
+    // loaded as early as the tile allows, so that their trip to memory
+    // overlaps the others of the tail: at once for a tile done in one piece;
+    // for a split tile, by its last workgroup together with the other
+    // splits' partial sums (128-token tiles: after those, the registers do
+    // not hold both); with the fused EC after its wait.  A chunk of ranks
+    // per trip, after everything else, cost 1-2 us per chunk.
+    GemmEc<ACT, BM, NWV, LDSB> ec;
+    if (BM == 64 && a.r > 0 && !fused && a.ksplit == 1)
+        ec.load(a, 0, m0, n0, false);
+
     // ---- split-K hand-over: the last workgroup of the tile sums the partials
     // (fragment layout [tile][split][wavefront][RB][JW][64 lanes], 16 bytes per lane)
     if (a.ksplit > 1) {
@@ -756,33 +900,58 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
             return;
         if (tid == 0)
             atomic_store_dev(&a.cnt[tile], 0u);
-        // splits added in order; all fragments of one split are in flight at once
+        if (BM == 64 && a.r > 0 && !fused)
+            ec.load(a, 0, m0, n0, false);
+        // splits added in order (from zero, as a plain sum would); the other
+        // splits' fragments are loaded SB splits at a time, all in flight at
+        // once (o-th other split: o, or o + 1 past this workgroup's own)
+        constexpr int SB = BM == 64 ? 3 : 1;
         floatx4 sum[RB][JW];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int j = 0; j < JW; ++j)
                 sum[rb][j] = (floatx4){0.f, 0.f, 0.f, 0.f};
-        for (int z = 0; z < a.ksplit; ++z) {
-            if (z == kz) {
+        bool own = false;                               // this workgroup's partial added
+        for (int o0 = 0; o0 < a.ksplit - 1; o0 += SB) {
+            floatx4 t[SB][RB][JW];
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+            for (int s = 0; s < SB; ++s) {
+                const int z = o0 + s + (o0 + s >= kz ? 1 : 0);
+                if (z < a.ksplit) {
 #pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        sum[rb][j] += acc[rb][j];
-            } else {
-                floatx4 t[RB][JW];
+                    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        t[rb][j] = ld16_sc1(prs, frag(z, rb, j));
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        sum[rb][j] += t[rb][j];
+                        for (int j = 0; j < JW; ++j)
+                            t[s][rb][j] = ld16_sc1(prs, frag(z, rb, j));
+                }
             }
+#pragma unroll
+            for (int s = 0; s < SB; ++s) {
+                const int z = o0 + s + (o0 + s >= kz ? 1 : 0);
+                if (z < a.ksplit) {
+                    if (!own && kz < z) {
+                        own = true;
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                            for (int j = 0; j < JW; ++j)
+                                sum[rb][j] += acc[rb][j];
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int j = 0; j < JW; ++j)
+                            sum[rb][j] += t[s][rb][j];
+                }
+            }
+        }
+        if (!own) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < JW; ++j)
+                    sum[rb][j] += acc[rb][j];
         }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -790,33 +959,40 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
             for (int j = 0; j < JW; ++j)
                 acc[rb][j] = sum[rb][j];
     }
+    if (BM != 64 && a.r > 0 && !fused)
+        ec.load(a, 0, m0, n0, false);
 
     // ---- fused EC: wait (bounded) until every unit of this tile row is done;
     // a wait that gave up stores NaN
     bool eclost = false;
-    if (BM == 64 && a.ec_q > 0) {
+    if (fused) {
         const int ucb = ec_a_blocks(a.r) > 0 ? ec_a_blocks(a.r) : 1;
         if (tid == 0)
             s_ec = ec_wait_ge(a, a.eccnt + 2 * a.mt + tm, (uint32_t)(RB * ucb)) ? 1u : 0u;
         __syncthreads();
         eclost = s_ec != 0;
+        if (a.r > 0)
+            ec.load(a, 0, m0, n0, true);
     }
 
-    // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r correction
-    // (with the fused EC, T_g and the activation sums are read past this
-    // XCD's L2: they were written during this kernel)
+    // ---- epilogue: per-channel zero point (bf16) and scale, gated rank-r
+    // correction.  The activation sums come from the LDS copy made at the
+    // tile's start (rsl), or with the fused EC from memory, read past this
+    // XCD's L2 (they were written during this kernel).
     if constexpr (BIAS) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float* ps = a.rowsum + m0 + rb * 16 + 4 * (l >> 4) + v;
-                const float sx = BM == 64 && a.ec_q > 0 ? ld_dev_f32(ps) : *ps;
+                const int row = rb * 16 + 4 * (l >> 4) + v;
+                const float sx = rsl ? rsl[row] : fused ? ld_dev_f32(a.rowsum + m0 + row) : a.rowsum[m0 + row];
 #pragma unroll
                 for (int j = 0; j < JW; ++j)
                     acc[rb][j][v] -= (128.0f + zf[j]) * sx;
             }
         }
+        if (rsl)
+            __syncthreads();                            // the LDS is reused below
     }
     if constexpr (ACT == ACT_F16 && !GROUPED) {
         // a fractional zero point among the tile's columns (the other forms
@@ -885,97 +1061,8 @@ __device__ __forceinline__ void gemm_tail(const GemmKArgs& a, floatx4 (&acc)[BM 
             for (int j = 0; j < JW; ++j)
                 acc[rb][j] *= sf[j];
     }
-    if (a.r > 0) {
-        // The rank dimension in chunks of RCH: B rows [c0, c0 + RCH) of the
-        // tile's 256 columns and the same ranks of T_g for the tile's BM
-        // tokens are loaded with every load of the chunk in flight, parked in
-        // LDS, and read back as MFMA operands (B through the transpose read;
-        // its rows are padded to 272 halves so that the read is free of bank
-        // conflicts).  The last main-loop barrier freed the LDS.
-        constexpr int BP = PF_BN + 16;                  // halves per LDS row of B
-        // 64 ranks per chunk where they fit (and BM = 128), else 32
-        constexpr int RCH = BM == 128 && 64 * BP * 2 + BM * 72 * 2 <= LDSB ? 64 : 32;
-        constexpr int TP = RCH + 8;                     // halves per LDS row of T_g
-        constexpr int BCH = RCH * (PF_BN / 8) / GEMM_THREADS;             // 16-byte B chunks per thread
-        constexpr int TCH = (BM * (RCH / 8) + GEMM_THREADS - 1) / GEMM_THREADS;
-        static_assert(RCH * BP * 2 + BM * TP * 2 <= LDSB, "EC staging fits the LDS");
-        uint16_t* bl = reinterpret_cast<uint16_t*>(smem);
-        uint16_t* tl = bl + RCH * BP;
-        const bool bvec = ((uintptr_t)a.B & 15) == 0 && (a.N & 7) == 0;
-        const int koff = 8 * (l >> 4);
-        const __amdgpu_buffer_rsrc_t tgs = dev_rsrc(a.tg, (uint32_t)((size_t)a.Mpad * a.r_pad * 2));
-        for (int c0 = 0; c0 < a.r_pad; c0 += RCH) {
-            u32x4 bv[BCH], tv[TCH];
-#pragma unroll
-            for (int i = 0; i < BCH; ++i) {
-                const int ch = tid + GEMM_THREADS * i;
-                const int jr = c0 + (ch >> 5), n = n0 + 8 * (ch & 31);
-                u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-                if (jr < a.r) {
-                    const uint16_t* src = a.B + (size_t)jr * a.N + n;
-                    if (bvec && n + 8 <= a.N) {
-                        v = ld16(src);
-                    } else {
-                        uint32_t hv[8];
-#pragma unroll
-                        for (int t = 0; t < 8; ++t)
-                            hv[t] = n + t < a.N ? (uint32_t)src[t] : 0u;
-                        v = (u32x4){hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16),
-                                    hv[6] | (hv[7] << 16)};
-                    }
-                }
-                bv[i] = v;
-            }
-            // (ranks past r_pad -- a last chunk wider than the rest -- are not
-            // loaded and not used)
-            if (BM == 64 && a.ec_q > 0) {
-#pragma unroll
-                for (int i = 0; i < TCH; ++i) {
-                    const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
-                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
-                    tv[i] = c0 + 8 * cc < a.r_pad ? __builtin_bit_cast(u32x4, ld16_sc1(tgs, (uint32_t)(((size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc) * 2)))
-                                                  : (u32x4){0u, 0u, 0u, 0u};
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < TCH; ++i) {
-                    const int ch = min(tid + GEMM_THREADS * i, BM * (RCH / 8) - 1);
-                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
-                    tv[i] = c0 + 8 * cc < a.r_pad ? ld16(a.tg + (size_t)(m0 + rr) * a.r_pad + c0 + 8 * cc)
-                                                  : (u32x4){0u, 0u, 0u, 0u};
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < BCH; ++i) {
-                const int ch = tid + GEMM_THREADS * i;
-                st16(bl + (ch >> 5) * BP + 8 * (ch & 31), bv[i]);
-            }
-#pragma unroll
-            for (int i = 0; i < TCH; ++i) {
-                const int ch = tid + GEMM_THREADS * i;
-                if (ch < BM * (RCH / 8)) {
-                    const int rr = ch / (RCH / 8), cc = ch - rr * (RCH / 8);
-                    st16(tl + rr * TP + 8 * cc, tv[i]);
-                }
-            }
-            __syncthreads();
-            const int ns = min(RCH, a.r_pad - c0) >> 5;
-            for (int rs = 0; rs < ns; ++rs) {
-                u32x4 bfr[JW];
-#pragma unroll
-                for (int j = 0; j < JW; ++j)
-                    bfr[j] = lds_bfrag(bl, BP, 16 * (JW * w + j), 32 * rs);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    const u32x4 af = *reinterpret_cast<const u32x4*>(tl + (rb * 16 + (l & 15)) * TP + 32 * rs + koff);
-#pragma unroll
-                    for (int j = 0; j < JW; ++j)
-                        acc[rb][j] = mfma16x16x32<ACT>(af, bfr[j], acc[rb][j]);
-                }
-            }
-            __syncthreads();                            // before the next chunk or the output tile reuses the LDS
-        }
-    }
+    if (a.r > 0)
+        ec.apply(a, acc, m0, n0, smem, fused);
 
     // ---- store: round to the activation format into an LDS tile, then
     // write whole rows of the tile with 16-byte stores (in passes of RBP
@@ -1037,7 +1124,9 @@ void prefill_gemm_kernel(GemmKArgs a)
     // registers allow.
     constexpr int XS = BM == 64 ? 4 : 2;
     static_assert(D % XS == 0, "activation sets must divide the ring");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[BM == 64 ? gemm_smem_bytes_of(BM) : gemm_lds_bytes<BM>()];
+    constexpr int LDSB = BM == 64 ? gemm_smem_bytes_of(BM) : gemm_lds_bytes<BM>();
+    static_assert(2 * BM * XROW_BYTES + BM * 4 <= LDSB, "the activation sums fit beside the X buffers");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[LDSB];
     __shared__ uint32_t s_old, s_ec;
 
     const int tid = threadIdx.x;
@@ -1189,6 +1278,18 @@ void prefill_gemm_kernel(GemmKArgs a)
         issue_w(u, u);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // bf16 with one zero point per column: the tokens' activation sums,
+    // copied to the end of the LDS (past the X buffers) for the epilogue,
+    // which then makes no trip to memory for them
+    const bool fused = FUSED && a.ec_q > 0;
+    float* rsl = nullptr;
+    if constexpr (BIAS) {
+        if (!fused) {
+            rsl = reinterpret_cast<float*>(smem + LDSB - BM * 4);
+            if (tid < BM)
+                rsl[tid] = a.rowsum[m0 + tid];
+        }
+    }
     store_x(0, 0);
     __syncthreads();
 
@@ -1300,7 +1401,7 @@ void prefill_gemm_kernel(GemmKArgs a)
 
     if (FUSED && a.ec_q > 0)
         ec_reduce_units<ACT, BM>(a, tm, m0, smem, s_ec);
-    gemm_tail<ACT, BM, GROUPED, 8, gemm_lds_bytes<BM>()>(a, acc, sf, zf, szsrc, tm, tn, kz, m0, n0, smem, s_old, s_ec);
+    gemm_tail<ACT, BM, GROUPED, 8, LDSB>(a, acc, sf, zf, szsrc, tm, tn, kz, m0, n0, smem, s_old, s_ec, rsl);
     // fused EC: the last workgroup of the tile row to be done with the
     // counters returns them to zero
     if (FUSED && a.ec_q > 0 && tid == 0) {
