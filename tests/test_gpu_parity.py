@@ -14,7 +14,7 @@ import oracle
 import w4_gemm_error_amd as w4
 from w4_gemm_error_amd import synth
 
-from gpu_util import (assert_close, dev_act, gpu_layer, gpu_quantize, host_bits, oracle_layer,
+from gpu_util import (assert_close, dev_act, gpu_layer, gpu_quantize, host_bits, new_workspace, oracle_layer,
                       sample_rows, torch)
 
 pytestmark = pytest.mark.gpu
@@ -81,6 +81,12 @@ SMALL = [
     # many tiles, ragged in M and N
     ("prefill", "fp16", 1000, 8000, 256, 16, 256),
     ("prefill", "bf16", 1030, 8008, 384, 24, 384),
+    # 128-token tiles without a K split (one row block of tiles per 128
+    # tokens, every workgroup a whole K): r = 64; r = 48 with the ranks of
+    # r_pad past r and a ragged N; r = 96 over K = 2048
+    ("prefill", "fp16", 1000, 4096, 768, 64, 768),
+    ("prefill", "fp16", 1100, 4000, 896, 48, 896),
+    ("prefill", "fp16", 700, 8192, 2048, 96, 2048),
 ]
 
 
@@ -115,6 +121,26 @@ def test_special_cases(phase, M, r):
     assert_close(opened, oracle_layer(d, codes, b_g=math.inf, with_gate=False), "fp16", "g=1")
     nogate = gpu_layer(d, packed, phase, b_g=0.25, with_gate=False)
     assert_close(nogate, oracle_layer(d, codes, b_g=0.25, with_gate=False), "fp16", "w_g=None")
+
+
+def test_special_cases_many_tiles():
+    # M=1000, N=4096, K=768: 128-token tiles without a K split
+    _print("special cases prefill M=1000 N=4096 K=768 r=64 (128-token tiles)")
+    d = small_layer("fp16", 1000, 4096, 768, 64, 768, seed=8)
+    _, _, _, packed = gpu_quantize(d)
+    codes = oracle.rtn_quantize(d["W"], 768)
+    plain_ref = oracle_layer(d, codes, r=0)
+    closed = gpu_layer(d, packed, "prefill", b_g=-math.inf)
+    assert_close(closed, plain_ref, "fp16", "g=0")
+    opened = gpu_layer(d, packed, "prefill", b_g=math.inf, with_gate=False)
+    assert_close(opened, oracle_layer(d, codes, b_g=math.inf, with_gate=False), "fp16", "g=1")
+    # repeated calls on one workspace (each leaves the hand-over state at
+    # zero, which gpu_layer checks), bit for bit the same
+    ws = new_workspace(w4.w4ec_workspace_bytes(d["M"], d["N"], d["K"], d["r"], d["group_size"]))
+    nogate = gpu_layer(d, packed, "prefill", b_g=0.25, with_gate=False, workspace=ws)
+    assert_close(nogate, oracle_layer(d, codes, b_g=0.25, with_gate=False), "fp16", "w_g=None")
+    again = gpu_layer(d, packed, "prefill", b_g=0.25, with_gate=False, workspace=ws)
+    assert np.array_equal(again, nogate)
 
 
 @pytest.mark.parametrize("M,K,G", [(64, 512, 512), (130, 1024, 1024), (40, 768, 256)])
