@@ -102,8 +102,13 @@ static void check_prefill_plan(const LayerArgs& a, const PrefillPlan& p, bool ge
         if (p.ksplit > 1)
             CHECK(p.mt * p.nt <= 256, "split tiles %d > 256 counters", p.mt * p.nt);
     }
-    CHECK(p.pre_kc % 64 == 0 && (long)p.pre_ks * p.pre_kc >= a.K && (long)(p.pre_ks - 1) * p.pre_kc < a.K,
-          "prepass slices ks=%d kc=%d K=%d", p.pre_ks, p.pre_kc, a.K);
+    // each prepass workgroup takes pre_nch chunks of pre_kc: the slices
+    // cover K and none is empty
+    const long slice = (long)p.pre_nch * p.pre_kc;
+    CHECK(p.pre_kc % 64 == 0 && p.pre_nch >= 1 && p.pre_nch <= 4 && (long)p.pre_ks * slice >= a.K &&
+              (long)(p.pre_ks - 1) * slice < a.K,
+          "prepass slices ks=%d nch=%d kc=%d K=%d", p.pre_ks, p.pre_nch, p.pre_kc, a.K);
+    CHECK(p.pre_nch == 1 || (long)p.pre_mt * p.pre_ks <= 512 || p.pre_nch == 4, "prepass chunks beyond one round");
     CHECK(prepass_lds_bytes(a.r, p.pre_kc) <= (80u << 10), "prepass LDS");
     CHECK(p.off_pre_partial >= STATE && p.off_tg >= p.off_pre_partial && p.off_rowsum >= p.off_tg &&
           p.off_gemm_partial >= p.off_rowsum && p.bytes >= p.off_gemm_partial, "region order");

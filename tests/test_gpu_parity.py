@@ -87,6 +87,9 @@ SMALL = [
     ("prefill", "fp16", 1000, 4096, 768, 64, 768),
     ("prefill", "fp16", 1100, 4000, 896, 48, 896),
     ("prefill", "fp16", 700, 8192, 2048, 96, 2048),
+    # a prepass of more than one round of workgroups: two chunks of K per
+    # workgroup, the last one past K
+    ("prefill", "fp16", 1100, 256, 8320, 128, 8320),
 ]
 
 

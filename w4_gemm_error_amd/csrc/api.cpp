@@ -138,6 +138,13 @@ PrefillPlan make_prefill_plan(int M, int N, int K, int r)
         const int ks = (K + kcmax - 1) / kcmax;
         p.pre_kc = ((K + ks - 1) / ks + 63) / 64 * 64;
         p.pre_ks = (K + p.pre_kc - 1) / p.pre_kc;
+        // a grid of more than one round of workgroups (two per CU): each
+        // takes several chunks of K one after another, so that the grid fits
+        // one round and writes fewer partial sums (up to four chunks)
+        p.pre_nch = 1;
+        while (p.pre_nch < 4 && (long long)p.pre_mt * ((p.pre_ks + p.pre_nch - 1) / p.pre_nch) > 2 * TARGET_WGS)
+            p.pre_nch *= 2;
+        p.pre_ks = (p.pre_ks + p.pre_nch - 1) / p.pre_nch;
     }
     // tile counters exist only for split work, which is chosen only while the
     // workgroup count is below TARGET_WGS: at most 256 of them

@@ -56,12 +56,14 @@ struct PrepassKArgs {
     const uint16_t* w_g;
     uint32_t one2;      // two ones in the activation format: also sum each token's activations (else 0)
     int M, K, r, kc, ks;
+    int nch;            // chunks of kc per workgroup (its slice: nch kc, the chunks one after another)
     floatx4* partial;   // [pre_mt][ks][4 wavefronts][ec_blocks(r)][64 lanes]
 };
 
 constexpr int PRE_MAXB = 17;   // column blocks of [A | w_g] (r <= 256), gate block included
 constexpr int PRE_MAXS = 16;   // 32-k steps per workgroup (kc <= 512)
 
+// adds this chunk's products into acc (the caller zeroes it once)
 template <int ACT, int NS>
 __device__ inline void prepass_mfma(const u32x4 (&xf)[PRE_MAXS], const uint16_t* at, const uint16_t* wgl, int r,
                                     bool gate, uint32_t one2, int nb, floatx4 (&acc)[PRE_MAXB])
@@ -69,7 +71,6 @@ __device__ inline void prepass_mfma(const u32x4 (&xf)[PRE_MAXS], const uint16_t*
     const int nba = ec_a_blocks(r);
 #pragma unroll
     for (int cb = 0; cb < PRE_MAXB; ++cb) {
-        acc[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
         if (cb < nb) {
             u32x4 bf[NS];
             if (cb < nba) {
@@ -103,36 +104,47 @@ void prepass_kernel(PrepassKArgs a)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int mt = blockIdx.x;
     const int z = blockIdx.y;
-    const int kbeg = z * a.kc;
-    const int len = min(a.kc, a.K - kbeg);          // multiple of 64
     const int xrow = min(mt * 64 + 16 * w + (l & 15), a.M - 1);
     const int nb = ec_blocks(a.r);
     const bool gate = a.w_g != nullptr;
     uint16_t* at = reinterpret_cast<uint16_t*>(psmem);
-    uint16_t* wgl = at + len * ec_pitch(a.r) + 16;
 
-    const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + 8 * (l >> 4);
-    u32x4 xf[PRE_MAXS];
-#pragma unroll
-    for (int s = 0; s < PRE_MAXS; ++s)                // steps past the slice are never used
-        xf[s] = ld16(xp + 32 * min(s, (len >> 5) - 1));
-    ec_stage<PF_THREADS, true>(a.A, a.w_g, a.r, kbeg, len, at, wgl);
-    wait_all_mem();
-    __syncthreads();
-
-    // per column block (wavefront-uniform branch), all fragment reads of the
-    // slice first, then the MFMAs; the step count is a template argument, so
-    // no MFMA of the chain sits behind a branch
     floatx4 acc[PRE_MAXB];
-    switch (len >> 6) {
-    case 1: prepass_mfma<ACT, 2>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    case 2: prepass_mfma<ACT, 4>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    case 3: prepass_mfma<ACT, 6>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    case 4: prepass_mfma<ACT, 8>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    case 5: prepass_mfma<ACT, 10>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    case 6: prepass_mfma<ACT, 12>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    case 7: prepass_mfma<ACT, 14>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
-    default: prepass_mfma<ACT, 16>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+#pragma unroll
+    for (int cb = 0; cb < PRE_MAXB; ++cb)
+        acc[cb] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    // the slice's chunks one after another (one, unless the grid would
+    // otherwise take several rounds of workgroups)
+    for (int c = 0; c < a.nch; ++c) {
+        const int kbeg = (z * a.nch + c) * a.kc;
+        if (kbeg >= a.K)
+            break;                                      // uniform
+        const int len = min(a.kc, a.K - kbeg);          // multiple of 64
+        uint16_t* wgl = at + len * ec_pitch(a.r) + 16;
+        if (c > 0)
+            __syncthreads();                            // the previous chunk's LDS reads are done
+        const uint16_t* xp = a.X + (size_t)xrow * a.K + kbeg + 8 * (l >> 4);
+        u32x4 xf[PRE_MAXS];
+#pragma unroll
+        for (int s = 0; s < PRE_MAXS; ++s)            // steps past the chunk are never used
+            xf[s] = ld16(xp + 32 * min(s, (len >> 5) - 1));
+        ec_stage<PF_THREADS, true>(a.A, a.w_g, a.r, kbeg, len, at, wgl);
+        wait_all_mem();
+        __syncthreads();
+
+        // per column block (wavefront-uniform branch), all fragment reads of
+        // the chunk first, then the MFMAs; the step count is a template
+        // argument, so no MFMA of the chain sits behind a branch
+        switch (len >> 6) {
+        case 1: prepass_mfma<ACT, 2>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        case 2: prepass_mfma<ACT, 4>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        case 3: prepass_mfma<ACT, 6>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        case 4: prepass_mfma<ACT, 8>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        case 5: prepass_mfma<ACT, 10>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        case 6: prepass_mfma<ACT, 12>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        case 7: prepass_mfma<ACT, 14>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        default: prepass_mfma<ACT, 16>(xf, at, wgl, a.r, gate, a.one2, nb, acc); break;
+        }
     }
     floatx4* mine = a.partial + ((size_t)(mt * a.ks + z) * 4 + w) * nb * 64;
 #pragma unroll
@@ -1443,7 +1455,7 @@ static hipError_t launch_prefill_ec_part(const LayerArgs& a, const PrefillPlan& 
         q.w_g = (const uint16_t*)a.w_g;
         q.one2 = !sums ? 0u : 0x3F803F80u;                   // bf16 ones
         q.M = a.M; q.K = a.K; q.r = a.r;
-        q.kc = p.pre_kc; q.ks = p.pre_ks;
+        q.kc = p.pre_kc; q.ks = p.pre_ks; q.nch = p.pre_nch;
         q.partial = (floatx4*)(a.ws + p.off_pre_partial);
         const size_t lds = prepass_lds_bytes(a.r, p.pre_kc);
         auto pk = a.act == ACT_F16 ? prepass_kernel<ACT_F16> : prepass_kernel<ACT_BF16>;

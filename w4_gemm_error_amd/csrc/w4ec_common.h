@@ -485,7 +485,8 @@ struct PrefillPlan {
     int ksplit;     // GEMM split over K
     int pre_mt;     // prepass tiles of 64 tokens
     int pre_ks;     // prepass split over K
-    int pre_kc;     // k per prepass split (multiple of 64, <= 512)
+    int pre_kc;     // k per prepass chunk (multiple of 64, <= 512)
+    int pre_nch;    // chunks per prepass workgroup (its K slice: pre_nch pre_kc)
     int r_pad, Mpad;
     int ec_q;       // fused EC: pieces of [T | l] per row of tiles (0: the prepass kernels instead)
     int ec_kc;      // fused EC: k per LDS slice of [A | w_g] (multiple of 64, <= 512)
